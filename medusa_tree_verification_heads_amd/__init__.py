@@ -1,0 +1,347 @@
+"""Python binding of libmdt, the MI355X (gfx950) Medusa draft-and-verify step.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libmdt.so``.  Tensors are torch CUDA (HIP) tensors; the binding passes their
+device pointers and the current torch stream to the C ABI declared in
+``include/mdt.h``.  The functions carry the C names without the ``mdt_`` prefix:
+
+    medusa_heads, topk_tree_expand, tree_attention, verify_logits,
+    accept_path, kv_compact
+
+plus the static tree helpers (``Tree``) and workspace queries.  Importing this
+module without a built ``libmdt.so`` raises ImportError: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmdt.so")
+
+MDT_F32, MDT_BF16 = 0, 1
+GREEDY, TYPICAL = 0, 1
+KV_CONTIG, KV_PAGED = 0, 1
+MAX_NODES, MAX_HEADS, MAX_TOPK = 256, 8, 32
+
+c_int, c_i32, c_size, c_void_p, c_float, c_double = (ctypes.c_int, ctypes.c_int32, ctypes.c_size_t,
+                                                      ctypes.c_void_p, ctypes.c_float, ctypes.c_double)
+
+
+class TreeHost(ctypes.Structure):
+    _fields_ = [("T", c_i32), ("max_depth", c_i32), ("max_rank", c_i32), ("anc_words", c_i32),
+                ("parent", ctypes.POINTER(c_i32)), ("depth", ctypes.POINTER(c_i32)),
+                ("rank", ctypes.POINTER(c_i32)), ("anc", ctypes.POINTER(ctypes.c_uint64))]
+
+
+class TreeDev(ctypes.Structure):
+    _fields_ = [("T", c_i32), ("max_depth", c_i32), ("max_rank", c_i32), ("anc_words", c_i32),
+                ("parent", c_void_p), ("depth", c_void_p), ("rank", c_void_p), ("anc", c_void_p)]
+
+
+class KVCacheDesc(ctypes.Structure):
+    _fields_ = [("layout", c_i32), ("capacity", c_i32), ("page_size", c_i32), ("max_pages", c_i32),
+                ("num_pages", c_i32), ("reserved", c_i32), ("k", c_void_p), ("v", c_void_p),
+                ("page_table", c_void_p)]
+
+
+# mdt_row_stats as a numpy record (16 bytes)
+ROW_STATS_DTYPE = np.dtype([("max", np.float32), ("argmax", np.int32), ("logZ", np.float32), ("entropy", np.float32)])
+
+# (name, restype, argtypes)
+_SIGS = [
+    ("mdt_abi_version", c_int, []),
+    ("mdt_status_string", ctypes.c_char_p, [c_int]),
+    ("mdt_last_error", ctypes.c_char_p, []),
+    ("mdt_tree_build_cartesian", c_int, [c_int, ctypes.POINTER(c_int), ctypes.POINTER(TreeHost)]),
+    ("mdt_tree_build_scored", c_int, [c_int, c_int, c_int, c_double, c_double, c_double, c_int, c_int,
+                                      ctypes.POINTER(TreeHost)]),
+    ("mdt_tree_free", None, [ctypes.POINTER(TreeHost)]),
+    ("mdt_tree_image_bytes", c_size, [c_int]),
+    ("mdt_tree_pack", c_int, [ctypes.POINTER(TreeHost), c_void_p, c_size]),
+    ("mdt_tree_dev_init", c_int, [ctypes.POINTER(TreeHost), c_void_p, ctypes.POINTER(TreeDev)]),
+    ("mdt_medusa_heads_workspace", c_size, [c_int, c_int, c_int]),
+    ("mdt_medusa_heads", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_size]),
+    ("mdt_topk_workspace", c_size, [c_int, c_int, c_int, c_int]),
+    ("mdt_topk_tree_expand", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(TreeDev),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size]),
+    ("mdt_tree_attention_workspace", c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    ("mdt_tree_attention", c_int, [c_void_p, c_int, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p,
+                                   c_void_p, c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_float, c_void_p,
+                                   c_void_p, c_void_p, c_size]),
+    ("mdt_verify_logits_workspace", c_size, [c_int, c_int, c_int, c_int, c_int]),
+    ("mdt_verify_logits", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                  ctypes.POINTER(TreeDev), c_void_p, c_float, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_size]),
+    ("mdt_accept_path", c_int, [c_void_p, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p, c_void_p, c_int,
+                                c_float, c_float, c_float, c_void_p, c_int, c_void_p]),
+    ("mdt_kv_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p,
+                               c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
+]
+
+EXPORTED = [name for name, _, _ in _SIGS]
+
+
+def _mapped_hip_runtimes():
+    libs = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1] if line.strip() else ""
+            if "libamdhip64" in path:
+                libs.add(os.path.realpath(path))
+    return libs
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m medusa_tree_verification_heads_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in _SIGS:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    rts = _mapped_hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError(f"libmdt and torch bind different HIP runtimes: {sorted(rts)}")
+    return lib
+
+
+lib = _load()
+
+
+class MdtError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.mdt_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.mdt_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise MdtError(st, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MDT_BF16
+    if t.dtype == torch.float32:
+        return MDT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), max(nbytes, 16)
+
+
+# ---------------------------------------------------------------------------
+# static tree
+# ---------------------------------------------------------------------------
+
+class Tree:
+    """A static candidate tree built by libmdt (host), with its packed image."""
+
+    def __init__(self, host: TreeHost):
+        self._host = host
+        T = host.T
+        self.T = T
+        self.max_depth = host.max_depth
+        self.max_rank = host.max_rank
+        self.anc_words = host.anc_words
+        self.parent = np.ctypeslib.as_array(host.parent, shape=(T,)).copy()
+        self.depth = np.ctypeslib.as_array(host.depth, shape=(T,)).copy()
+        self.rank = np.ctypeslib.as_array(host.rank, shape=(T,)).copy()
+        self.anc = np.ctypeslib.as_array(host.anc, shape=(T * host.anc_words,)).copy().reshape(T, host.anc_words)
+        n = lib.mdt_tree_image_bytes(T)
+        self.image = np.zeros(n, dtype=np.uint8)
+        _check(lib.mdt_tree_pack(ctypes.byref(host), self.image.ctypes.data_as(c_void_p), n), "tree_pack")
+
+    def __del__(self):
+        try:
+            lib.mdt_tree_free(ctypes.byref(self._host))
+        except Exception:
+            pass
+
+    @classmethod
+    def cartesian(cls, s: Sequence[int]) -> "Tree":
+        h = TreeHost()
+        arr = (c_int * max(1, len(s)))(*s)
+        _check(lib.mdt_tree_build_cartesian(len(s), arr, ctypes.byref(h)), "tree_build_cartesian")
+        return cls(h)
+
+    @classmethod
+    def scored(cls, K: int, k_cfg: int, T: int, a0=0.6, rho=0.7, gamma=0.8, rank_base=0, depth_base=0) -> "Tree":
+        h = TreeHost()
+        _check(lib.mdt_tree_build_scored(K, k_cfg, T, a0, rho, gamma, rank_base, depth_base, ctypes.byref(h)),
+               "tree_build_scored")
+        return cls(h)
+
+    @classmethod
+    def for_workload(cls, w) -> "Tree":
+        if w.tree_kind == "cartesian":
+            return cls.cartesian(w.tree_s)
+        return cls.scored(w.K, w.k_cfg, w.T, w.a0, w.rho, w.gamma)
+
+    def to_device(self, device="cuda") -> "DeviceTree":
+        return DeviceTree(self, device)
+
+
+class DeviceTree:
+    """Device copy of a tree's packed image and the mdt_tree_dev describing it."""
+
+    def __init__(self, tree: Tree, device):
+        self.tree = tree
+        self.image = torch.from_numpy(tree.image).to(device)
+        self.desc = TreeDev()
+        _check(lib.mdt_tree_dev_init(ctypes.byref(tree._host), c_void_p(self.image.data_ptr()),
+                                     ctypes.byref(self.desc)), "tree_dev_init")
+
+    @property
+    def T(self):
+        return self.tree.T
+
+
+class KVCache:
+    """Caller-owned prefix cache: contiguous [B][capacity][H][Dh] or paged pool + page table."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                 page_size: int = 16):
+        self.k, self.v, self.page_table = k, v, page_table
+        d = KVCacheDesc()
+        if page_table is None:
+            d.layout = KV_CONTIG
+            d.capacity = k.shape[1]
+        else:
+            d.layout = KV_PAGED
+            d.page_size = page_size
+            d.max_pages = page_table.shape[1]
+            d.num_pages = k.shape[0]
+            d.capacity = d.max_pages * page_size
+            d.page_table = page_table.data_ptr()
+        d.k = k.data_ptr()
+        d.v = v.data_ptr()
+        self.desc = d
+
+
+# ---------------------------------------------------------------------------
+# the six calls
+# ---------------------------------------------------------------------------
+
+def medusa_heads_workspace(B, d, K) -> int:
+    return lib.mdt_medusa_heads_workspace(B, d, K)
+
+
+def medusa_heads(h, W1, W2, Wlm, logits=None, ws=None, stream=None):
+    """logits[b][0] = Wlm h_b; logits[b][k] = W2_k (SiLU(W1_k h_b) + h_b)."""
+    B, d = h.shape
+    K, V = W1.shape[0], Wlm.shape[0]
+    if logits is None:
+        logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=h.device)
+    ws, nb = _ws(medusa_heads_workspace(B, d, K), h.device, ws)
+    _check(lib.mdt_medusa_heads(_stream(stream), _dtype_code(h), B, d, V, K, _ptr(h), _ptr(W1), _ptr(W2), _ptr(Wlm),
+                                _ptr(logits), _ptr(ws), nb), "medusa_heads")
+    return logits
+
+
+def topk_workspace(B, K, V, k_cfg) -> int:
+    return lib.mdt_topk_workspace(B, K, V, k_cfg)
+
+
+def topk_tree_expand(logits, k_cfg: int, tree: DeviceTree, prefix_len, topk_idx=None, topk_val=None,
+                     tree_tokens=None, pos_ids=None, ws=None, stream=None):
+    B, K1, V = logits.shape
+    dev = logits.device
+    T = tree.T
+    topk_idx = torch.empty((B, K1, k_cfg), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_val = torch.empty((B, K1, k_cfg), dtype=torch.float32, device=dev) if topk_val is None else topk_val
+    tree_tokens = torch.empty((B, T), dtype=torch.int32, device=dev) if tree_tokens is None else tree_tokens
+    pos_ids = torch.empty((B, T), dtype=torch.int32, device=dev) if pos_ids is None else pos_ids
+    ws, nb = _ws(topk_workspace(B, K1 - 1, V, k_cfg), dev, ws)
+    _check(lib.mdt_topk_tree_expand(_stream(stream), B, K1 - 1, V, k_cfg, _ptr(logits), ctypes.byref(tree.desc),
+                                    _ptr(prefix_len), _ptr(topk_idx), _ptr(topk_val), _ptr(tree_tokens),
+                                    _ptr(pos_ids), _ptr(ws), nb), "topk_tree_expand")
+    return topk_idx, topk_val, tree_tokens, pos_ids
+
+
+def tree_attention_workspace(dtype_code, B, T, H, Dh, capacity) -> int:
+    return lib.mdt_tree_attention_workspace(dtype_code, B, T, H, Dh, capacity)
+
+
+def tree_attention(q, k, v, cache: KVCache, prefix_len, tree: DeviceTree, rope_theta=10000.0, out=None, k_rot=None,
+                   ws=None, stream=None):
+    B, T, H, Dh = q.shape
+    out = torch.empty_like(q) if out is None else out
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    dt = _dtype_code(q)
+    ws, nb = _ws(tree_attention_workspace(dt, B, T, H, Dh, cache.desc.capacity), q.device, ws)
+    _check(lib.mdt_tree_attention(_stream(stream), dt, B, H, Dh, ctypes.byref(tree.desc), _ptr(q), _ptr(k), _ptr(v),
+                                  ctypes.byref(cache.desc), _ptr(prefix_len), float(rope_theta), _ptr(out),
+                                  _ptr(k_rot), _ptr(ws), nb), "tree_attention")
+    return out, k_rot
+
+
+def verify_logits_workspace(dtype_code, B, T, d, V) -> int:
+    return lib.mdt_verify_logits_workspace(dtype_code, B, T, d, V)
+
+
+def verify_logits(x, Wlm, tree: DeviceTree, tree_tokens, temperature: float, stats=None, edge=None,
+                  want_logits=False, logits=None, ws=None, stream=None):
+    """x [B*T][d]; returns (stats as int32 [B*T][4] view, edge [B][T], logits or None)."""
+    M, d = x.shape
+    V = Wlm.shape[0]
+    T = tree.T
+    B = M // T
+    dev = x.device
+    stats = torch.empty((M, 4), dtype=torch.int32, device=dev) if stats is None else stats
+    edge = torch.empty((B, T), dtype=torch.float32, device=dev) if edge is None else edge
+    if want_logits and logits is None:
+        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    dt = _dtype_code(x)
+    ws, nb = _ws(verify_logits_workspace(dt, B, T, d, V), dev, ws)
+    _check(lib.mdt_verify_logits(_stream(stream), dt, B, T, d, V, _ptr(x), _ptr(Wlm), ctypes.byref(tree.desc),
+                                 _ptr(tree_tokens), float(temperature), _ptr(stats), _ptr(edge), _ptr(logits),
+                                 _ptr(ws), nb), "verify_logits")
+    return stats, edge, logits
+
+
+def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:
+    """Device mdt_row_stats buffer -> numpy record array (max, argmax, logZ, entropy)."""
+    return stats.cpu().numpy().view(ROW_STATS_DTYPE).reshape(-1)
+
+
+def accept_path(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps=0.09, delta=0.3, temperature=0.0,
+                path=None, n_acc=None, path_stride=None, stream=None):
+    B, T = tree_tokens.shape
+    dev = tree_tokens.device
+    path_stride = tree.tree.max_depth + 1 if path_stride is None else path_stride
+    path = torch.empty((B, path_stride), dtype=torch.int32, device=dev) if path is None else path
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    _check(lib.mdt_accept_path(_stream(stream), B, ctypes.byref(tree.desc), _ptr(stats), _ptr(edge),
+                               _ptr(tree_tokens), int(mode), float(eps), float(delta), float(temperature),
+                               _ptr(path), path_stride, _ptr(n_acc)), "accept_path")
+    return path, n_acc
+
+
+def kv_compact(path, n_acc, k_rot, v, cache: KVCache, prefix_len, new_prefix_len=None, stream=None):
+    B, T, H, Dh = k_rot.shape
+    new_prefix_len = torch.empty_like(prefix_len) if new_prefix_len is None else new_prefix_len
+    _check(lib.mdt_kv_compact(_stream(stream), _dtype_code(k_rot), B, T, H, Dh, _ptr(path), path.shape[1],
+                              _ptr(n_acc), _ptr(k_rot), _ptr(v), ctypes.byref(cache.desc), _ptr(prefix_len),
+                              _ptr(new_prefix_len)), "kv_compact")
+    return new_prefix_len

@@ -1,0 +1,91 @@
+// Internal helpers shared by the HIP kernels and the host layer of libmdt.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mdt.h"
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+// Record a formatted error for mdt_last_error() and return `st`.
+mdt_status mdt_fail(mdt_status st, const char* fmt, ...);
+// Map a HIP error of the last launch to MDT_ERR_HIP (with its message) or MDT_OK.
+mdt_status mdt_check_launch(const char* what);
+// Number of compute units of the current device (cached per device).
+int mdt_num_cus();
+// Validate the host-side scalars and pointers of a device tree.
+mdt_status mdt_check_tree(const mdt_tree_dev* t);
+
+#define MDT_REQUIRE(cond, st, ...)                         \
+    do {                                                   \
+        if (!(cond)) return mdt_fail((st), __VA_ARGS__);   \
+    } while (0)
+
+inline bool mdt_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// device side
+// ---------------------------------------------------------------------------
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round a float to bf16, nearest, ties to even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;  // NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// Round a double to bf16 directly (one rounding), nearest, ties to even.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    uint64_t lsb = (u >> 45) & 1ull;
+    u = (u + ((1ull << 44) - 1ull) + lsb) & ~((1ull << 45) - 1ull);
+    // the result has at most 8 significant bits: float conversion is exact
+    return f32_to_bf16((float)__longlong_as_double((long long)u));
+}
+
+// Storage-type traits: load/store one element as float.
+template <typename ST> struct Elt;
+template <> struct Elt<float> {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+    static __device__ __forceinline__ void st64(float* p, double v) { *p = (float)v; }
+};
+template <> struct Elt<bf16_t> {
+    static __device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+    static __device__ __forceinline__ void st64(bf16_t* p, double v) { *p = f64_to_bf16(v); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// (value desc, index asc) total order used by every top-k / argmax decision.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        float ov = __shfl_xor(v, off, 64);
+        int oi = __shfl_xor(i, off, 64);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}

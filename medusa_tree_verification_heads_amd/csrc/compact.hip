@@ -1,0 +1,93 @@
+// mdt_kv_compact: append the accepted path's keys/values after the prefix.
+//
+// "MEDUSA 精读", section 3 (after selecting the accepted path, the KV cache keeps
+// only that path) and section 6 (implementation checklist: compact the KV cache).
+// The key rows come from k_rot, already rotated at prefix_len + depth; node
+// path[j] has depth j, so slot prefix_len + j gets exactly the position it was
+// rotated for.
+//
+// Grid (B, path_stride): workgroup (b, j) copies one row of H*Dh keys and values
+// with 16-byte vector moves.  Every workgroup of a sequence first validates the
+// whole sequence (path nodes, length, destination slots, pages), so either the
+// full path is written or nothing of it.
+#include "common.h"
+
+namespace {
+
+struct Cache {
+    void* k;
+    void* v;
+    const int32_t* table;
+    int layout, capacity, page_size, max_pages, num_pages;
+};
+
+__device__ __forceinline__ long slot_row(const Cache& c, int b, int slot) {
+    if (slot < 0 || slot >= c.capacity) return -1;
+    if (c.layout == MDT_KV_CONTIG) return (long)b * c.capacity + slot;
+    const int pg = slot / c.page_size;
+    if (pg >= c.max_pages) return -1;
+    const int page = c.table[(long)b * c.max_pages + pg];
+    if (page < 0 || page >= c.num_pages) return -1;
+    return (long)page * c.page_size + slot % c.page_size;
+}
+
+__global__ __launch_bounds__(256) void compact_kernel(Cache cache, const int32_t* __restrict__ path, int path_stride,
+                                                      const int32_t* __restrict__ n_acc, const uint4* __restrict__ k_rot,
+                                                      const uint4* __restrict__ v, int T, int row_vec,
+                                                      const int32_t* __restrict__ prefix_len,
+                                                      int32_t* __restrict__ new_len) {
+    const int b = blockIdx.x, j = blockIdx.y;
+    const int n = n_acc[b];
+    const int L = prefix_len[b];
+    bool ok = n >= 1 && n <= path_stride && L >= 0;
+    for (int q = 0; q < path_stride && ok; ++q) {
+        if (q >= n) break;
+        const int node = path[(long)b * path_stride + q];
+        ok = node >= 0 && node < T && slot_row(cache, b, L + q) >= 0;
+    }
+    if (j == 0 && threadIdx.x == 0) new_len[b] = ok ? L + n : -1;
+    if (!ok || j >= n) return;
+    const int node = path[(long)b * path_stride + j];
+    const long dst = slot_row(cache, b, L + j) * row_vec;
+    const long src = ((long)b * T + node) * row_vec;
+    uint4* K = (uint4*)cache.k;
+    uint4* Vv = (uint4*)cache.v;
+    for (int e = threadIdx.x; e < row_vec; e += blockDim.x) {
+        K[dst + e] = k_rot[src + e];
+        Vv[dst + e] = v[src + e];
+    }
+}
+
+}  // namespace
+
+extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, int H, int Dh, const int32_t* path,
+                                     int path_stride, const int32_t* n_acc, const void* k_rot, const void* v,
+                                     const mdt_kv_cache* cache, const int32_t* prefix_len,
+                                     int32_t* new_prefix_len) {
+    MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    MDT_REQUIRE(B >= 1 && B <= 65535 && T >= 1 && T <= MDT_MAX_NODES && H >= 1 && Dh >= 1, MDT_ERR_SHAPE,
+                "bad shape B=%d T=%d H=%d Dh=%d", B, T, H, Dh);
+    MDT_REQUIRE(path_stride >= 1 && path_stride <= MDT_MAX_NODES, MDT_ERR_SHAPE, "path_stride out of range");
+    const size_t row_bytes = (size_t)H * Dh * (dt == MDT_BF16 ? 2 : 4);
+    MDT_REQUIRE(row_bytes % 16 == 0, MDT_ERR_SHAPE, "H*Dh*element size must be a multiple of 16 bytes");
+    MDT_REQUIRE(cache, MDT_ERR_NULL, "cache is NULL");
+    MDT_REQUIRE(path && n_acc && k_rot && v && prefix_len && new_prefix_len && cache->k && cache->v, MDT_ERR_NULL,
+                "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(k_rot) && mdt_aligned16(v) && mdt_aligned16(cache->k) && mdt_aligned16(cache->v),
+                MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (cache->layout == MDT_KV_PAGED) {
+        MDT_REQUIRE(cache->page_table, MDT_ERR_NULL, "page_table is NULL");
+        MDT_REQUIRE(cache->page_size >= 1 && cache->max_pages >= 1 && cache->num_pages >= 1 &&
+                        (long)cache->max_pages * cache->page_size == cache->capacity,
+                    MDT_ERR_SHAPE, "bad paged-cache geometry");
+    } else {
+        MDT_REQUIRE(cache->layout == MDT_KV_CONTIG, MDT_ERR_VALUE, "unknown cache layout %d", cache->layout);
+        MDT_REQUIRE(cache->capacity >= 0, MDT_ERR_SHAPE, "capacity must be >= 0");
+    }
+    Cache c{cache->k, cache->v, cache->page_table, cache->layout, cache->capacity, cache->page_size,
+            cache->max_pages, cache->num_pages};
+    const int row_vec = (int)(row_bytes / 16);
+    hipLaunchKernelGGL(compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path, path_stride,
+                       n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
+    return mdt_check_launch("kv_compact");
+}

@@ -1,0 +1,278 @@
+// mdt_medusa_heads: the K Medusa heads and the LM head on the last hidden state.
+//
+// Summary page "Medusa: Simple LLM Inference Acceleration Framework with Multiple
+// Decoding Heads", section "MEDUSA Heads": logits_k = W2_k (SiLU(W1_k h) + h); the
+// LM head gives logits_0 = W_lm h (section 3.2).
+//
+// At batch 1 every weight byte is used for one multiply-add: the call is a pure
+// HBM stream of K*d*d + (K+1)*d*V weights.  Each output row is a dot product of a
+// contiguous weight row with an activation vector held in LDS as fp32.  A wave
+// owns two rows at a time; each lane loads 16-byte chunks lane, lane+64, ... of
+// both rows, so a wave instruction reads 1 KiB of contiguous weights per row.
+//
+// Launch 1 streams W1 (-> a_k = SiLU(u) + h, fp32 in the workspace) together with
+// W_lm (-> logits_0), which only needs h; launch 2 streams W2 (-> logits_1..K).
+// Rows of all heads of a launch form one grid; a workgroup owns a contiguous row
+// block of one head.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSeg = 2 * MDT_MAX_HEADS + 1;
+constexpr int kLdsBytes = 64 * 1024;
+
+struct GemvSeg {
+    const void* W;        // [nrows][d], storage type
+    const void* x;        // activation vectors: x + b * x_bstride (elements)
+    const void* resid;    // SiLU epilogue residual (storage type): resid + b * resid_bstride + row
+    float* out;           // out + b * out_bstride + row
+    long x_bstride;
+    long resid_bstride;
+    long out_bstride;
+    int nrows;
+    int rows_per_wg;
+    int wg_begin;
+    int x_f32;            // activation stored as fp32 (else storage type)
+    int silu;             // epilogue: SiLU(u) + resid
+    int pad;
+};
+
+struct GemvLaunch {
+    GemvSeg seg[kMaxSeg];
+    int nseg;
+    int d;
+    int B;
+    int pad;
+};
+
+template <typename WT>
+__device__ __forceinline__ float load_act(const void* x, long i, bool f32) {
+    return f32 ? ((const float*)x)[i] : Elt<WT>::ld((const WT*)x + i);
+}
+
+// Multiply-add one 16-byte weight chunk with the matching activations.
+template <typename WT> struct Chunk;
+template <> struct Chunk<bf16_t> {
+    static constexpr int kElems = 8;
+    static __device__ __forceinline__ float dot(const uint4& w, const float* x) {
+        const float4 a = *(const float4*)x;
+        const float4 b = *(const float4*)(x + 4);
+        float s = __uint_as_float(w.x << 16) * a.x;
+        s = fmaf(__uint_as_float(w.x & 0xffff0000u), a.y, s);
+        s = fmaf(__uint_as_float(w.y << 16), a.z, s);
+        s = fmaf(__uint_as_float(w.y & 0xffff0000u), a.w, s);
+        s = fmaf(__uint_as_float(w.z << 16), b.x, s);
+        s = fmaf(__uint_as_float(w.z & 0xffff0000u), b.y, s);
+        s = fmaf(__uint_as_float(w.w << 16), b.z, s);
+        s = fmaf(__uint_as_float(w.w & 0xffff0000u), b.w, s);
+        return s;
+    }
+};
+template <> struct Chunk<float> {
+    static constexpr int kElems = 4;
+    static __device__ __forceinline__ float dot(const uint4& w, const float* x) {
+        const float4 a = *(const float4*)x;
+        float s = __uint_as_float(w.x) * a.x;
+        s = fmaf(__uint_as_float(w.y), a.y, s);
+        s = fmaf(__uint_as_float(w.z), a.z, s);
+        s = fmaf(__uint_as_float(w.w), a.w, s);
+        return s;
+    }
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Weights are read exactly once per call: load them non-temporally.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename WT, int NV>
+__global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
+    extern __shared__ float xs[];  // [NV][d]
+    const int wg = blockIdx.x;
+    int s = 0;
+    while (s + 1 < P.nseg && wg >= P.seg[s + 1].wg_begin) ++s;
+    const GemvSeg S = P.seg[s];
+    const int d = P.d;
+    const int b0 = blockIdx.y * NV;
+    const int nv = min(NV, P.B - b0);
+
+    for (int v = 0; v < nv; ++v)
+        for (int e = threadIdx.x; e < d; e += kThreads)
+            xs[v * d + e] = load_act<WT>(S.x, (long)(b0 + v) * S.x_bstride + e, S.x_f32 != 0);
+    __syncthreads();
+
+    constexpr int VEC = Chunk<WT>::kElems;
+    const int nchunk = d / VEC;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r0 = (wg - S.wg_begin) * S.rows_per_wg;
+    const int r1 = min(S.nrows, r0 + S.rows_per_wg);
+    const WT* W = (const WT*)S.W;
+
+    for (int r = r0 + 2 * wave; r < r1; r += 2 * (kThreads / 64)) {
+        const bool two = r + 1 < r1;
+        const uint4* w0 = (const uint4*)(W + (size_t)r * d);
+        const uint4* w1 = (const uint4*)(W + (size_t)(two ? r + 1 : r) * d);
+        float acc0[NV], acc1[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
+        int c = lane;
+        // four chunks of each row in flight per iteration
+        for (; c + 192 < nchunk; c += 256) {
+            uint4 a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = ld_stream(w0 + c + 64 * u);
+                b[u] = ld_stream(w1 + c + 64 * u);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const float* xp = xs + v * d + (c + 64 * u) * VEC;
+                    acc0[v] += Chunk<WT>::dot(a[u], xp);
+                    acc1[v] += Chunk<WT>::dot(b[u], xp);
+                }
+        }
+        for (; c < nchunk; c += 64) {
+            const uint4 a = ld_stream(w0 + c);
+            const uint4 b = ld_stream(w1 + c);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float* xp = xs + v * d + c * VEC;
+                acc0[v] += Chunk<WT>::dot(a, xp);
+                acc1[v] += Chunk<WT>::dot(b, xp);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            acc0[v] = wave_sum(acc0[v]);
+            acc1[v] = wave_sum(acc1[v]);
+        }
+        if (lane == 0) {
+            for (int v = 0; v < nv; ++v) {
+                const long b = b0 + v;
+                for (int q = 0; q < (two ? 2 : 1); ++q) {
+                    const int row = r + q;
+                    float u = q ? acc1[v] : acc0[v];
+                    if (S.silu) u = u / (1.f + expf(-u)) + Elt<WT>::ld((const WT*)S.resid + b * S.resid_bstride + row);
+                    S.out[b * S.out_bstride + row] = u;
+                }
+            }
+        }
+    }
+}
+
+// Split a launch's rows into workgroups: about `target` workgroups in total,
+// proportional to each segment's rows, each block a multiple of 8 rows.
+int plan_segments(GemvLaunch& P, int target) {
+    long total = 0;
+    for (int s = 0; s < P.nseg; ++s) total += P.seg[s].nrows;
+    int wg = 0;
+    for (int s = 0; s < P.nseg; ++s) {
+        GemvSeg& S = P.seg[s];
+        long g = (long)((double)target * S.nrows / (double)total + 0.5);
+        if (g < 1) g = 1;
+        long rpw = (S.nrows + g - 1) / g;
+        rpw = (rpw + 7) / 8 * 8;
+        S.rows_per_wg = (int)rpw;
+        S.wg_begin = wg;
+        wg += (int)((S.nrows + rpw - 1) / rpw);
+    }
+    return wg;
+}
+
+template <typename WT>
+mdt_status launch(GemvLaunch& P, hipStream_t stream) {
+    const int d = P.d;
+    int nv = 1;
+    while (nv * 2 <= 8 && nv * 2 <= P.B && (size_t)(nv * 2) * d * sizeof(float) <= (size_t)kLdsBytes) nv *= 2;
+    const int nwg = plan_segments(P, mdt_num_cus() * 8);
+    dim3 grid(nwg, (P.B + nv - 1) / nv);
+    const size_t lds = (size_t)nv * d * sizeof(float);
+    switch (nv) {
+        case 1: hipLaunchKernelGGL((heads_gemv<WT, 1>), grid, dim3(kThreads), lds, stream, P); break;
+        case 2: hipLaunchKernelGGL((heads_gemv<WT, 2>), grid, dim3(kThreads), lds, stream, P); break;
+        case 4: hipLaunchKernelGGL((heads_gemv<WT, 4>), grid, dim3(kThreads), lds, stream, P); break;
+        default: hipLaunchKernelGGL((heads_gemv<WT, 8>), grid, dim3(kThreads), lds, stream, P); break;
+    }
+    return mdt_check_launch("medusa_heads");
+}
+
+template <typename WT>
+mdt_status run(hipStream_t stream, int B, int d, int V, int K, const void* h, const void* W1, const void* W2,
+               const void* Wlm, float* logits, float* a) {
+    GemvLaunch P1{};
+    P1.d = d;
+    P1.B = B;
+    for (int k = 0; k < K; ++k) {
+        GemvSeg& S = P1.seg[P1.nseg++];
+        S.W = (const WT*)W1 + (size_t)k * d * d;
+        S.x = h;
+        S.x_bstride = d;
+        S.resid = h;
+        S.resid_bstride = d;
+        S.out = a + (size_t)k * d;
+        S.out_bstride = (long)K * d;
+        S.nrows = d;
+        S.silu = 1;
+    }
+    {
+        GemvSeg& S = P1.seg[P1.nseg++];
+        S.W = Wlm;
+        S.x = h;
+        S.x_bstride = d;
+        S.out = logits;
+        S.out_bstride = (long)(K + 1) * V;
+        S.nrows = V;
+    }
+    mdt_status st = launch<WT>(P1, stream);
+    if (st != MDT_OK) return st;
+
+    GemvLaunch P2{};
+    P2.d = d;
+    P2.B = B;
+    for (int k = 0; k < K; ++k) {
+        GemvSeg& S = P2.seg[P2.nseg++];
+        S.W = (const WT*)W2 + (size_t)k * V * d;
+        S.x = a + (size_t)k * d;
+        S.x_f32 = 1;
+        S.x_bstride = (long)K * d;
+        S.out = logits + (size_t)(k + 1) * V;
+        S.out_bstride = (long)(K + 1) * V;
+        S.nrows = V;
+    }
+    return launch<WT>(P2, stream);
+}
+
+}  // namespace
+
+extern "C" size_t mdt_medusa_heads_workspace(int B, int d, int K) {
+    if (B < 1 || d < 1 || K < 1) return 0;
+    return (size_t)B * K * d * sizeof(float);
+}
+
+extern "C" mdt_status mdt_medusa_heads(void* stream, mdt_dtype dt, int B, int d, int V, int K, const void* h,
+                                       const void* W1, const void* W2, const void* Wlm, float* logits, void* ws,
+                                       size_t ws_bytes) {
+    MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    MDT_REQUIRE(B >= 1 && B <= 1024, MDT_ERR_SHAPE, "B=%d out of range 1..1024", B);
+    MDT_REQUIRE(d >= 8 && d % 8 == 0 && d <= 16384, MDT_ERR_SHAPE, "d=%d must be a multiple of 8 in 8..16384", d);
+    MDT_REQUIRE(V >= 1, MDT_ERR_SHAPE, "V=%d must be >= 1", V);
+    MDT_REQUIRE(K >= 1 && K <= MDT_MAX_HEADS, MDT_ERR_SHAPE, "K=%d out of range 1..%d", K, MDT_MAX_HEADS);
+    MDT_REQUIRE(h && W1 && W2 && Wlm && logits, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(h) && mdt_aligned16(W1) && mdt_aligned16(W2) && mdt_aligned16(Wlm) &&
+                    mdt_aligned16(logits),
+                MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
+    MDT_REQUIRE(ws_bytes >= mdt_medusa_heads_workspace(B, d, K), MDT_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                ws_bytes, mdt_medusa_heads_workspace(B, d, K));
+    MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    if (dt == MDT_BF16) return run<bf16_t>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
+    return run<float>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
+}

@@ -1,0 +1,160 @@
+// mdt_topk_tree_expand: per-head top-k over the vocabulary and the tree's tokens/positions.
+//
+// Summary page "Medusa: Simple LLM Inference Acceleration Framework with Multiple
+// Decoding Heads", section "Tree Attention", steps 1-2 (top-s_k of every head,
+// the candidates fill the tree level by level; the root is the LM head's top
+// token) and step 4 (position id = prefix length + depth).
+//
+// Selection is a total order: larger value first, equal values by smaller index.
+// A wave selects its k best elements in k rounds; each round every lane offers
+// its best element that comes after the previous winner, and a butterfly
+// reduction picks the winner.  Stage A: every workgroup reduces a 2048-element
+// slice of one row to k candidates (four waves, then one merge wave).  Stage B:
+// one workgroup per sequence, one wave per head row merges the slices' candidates
+// and then all threads fill the tree tokens and positions.
+#include <climits>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kSlice = 2048;          // elements per stage-A workgroup
+constexpr int kPerLaneA = kSlice / 256;
+constexpr int kMaxPerLaneB = 8;       // stage-B candidates per lane
+
+struct Cand {
+    float v;
+    int i;
+};
+
+// k rounds of wave-wide selection over E elements per lane; winners go to out[0..k).
+template <int E>
+__device__ void wave_select(const float (&v)[E], const int (&idx)[E], int k, Cand* out) {
+    float lv = INFINITY;
+    int li = -1;
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool after = better(lv, li, v[e], idx[e]);
+            if (after && better(v[e], idx[e], bv, bi)) {
+                bv = v[e];
+                bi = idx[e];
+            }
+        }
+        wave_argmax(bv, bi);
+        if ((threadIdx.x & 63) == 0) out[r] = Cand{bv, bi};
+        lv = bv;
+        li = bi;
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_slices(const float* __restrict__ logits, int V, int k, int nslice,
+                                                   Cand* __restrict__ cand) {
+    __shared__ Cand wave_best[4 * MDT_MAX_TOPK];
+    const int row = blockIdx.y;
+    const int slice = blockIdx.x;
+    const float* x = logits + (size_t)row * V;
+    const int base = slice * kSlice;
+    float v[kPerLaneA];
+    int idx[kPerLaneA];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < kPerLaneA; ++j) {
+        // wave w owns elements base + w*512 + [0, 512): coalesced 256-byte rows
+        const int e = base + wave * (kSlice / 4) + j * 64 + lane;
+        v[j] = e < V ? x[e] : -INFINITY;
+        idx[j] = e < V ? e : INT_MAX;
+    }
+    wave_select<kPerLaneA>(v, idx, k, wave_best + wave * k);
+    __syncthreads();
+    if (wave == 0) {
+        float mv[2];
+        int mi[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = lane + 64 * j;
+            mv[j] = c < 4 * k ? wave_best[c].v : -INFINITY;
+            mi[j] = c < 4 * k ? wave_best[c].i : INT_MAX;
+        }
+        wave_select<2>(mv, mi, k, cand + ((size_t)row * nslice + slice) * k);
+    }
+}
+
+__global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, int nslice,
+                                  const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
+                                  const int32_t* __restrict__ rank, int T, const int32_t* __restrict__ prefix_len,
+                                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_val,
+                                  int32_t* __restrict__ tokens, int32_t* __restrict__ pos) {
+    __shared__ Cand best[(MDT_MAX_HEADS + 1) * MDT_MAX_TOPK];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    {  // the block has exactly K1 waves: wave w merges head row w
+        const int row = b * K1 + wave;
+        const Cand* c = cand + (size_t)row * nslice * k;
+        const int n = nslice * k;
+        float v[kMaxPerLaneB];
+        int idx[kMaxPerLaneB];
+#pragma unroll
+        for (int j = 0; j < kMaxPerLaneB; ++j) {
+            const int e = lane + 64 * j;
+            v[j] = e < n ? c[e].v : -INFINITY;
+            idx[j] = e < n ? c[e].i : INT_MAX;
+        }
+        wave_select<kMaxPerLaneB>(v, idx, k, best + wave * k);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < K1 * k; e += blockDim.x) {
+        topk_idx[(size_t)b * K1 * k + e] = best[e].i;
+        topk_val[(size_t)b * K1 * k + e] = best[e].v;
+    }
+    const int L = prefix_len[b];
+    for (int i = threadIdx.x; i < T; i += blockDim.x) {
+        const int dep = depth[i], rk = rank[i];
+        const bool ok = dep >= 0 && dep < K1 && rk >= 0 && rk < k && (i == 0 ? dep == 0 : parent[i] < i);
+        tokens[(size_t)b * T + i] = ok ? best[dep * k + rk].i : -1;
+        pos[(size_t)b * T + i] = L + dep;
+    }
+}
+
+int num_slices(int V) { return (V + kSlice - 1) / kSlice; }
+
+}  // namespace
+
+extern "C" size_t mdt_topk_workspace(int B, int K, int V, int k_cfg) {
+    if (B < 1 || K < 0 || V < 1 || k_cfg < 1) return 0;
+    return (size_t)B * (K + 1) * num_slices(V) * k_cfg * sizeof(Cand);
+}
+
+extern "C" mdt_status mdt_topk_tree_expand(void* stream, int B, int K, int V, int k_cfg, const float* logits,
+                                           const mdt_tree_dev* tree, const int32_t* prefix_len, int32_t* topk_idx,
+                                           float* topk_val, int32_t* tree_tokens, int32_t* pos_ids, void* ws,
+                                           size_t ws_bytes) {
+    MDT_REQUIRE(B >= 1 && B <= 65535, MDT_ERR_SHAPE, "B=%d out of range", B);
+    MDT_REQUIRE(K >= 1 && K <= MDT_MAX_HEADS, MDT_ERR_SHAPE, "K=%d out of range 1..%d", K, MDT_MAX_HEADS);
+    MDT_REQUIRE(k_cfg >= 1 && k_cfg <= MDT_MAX_TOPK && k_cfg <= V, MDT_ERR_SHAPE, "k_cfg=%d out of range 1..%d",
+                k_cfg, MDT_MAX_TOPK);
+    MDT_REQUIRE(V >= 1, MDT_ERR_SHAPE, "V=%d out of range", V);
+    MDT_REQUIRE((long)num_slices(V) * k_cfg <= 64L * kMaxPerLaneB, MDT_ERR_UNSUPPORTED,
+                "V=%d with k=%d exceeds the merge capacity", V, k_cfg);
+    mdt_status st = mdt_check_tree(tree);
+    if (st != MDT_OK) return st;
+    MDT_REQUIRE(tree->max_depth <= K, MDT_ERR_TREE, "tree depth %d exceeds K=%d", tree->max_depth, K);
+    MDT_REQUIRE(tree->max_rank < k_cfg, MDT_ERR_TREE, "tree rank %d needs top-k > k_cfg=%d", tree->max_rank, k_cfg);
+    MDT_REQUIRE(logits && prefix_len && topk_idx && topk_val && tree_tokens && pos_ids, MDT_ERR_NULL,
+                "a tensor pointer is NULL");
+    MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
+    MDT_REQUIRE(ws_bytes >= mdt_topk_workspace(B, K, V, k_cfg), MDT_ERR_WORKSPACE, "workspace too small");
+    MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int K1 = K + 1;
+    const int ns = num_slices(V);
+    Cand* cand = (Cand*)ws;
+    hipLaunchKernelGGL(topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);
+    st = mdt_check_launch("topk_slices");
+    if (st != MDT_OK) return st;
+    hipLaunchKernelGGL(topk_merge_expand, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns, tree->parent,
+                       tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
+    return mdt_check_launch("topk_merge_expand");
+}

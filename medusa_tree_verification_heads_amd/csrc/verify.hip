@@ -1,0 +1,297 @@
+// mdt_verify_logits: LM head on every tree node, with per-row statistics and edge logits.
+//
+// Summary page "Medusa: Simple LLM Inference Acceleration Framework with Multiple
+// Decoding Heads", section "Tree Attention", steps 5-6 (one pass gives logits
+// for every candidate, conditioned on its branch) and section "Typical
+// Acceptance Scheme" (the verifier's probability of the candidate and the
+// entropy in nats of its distribution); "Notes on Medusa", section 3 (the node
+// outputs go through the LM head).
+//
+// The rows of x (B*T nodes) share every weight row, so this is a real dense
+// contraction: bf16 MFMA 16x16x32 with fp32 accumulation.  A workgroup owns 64
+// vocabulary columns and 64 node rows; each wave owns 16 columns and streams
+// their weight rows straight from HBM into the B operand, while the 64 x rows are
+// staged in LDS 256 dims at a time and shared by the four waves.  The epilogue
+// keeps the logits tile in LDS and reduces it to per-row partial statistics over
+// the 64 columns -- max, argmax, s = sum exp((z-m)/tau), u = sum exp((z-m)/tau) (z-m)/tau --
+// and picks the edge logits whose token falls in the tile.  A second kernel
+// merges the partials of a row in column-block order:
+//   logZ = M/tau + ln S,  H = ln S - U/S.
+#include <climits>
+#include <math.h>
+
+#include "common.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNB = 64;          // vocabulary columns per workgroup
+constexpr int kMB = 64;          // node rows per workgroup (bf16 path)
+constexpr int kKC = 256;         // dims per staged x chunk
+constexpr int kXStride = kKC + 8;
+constexpr int kZStride = kNB + 1;
+
+struct Part {
+    float m;
+    int a;
+    float s;
+    float u;
+};
+
+__device__ __forceinline__ Part part_merge(Part p, Part q, float tau) {
+    if (q.m == -INFINITY) return p;
+    if (p.m == -INFINITY) return q;
+    Part r;
+    r.m = fmaxf(p.m, q.m);
+    r.a = better(p.m, p.a, q.m, q.a) ? p.a : q.a;
+    if (tau > 0.f) {
+        const float dp = (p.m - r.m) / tau, dq = (q.m - r.m) / tau;
+        const float fp = expf(dp), fq = expf(dq);
+        r.s = fp * p.s + fq * q.s;
+        r.u = fp * (p.u + p.s * dp) + fq * (q.u + q.s * dq);
+    } else {
+        r.s = r.u = 0.f;
+    }
+    return r;
+}
+
+__device__ __forceinline__ Part shfl_xor_part(Part p, int off) {
+    Part q;
+    q.m = __shfl_xor(p.m, off, 64);
+    q.a = __shfl_xor(p.a, off, 64);
+    q.s = __shfl_xor(p.s, off, 64);
+    q.u = __shfl_xor(p.u, off, 64);
+    return q;
+}
+
+// Reduce a logits tile zt[MT][kZStride] (rows m0.., cols n0..) to per-row partials,
+// write optional full logits and the edge logits that fall inside the tile.
+template <int MT>
+__device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, float tau, int nblk_n,
+                              Part* __restrict__ part, float* __restrict__ logits_opt,
+                              const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens, int T,
+                              float* __restrict__ edge) {
+    constexpr int TPR = 256 / MT;       // threads per row
+    constexpr int CPT = kNB / TPR;      // columns per thread
+    const int t = threadIdx.x;
+    const int r = t / TPR, q = t % TPR;
+    const int row = m0 + r;
+    const int ncol = min(kNB, V - n0);
+    Part p{-INFINITY, INT_MAX, 0.f, 0.f};
+    const float* z = zt + r * kZStride;
+    for (int c = q * CPT; c < q * CPT + CPT; ++c) {
+        if (c >= ncol) break;
+        if (better(z[c], n0 + c, p.m, p.a)) {
+            p.m = z[c];
+            p.a = n0 + c;
+        }
+    }
+    if (tau > 0.f && p.m != -INFINITY) {
+        for (int c = q * CPT; c < q * CPT + CPT; ++c) {
+            if (c >= ncol) break;
+            const float dz = (z[c] - p.m) / tau;
+            const float e = __expf(dz);
+            p.s += e;
+            p.u += e * dz;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
+    if (q == 0 && row < M) part[(long)row * nblk_n + blockIdx.x] = p;
+    if (logits_opt && row < M)
+        for (int c = q * CPT; c < q * CPT + CPT && c < ncol; ++c) logits_opt[(long)row * V + n0 + c] = z[c];
+    // edges: node c of sequence b reads row b*T + parent(c) at column token(b, c)
+    const int first_b = m0 / T, last_b = min(M - 1, m0 + MT - 1) / T;
+    for (int idx = first_b * T + t; idx <= last_b * T + T - 1; idx += 256) {
+        const int b = idx / T, c = idx % T;
+        if (c == 0) continue;
+        const int pr = parent[c];
+        if (pr < 0 || pr >= T) continue;
+        const int rr = b * T + pr;
+        const int tok = tokens[idx];
+        if (rr >= m0 && rr < m0 + MT && rr < M && tok >= n0 && tok < n0 + ncol) edge[idx] = zt[(rr - m0) * kZStride + tok - n0];
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+
+// grid (ceil(V/64), ceil(M/64)), block 256
+__global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
+                                                   int d, int V, float tau, int nblk_n, Part* __restrict__ part,
+                                                   float* __restrict__ logits_opt, const int32_t* __restrict__ parent,
+                                                   const int32_t* __restrict__ tokens, int T,
+                                                   float* __restrict__ edge) {
+    __shared__ __attribute__((aligned(16))) char smem[kMB * kXStride * sizeof(bf16_t)];
+    bf16_t* xs = (bf16_t*)smem;
+    const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int col = n0 + wave * 16 + c16;
+    const bool col_ok = col < V;
+    const bf16_t* wrow = W + (size_t)(col_ok ? col : 0) * d;
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < d; k0 += kKC) {
+        const int kc = min(kKC, d - k0);  // multiple of 32
+        const int nsteps = kc / 32;
+        // weight fragments of this chunk: dims k0 + 32s + 8g .. +8 of column `col`
+        u32x4 wf[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            wf[s] = (col_ok && s < nsteps) ? ld_stream(wrow + k0 + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+        __syncthreads();
+        for (int c = threadIdx.x; c < kMB * (kKC / 8); c += 256) {
+            const int r = c / (kKC / 8), cc = c % (kKC / 8);
+            u32x4 val = {0, 0, 0, 0};
+            if (m0 + r < M && 8 * cc < kc) val = *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + 8 * cc);
+            *(u32x4*)(xs + r * kXStride + 8 * cc) = val;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s < nsteps) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kXStride + 32 * s + 8 * g);
+                    acc[mt] = mfma16(a, wf[s], acc[mt]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float* zt = (float*)smem;  // [64][kZStride]
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZStride + wave * 16 + c16] = acc[mt][e];
+    __syncthreads();
+    tile_epilogue<kMB>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge);
+}
+
+// fp32 path: grid (ceil(V/64), ceil(M/16)), block 256; x rows staged in LDS as fp32.
+__global__ __launch_bounds__(256) void verify_f32(const float* __restrict__ x, const float* __restrict__ W, int M,
+                                                  int d, int V, float tau, int nblk_n, Part* __restrict__ part,
+                                                  float* __restrict__ logits_opt, const int32_t* __restrict__ parent,
+                                                  const int32_t* __restrict__ tokens, int T,
+                                                  float* __restrict__ edge) {
+    extern __shared__ float xsf[];  // [16][d], then reused as zt[16][kZStride]
+    const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * 16;
+    for (int e = threadIdx.x; e < 16 * d; e += 256) {
+        const int r = e / d, k = e % d;
+        xsf[e] = (m0 + r < M) ? x[(size_t)(m0 + r) * d + k] : 0.f;
+    }
+    __syncthreads();
+    const int cl = threadIdx.x % kNB, rg = threadIdx.x / kNB;  // 4 row groups of 4 rows
+    const int col = n0 + cl;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (col < V) {
+        const float* w = W + (size_t)col * d;
+        for (int k = 0; k < d; ++k) {
+            const float wv = w[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(xsf[(rg * 4 + j) * d + k], wv, acc[j]);
+        }
+    }
+    __syncthreads();
+    float* zt = xsf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zt[(rg * 4 + j) * kZStride + cl] = acc[j];
+    __syncthreads();
+    tile_epilogue<16>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge);
+}
+
+// Merge row partials in block order; grid (M), block 64.  Also writes the edge
+// entries that no tile owns (root, out-of-range tokens).
+__global__ __launch_bounds__(64) void verify_merge(const Part* __restrict__ part, int nblk_n, int V, float tau,
+                                                   mdt_row_stats* __restrict__ stats, const int32_t* __restrict__ tokens,
+                                                   const int32_t* __restrict__ parent, int T, float* __restrict__ edge) {
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x;
+    Part p{-INFINITY, INT_MAX, 0.f, 0.f};
+    for (int j = lane; j < nblk_n; j += 64) p = part_merge(p, part[(long)row * nblk_n + j], tau);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
+    if (lane == 0) {
+        mdt_row_stats st;
+        st.max = p.m;
+        st.argmax = p.a;
+        if (tau > 0.f) {
+            const float lnS = logf(p.s);
+            st.logZ = p.m / tau + lnS;
+            st.entropy = lnS - p.u / p.s;
+        } else {
+            st.logZ = 0.f;
+            st.entropy = 0.f;
+        }
+        stats[row] = st;
+        const int c = row % T;
+        const int tok = tokens[row];
+        const int pr = parent[c];
+        if (c == 0)
+            edge[row] = 0.f;
+        else if (tok < 0 || tok >= V || pr < 0 || pr >= T)
+            edge[row] = -INFINITY;
+    }
+}
+
+}  // namespace
+
+extern "C" size_t mdt_verify_logits_workspace(mdt_dtype dt, int B, int T, int d, int V) {
+    (void)dt;
+    (void)d;
+    if (B < 1 || T < 1 || V < 1) return 0;
+    return (size_t)B * T * ((V + kNB - 1) / kNB) * sizeof(Part);
+}
+
+extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T, int d, int V, const void* x,
+                                        const void* Wlm, const mdt_tree_dev* tree, const int32_t* tree_tokens,
+                                        float temperature, mdt_row_stats* stats, float* edge_logit,
+                                        float* logits_opt, void* ws, size_t ws_bytes) {
+    MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    mdt_status st = mdt_check_tree(tree);
+    if (st != MDT_OK) return st;
+    MDT_REQUIRE(T == tree->T, MDT_ERR_SHAPE, "T=%d differs from the tree's %d nodes", T, tree->T);
+    MDT_REQUIRE(B >= 1 && (long)B * T <= 65535L * kMB, MDT_ERR_SHAPE, "B=%d out of range", B);
+    MDT_REQUIRE(V >= 1 && V <= 64 * 65535, MDT_ERR_SHAPE, "V=%d out of range", V);
+    if (dt == MDT_BF16)
+        MDT_REQUIRE(d >= 32 && d % 32 == 0, MDT_ERR_SHAPE, "bf16 verify needs d a multiple of 32 (got %d)", d);
+    else
+        MDT_REQUIRE(d >= 1 && d <= 1024, MDT_ERR_UNSUPPORTED, "fp32 verify supports d <= 1024 (got %d)", d);
+    MDT_REQUIRE(temperature >= 0.f && temperature == temperature, MDT_ERR_VALUE, "temperature must be >= 0");
+    MDT_REQUIRE(x && Wlm && tree_tokens && stats && edge_logit, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(Wlm) && (!logits_opt || mdt_aligned16(logits_opt)), MDT_ERR_ALIGN,
+                "tensor pointers must be 16-byte aligned");
+    MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
+    MDT_REQUIRE(ws_bytes >= mdt_verify_logits_workspace(dt, B, T, d, V), MDT_ERR_WORKSPACE, "workspace too small");
+    MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int M = B * T;
+    const int nblk_n = (V + kNB - 1) / kNB;
+    Part* part = (Part*)ws;
+    if (dt == MDT_BF16) {
+        hipLaunchKernelGGL(verify_mfma, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s, (const bf16_t*)x,
+                           (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
+                           tree_tokens, T, edge_logit);
+    } else {
+        const size_t lds = (size_t)16 * (d > kZStride ? d : kZStride) * sizeof(float);
+        hipLaunchKernelGGL(verify_f32, dim3(nblk_n, (M + 15) / 16), dim3(256), lds, s, (const float*)x,
+                           (const float*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
+                           tree_tokens, T, edge_logit);
+    }
+    st = mdt_check_launch("verify_logits gemm");
+    if (st != MDT_OK) return st;
+    hipLaunchKernelGGL(verify_merge, dim3(M), dim3(64), 0, s, part, nblk_n, V, temperature, stats, tree_tokens,
+                       tree->parent, T, edge_logit);
+    return mdt_check_launch("verify_logits merge");
+}

@@ -8,3 +8,14 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def _ensure_built():
+    """Tests load the in-tree libmdt.so; build it once if nothing is built yet."""
+    lib = os.path.join(ROOT, "medusa_tree_verification_heads_amd", "libmdt.so")
+    if not os.path.exists(lib):
+        from medusa_tree_verification_heads_amd import build as _b
+        _b.build(verbose=False)
+
+
+_ensure_built()
