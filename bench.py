@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the Medusa draft-and-verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 7b-T64-L1024] [--mode typical]
+
+A step is one pass of the whole path -- medusa_heads, topk_tree_expand,
+tree_attention, verify_logits, accept_path, kv_compact -- over one batch of
+synthetic inputs already resident in HBM.  W untimed warm-up steps run first;
+then exactly K steps are timed between two torch.cuda.synchronize() calls.  A
+timing event is recorded after every kernel on its launch stream, which gives
+each kernel's duration inside the timed region.  The roofline object describes
+the dominant kernel (the W2 head GEMV stream).  The CPU oracle is timed on the
+host on one full step of the same workload.  One JSON line goes to stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+METRIC = "Medusa verify-steps/s + achieved HBM GB/s vs peak, 7B-shape 64-node tree"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, T, lens):
+    """Bytes the step must move (each weight once per use, prefix KV once, tree tensors once)."""
+    e = w.elt_bytes
+    B, d, V, K, H, Dh = w.B, w.d, w.V, w.K, w.H, w.Dh
+    heads_w1_lm = e * (K * d * d + d * V) + B * e * d + B * 4 * (K * d + V)
+    heads_w2 = e * K * V * d + B * 4 * K * d + B * 4 * K * V
+    topk = B * 4 * (K + 1) * V
+    attn = e * 2 * int(sum(int(x) for x in lens)) * H * Dh + e * B * T * 5 * d
+    verify = e * V * d + e * B * T * d
+    compact = 2 * 2 * e * B * (K + 1) * d
+    total = heads_w1_lm + heads_w2 + topk + attn + verify + compact
+    return dict(heads_gemv_w1_lm=heads_w1_lm, heads_gemv_w2=heads_w2, topk=topk, attention=attn,
+                verify_mfma=verify, compact=compact, total=total)
+
+
+def src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "medusa_tree_verification_heads_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("src_digest") != digest:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(w, inp, mode, tau, eps, delta):
+    """The oracle as it stands, one full step on the host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import step as ostep
+    from oracle import tree as otree
+    tree = otree.build_tree(w)
+    t0 = time.perf_counter()
+    ostep.step(w, inp, tree, mode, tau, eps, delta)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": round(1.0 / dt, 6), "unit": "verify-steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 full oracle step of {w.name} (all six stages, float64 NumPy, bf16 weights upcast "
+                      f"inside the step), inputs in host memory; {dt:.1f} s; host {platform.processor() or 'cpu'}, "
+                      f"{len(os.sched_getaffinity(0))} affinity cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--mode", default="typical", choices=["typical", "greedy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU layout is a design note, not a built path", file=sys.stderr)
+        sys.exit(2)
+
+    if not os.path.exists(os.path.join(ROOT, "medusa_tree_verification_heads_amd", "libmdt.so")):
+        from medusa_tree_verification_heads_amd import build as b
+        b.build()
+    import numpy as np
+    import torch
+    import medusa_tree_verification_heads_amd as mdt
+    from medusa_tree_verification_heads_amd.step import VerifyStep
+    from workloads import make_inputs
+    from workloads.configs import HEADLINE, get_case
+
+    name = args.workload or HEADLINE
+    w = get_case(name)
+    seeds = json.load(open(os.path.join(ROOT, "workloads", "seeds.json")))
+    seed = seeds.get(name, {"seed": 0})["seed"]
+    run = next((r for r in w.accept if r.mode == args.mode), None)
+    tau = run.temperature if run else (0.7 if args.mode == "typical" else 0.0)
+    eps, delta = (run.eps, run.delta) if run else (0.09, 0.3)
+    t0 = time.perf_counter()
+    inp = make_inputs(w, seed)
+    log(f"inputs for {name} (seed {seed}) drawn in {time.perf_counter() - t0:.1f}s")
+    step = VerifyStep(w, inp, args.mode, tau, eps, delta)
+    T = step.tree.T
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    # timed region: K eager steps, one event after every kernel
+    per_step = 16   # >= kernels per step (11)
+    timer = mdt.KernelTimer(per_step * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with timer:
+        for _ in range(args.steps):
+            step.run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = timer.durations_ms()
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    per_kernel = {}
+    for kname, ms in durs:
+        per_kernel.setdefault(kname, []).append(ms)
+    per_kernel_us = {k: round(1e3 * float(np.mean(v)), 2) for k, v in per_kernel.items()}
+
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step.run()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step.run()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        log(f"graph replay: {graph_ms * 1e3:.1f} us/step")
+
+    lens = inp["prefix_len"]
+    ab = algorithmic_bytes(w, T, lens)
+    dom = "heads_gemv_w2"
+    dom_us = per_kernel_us.get(dom)
+    achieved = ab[dom] / (dom_us * 1e-6) / 1e9 if dom_us else None
+    digest = src_digest("heads.hip", "common.h")
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4) if achieved else None,
+                "traffic": measured_traffic(dom, name, digest),
+                "bytes_per_launch": ab[dom], "avg_launch_us": dom_us}
+    step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "verify-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "d": w.d, "H": w.H, "Dh": w.Dh, "V": w.V, "K": w.K,
+                   "k_cfg": w.k_cfg, "T": T, "prefix": [int(x) for x in lens][:4] if w.B > 4 else
+                   [int(x) for x in lens], "paged": w.paged, "accept": args.mode, "tau": tau, "eps": eps,
+                   "delta": delta, "seed": seed, "parallelism": "none (1 GPU)"},
+        "tree_tokens_per_s": round(1e3 / ms_per_step * w.B * T, 1),
+        "step_hbm": {"algorithmic_bytes": ab["total"], "achieved": round(step_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(step_gbps / PEAK_HBM_GBPS, 4)},
+        "per_kernel_us": per_kernel_us,
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
+        "n_acc": step.n_acc.cpu().tolist()[:8],
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one step ...")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.mode, tau, eps, delta)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,8 @@
  *    initialised and are undefined afterwards.  Two calls in flight at the same
  *    time must not share a workspace.
  *  - The library allocates no device memory and keeps no global mutable state
- *    apart from the thread-local error message and a per-device cache of the
+ *    apart from thread-local state (the error message and an optional profiling
+ *    attachment, see mdt_profile_attach) and a per-device cache of the
  *    compute-unit count, so calls are thread-safe.
  */
 #ifndef MDT_H
@@ -359,6 +360,21 @@ mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, int H, int D
 /* ------------------------------------------------------------------------- */
 
 int mdt_abi_version(void);
+
+/*
+ * Kernel timing hook (instrumentation, not part of the step).  While attached on
+ * the calling thread, every kernel the library launches is followed by
+ * hipEventRecord(events[i], stream) with i counting launches from 0; launches
+ * beyond `capacity` record nothing.  The caller creates the events (hipEvent_t,
+ * timing enabled), reads elapsed times between consecutive events after
+ * synchronising, and names launch i with mdt_profile_kernel(i).
+ * Errors: MDT_ERR_NULL (events NULL with capacity > 0), MDT_ERR_SHAPE (capacity < 0).
+ */
+mdt_status mdt_profile_attach(void** events, int capacity);
+/* Stop recording; returns the number of launches seen since attach. */
+int mdt_profile_detach(void);
+/* Name of the kernel of launch i since the last attach ("" if out of range). */
+const char* mdt_profile_kernel(int i);
 const char* mdt_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */
 const char* mdt_last_error(void);

@@ -56,6 +56,9 @@ ROW_STATS_DTYPE = np.dtype([("max", np.float32), ("argmax", np.int32), ("logZ", 
 # (name, restype, argtypes)
 _SIGS = [
     ("mdt_abi_version", c_int, []),
+    ("mdt_profile_attach", c_int, [ctypes.POINTER(c_void_p), c_int]),
+    ("mdt_profile_detach", c_int, []),
+    ("mdt_profile_kernel", ctypes.c_char_p, [c_int]),
     ("mdt_status_string", ctypes.c_char_p, [c_int]),
     ("mdt_last_error", ctypes.c_char_p, []),
     ("mdt_tree_build_cartesian", c_int, [c_int, ctypes.POINTER(c_int), ctypes.POINTER(TreeHost)]),
@@ -318,6 +321,41 @@ def verify_logits(x, Wlm, tree: DeviceTree, tree_tokens, temperature: float, sta
                                  _ptr(tree_tokens), float(temperature), _ptr(stats), _ptr(edge), _ptr(logits),
                                  _ptr(ws), nb), "verify_logits")
     return stats, edge, logits
+
+
+class KernelTimer:
+    """Records a timing event after every kernel the library launches (on the launch stream).
+
+    with KernelTimer(n) as kt:  ... library calls ...
+    then kt.durations_ms() -> list of (kernel name, ms) measured between consecutive events.
+    """
+
+    def __init__(self, capacity: int):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.events:      # materialise the underlying HIP events
+            e.record()
+        self.start = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        self._arr = (c_void_p * capacity)(*[e.cuda_event for e in self.events])
+        self.count = 0
+
+    def __enter__(self):
+        _check(lib.mdt_profile_attach(self._arr, len(self.events)), "profile_attach")
+        self.start.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.count = lib.mdt_profile_detach()
+        self.names = [lib.mdt_profile_kernel(i).decode() for i in range(min(self.count, len(self.events)))]
+        return False
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        out, prev = [], self.start
+        for name, ev in zip(self.names, self.events):
+            out.append((name, prev.elapsed_time(ev)))
+            prev = ev
+        return out
 
 
 def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:

@@ -101,5 +101,5 @@ extern "C" mdt_status mdt_accept_path(void* stream, int B, const mdt_tree_dev* t
                        tree->parent, tree->depth, tree->anc, tree->T, tree->anc_words, mode,
                        mode == MDT_ACCEPT_TYPICAL ? eps : 1.f, mode == MDT_ACCEPT_TYPICAL ? delta : 1.f, temperature,
                        path, path_stride, n_acc);
-    return mdt_check_launch("accept_path");
+    return mdt_launched((hipStream_t)stream, "accept_kernel");
 }

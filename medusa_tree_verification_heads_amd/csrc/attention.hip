@@ -7,18 +7,18 @@
 // over all nodes).  "Notes on Medusa", section 3: the tree is flattened into
 // one sequence and masked.
 //
-// bf16 path (Dh = 128), three kernels:
-//  1. rope:    rotate the tree's q and k at their depth positions; k_rot is an
-//              output (it is what gets cached), q_rot (bf16) goes to the workspace.
-//  2. prefix:  split-KV flash pass over the prefix cache.  A workgroup owns one
-//              (sequence, head, key range); its waves each own 16 tree queries.
-//              64-key K and V tiles are staged in LDS (V transposed), and both
-//              products run on MFMA 16x16x32 bf16: S^T = K Q^T, then O^T = V^T P^T,
-//              so the probabilities stay in registers between the two.  Online
-//              softmax keeps (max, sum) per query; partial (m, l, O) go to the
-//              workspace.
-//  3. combine: per (sequence, head, node) merge the partials with the node's
-//              tree keys (ancestor-or-self bitmask row) and write o (bf16).
+// bf16 path (Dh = 128), two kernels:
+//  1. attn_tree_mfma: split-KV flash pass.  A workgroup owns one (sequence, head,
+//     prefix key range); its waves each own 16 tree queries, rotated in registers.
+//     64-key K and V tiles are staged in LDS (V transposed), the next tile already
+//     in flight in registers, and both products run on MFMA 16x16x32 bf16:
+//     S^T = K Q^T, then O^T = V^T P^T, so the probabilities stay in registers
+//     between the two.  Online softmax keeps (max, sum) per query.  One extra
+//     workgroup per (sequence, head) rotates the tree keys at their depth
+//     positions (writing k_rot, which is what gets cached) and attends to them
+//     under the ancestor-or-self bitmask.  Rotation angles come from a per-depth
+//     cos/sin table built in LDS.  Partial (m, l, O) go to the workspace.
+//  2. attn_combine: per (sequence, head, node) merge the partials, write o (bf16).
 // fp32 path: one wave per (sequence, head, node) walks all allowed keys on VALU.
 #include <math.h>
 
@@ -177,90 +177,130 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// q_rot [B][H][Tpad][Dh] (bf16, rows >= T zero) and k_rot [B][T][H][Dh].
-__global__ __launch_bounds__(256) void attn_rope(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                 const int32_t* __restrict__ prefix_len,
-                                                 const int32_t* __restrict__ depth, int capacity, int T, int Tpad,
-                                                 int H, double theta, bf16_t* __restrict__ q_rot,
-                                                 bf16_t* __restrict__ k_rot) {
-    const int i = blockIdx.x, b = blockIdx.y;
-    const int half = kDh / 2;
-    const int L = clamp_len(prefix_len, b, capacity);
-    for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
-        const int h = e / half, m = e % half;
-        bf16_t* qo = q_rot + (((long)b * H + h) * Tpad + i) * kDh;
-        if (i >= T) {
-            qo[m] = 0;
-            qo[m + half] = 0;
-            continue;
-        }
-        double c, s;
-        rope_cs(L + depth[i], m, kDh, theta, c, s);
-        const long node = (((long)b * T + i) * H + h) * kDh;
-        const double x1 = bf16_to_f32(q[node + m]), x2 = bf16_to_f32(q[node + m + half]);
-        qo[m] = f64_to_bf16(x1 * c - x2 * s);
-        qo[m + half] = f64_to_bf16(x2 * c + x1 * s);
-        const double y1 = bf16_to_f32(k[node + m]), y2 = bf16_to_f32(k[node + m + half]);
-        k_rot[node + m] = f64_to_bf16(y1 * c - y2 * s);
-        k_rot[node + m + half] = f64_to_bf16(y2 * c + y1 * s);
-    }
+__device__ __forceinline__ float elt(const u32x4& v, int t) {
+    const uint32_t w = v[t >> 1];
+    return __uint_as_float((t & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// Prefix pass: grid (nsplit, H, B), block 64 * nw (nw = Tpad / 16 waves).
-__global__ __launch_bounds__(1024) void attn_prefix_mfma(KV cache, const bf16_t* __restrict__ q_rot,
-                                                         const int32_t* __restrict__ prefix_len, int H, int Tpad,
-                                                         int tiles_per_split, int nsplit, float* __restrict__ part_o,
-                                                         float* __restrict__ part_ml) {
+// cos/sin of pos * theta^(-2m/Dh): the angle is formed and reduced to [-pi, pi] in
+// double precision, then evaluated in single precision.
+__device__ __forceinline__ float2 rope_cs_table_entry(int pos, int m, double theta) {
+    const double a = (double)pos * pow(theta, -2.0 * (double)m / (double)kDh);
+    const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+    float s, c;
+    sincosf((float)r, &s, &c);
+    return make_float2(c, s);
+}
+
+// Rotate the 8 pairs (lo[t], hi[t]) = (x_m, x_{m+64}), m = m0 + t, with cos/sin row cs.
+__device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const float2* cs, int m0) {
+    u32x4 a, b;
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        const float2 r0 = cs[m0 + t], r1 = cs[m0 + t + 1];
+        const float x0 = elt(lo, t), y0 = elt(hi, t), x1 = elt(lo, t + 1), y1 = elt(hi, t + 1);
+        a[t >> 1] = pack_bf16(x0 * r0.x - y0 * r0.y, x1 * r1.x - y1 * r1.y);
+        b[t >> 1] = pack_bf16(y0 * r0.x + x0 * r0.y, y1 * r1.x + x1 * r1.y);
+    }
+    lo = a;
+    hi = b;
+}
+
+struct AttnArgs {
+    KV cache;
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const int32_t* prefix_len;
+    const int32_t* depth;
+    const uint64_t* anc;
+    bf16_t* k_rot;
+    float* part_o;
+    float* part_ml;
+    double theta;
+    int T, Tpad, H, W, nsplit, tiles_per_split, max_depth;
+};
+
+// One (sequence, head, key split) per workgroup; NWB waves, wave w owns queries 16w..16w+15.
+// Workgroups 0..nsplit-1 attend to prefix key ranges; workgroup nsplit rotates the tree
+// keys (writing k_rot) and attends to them, masked by the ancestor-or-self bitmask.
+// Grid (nsplit + 1, H, B); all partials are merged by attn_combine.
+template <int NWB>
+__global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
+    constexpr int NT = 64 * NWB;
+    constexpr int PPT = kTile * (kDh / 8) / NT;  // 16-byte K (and V) pieces per thread per tile
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) bf16_t Vt[kDh * kVStride];
+    __shared__ float2 cs[(MDT_MAX_HEADS + 1) * (kDh / 2)];  // cos/sin per (depth, pair)
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool tree_split = split == A.nsplit;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int nthreads = blockDim.x;
-    const int L = clamp_len(prefix_len, b, cache.capacity);
-    const int j_begin = split * tiles_per_split * kTile;
-    const int j_end = min(L, j_begin + tiles_per_split * kTile);
+    const int H = A.H, T = A.T;
+    const int L = clamp_len(A.prefix_len, b, A.cache.capacity);
+    const int j_begin = tree_split ? 0 : split * A.tiles_per_split * kTile;
+    const int j_end = tree_split ? 0 : min(L, j_begin + A.tiles_per_split * kTile);
     const float scale = 1.f / sqrtf((float)kDh);
+    const bf16_t* Kg = (const bf16_t*)A.cache.k;
+    const bf16_t* Vg = (const bf16_t*)A.cache.v;
+    for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
+        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), e % (kDh / 2), A.theta);
 
-    // this wave's 16 queries as the B operand of S^T = K Q^T: lane holds query c16, dims 32s + 8g .. +8
-    const int q0 = wave * 16;
-    u32x4 bq[4];
-    const bf16_t* qrow = q_rot + (((long)b * H + h) * Tpad + q0 + c16) * kDh;
+    // prefix tile staging through registers: piece c = tid + NT*p is (key c/16, dims 8*(c%16)..)
+    u32x4 kr[PPT], vr[PPT];
+    auto load_prefix = [&](int t0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bq[s] = *(const u32x4*)(qrow + 32 * s + 8 * g);
+        for (int p = 0; p < PPT; ++p) {
+            const int c = tid + NT * p;
+            const int j = t0 + (c >> 4), dc = c & 15;
+            kr[p] = u32x4{0, 0, 0, 0};
+            vr[p] = u32x4{0, 0, 0, 0};
+            if (j < j_end) {
+                const long off = kv_offset(A.cache, b, j, h, H, kDh);
+                if (off >= 0) {
+                    kr[p] = *(const u32x4*)(Kg + off + 8 * dc);
+                    vr[p] = *(const u32x4*)(Vg + off + 8 * dc);
+                }
+            }
+        }
+    };
+    auto store_piece = [&](int key, int dc, const u32x4& kv, const u32x4& vv) {
+        *(u32x4*)(Ks + key * kKStride + 8 * dc) = kv;
+        bf16_t* vt = Vt + (8 * dc) * kVStride + key;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            vt[(2 * t) * kVStride] = (bf16_t)(vv[t] & 0xffffu);
+            vt[(2 * t + 1) * kVStride] = (bf16_t)(vv[t] >> 16);
+        }
+    };
+    if (j_begin < j_end) load_prefix(j_begin);
+    __syncthreads();  // cos/sin table ready
+
+    // this wave's 16 queries, rotated, as the B operand of S^T = K Q^T:
+    // lane holds query qi, dims 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
+    const int qi = wave * 16 + c16;
+    const bool q_ok = qi < T;
+    u32x4 bq[4];
+    uint64_t qa[MDT_MAX_NODES / 64] = {0, 0, 0, 0};
+    {
+        const long node = (((long)b * T + (q_ok ? qi : 0)) * H + h) * kDh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[s] = q_ok ? *(const u32x4*)(A.q + node + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+        const int dq = q_ok ? min(max(A.depth[qi], 0), A.max_depth) : 0;
+        const float2* row = cs + dq * (kDh / 2);
+        rotate8(bq[0], bq[2], row, 8 * g);
+        rotate8(bq[1], bq[3], row, 32 + 8 * g);
+        if (tree_split && q_ok)
+            for (int w = 0; w < A.W; ++w) qa[w] = A.anc[(long)qi * A.W + w];
+    }
 
     f32x4 oacc[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;  // for query c16 (replicated over g)
+    float m_run = -INFINITY, l_run = 0.f;  // of query qi, replicated over g
 
-    const bf16_t* Kg = (const bf16_t*)cache.k;
-    const bf16_t* Vg = (const bf16_t*)cache.v;
-    for (int t0 = j_begin; t0 < j_end; t0 += kTile) {
-        // stage the tile: 64 keys x 128 dims of K (row-major) and V (transposed)
-        __syncthreads();
-        for (int c = threadIdx.x; c < kTile * (kDh / 8); c += nthreads) {
-            const int key = c >> 4, dc = c & 15;
-            const int j = t0 + key;
-            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (j < j_end) {
-                const long off = kv_offset(cache, b, j, h, H, kDh);
-                if (off >= 0) {
-                    kv = *(const u32x4*)(Kg + off + 8 * dc);
-                    vv = *(const u32x4*)(Vg + off + 8 * dc);
-                }
-            }
-            *(u32x4*)(Ks + key * kKStride + 8 * dc) = kv;
-            bf16_t* vt = Vt + (8 * dc) * kVStride + key;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                vt[(2 * t) * kVStride] = (bf16_t)(vv[t] & 0xffffu);
-                vt[(2 * t + 1) * kVStride] = (bf16_t)(vv[t] >> 16);
-            }
-        }
-        __syncthreads();
-
-        // S^T tile: 4 key blocks of 16; lane holds keys kb*16 + 4g + e for query c16
+    // one staged tile: keys base..base+63 (nvalid of them real); tree tiles use the bitmask
+    auto attend_tile = [&](int base, int nvalid, bool tree) {
         f32x4 sacc[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -270,27 +310,31 @@ __global__ __launch_bounds__(1024) void attn_prefix_mfma(KV cache, const bf16_t*
             for (int s = 0; s < 4; ++s) acc = mfma16(*(const u32x4*)(krow + 32 * s), bq[s], acc);
             sacc[kb] = acc;
         }
-        // online softmax over the tile for query c16
+        // tiles start at multiples of 64, so a tree tile reads one word of the query's mask row
+        const int wi = base >> 6;
+        const uint64_t qw = !tree ? ~0ull : (wi == 0 ? qa[0] : wi == 1 ? qa[1] : wi == 2 ? qa[2] : qa[3]);
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = t0 + kb * 16 + 4 * g + e;
-                const float sv = (j < j_end) ? sacc[kb][e] * scale : -INFINITY;
+                const int jj = kb * 16 + 4 * g + e;
+                const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
+                const float sv = ok ? sacc[kb][e] * scale : -INFINITY;
                 sacc[kb][e] = sv;
                 tmax = fmaxf(tmax, sv);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m_run, tmax);
-        const float corr = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
+        const bool live = m_new != -INFINITY;
+        const float corr = live ? expf(m_run - m_new) : 1.f;
         float tsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = (m_new == -INFINITY) ? 0.f : expf(sacc[kb][e] - m_new);
+                const float p = live ? expf(sacc[kb][e] - m_new) : 0.f;
                 sacc[kb][e] = p;
                 tsum += p;
             }
@@ -300,8 +344,7 @@ __global__ __launch_bounds__(1024) void attn_prefix_mfma(KV cache, const bf16_t*
         m_run = m_new;
 #pragma unroll
         for (int db = 0; db < 8; ++db) oacc[db] *= corr;
-
-        // O^T += V^T P^T: two key steps of 32; key order within a step: 4g+t (t<4) then 16+4g+(t-4)
+        // O^T += V^T P^T; within a 32-key step the key order is 4g+t (t<4), then 16+4g+(t-4)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             u32x4 bp;
@@ -318,52 +361,67 @@ __global__ __launch_bounds__(1024) void attn_prefix_mfma(KV cache, const bf16_t*
                 oacc[db] = mfma16(av, bp, oacc[db]);
             }
         }
+    };
+
+    // prefix keys of this split: register prefetch of the next tile while the current one runs
+    for (int t0 = j_begin; t0 < j_end; t0 += kTile) {
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int c = tid + NT * p;
+            store_piece(c >> 4, c & 15, kr[p], vr[p]);
+        }
+        __syncthreads();
+        if (t0 + kTile < j_end) load_prefix(t0 + kTile);
+        attend_tile(t0, j_end - t0, false);
     }
 
-    // partial results for queries q0 + c16: O^T rows dims db*16 + 4g + e
-    const long base = (((long)b * H + h) * nsplit + split) * Tpad + q0 + c16;
-    float* po = part_o + base * kDh;
+    // tree keys: rotate k at L + depth, store k_rot, attend under the bitmask
+    if (tree_split) {
+        for (int tb = 0; tb < T; tb += kTile) {
+            __syncthreads();
+            for (int c = tid; c < kTile * 8; c += NT) {
+                const int key = c >> 3, dc = c & 7, j = tb + key;
+                u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0}, vlo = {0, 0, 0, 0}, vhi = {0, 0, 0, 0};
+                if (j < T) {
+                    const long node = (((long)b * T + j) * H + h) * kDh;
+                    klo = *(const u32x4*)(A.k + node + 8 * dc);
+                    khi = *(const u32x4*)(A.k + node + 64 + 8 * dc);
+                    vlo = *(const u32x4*)(A.v + node + 8 * dc);
+                    vhi = *(const u32x4*)(A.v + node + 64 + 8 * dc);
+                    rotate8(klo, khi, cs + min(max(A.depth[j], 0), A.max_depth) * (kDh / 2), 8 * dc);
+                    *(u32x4*)(A.k_rot + node + 8 * dc) = klo;
+                    *(u32x4*)(A.k_rot + node + 64 + 8 * dc) = khi;
+                }
+                store_piece(key, dc, klo, vlo);
+                store_piece(key, dc + 8, khi, vhi);
+            }
+            __syncthreads();
+            attend_tile(tb, min(kTile, T - tb), true);
+        }
+    }
+
+    if (qi < A.Tpad) {
+        const long base = (((long)b * H + h) * (A.nsplit + 1) + split) * A.Tpad + qi;
+        float* po = A.part_o + base * kDh;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[db][e];
-    if (g == 0) {
-        part_ml[base * 2 + 0] = m_run;
-        part_ml[base * 2 + 1] = l_run;
+            for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[db][e];
+        if (g == 0) {
+            A.part_ml[base * 2 + 0] = m_run;
+            A.part_ml[base * 2 + 1] = l_run;
+        }
     }
 }
 
-// Merge the prefix partials with the node's tree keys. grid (T, H, B), block 64.
-__global__ __launch_bounds__(64) void attn_combine(const bf16_t* __restrict__ q_rot, const bf16_t* __restrict__ k_rot,
-                                                   const bf16_t* __restrict__ v, const float* __restrict__ part_o,
-                                                   const float* __restrict__ part_ml,
-                                                   const uint64_t* __restrict__ anc, int T, int Tpad, int H, int W,
-                                                   int nsplit, bf16_t* __restrict__ out) {
+// Merge the split partials of every (sequence, head, node). grid (T, H, B), block 64.
+__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                   int T, int Tpad, int H, int nsplit, bf16_t* __restrict__ out) {
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const float scale = 1.f / sqrtf((float)kDh);
-    const bf16_t* qi = q_rot + (((long)b * H + h) * Tpad + i) * kDh;
-    const float qa = bf16_to_f32(qi[lane]), qb = bf16_to_f32(qi[lane + 64]);
-    // tree scores
-    float ts[MDT_MAX_HEADS + 1];
-    int tj[MDT_MAX_HEADS + 1];
-    int nt = 0;
-    float M = -INFINITY;
-    for (int w = 0; w < W; ++w) {
-        uint64_t bits = anc[(long)i * W + w];
-        while (bits && nt <= MDT_MAX_HEADS) {
-            const int j = w * 64 + __builtin_ctzll(bits);
-            bits &= bits - 1;
-            if (j >= T) break;
-            const bf16_t* kj = k_rot + (((long)b * T + j) * H + h) * kDh;
-            const float s = wave_sum(qa * bf16_to_f32(kj[lane]) + qb * bf16_to_f32(kj[lane + 64])) * scale;
-            ts[nt] = s;
-            tj[nt] = j;
-            ++nt;
-            M = fmaxf(M, s);
-        }
-    }
     const long pbase = ((long)b * H + h) * nsplit * Tpad + i;
+    float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(pbase + (long)s * Tpad) * 2]);
     float den = 0.f, na = 0.f, nb = 0.f;
     for (int s = 0; s < nsplit; ++s) {
@@ -375,26 +433,21 @@ __global__ __launch_bounds__(64) void attn_combine(const bf16_t* __restrict__ q_
         na += part_o[p * kDh + lane] * wgt;
         nb += part_o[p * kDh + lane + 64] * wgt;
     }
-    for (int t = 0; t < nt; ++t) {
-        const float wgt = expf(ts[t] - M);
-        const bf16_t* vj = v + (((long)b * T + tj[t]) * H + h) * kDh;
-        den += wgt;
-        na += wgt * bf16_to_f32(vj[lane]);
-        nb += wgt * bf16_to_f32(vj[lane + 64]);
-    }
     bf16_t* o = out + (((long)b * T + i) * H + h) * kDh;
     o[lane] = f32_to_bf16(na / den);
     o[lane + 64] = f32_to_bf16(nb / den);
 }
 
 struct Plan {
-    int Tpad, nsplit, tiles_per_split;
-    size_t q_bytes, po_bytes, pml_bytes;
+    int Tpad, nsplit, tiles_per_split, nwb;
+    size_t po_bytes, pml_bytes;
 };
 
 Plan plan(int B, int T, int H, int capacity) {
     Plan p;
     p.Tpad = (T + 15) / 16 * 16;
+    const int waves = p.Tpad / 16;
+    p.nwb = waves <= 4 ? 4 : (waves <= 8 ? 8 : 16);
     const int tiles = capacity > 0 ? (capacity + kTile - 1) / kTile : 1;
     long want = (512 + (long)B * H - 1) / ((long)B * H);
     if (want < 1) want = 1;
@@ -402,9 +455,9 @@ Plan plan(int B, int T, int H, int capacity) {
     if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
     p.tiles_per_split = tps;
     p.nsplit = (tiles + tps - 1) / tps;
-    p.q_bytes = ((size_t)B * H * p.Tpad * kDh * sizeof(bf16_t) + 255) & ~(size_t)255;
-    p.po_bytes = ((size_t)B * H * p.nsplit * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
-    p.pml_bytes = (size_t)B * H * p.nsplit * p.Tpad * 2 * sizeof(float);
+    // prefix splits plus one tree split
+    p.po_bytes = ((size_t)B * H * (p.nsplit + 1) * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
+    p.pml_bytes = (size_t)B * H * (p.nsplit + 1) * p.Tpad * 2 * sizeof(float);
     return p;
 }
 
@@ -414,7 +467,7 @@ extern "C" size_t mdt_tree_attention_workspace(mdt_dtype dt, int B, int T, int H
     if (dt != MDT_BF16 || B < 1 || T < 1 || H < 1) return 0;
     (void)Dh;
     const Plan p = plan(B, T, H, capacity);
-    return p.q_bytes + p.po_bytes + p.pml_bytes;
+    return p.po_bytes + p.pml_bytes;
 }
 
 extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int H, int Dh, const mdt_tree_dev* tree,
@@ -456,24 +509,25 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
         hipLaunchKernelGGL(attn_valu<float>, dim3(T, H, B), dim3(64), 0, s, kv, (const float*)q, (const float*)k,
                            (const float*)v, prefix_len, tree->depth, tree->anc, T, H, Dh, tree->anc_words, theta,
                            (float*)out, (float*)k_rot);
-        return mdt_check_launch("tree_attention");
+        return mdt_launched(s, "attn_valu");
     }
     const Plan p = plan(B, T, H, cache->capacity);
     MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
-    MDT_REQUIRE(ws_bytes >= p.q_bytes + p.po_bytes + p.pml_bytes, MDT_ERR_WORKSPACE, "workspace too small");
-    bf16_t* q_rot = (bf16_t*)ws;
-    float* part_o = (float*)((char*)ws + p.q_bytes);
-    float* part_ml = (float*)((char*)ws + p.q_bytes + p.po_bytes);
-    hipLaunchKernelGGL(attn_rope, dim3(p.Tpad, B), dim3(256), 0, s, (const bf16_t*)q, (const bf16_t*)k, prefix_len,
-                       tree->depth, cache->capacity, T, p.Tpad, H, theta, q_rot, (bf16_t*)k_rot);
-    st = mdt_check_launch("tree_attention rope");
+    MDT_REQUIRE(ws_bytes >= p.po_bytes + p.pml_bytes, MDT_ERR_WORKSPACE, "workspace too small");
+    AttnArgs A{kv, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix_len, tree->depth, tree->anc,
+               (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
+               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth};
+    const dim3 grid(p.nsplit + 1, H, B);
+    if (p.nwb == 4)
+        hipLaunchKernelGGL(attn_tree_mfma<4>, grid, dim3(256), 0, s, A);
+    else if (p.nwb == 8)
+        hipLaunchKernelGGL(attn_tree_mfma<8>, grid, dim3(512), 0, s, A);
+    else
+        hipLaunchKernelGGL(attn_tree_mfma<16>, grid, dim3(1024), 0, s, A);
+    st = mdt_launched(s, "attn_tree_mfma");
     if (st != MDT_OK) return st;
-    hipLaunchKernelGGL(attn_prefix_mfma, dim3(p.nsplit, H, B), dim3(64 * (p.Tpad / 16)), 0, s, kv, q_rot,
-                       prefix_len, H, p.Tpad, p.tiles_per_split, p.nsplit, part_o, part_ml);
-    st = mdt_check_launch("tree_attention prefix");
-    if (st != MDT_OK) return st;
-    hipLaunchKernelGGL(attn_combine, dim3(T, H, B), dim3(64), 0, s, q_rot, (const bf16_t*)k_rot, (const bf16_t*)v,
-                       part_o, part_ml, tree->anc, T, p.Tpad, H, tree->anc_words, p.nsplit, (bf16_t*)out);
-    return mdt_check_launch("tree_attention combine");
+    hipLaunchKernelGGL(attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,
+                       p.nsplit + 1, (bf16_t*)out);
+    return mdt_launched(s, "attn_combine");
 }

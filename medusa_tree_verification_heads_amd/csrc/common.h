@@ -12,8 +12,9 @@
 
 // Record a formatted error for mdt_last_error() and return `st`.
 mdt_status mdt_fail(mdt_status st, const char* fmt, ...);
-// Map a HIP error of the last launch to MDT_ERR_HIP (with its message) or MDT_OK.
-mdt_status mdt_check_launch(const char* what);
+// After a kernel launch: map a HIP launch error to MDT_ERR_HIP (with its message),
+// and record the thread's profiling event for this launch if one is attached.
+mdt_status mdt_launched(hipStream_t stream, const char* kernel);
 // Number of compute units of the current device (cached per device).
 int mdt_num_cus();
 // Validate the host-side scalars and pointers of a device tree.
@@ -88,4 +89,31 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
         int oi = __shfl_xor(i, off, 64);
         if (better(ov, oi, v, i)) { v = ov; i = oi; }
     }
+}
+
+// One DPP step of a (value desc, index asc) reduction: combine with the lane that the
+// data-parallel-primitive control CTRL selects; lanes outside ROW_MASK keep their pair.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_argmax_step(float& v, int& i) {
+    const int vb = __builtin_bit_cast(int, v);
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, ROW_MASK, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
+    if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Best (value, index) of the wave, returned uniformly to all lanes.  Swaps within
+// quads, then row half-mirror and mirror give every lane its 16-lane row's best;
+// row broadcasts 15 and 31 carry rows 0-2 into row 3; lane 63 is read out.
+__device__ __forceinline__ void wave_argmax_dpp(float& v, int& i) {
+    dpp_argmax_step<0xB1, 0xf>(v, i);   // quad_perm [1,0,3,2]
+    dpp_argmax_step<0x4E, 0xf>(v, i);   // quad_perm [2,3,0,1]
+    dpp_argmax_step<0x141, 0xf>(v, i);  // row_half_mirror
+    dpp_argmax_step<0x140, 0xf>(v, i);  // row_mirror
+    dpp_argmax_step<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
+    dpp_argmax_step<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
 }

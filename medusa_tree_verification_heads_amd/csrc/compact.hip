@@ -89,5 +89,5 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
     const int row_vec = (int)(row_bytes / 16);
     hipLaunchKernelGGL(compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path, path_stride,
                        n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
-    return mdt_check_launch("kv_compact");
+    return mdt_launched((hipStream_t)stream, "compact_kernel");
 }

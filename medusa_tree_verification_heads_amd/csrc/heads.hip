@@ -89,7 +89,8 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <typename WT, int NV>
+// STAGE only names the launch (1: W1 + LM head, 2: W2) so that profiles separate the two.
+template <typename WT, int NV, int STAGE>
 __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
     extern __shared__ float xs[];  // [NV][d]
     const int wg = blockIdx.x;
@@ -186,7 +187,7 @@ int plan_segments(GemvLaunch& P, int target) {
     return wg;
 }
 
-template <typename WT>
+template <typename WT, int STAGE>
 mdt_status launch(GemvLaunch& P, hipStream_t stream) {
     const int d = P.d;
     int nv = 1;
@@ -195,12 +196,12 @@ mdt_status launch(GemvLaunch& P, hipStream_t stream) {
     dim3 grid(nwg, (P.B + nv - 1) / nv);
     const size_t lds = (size_t)nv * d * sizeof(float);
     switch (nv) {
-        case 1: hipLaunchKernelGGL((heads_gemv<WT, 1>), grid, dim3(kThreads), lds, stream, P); break;
-        case 2: hipLaunchKernelGGL((heads_gemv<WT, 2>), grid, dim3(kThreads), lds, stream, P); break;
-        case 4: hipLaunchKernelGGL((heads_gemv<WT, 4>), grid, dim3(kThreads), lds, stream, P); break;
-        default: hipLaunchKernelGGL((heads_gemv<WT, 8>), grid, dim3(kThreads), lds, stream, P); break;
+        case 1: hipLaunchKernelGGL((heads_gemv<WT, 1, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 2: hipLaunchKernelGGL((heads_gemv<WT, 2, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 4: hipLaunchKernelGGL((heads_gemv<WT, 4, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        default: hipLaunchKernelGGL((heads_gemv<WT, 8, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
     }
-    return mdt_check_launch("medusa_heads");
+    return mdt_launched(stream, STAGE == 1 ? "heads_gemv_w1_lm" : "heads_gemv_w2");
 }
 
 template <typename WT>
@@ -230,7 +231,7 @@ mdt_status run(hipStream_t stream, int B, int d, int V, int K, const void* h, co
         S.out_bstride = (long)(K + 1) * V;
         S.nrows = V;
     }
-    mdt_status st = launch<WT>(P1, stream);
+    mdt_status st = launch<WT, 1>(P1, stream);
     if (st != MDT_OK) return st;
 
     GemvLaunch P2{};
@@ -246,7 +247,7 @@ mdt_status run(hipStream_t stream, int B, int d, int V, int K, const void* h, co
         S.out_bstride = (long)(K + 1) * V;
         S.nrows = V;
     }
-    return launch<WT>(P2, stream);
+    return launch<WT, 2>(P2, stream);
 }
 
 }  // namespace

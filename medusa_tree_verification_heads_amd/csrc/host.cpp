@@ -22,6 +22,12 @@
 namespace {
 thread_local char g_last_error[512] = "";
 
+constexpr int kMaxProfiled = 4096;
+thread_local void** g_prof_events = nullptr;
+thread_local int g_prof_capacity = 0;
+thread_local int g_prof_count = 0;
+thread_local const char* g_prof_names[kMaxProfiled];
+
 struct Node {
     std::vector<int> path;  // rank path r_1..r_l
 };
@@ -103,9 +109,17 @@ mdt_status mdt_fail(mdt_status st, const char* fmt, ...) {
     return st;
 }
 
-mdt_status mdt_check_launch(const char* what) {
+mdt_status mdt_launched(hipStream_t stream, const char* kernel) {
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return mdt_fail(MDT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (e != hipSuccess) return mdt_fail(MDT_ERR_HIP, "%s: %s", kernel, hipGetErrorString(e));
+    if (g_prof_events) {
+        const int i = g_prof_count++;
+        if (i < kMaxProfiled) g_prof_names[i] = kernel;
+        if (i < g_prof_capacity) {
+            e = hipEventRecord((hipEvent_t)g_prof_events[i], stream);
+            if (e != hipSuccess) return mdt_fail(MDT_ERR_HIP, "profile event: %s", hipGetErrorString(e));
+        }
+    }
     return MDT_OK;
 }
 
@@ -126,6 +140,26 @@ int mdt_num_cus() {
 extern "C" {
 
 int mdt_abi_version(void) { return MDT_ABI_VERSION; }
+
+mdt_status mdt_profile_attach(void** events, int capacity) {
+    MDT_REQUIRE(capacity >= 0, MDT_ERR_SHAPE, "capacity must be >= 0");
+    MDT_REQUIRE(events || capacity == 0, MDT_ERR_NULL, "events is NULL");
+    g_prof_events = capacity > 0 ? events : nullptr;
+    g_prof_capacity = capacity;
+    g_prof_count = 0;
+    return MDT_OK;
+}
+
+int mdt_profile_detach(void) {
+    g_prof_events = nullptr;
+    g_prof_capacity = 0;
+    return g_prof_count;
+}
+
+const char* mdt_profile_kernel(int i) {
+    if (i < 0 || i >= g_prof_count || i >= kMaxProfiled) return "";
+    return g_prof_names[i];
+}
 
 const char* mdt_last_error(void) { return g_last_error; }
 

@@ -7,7 +7,7 @@
 //
 // Selection is a total order: larger value first, equal values by smaller index.
 // A wave selects its k best elements in k rounds; each round every lane offers
-// its best element that comes after the previous winner, and a butterfly
+// its best element that comes after the previous winner, and a DPP row-op
 // reduction picks the winner.  Stage A: every workgroup reduces a 2048-element
 // slice of one row to k candidates (four waves, then one merge wave).  Stage B:
 // one workgroup per sequence, one wave per head row merges the slices' candidates
@@ -43,7 +43,7 @@ __device__ void wave_select(const float (&v)[E], const int (&idx)[E], int k, Can
                 bi = idx[e];
             }
         }
-        wave_argmax(bv, bi);
+        wave_argmax_dpp(bv, bi);
         if ((threadIdx.x & 63) == 0) out[r] = Cand{bv, bi};
         lv = bv;
         li = bi;
@@ -152,9 +152,9 @@ extern "C" mdt_status mdt_topk_tree_expand(void* stream, int B, int K, int V, in
     const int ns = num_slices(V);
     Cand* cand = (Cand*)ws;
     hipLaunchKernelGGL(topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);
-    st = mdt_check_launch("topk_slices");
+    st = mdt_launched(s, "topk_slices");
     if (st != MDT_OK) return st;
     hipLaunchKernelGGL(topk_merge_expand, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns, tree->parent,
                        tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
-    return mdt_check_launch("topk_merge_expand");
+    return mdt_launched(s, "topk_merge_expand");
 }

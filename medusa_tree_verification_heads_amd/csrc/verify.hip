@@ -123,13 +123,17 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 
-// grid (ceil(V/64), ceil(M/64)), block 256
+// grid (ceil(V/64), ceil(M/64)), block 256.  Software-pipelined over 256-dim chunks:
+// while chunk c is multiplied from LDS buffer c%2, the x rows of chunk c+1 and the
+// weight fragments of chunks c+1 and c+2 are in flight in registers.
 __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
                                                    int d, int V, float tau, int nblk_n, Part* __restrict__ part,
                                                    float* __restrict__ logits_opt, const int32_t* __restrict__ parent,
                                                    const int32_t* __restrict__ tokens, int T,
                                                    float* __restrict__ edge) {
-    __shared__ __attribute__((aligned(16))) char smem[kMB * kXStride * sizeof(bf16_t)];
+    constexpr int kBuf = kMB * kXStride;  // elements per x buffer
+    constexpr int kXPerThread = kMB * (kKC / 8) / 256;
+    __shared__ __attribute__((aligned(16))) char smem[2 * kBuf * sizeof(bf16_t)];
     bf16_t* xs = (bf16_t*)smem;
     const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -137,40 +141,71 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     const int col = n0 + wave * 16 + c16;
     const bool col_ok = col < V;
     const bf16_t* wrow = W + (size_t)(col_ok ? col : 0) * d;
+    const int nchunks = (d + kKC - 1) / kKC;
+
+    // weight fragments of chunk c: dims c*KC + 32s + 8g .. +8 of column `col`
+    auto load_w = [&](int c, u32x4 (&wf)[8]) {
+        const int k0 = c * kKC, kc = min(kKC, d - k0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            wf[s] = (col_ok && 32 * s < kc) ? ld_stream(wrow + k0 + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+    };
+    // x rows m0..m0+63 of chunk c: thread t moves 16-byte pieces t, t+256, ...
+    auto load_x = [&](int c, u32x4 (&xr)[kXPerThread]) {
+        const int k0 = c * kKC, kc = min(kKC, d - k0);
+#pragma unroll
+        for (int j = 0; j < kXPerThread; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            const int r = e / (kKC / 8), cc = e % (kKC / 8);
+            xr[j] = (m0 + r < M && 8 * cc < kc) ? *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + 8 * cc)
+                                                : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_x = [&](bf16_t* buf, const u32x4 (&xr)[kXPerThread]) {
+#pragma unroll
+        for (int j = 0; j < kXPerThread; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            const int r = e / (kKC / 8), cc = e % (kKC / 8);
+            *(u32x4*)(buf + r * kXStride + 8 * cc) = xr[j];
+        }
+    };
 
     f32x4 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < d; k0 += kKC) {
-        const int kc = min(kKC, d - k0);  // multiple of 32
-        const int nsteps = kc / 32;
-        // weight fragments of this chunk: dims k0 + 32s + 8g .. +8 of column `col`
-        u32x4 wf[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            wf[s] = (col_ok && s < nsteps) ? ld_stream(wrow + k0 + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
-        __syncthreads();
-        for (int c = threadIdx.x; c < kMB * (kKC / 8); c += 256) {
-            const int r = c / (kKC / 8), cc = c % (kKC / 8);
-            u32x4 val = {0, 0, 0, 0};
-            if (m0 + r < M && 8 * cc < kc) val = *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + 8 * cc);
-            *(u32x4*)(xs + r * kXStride + 8 * cc) = val;
-        }
-        __syncthreads();
+    // weight fragments run two chunks ahead (HBM latency), x one chunk ahead (L2 latency);
+    // x of chunk c+1 is requested before the weights of chunk c+2 so that waiting for it
+    // leaves the weight loads in flight
+    u32x4 w0[8], w1[8], w2[8], xr[kXPerThread];
+    load_w(0, w0);
+    if (nchunks > 1) load_w(1, w1);
+    load_x(0, xr);
+    store_x(xs, xr);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) load_x(c + 1, xr);
+        if (c + 2 < nchunks) load_w(c + 2, w2);
+        const bf16_t* buf = xs + (c & 1) * kBuf;
+        const int nsteps = min(kKC, d - c * kKC) / 32;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             if (s < nsteps) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kXStride + 32 * s + 8 * g);
-                    acc[mt] = mfma16(a, wf[s], acc[mt]);
+                    const u32x4 a = *(const u32x4*)(buf + (mt * 16 + c16) * kXStride + 32 * s + 8 * g);
+                    acc[mt] = mfma16(a, w0[s], acc[mt]);
                 }
             }
         }
+        if (c + 1 < nchunks) store_x(xs + ((c + 1) & 1) * kBuf, xr);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            w0[s] = w1[s];
+            w1[s] = w2[s];
+        }
     }
-    __syncthreads();
-    float* zt = (float*)smem;  // [64][kZStride]
+    float* zt = (float*)smem;  // [64][kZStride], reuses the x buffers
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -289,9 +324,9 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
                            (const float*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
     }
-    st = mdt_check_launch("verify_logits gemm");
+    st = mdt_launched(s, dt == MDT_BF16 ? "verify_mfma" : "verify_f32");
     if (st != MDT_OK) return st;
     hipLaunchKernelGGL(verify_merge, dim3(M), dim3(64), 0, s, part, nblk_n, V, temperature, stats, tree_tokens,
                        tree->parent, T, edge_logit);
-    return mdt_check_launch("verify_logits merge");
+    return mdt_launched(s, "verify_merge");
 }
