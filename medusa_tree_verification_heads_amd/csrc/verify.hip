@@ -9,9 +9,9 @@
 //
 // The rows of x (B*T nodes) share every weight row, so this is a real dense
 // contraction: bf16 MFMA 16x16x32 with fp32 accumulation.  A workgroup owns 64
-// vocabulary columns and 64 node rows; each wave owns 16 columns and streams
-// their weight rows straight from HBM into the B operand, while the 64 x rows are
-// staged in LDS 256 dims at a time and shared by the four waves.  The epilogue
+// vocabulary columns and 64 node rows.  Weight rows are read from HBM in long
+// row-contiguous runs and transposed into MFMA fragments through LDS, together
+// with the 64 x rows (shared by the four waves, each owning 16 columns).  The epilogue
 // keeps the logits tile in LDS and reduces it to per-row partial statistics over
 // the 64 columns -- max, argmax, s = sum exp((z-m)/tau), u = sum exp((z-m)/tau) (z-m)/tau --
 // and picks the edge logits whose token falls in the tile.  A second kernel
@@ -30,9 +30,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNB = 64;          // vocabulary columns per workgroup
 constexpr int kMB = 64;          // node rows per workgroup (bf16 path)
-constexpr int kKC = 256;         // dims per staged x chunk
-constexpr int kXStride = kKC + 8;
 constexpr int kZStride = kNB + 1;
+#ifndef MDT_VERIFY_KC
+#define MDT_VERIFY_KC 256        // dims per staged chunk (LDS holds one 64-row tile of x and of W)
+#endif
 
 struct Part {
     float m;
@@ -123,89 +124,98 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 
-// grid (ceil(V/64), ceil(M/64)), block 256.  Software-pipelined over 256-dim chunks:
-// while chunk c is multiplied from LDS buffer c%2, the x rows of chunk c+1 and the
-// weight fragments of chunks c+1 and c+2 are in flight in registers.
+// grid (ceil(V/64), ceil(M/64)), block 256.  Per chunk of KC dims, the workgroup moves
+// its 64 weight rows and 64 x rows into LDS with row-contiguous 16-byte loads (each
+// wave instruction covers whole 1 KiB row runs, the pattern HBM streams best), then
+// every wave reads MFMA fragments out of LDS: B = its 16 weight rows, A = the 64 x rows.
+// While chunk c is multiplied, weight rows of chunks c+1, c+2 and x rows of chunk c+1
+// are in flight in registers; two workgroups share a CU's LDS.
+template <int KC>
 __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
                                                    int d, int V, float tau, int nblk_n, Part* __restrict__ part,
                                                    float* __restrict__ logits_opt, const int32_t* __restrict__ parent,
                                                    const int32_t* __restrict__ tokens, int T,
                                                    float* __restrict__ edge) {
-    constexpr int kBuf = kMB * kXStride;  // elements per x buffer
-    constexpr int kXPerThread = kMB * (kKC / 8) / 256;
-    __shared__ __attribute__((aligned(16))) char smem[2 * kBuf * sizeof(bf16_t)];
+    constexpr int kStride = KC + 8;               // LDS row stride (elements)
+    constexpr int kPR = KC / 8;                   // 16-byte pieces per row per chunk
+    constexpr int kPPT = 64 * kPR / 256;          // pieces per thread per chunk (per matrix)
+    constexpr int kTileBytes = 64 * kStride * 2;  // one 64-row tile
+    static_assert(2 * kTileBytes >= 64 * kZStride * 4, "epilogue tile must fit");
+    __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
     bf16_t* xs = (bf16_t*)smem;
+    bf16_t* ws = (bf16_t*)(smem + kTileBytes);
     const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int col = n0 + wave * 16 + c16;
-    const bool col_ok = col < V;
-    const bf16_t* wrow = W + (size_t)(col_ok ? col : 0) * d;
-    const int nchunks = (d + kKC - 1) / kKC;
+    const int nchunks = (d + KC - 1) / KC;
 
-    // weight fragments of chunk c: dims c*KC + 32s + 8g .. +8 of column `col`
-    auto load_w = [&](int c, u32x4 (&wf)[8]) {
-        const int k0 = c * kKC, kc = min(kKC, d - k0);
+    // weight rows run two chunks ahead (HBM latency), x rows one chunk ahead (L2); x of
+    // chunk c+1 is requested before the weights of chunk c+2, so waiting for it leaves
+    // those weight loads in flight
+    u32x4 wa[kPPT], wb[kPPT], xr[kPPT];
+    auto load_w = [&](int c, u32x4 (&wr)[kPPT]) {
+        const int k0 = c * KC, kc = min(KC, d - k0);
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            wf[s] = (col_ok && 32 * s < kc) ? ld_stream(wrow + k0 + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
-    };
-    // x rows m0..m0+63 of chunk c: thread t moves 16-byte pieces t, t+256, ...
-    auto load_x = [&](int c, u32x4 (&xr)[kXPerThread]) {
-        const int k0 = c * kKC, kc = min(kKC, d - k0);
-#pragma unroll
-        for (int j = 0; j < kXPerThread; ++j) {
-            const int e = threadIdx.x + 256 * j;
-            const int r = e / (kKC / 8), cc = e % (kKC / 8);
-            xr[j] = (m0 + r < M && 8 * cc < kc) ? *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + 8 * cc)
-                                                : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < kPPT; ++j) {
+            const int p = threadIdx.x + 256 * j;
+            const int r = p / kPR, off = 8 * (p % kPR);
+            wr[j] = (off < kc && n0 + r < V) ? ld_stream(W + (size_t)(n0 + r) * d + k0 + off) : u32x4{0, 0, 0, 0};
         }
     };
-    auto store_x = [&](bf16_t* buf, const u32x4 (&xr)[kXPerThread]) {
+    auto load_x = [&](int c) {
+        const int k0 = c * KC, kc = min(KC, d - k0);
 #pragma unroll
-        for (int j = 0; j < kXPerThread; ++j) {
-            const int e = threadIdx.x + 256 * j;
-            const int r = e / (kKC / 8), cc = e % (kKC / 8);
-            *(u32x4*)(buf + r * kXStride + 8 * cc) = xr[j];
+        for (int j = 0; j < kPPT; ++j) {
+            const int p = threadIdx.x + 256 * j;
+            const int r = p / kPR, off = 8 * (p % kPR);
+            xr[j] = (off < kc && m0 + r < M) ? *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + off) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store = [&](const u32x4 (&wr)[kPPT]) {
+#pragma unroll
+        for (int j = 0; j < kPPT; ++j) {
+            const int p = threadIdx.x + 256 * j;
+            const int r = p / kPR, off = 8 * (p % kPR);
+            *(u32x4*)(ws + r * kStride + off) = wr[j];
+            *(u32x4*)(xs + r * kStride + off) = xr[j];
         }
     };
 
     f32x4 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // weight fragments run two chunks ahead (HBM latency), x one chunk ahead (L2 latency);
-    // x of chunk c+1 is requested before the weights of chunk c+2 so that waiting for it
-    // leaves the weight loads in flight
-    u32x4 w0[8], w1[8], w2[8], xr[kXPerThread];
-    load_w(0, w0);
-    if (nchunks > 1) load_w(1, w1);
-    load_x(0, xr);
-    store_x(xs, xr);
+    load_w(0, wa);
+    load_x(0);
+    if (nchunks > 1) load_w(1, wb);
+    store(wa);
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) load_x(c + 1, xr);
-        if (c + 2 < nchunks) load_w(c + 2, w2);
-        const bf16_t* buf = xs + (c & 1) * kBuf;
-        const int nsteps = min(kKC, d - c * kKC) / 32;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+    for (int j = 0; j < kPPT; ++j) wa[j] = wb[j];
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) load_x(c + 1);
+        if (c + 2 < nchunks) load_w(c + 2, wb);
+        const int nsteps = min(KC, d - c * KC) / 32;
+        const bf16_t* wrow = ws + (wave * 16 + c16) * kStride + 8 * g;
+#pragma unroll 4
+        for (int s = 0; s < KC / 32; ++s) {
             if (s < nsteps) {
+                const u32x4 b = *(const u32x4*)(wrow + 32 * s);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    const u32x4 a = *(const u32x4*)(buf + (mt * 16 + c16) * kXStride + 32 * s + 8 * g);
-                    acc[mt] = mfma16(a, w0[s], acc[mt]);
+                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kStride + 32 * s + 8 * g);
+                    acc[mt] = mfma16(a, b, acc[mt]);
                 }
             }
         }
-        if (c + 1 < nchunks) store_x(xs + ((c + 1) & 1) * kBuf, xr);
         __syncthreads();
+        if (c + 1 < nchunks) {
+            store(wa);
+            __syncthreads();
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            w0[s] = w1[s];
-            w1[s] = w2[s];
+            for (int j = 0; j < kPPT; ++j) wa[j] = wb[j];
         }
     }
-    float* zt = (float*)smem;  // [64][kZStride], reuses the x buffers
+    float* zt = (float*)smem;  // [64][kZStride], reuses the tiles
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -315,7 +325,7 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     const int nblk_n = (V + kNB - 1) / kNB;
     Part* part = (Part*)ws;
     if (dt == MDT_BF16) {
-        hipLaunchKernelGGL(verify_mfma, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s, (const bf16_t*)x,
+        hipLaunchKernelGGL(verify_mfma<MDT_VERIFY_KC>, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s, (const bf16_t*)x,
                            (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
     } else {
