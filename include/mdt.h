@@ -363,11 +363,12 @@ int mdt_abi_version(void);
 
 /*
  * Kernel timing hook (instrumentation, not part of the step).  While attached on
- * the calling thread, every kernel the library launches is followed by
- * hipEventRecord(events[i], stream) with i counting launches from 0; launches
- * beyond `capacity` record nothing.  The caller creates the events (hipEvent_t,
- * timing enabled), reads elapsed times between consecutive events after
- * synchronising, and names launch i with mdt_profile_kernel(i).
+ * the calling thread, launch i of the library (counting from 0) is made with
+ * hipExtLaunchKernelGGL and the start/stop events events[2i], events[2i+1], which
+ * the runtime stamps when that kernel starts and ends on its stream; launches whose
+ * pair lies beyond `capacity` events record nothing.  The caller creates the
+ * events (hipEvent_t, timing enabled), reads hipEventElapsedTime(start, stop) of
+ * each pair after synchronising, and names launch i with mdt_profile_kernel(i).
  * Errors: MDT_ERR_NULL (events NULL with capacity > 0), MDT_ERR_SHAPE (capacity < 0).
  */
 mdt_status mdt_profile_attach(void** events, int capacity);

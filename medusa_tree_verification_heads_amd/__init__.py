@@ -147,10 +147,16 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace buffer (zero-filled so that its contents are deterministic)."""
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), max(nbytes, 16)
+    t = new_workspace(nbytes, device)
+    return t, t.numel()
 
 
 # ---------------------------------------------------------------------------
@@ -324,38 +330,34 @@ def verify_logits(x, Wlm, tree: DeviceTree, tree_tokens, temperature: float, sta
 
 
 class KernelTimer:
-    """Records a timing event after every kernel the library launches (on the launch stream).
+    """Start/stop timing events around every kernel the library launches (on its stream).
 
-    with KernelTimer(n) as kt:  ... library calls ...
-    then kt.durations_ms() -> list of (kernel name, ms) measured between consecutive events.
+    with KernelTimer(n_launches) as kt:  ... library calls ...
+    then kt.durations_ms() -> list of (kernel name, ms between the kernel's start and end).
     """
 
     def __init__(self, capacity: int):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * capacity)]
         for e in self.events:      # materialise the underlying HIP events
             e.record()
-        self.start = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        self._arr = (c_void_p * capacity)(*[e.cuda_event for e in self.events])
+        self._arr = (c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
         self.count = 0
+        self.names = []
 
     def __enter__(self):
         _check(lib.mdt_profile_attach(self._arr, len(self.events)), "profile_attach")
-        self.start.record()
         return self
 
     def __exit__(self, *exc):
         self.count = lib.mdt_profile_detach()
-        self.names = [lib.mdt_profile_kernel(i).decode() for i in range(min(self.count, len(self.events)))]
+        n = min(self.count, len(self.events) // 2)
+        self.names = [lib.mdt_profile_kernel(i).decode() for i in range(n)]
         return False
 
     def durations_ms(self):
         torch.cuda.synchronize()
-        out, prev = [], self.start
-        for name, ev in zip(self.names, self.events):
-            out.append((name, prev.elapsed_time(ev)))
-            prev = ev
-        return out
+        return [(name, self.events[2 * i].elapsed_time(self.events[2 * i + 1])) for i, name in enumerate(self.names)]
 
 
 def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:

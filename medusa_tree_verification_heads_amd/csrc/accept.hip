@@ -97,9 +97,9 @@ extern "C" mdt_status mdt_accept_path(void* stream, int B, const mdt_tree_dev* t
         MDT_REQUIRE(eps > 0.f && delta > 0.f, MDT_ERR_VALUE, "eps and delta must be > 0");
     MDT_REQUIRE(path_stride >= tree->max_depth + 1, MDT_ERR_SHAPE, "path_stride %d < max_depth + 1", path_stride);
     MDT_REQUIRE(stats && edge_logit && tree_tokens && path && n_acc, MDT_ERR_NULL, "a tensor pointer is NULL");
-    hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, (hipStream_t)stream, stats, edge_logit, tree_tokens,
-                       tree->parent, tree->depth, tree->anc, tree->T, tree->anc_words, mode,
-                       mode == MDT_ACCEPT_TYPICAL ? eps : 1.f, mode == MDT_ACCEPT_TYPICAL ? delta : 1.f, temperature,
-                       path, path_stride, n_acc);
-    return mdt_launched((hipStream_t)stream, "accept_kernel");
+    MDT_LAUNCH("accept_kernel", accept_kernel, dim3(B), dim3(64), 0, (hipStream_t)stream, stats, edge_logit,
+               tree_tokens, tree->parent, tree->depth, tree->anc, tree->T, tree->anc_words, mode,
+               mode == MDT_ACCEPT_TYPICAL ? eps : 1.f, mode == MDT_ACCEPT_TYPICAL ? delta : 1.f, temperature, path,
+               path_stride, n_acc);
+    return mdt_launched("accept_kernel");
 }

@@ -506,10 +506,10 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     hipStream_t s = (hipStream_t)stream;
     const double theta = (double)rope_theta;
     if (dt == MDT_F32) {
-        hipLaunchKernelGGL(attn_valu<float>, dim3(T, H, B), dim3(64), 0, s, kv, (const float*)q, (const float*)k,
-                           (const float*)v, prefix_len, tree->depth, tree->anc, T, H, Dh, tree->anc_words, theta,
-                           (float*)out, (float*)k_rot);
-        return mdt_launched(s, "attn_valu");
+        MDT_LAUNCH("attn_valu", attn_valu<float>, dim3(T, H, B), dim3(64), 0, s, kv, (const float*)q,
+                   (const float*)k, (const float*)v, prefix_len, tree->depth, tree->anc, T, H, Dh, tree->anc_words,
+                   theta, (float*)out, (float*)k_rot);
+        return mdt_launched("attn_valu");
     }
     const Plan p = plan(B, T, H, cache->capacity);
     MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
@@ -520,14 +520,14 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
                tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth};
     const dim3 grid(p.nsplit + 1, H, B);
     if (p.nwb == 4)
-        hipLaunchKernelGGL(attn_tree_mfma<4>, grid, dim3(256), 0, s, A);
+        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<4>, grid, dim3(256), 0, s, A);
     else if (p.nwb == 8)
-        hipLaunchKernelGGL(attn_tree_mfma<8>, grid, dim3(512), 0, s, A);
+        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<8>, grid, dim3(512), 0, s, A);
     else
-        hipLaunchKernelGGL(attn_tree_mfma<16>, grid, dim3(1024), 0, s, A);
-    st = mdt_launched(s, "attn_tree_mfma");
+        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<16>, grid, dim3(1024), 0, s, A);
+    st = mdt_launched("attn_tree_mfma");
     if (st != MDT_OK) return st;
-    hipLaunchKernelGGL(attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,
-                       p.nsplit + 1, (bf16_t*)out);
-    return mdt_launched(s, "attn_combine");
+    MDT_LAUNCH("attn_combine", attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,
+               p.nsplit + 1, (bf16_t*)out);
+    return mdt_launched("attn_combine");
 }

@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP kernels and the host layer of libmdt.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -12,9 +13,20 @@
 
 // Record a formatted error for mdt_last_error() and return `st`.
 mdt_status mdt_fail(mdt_status st, const char* fmt, ...);
-// After a kernel launch: map a HIP launch error to MDT_ERR_HIP (with its message),
-// and record the thread's profiling event for this launch if one is attached.
-mdt_status mdt_launched(hipStream_t stream, const char* kernel);
+// After a kernel launch: map a HIP launch error to MDT_ERR_HIP (with its message).
+mdt_status mdt_launched(const char* kernel);
+// Start/stop events for the next launch when a profiling attachment is active on this
+// thread (both null otherwise); names the launch for mdt_profile_kernel().
+void mdt_profile_slot(const char* kernel, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch through hipExtLaunchKernelGGL so that an attached profiler gets the kernel's own
+// start and stop timestamps.
+#define MDT_LAUNCH(name, kernel, grid, block, lds, stream, ...)                              \
+    do {                                                                                    \
+        hipEvent_t mdt_e0_, mdt_e1_;                                                        \
+        mdt_profile_slot(name, &mdt_e0_, &mdt_e1_);                                         \
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, mdt_e0_, mdt_e1_, 0, __VA_ARGS__); \
+    } while (0)
 // Number of compute units of the current device (cached per device).
 int mdt_num_cus();
 // Validate the host-side scalars and pointers of a device tree.

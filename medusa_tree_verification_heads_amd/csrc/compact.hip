@@ -87,7 +87,7 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
     Cache c{cache->k, cache->v, cache->page_table, cache->layout, cache->capacity, cache->page_size,
             cache->max_pages, cache->num_pages};
     const int row_vec = (int)(row_bytes / 16);
-    hipLaunchKernelGGL(compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path, path_stride,
-                       n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
-    return mdt_launched((hipStream_t)stream, "compact_kernel");
+    MDT_LAUNCH("compact_kernel", compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path,
+               path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
+    return mdt_launched("compact_kernel");
 }

@@ -195,13 +195,14 @@ mdt_status launch(GemvLaunch& P, hipStream_t stream) {
     const int nwg = plan_segments(P, mdt_num_cus() * 8);
     dim3 grid(nwg, (P.B + nv - 1) / nv);
     const size_t lds = (size_t)nv * d * sizeof(float);
+    const char* name = STAGE == 1 ? "heads_gemv_w1_lm" : "heads_gemv_w2";
     switch (nv) {
-        case 1: hipLaunchKernelGGL((heads_gemv<WT, 1, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        case 2: hipLaunchKernelGGL((heads_gemv<WT, 2, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        case 4: hipLaunchKernelGGL((heads_gemv<WT, 4, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        default: hipLaunchKernelGGL((heads_gemv<WT, 8, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 1: MDT_LAUNCH(name, (heads_gemv<WT, 1, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 2: MDT_LAUNCH(name, (heads_gemv<WT, 2, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 4: MDT_LAUNCH(name, (heads_gemv<WT, 4, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        default: MDT_LAUNCH(name, (heads_gemv<WT, 8, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
     }
-    return mdt_launched(stream, STAGE == 1 ? "heads_gemv_w1_lm" : "heads_gemv_w2");
+    return mdt_launched(name);
 }
 
 template <typename WT>

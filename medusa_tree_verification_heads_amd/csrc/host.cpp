@@ -109,18 +109,21 @@ mdt_status mdt_fail(mdt_status st, const char* fmt, ...) {
     return st;
 }
 
-mdt_status mdt_launched(hipStream_t stream, const char* kernel) {
+mdt_status mdt_launched(const char* kernel) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return mdt_fail(MDT_ERR_HIP, "%s: %s", kernel, hipGetErrorString(e));
-    if (g_prof_events) {
-        const int i = g_prof_count++;
-        if (i < kMaxProfiled) g_prof_names[i] = kernel;
-        if (i < g_prof_capacity) {
-            e = hipEventRecord((hipEvent_t)g_prof_events[i], stream);
-            if (e != hipSuccess) return mdt_fail(MDT_ERR_HIP, "profile event: %s", hipGetErrorString(e));
-        }
-    }
     return MDT_OK;
+}
+
+void mdt_profile_slot(const char* kernel, hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    if (!g_prof_events) return;
+    const int i = g_prof_count++;
+    if (i < kMaxProfiled) g_prof_names[i] = kernel;
+    if (2 * i + 1 < g_prof_capacity) {
+        *start = (hipEvent_t)g_prof_events[2 * i];
+        *stop = (hipEvent_t)g_prof_events[2 * i + 1];
+    }
 }
 
 int mdt_num_cus() {

@@ -151,10 +151,10 @@ extern "C" mdt_status mdt_topk_tree_expand(void* stream, int B, int K, int V, in
     const int K1 = K + 1;
     const int ns = num_slices(V);
     Cand* cand = (Cand*)ws;
-    hipLaunchKernelGGL(topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);
-    st = mdt_launched(s, "topk_slices");
+    MDT_LAUNCH("topk_slices", topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);
+    st = mdt_launched("topk_slices");
     if (st != MDT_OK) return st;
-    hipLaunchKernelGGL(topk_merge_expand, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns, tree->parent,
-                       tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
-    return mdt_launched(s, "topk_merge_expand");
+    MDT_LAUNCH("topk_merge_expand", topk_merge_expand, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns,
+               tree->parent, tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
+    return mdt_launched("topk_merge_expand");
 }

@@ -325,18 +325,19 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     const int nblk_n = (V + kNB - 1) / kNB;
     Part* part = (Part*)ws;
     if (dt == MDT_BF16) {
-        hipLaunchKernelGGL(verify_mfma<MDT_VERIFY_KC>, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s, (const bf16_t*)x,
+        MDT_LAUNCH("verify_mfma", verify_mfma<MDT_VERIFY_KC>, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s,
+                   (const bf16_t*)x,
                            (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
     } else {
         const size_t lds = (size_t)16 * (d > kZStride ? d : kZStride) * sizeof(float);
-        hipLaunchKernelGGL(verify_f32, dim3(nblk_n, (M + 15) / 16), dim3(256), lds, s, (const float*)x,
+        MDT_LAUNCH("verify_f32", verify_f32, dim3(nblk_n, (M + 15) / 16), dim3(256), lds, s, (const float*)x,
                            (const float*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
     }
-    st = mdt_launched(s, dt == MDT_BF16 ? "verify_mfma" : "verify_f32");
+    st = mdt_launched(dt == MDT_BF16 ? "verify_mfma" : "verify_f32");
     if (st != MDT_OK) return st;
-    hipLaunchKernelGGL(verify_merge, dim3(M), dim3(64), 0, s, part, nblk_n, V, temperature, stats, tree_tokens,
+    MDT_LAUNCH("verify_merge", verify_merge, dim3(M), dim3(64), 0, s, part, nblk_n, V, temperature, stats, tree_tokens,
                        tree->parent, T, edge_logit);
-    return mdt_launched(s, "verify_merge");
+    return mdt_launched("verify_merge");
 }

@@ -17,8 +17,8 @@ import numpy as np
 import torch
 
 from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_path, kv_compact, medusa_heads,
-               medusa_heads_workspace, topk_tree_expand, topk_workspace, tree_attention, tree_attention_workspace,
-               verify_logits, verify_logits_workspace)
+               medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
+               tree_attention_workspace, verify_logits, verify_logits_workspace)
 
 
 def to_device(a: np.ndarray, device) -> torch.Tensor:
@@ -60,11 +60,10 @@ class VerifyStep:
         self.n_acc = torch.empty((B,), **i32)
         self.new_len = torch.empty((B,), **i32)
         dt = MDT_BF16 if w.dtype == "bf16" else MDT_F32
-        u8 = dict(dtype=torch.uint8, device=dev)
-        self.ws_heads = torch.empty(max(16, medusa_heads_workspace(B, d, K)), **u8)
-        self.ws_topk = torch.empty(max(16, topk_workspace(B, K, V, k_cfg)), **u8)
-        self.ws_attn = torch.empty(max(16, tree_attention_workspace(dt, B, T, H, Dh, self.cache.desc.capacity)), **u8)
-        self.ws_verify = torch.empty(max(16, verify_logits_workspace(dt, B, T, d, V)), **u8)
+        self.ws_heads = new_workspace(medusa_heads_workspace(B, d, K), dev)
+        self.ws_topk = new_workspace(topk_workspace(B, K, V, k_cfg), dev)
+        self.ws_attn = new_workspace(tree_attention_workspace(dt, B, T, H, Dh, self.cache.desc.capacity), dev)
+        self.ws_verify = new_workspace(verify_logits_workspace(dt, B, T, d, V), dev)
 
     def run(self, stream=None):
         t, w = self.t, self.w
