@@ -85,19 +85,11 @@ def medusa_heads(h, W1, W2, Wlm):
     V = Wlm.shape[0]
     logits = np.empty((B, K + 1, V))
     a = np.empty((B, K, d))
-    wlm = to_f64(Wlm)
-    for b in range(B):
-        logits[b, 0] = wlm @ hb[b]
-    del wlm
+    # every sequence's vector is multiplied by the same weights: one matrix product per weight
+    logits[:, 0] = (to_f64(Wlm) @ hb.T).T
     for k in range(K):
-        w1 = to_f64(W1[k])
-        for b in range(B):
-            a[b, k] = silu(w1 @ hb[b]) + hb[b]
-        del w1
-        w2 = to_f64(W2[k])
-        for b in range(B):
-            logits[b, 1 + k] = w2 @ a[b, k]
-        del w2
+        a[:, k] = silu((to_f64(W1[k]) @ hb.T).T) + hb
+        logits[:, 1 + k] = (to_f64(W2[k]) @ a[:, k].T).T
     return logits, a
 
 
@@ -151,11 +143,13 @@ def cache_rows(Kc, Vc, b: int, L: int, page_table=None, page_size: int = 16):
 
 
 def tree_attention(q, k, v, Kc, Vc, prefix_len, tree: OracleTree, theta=10000.0,
-                   bf16_store=True, page_table=None, page_size=16):
+                   bf16_store=True, page_table=None, page_size=16, heads=None, queries=None):
     """Node outputs o [B][T][H][Dh] and rotated tree keys k_rot [B][T][H][Dh].
 
     For every (b, h, i) the allowed keys are the L_b prefix keys followed by the
     rotated keys of i's ancestors-or-self; softmax over exactly those keys.
+    ``heads`` / ``queries`` optionally restrict which (h, i) are computed (the
+    others are left NaN); used to sample full-size workloads.
     """
     qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
     B, T, H, Dh = qf.shape
@@ -171,20 +165,21 @@ def tree_attention(q, k, v, Kc, Vc, prefix_len, tree: OracleTree, theta=10000.0,
     allowed = np.zeros((T, T), dtype=bool)
     for i in range(T):
         allowed[i, ancestors(tree, i)] = True
-    o = np.empty((B, T, H, Dh))
+    qs = np.arange(T) if queries is None else np.asarray(queries)
+    o = np.full((B, T, H, Dh), np.nan)
     for b in range(B):
         L = int(prefix_len[b])
         pk, pv = cache_rows(Kc, Vc, b, L, page_table, page_size)
-        for h in range(H):
-            s_pre = (q_rot[b, :, h] @ pk[:, h].T) * scale            # [T][L]
-            s_tree = (q_rot[b, :, h] @ k_rot[b, :, h].T) * scale     # [T][T]
-            s_tree = np.where(allowed, s_tree, -np.inf)
+        for h in (range(H) if heads is None else heads):
+            s_pre = (q_rot[b, qs, h] @ pk[:, h].T) * scale           # [nq][L]
+            s_tree = (q_rot[b, qs, h] @ k_rot[b, :, h].T) * scale    # [nq][T]
+            s_tree = np.where(allowed[qs], s_tree, -np.inf)
             mx = np.maximum(s_pre.max(axis=1, initial=-np.inf), s_tree.max(axis=1))
             e_pre = np.exp(s_pre - mx[:, None])
             e_tree = np.exp(s_tree - mx[:, None])                   # masked entries give exact zeros
             den = e_pre.sum(axis=1) + e_tree.sum(axis=1)
             num = e_pre @ pv[:, h] + e_tree @ vf[b, :, h]
-            o[b, :, h] = store(num / den[:, None])
+            o[b, qs, h] = store(num / den[:, None])
     return o, k_rot
 
 
