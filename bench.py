@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--mode", default="typical", choices=["typical", "greedy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -102,9 +104,20 @@ def main():
               "the multi-GPU layout is a design note, not a built path", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+
     if not os.path.exists(os.path.join(ROOT, "medusa_tree_verification_heads_amd", "libmdt.so")):
-        from medusa_tree_verification_heads_amd import build as b
-        b.build()
+        from __graft_entry__ import _builder
+        _builder().build()
     import numpy as np
     import torch
     import medusa_tree_verification_heads_amd as mdt

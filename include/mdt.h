@@ -9,6 +9,7 @@
  *   mdt_verify_logits     LM head on every tree node -> per-row argmax / log-partition / entropy
  *   mdt_accept_path       greedy or typical acceptance -> longest accepted path
  *   mdt_kv_compact        append the accepted path's keys/values to the cache
+ *   mdt_accept_compact    the last two in one launch (same results)
  *
  * The pages this follows are the Medusa pages: "Medusa: Simple LLM Inference
  * Acceleration Framework with Multiple Decoding Heads" (summary page, section 3.2
@@ -354,6 +355,20 @@ mdt_status mdt_accept_path(void* stream, int B, const mdt_tree_dev* tree, const 
 mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, int H, int Dh, const int32_t* path,
                           int path_stride, const int32_t* n_acc, const void* k_rot, const void* v,
                           const mdt_kv_cache* cache, const int32_t* prefix_len, int32_t* new_prefix_len);
+
+/*
+ * mdt_accept_path followed by mdt_kv_compact in one launch: one workgroup per
+ * sequence selects the path and appends its keys/values to the cache (the end of
+ * a step on the summary page, section 3.2, and "MEDUSA 精读", section 3).  Every
+ * output -- path, n_acc, the cache rows, new_prefix_len -- is exactly what the two
+ * calls write in sequence with the same arguments; the arguments are those of the
+ * two calls (T is tree->T), with the same checks and error codes.
+ */
+mdt_status mdt_accept_compact(void* stream, mdt_dtype dt, int B, int H, int Dh, const mdt_tree_dev* tree,
+                              const mdt_row_stats* stats, const float* edge_logit, const int32_t* tree_tokens,
+                              int mode, float eps, float delta, float temperature, int32_t* path, int path_stride,
+                              int32_t* n_acc, const void* k_rot, const void* v, const mdt_kv_cache* cache,
+                              const int32_t* prefix_len, int32_t* new_prefix_len);
 
 /* ------------------------------------------------------------------------- */
 /* Misc                                                                       */

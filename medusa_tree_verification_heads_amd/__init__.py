@@ -6,7 +6,7 @@ device pointers and the current torch stream to the C ABI declared in
 ``include/mdt.h``.  The functions carry the C names without the ``mdt_`` prefix:
 
     medusa_heads, topk_tree_expand, tree_attention, verify_logits,
-    accept_path, kv_compact
+    accept_path, kv_compact, accept_compact (the last two in one launch)
 
 plus the static tree helpers (``Tree``) and workspace queries.  Importing this
 module without a built ``libmdt.so`` raises ImportError: there is no fallback.
@@ -86,6 +86,9 @@ _SIGS = [
                                 c_float, c_float, c_float, c_void_p, c_int, c_void_p]),
     ("mdt_kv_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p,
                                c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
+    ("mdt_accept_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
+                                   c_void_p, c_int, c_float, c_float, c_float, c_void_p, c_int, c_void_p, c_void_p,
+                                   c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
 ]
 
 EXPORTED = [name for name, _, _ in _SIGS]
@@ -385,3 +388,21 @@ def kv_compact(path, n_acc, k_rot, v, cache: KVCache, prefix_len, new_prefix_len
                               _ptr(n_acc), _ptr(k_rot), _ptr(v), ctypes.byref(cache.desc), _ptr(prefix_len),
                               _ptr(new_prefix_len)), "kv_compact")
     return new_prefix_len
+
+
+def accept_compact(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps, delta, temperature, k_rot, v,
+                   cache: KVCache, prefix_len, path=None, n_acc=None, new_prefix_len=None, path_stride=None,
+                   stream=None):
+    """accept_path then kv_compact in one launch; returns (path, n_acc, new_prefix_len)."""
+    B, T, H, Dh = k_rot.shape
+    dev = k_rot.device
+    path_stride = tree.tree.max_depth + 1 if path_stride is None else path_stride
+    path = torch.empty((B, path_stride), dtype=torch.int32, device=dev) if path is None else path
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    new_prefix_len = torch.empty_like(prefix_len) if new_prefix_len is None else new_prefix_len
+    _check(lib.mdt_accept_compact(_stream(stream), _dtype_code(k_rot), B, H, Dh, ctypes.byref(tree.desc), _ptr(stats),
+                                  _ptr(edge), _ptr(tree_tokens), int(mode), float(eps), float(delta),
+                                  float(temperature), _ptr(path), path_stride, _ptr(n_acc), _ptr(k_rot), _ptr(v),
+                                  ctypes.byref(cache.desc), _ptr(prefix_len), _ptr(new_prefix_len)),
+           "accept_compact")
+    return path, n_acc, new_prefix_len

@@ -228,7 +228,7 @@ struct AttnArgs {
 template <int NWB>
 __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     constexpr int NT = 64 * NWB;
-    constexpr int PPT = kTile * (kDh / 8) / NT;  // 16-byte K (and V) pieces per thread per tile
+    constexpr int PPT = kTile * (kDh / 8) / NT;  // 16-byte K pieces per thread per tile
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) bf16_t Vt[kDh * kVStride];
     __shared__ float2 cs[(MDT_MAX_HEADS + 1) * (kDh / 2)];  // cos/sin per (depth, pair)
@@ -246,34 +246,55 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
         cs[e] = rope_cs_table_entry(L + e / (kDh / 2), e % (kDh / 2), A.theta);
 
-    // prefix tile staging through registers: piece c = tid + NT*p is (key c/16, dims 8*(c%16)..)
-    u32x4 kr[PPT], vr[PPT];
-    auto load_prefix = [&](int t0) {
+    // prefix tile staging through registers.  K: piece c = tid + NT*p is (key c/16, dims
+    // 8*(c%16)..), stored row-major.  V: item c is (key pair c%32, dims 8*(c/32)..); the two
+    // keys' values are packed per dimension into one dword, so the transposed LDS writes of
+    // a wave hit consecutive dwords.
+    constexpr int VPT = (kTile / 2) * (kDh / 8) / NT > 0 ? (kTile / 2) * (kDh / 8) / NT : 1;
+    // PF register slots: the PF tiles after the current one are in flight while it runs
+    constexpr int PF = NWB >= 16 ? 1 : 2;
+    u32x4 kr[PF][PPT], va[PF][VPT], vb[PF][VPT];
+    auto load_prefix = [&](int t0, int slot) {
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int c = tid + NT * p;
             const int j = t0 + (c >> 4), dc = c & 15;
-            kr[p] = u32x4{0, 0, 0, 0};
-            vr[p] = u32x4{0, 0, 0, 0};
+            kr[slot][p] = u32x4{0, 0, 0, 0};
             if (j < j_end) {
                 const long off = kv_offset(A.cache, b, j, h, H, kDh);
-                if (off >= 0) {
-                    kr[p] = *(const u32x4*)(Kg + off + 8 * dc);
-                    vr[p] = *(const u32x4*)(Vg + off + 8 * dc);
+                if (off >= 0) kr[slot][p] = *(const u32x4*)(Kg + off + 8 * dc);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < VPT; ++p) {
+            const int c = tid + NT * p;
+            const int j = t0 + 2 * (c & 31), dc = c >> 5;
+            va[slot][p] = vb[slot][p] = u32x4{0, 0, 0, 0};
+            if (c < (kTile / 2) * (kDh / 8)) {
+                if (j < j_end) {
+                    const long off = kv_offset(A.cache, b, j, h, H, kDh);
+                    if (off >= 0) va[slot][p] = *(const u32x4*)(Vg + off + 8 * dc);
+                }
+                if (j + 1 < j_end) {
+                    const long off = kv_offset(A.cache, b, j + 1, h, H, kDh);
+                    if (off >= 0) vb[slot][p] = *(const u32x4*)(Vg + off + 8 * dc);
                 }
             }
         }
     };
-    auto store_piece = [&](int key, int dc, const u32x4& kv, const u32x4& vv) {
-        *(u32x4*)(Ks + key * kKStride + 8 * dc) = kv;
-        bf16_t* vt = Vt + (8 * dc) * kVStride + key;
+    auto store_k = [&](int key, int dc, const u32x4& kv) { *(u32x4*)(Ks + key * kKStride + 8 * dc) = kv; };
+    // keys 2*kp, 2*kp+1, dims 8*dc .. 8*dc+7 into the transposed V tile
+    auto store_v_pair = [&](int kp, int dc, const u32x4& v0, const u32x4& v1) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            vt[(2 * t) * kVStride] = (bf16_t)(vv[t] & 0xffffu);
-            vt[(2 * t + 1) * kVStride] = (bf16_t)(vv[t] >> 16);
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t sh = 16 * (t & 1);
+            const uint32_t lo = (v0[t >> 1] >> sh) & 0xffffu, hi = (v1[t >> 1] >> sh) & 0xffffu;
+            ((uint32_t*)(Vt + (8 * dc + t) * kVStride))[kp] = lo | (hi << 16);
         }
     };
-    if (j_begin < j_end) load_prefix(j_begin);
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+        if (j_begin + s * kTile < j_end) load_prefix(j_begin + s * kTile, s);
     __syncthreads();  // cos/sin table ready
 
     // this wave's 16 queries, rotated, as the B operand of S^T = K Q^T:
@@ -363,17 +384,28 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
         }
     };
 
-    // prefix keys of this split: register prefetch of the next tile while the current one runs
-    for (int t0 = j_begin; t0 < j_end; t0 += kTile) {
-        __syncthreads();
+    // prefix keys of this split
+    for (int t0 = j_begin; t0 < j_end; t0 += PF * kTile) {
 #pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int c = tid + NT * p;
-            store_piece(c >> 4, c & 15, kr[p], vr[p]);
+        for (int half = 0; half < PF; ++half) {
+            const int tt = t0 + half * kTile;
+            if (tt < j_end) {
+                __syncthreads();
+#pragma unroll
+                for (int p = 0; p < PPT; ++p) {
+                    const int c = tid + NT * p;
+                    store_k(c >> 4, c & 15, kr[half][p]);
+                }
+#pragma unroll
+                for (int p = 0; p < VPT; ++p) {
+                    const int c = tid + NT * p;
+                    if (c < (kTile / 2) * (kDh / 8)) store_v_pair(c & 31, c >> 5, va[half][p], vb[half][p]);
+                }
+                __syncthreads();
+                if (tt + PF * kTile < j_end) load_prefix(tt + PF * kTile, half);
+                attend_tile(tt, j_end - tt, false);
+            }
         }
-        __syncthreads();
-        if (t0 + kTile < j_end) load_prefix(t0 + kTile);
-        attend_tile(t0, j_end - t0, false);
     }
 
     // tree keys: rotate k at L + depth, store k_rot, attend under the bitmask
@@ -382,19 +414,24 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
             __syncthreads();
             for (int c = tid; c < kTile * 8; c += NT) {
                 const int key = c >> 3, dc = c & 7, j = tb + key;
-                u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0}, vlo = {0, 0, 0, 0}, vhi = {0, 0, 0, 0};
+                u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
                 if (j < T) {
                     const long node = (((long)b * T + j) * H + h) * kDh;
                     klo = *(const u32x4*)(A.k + node + 8 * dc);
                     khi = *(const u32x4*)(A.k + node + 64 + 8 * dc);
-                    vlo = *(const u32x4*)(A.v + node + 8 * dc);
-                    vhi = *(const u32x4*)(A.v + node + 64 + 8 * dc);
                     rotate8(klo, khi, cs + min(max(A.depth[j], 0), A.max_depth) * (kDh / 2), 8 * dc);
                     *(u32x4*)(A.k_rot + node + 8 * dc) = klo;
                     *(u32x4*)(A.k_rot + node + 64 + 8 * dc) = khi;
                 }
-                store_piece(key, dc, klo, vlo);
-                store_piece(key, dc + 8, khi, vhi);
+                store_k(key, dc, klo);
+                store_k(key, dc + 8, khi);
+            }
+            for (int c = tid; c < (kTile / 2) * (kDh / 8); c += NT) {
+                const int kp = c & 31, dc = c >> 5, j = tb + 2 * kp;
+                u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+                if (j < T) v0 = *(const u32x4*)(A.v + (((long)b * T + j) * H + h) * kDh + 8 * dc);
+                if (j + 1 < T) v1 = *(const u32x4*)(A.v + (((long)b * T + j + 1) * H + h) * kDh + 8 * dc);
+                store_v_pair(kp, dc, v0, v1);
             }
             __syncthreads();
             attend_tile(tb, min(kTile, T - tb), true);

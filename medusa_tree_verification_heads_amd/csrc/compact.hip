@@ -10,28 +10,11 @@
 // with 16-byte vector moves.  Every workgroup of a sequence first validates the
 // whole sequence (path nodes, length, destination slots, pages), so either the
 // full path is written or nothing of it.
-#include "common.h"
+#include "kv_slot.h"
 
 namespace {
 
-struct Cache {
-    void* k;
-    void* v;
-    const int32_t* table;
-    int layout, capacity, page_size, max_pages, num_pages;
-};
-
-__device__ __forceinline__ long slot_row(const Cache& c, int b, int slot) {
-    if (slot < 0 || slot >= c.capacity) return -1;
-    if (c.layout == MDT_KV_CONTIG) return (long)b * c.capacity + slot;
-    const int pg = slot / c.page_size;
-    if (pg >= c.max_pages) return -1;
-    const int page = c.table[(long)b * c.max_pages + pg];
-    if (page < 0 || page >= c.num_pages) return -1;
-    return (long)page * c.page_size + slot % c.page_size;
-}
-
-__global__ __launch_bounds__(256) void compact_kernel(Cache cache, const int32_t* __restrict__ path, int path_stride,
+__global__ __launch_bounds__(256) void compact_kernel(KvSlots cache, const int32_t* __restrict__ path, int path_stride,
                                                       const int32_t* __restrict__ n_acc, const uint4* __restrict__ k_rot,
                                                       const uint4* __restrict__ v, int T, int row_vec,
                                                       const int32_t* __restrict__ prefix_len,
@@ -60,10 +43,9 @@ __global__ __launch_bounds__(256) void compact_kernel(Cache cache, const int32_t
 
 }  // namespace
 
-extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, int H, int Dh, const int32_t* path,
-                                     int path_stride, const int32_t* n_acc, const void* k_rot, const void* v,
-                                     const mdt_kv_cache* cache, const int32_t* prefix_len,
-                                     int32_t* new_prefix_len) {
+mdt_status mdt_check_compact_args(mdt_dtype dt, int B, int T, int H, int Dh, int path_stride, const void* k_rot,
+                                  const void* v, const mdt_kv_cache* cache, const int32_t* prefix_len,
+                                  const int32_t* new_prefix_len, KvSlots* slots, int* row_vec) {
     MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
     MDT_REQUIRE(B >= 1 && B <= 65535 && T >= 1 && T <= MDT_MAX_NODES && H >= 1 && Dh >= 1, MDT_ERR_SHAPE,
                 "bad shape B=%d T=%d H=%d Dh=%d", B, T, H, Dh);
@@ -71,7 +53,7 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
     const size_t row_bytes = (size_t)H * Dh * (dt == MDT_BF16 ? 2 : 4);
     MDT_REQUIRE(row_bytes % 16 == 0, MDT_ERR_SHAPE, "H*Dh*element size must be a multiple of 16 bytes");
     MDT_REQUIRE(cache, MDT_ERR_NULL, "cache is NULL");
-    MDT_REQUIRE(path && n_acc && k_rot && v && prefix_len && new_prefix_len && cache->k && cache->v, MDT_ERR_NULL,
+    MDT_REQUIRE(k_rot && v && prefix_len && new_prefix_len && cache->k && cache->v, MDT_ERR_NULL,
                 "a tensor pointer is NULL");
     MDT_REQUIRE(mdt_aligned16(k_rot) && mdt_aligned16(v) && mdt_aligned16(cache->k) && mdt_aligned16(cache->v),
                 MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -84,9 +66,22 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
         MDT_REQUIRE(cache->layout == MDT_KV_CONTIG, MDT_ERR_VALUE, "unknown cache layout %d", cache->layout);
         MDT_REQUIRE(cache->capacity >= 0, MDT_ERR_SHAPE, "capacity must be >= 0");
     }
-    Cache c{cache->k, cache->v, cache->page_table, cache->layout, cache->capacity, cache->page_size,
-            cache->max_pages, cache->num_pages};
-    const int row_vec = (int)(row_bytes / 16);
+    *slots = KvSlots{cache->k, cache->v, cache->page_table, cache->layout, cache->capacity, cache->page_size,
+                     cache->max_pages, cache->num_pages};
+    *row_vec = (int)(row_bytes / 16);
+    return MDT_OK;
+}
+
+extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, int H, int Dh, const int32_t* path,
+                                     int path_stride, const int32_t* n_acc, const void* k_rot, const void* v,
+                                     const mdt_kv_cache* cache, const int32_t* prefix_len,
+                                     int32_t* new_prefix_len) {
+    KvSlots c;
+    int row_vec = 0;
+    mdt_status st = mdt_check_compact_args(dt, B, T, H, Dh, path_stride, k_rot, v, cache, prefix_len,
+                                           new_prefix_len, &c, &row_vec);
+    if (st != MDT_OK) return st;
+    MDT_REQUIRE(path && n_acc, MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_LAUNCH("compact_kernel", compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path,
                path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
     return mdt_launched("compact_kernel");

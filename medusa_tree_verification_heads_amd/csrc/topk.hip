@@ -8,10 +8,19 @@
 // Selection is a total order: larger value first, equal values by smaller index.
 // A wave selects its k best elements in k rounds; each round every lane offers
 // its best element that comes after the previous winner, and a DPP row-op
-// reduction picks the winner.  Stage A: every workgroup reduces a 2048-element
-// slice of one row to k candidates (four waves, then one merge wave).  Stage B:
-// one workgroup per sequence, one wave per head row merges the slices' candidates
-// and then all threads fill the tree tokens and positions.
+// reduction picks the winner.
+//
+// Stage A: every workgroup reduces a 2048-element slice of one row to k
+// candidates.  Rounds over all 2048 elements would cost k full scans, so a
+// threshold first discards almost everything: in each wave the k-th largest of
+// the 64 lane maxima (counted with multiplicity) is a value that at least k of the
+// wave's elements reach, so the slice's k best all lie at or above the largest of
+// the four wave thresholds.  The elements that reach it (typically little more
+// than k) are packed into LDS and one wave selects among them.  If more than
+// kCap elements reach it (many equal values), the workgroup falls back to rounds
+// over every element.  Stage B: one workgroup per sequence, one wave per head row
+// merges the slices' candidates and then all threads fill the tree tokens and
+// positions.
 #include <climits>
 
 #include "common.h"
@@ -20,6 +29,7 @@ namespace {
 
 constexpr int kSlice = 2048;          // elements per stage-A workgroup
 constexpr int kPerLaneA = kSlice / 256;
+constexpr int kCap = 256;             // threshold survivors a stage-A workgroup keeps
 constexpr int kMaxPerLaneB = 8;       // stage-B candidates per lane
 
 struct Cand {
@@ -50,23 +60,103 @@ __device__ void wave_select(const float (&v)[E], const int (&idx)[E], int k, Can
     }
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float v) {
+    const int vb = __builtin_bit_cast(int, v);
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(vb, vb, CTRL, ROW_MASK, 0xf, false)));
+}
+
+// Maximum over the wave, uniform (same DPP sequence as wave_argmax_dpp).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = dpp_max_step<0xB1, 0xf>(v);
+    v = dpp_max_step<0x4E, 0xf>(v);
+    v = dpp_max_step<0x141, 0xf>(v);
+    v = dpp_max_step<0x140, 0xf>(v);
+    v = dpp_max_step<0x142, 0xa>(v);
+    v = dpp_max_step<0x143, 0xc>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// k-th largest of the lanes' m, equal values counted separately (-inf if the wave
+// holds fewer than k finite values).
+__device__ float wave_kth_largest(float m, int k) {
+    float t = -INFINITY;
+    int cnt = 0;
+    for (int r = 0; r < k; ++r) {
+        const float mx = wave_max_dpp(m);
+        t = mx;
+        cnt += __popcll(__ballot(m == mx));
+        if (cnt >= k || mx == -INFINITY) break;
+        if (m == mx) m = -INFINITY;
+    }
+    return t;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
 __global__ __launch_bounds__(256) void topk_slices(const float* __restrict__ logits, int V, int k, int nslice,
                                                    Cand* __restrict__ cand) {
+    __shared__ Cand surv[kCap];
     __shared__ Cand wave_best[4 * MDT_MAX_TOPK];
+    __shared__ float wave_t[4];
+    __shared__ int n_surv;
     const int row = blockIdx.y;
     const int slice = blockIdx.x;
     const float* x = logits + (size_t)row * V;
-    const int base = slice * kSlice;
-    float v[kPerLaneA];
-    int idx[kPerLaneA];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave w owns elements base + w*512 + [0, 512): coalesced 256-byte rows
+    const int base = slice * kSlice + wave * (kSlice / 4) + lane;
+    float v[kPerLaneA];
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kPerLaneA; ++j) {
-        // wave w owns elements base + w*512 + [0, 512): coalesced 256-byte rows
-        const int e = base + wave * (kSlice / 4) + j * 64 + lane;
+        const int e = base + 64 * j;
         v[j] = e < V ? x[e] : -INFINITY;
-        idx[j] = e < V ? e : INT_MAX;
+        m = fmaxf(m, v[j]);
     }
+    const float tw = wave_kth_largest(m, k);
+    if (lane == 0) wave_t[wave] = tw;
+    if (threadIdx.x == 0) n_surv = 0;
+    __syncthreads();
+    const float thr = fmaxf(fmaxf(wave_t[0], wave_t[1]), fmaxf(wave_t[2], wave_t[3]));
+    int nw = 0;
+#pragma unroll
+    for (int j = 0; j < kPerLaneA; ++j) nw += __popcll(__ballot(base + 64 * j < V && v[j] >= thr));
+    int at = 0;
+    if (lane == 0 && nw > 0) at = atomicAdd(&n_surv, nw);
+    at = __shfl(at, 0, 64);
+#pragma unroll
+    for (int j = 0; j < kPerLaneA; ++j) {
+        const int e = base + 64 * j;
+        const bool keep = e < V && v[j] >= thr;
+        const uint64_t bal = __ballot(keep);
+        const int slot = at + lanes_below(bal);
+        if (keep && slot < kCap) surv[slot] = Cand{v[j], e};
+        at += __popcll(bal);
+    }
+    __syncthreads();
+    const int n = n_surv;  // uniform over the workgroup
+    Cand* out = cand + ((size_t)row * nslice + slice) * k;
+    if (n <= kCap) {
+        if (wave == 0) {
+            float cv[kCap / 64];
+            int ci[kCap / 64];
+#pragma unroll
+            for (int j = 0; j < kCap / 64; ++j) {
+                const int c = lane + 64 * j;
+                cv[j] = c < n ? surv[c].v : -INFINITY;
+                ci[j] = c < n ? surv[c].i : INT_MAX;
+            }
+            wave_select<kCap / 64>(cv, ci, k, out);
+        }
+        return;
+    }
+    // many equal values at the threshold: rounds over every element
+    int idx[kPerLaneA];
+#pragma unroll
+    for (int j = 0; j < kPerLaneA; ++j) idx[j] = base + 64 * j < V ? base + 64 * j : INT_MAX;
     wave_select<kPerLaneA>(v, idx, k, wave_best + wave * k);
     __syncthreads();
     if (wave == 0) {
@@ -78,10 +168,11 @@ __global__ __launch_bounds__(256) void topk_slices(const float* __restrict__ log
             mv[j] = c < 4 * k ? wave_best[c].v : -INFINITY;
             mi[j] = c < 4 * k ? wave_best[c].i : INT_MAX;
         }
-        wave_select<2>(mv, mi, k, cand + ((size_t)row * nslice + slice) * k);
+        wave_select<2>(mv, mi, k, out);
     }
 }
 
+template <int E>
 __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, int nslice,
                                   const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
                                   const int32_t* __restrict__ rank, int T, const int32_t* __restrict__ prefix_len,
@@ -94,15 +185,15 @@ __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, 
         const int row = b * K1 + wave;
         const Cand* c = cand + (size_t)row * nslice * k;
         const int n = nslice * k;
-        float v[kMaxPerLaneB];
-        int idx[kMaxPerLaneB];
+        float v[E];
+        int idx[E];
 #pragma unroll
-        for (int j = 0; j < kMaxPerLaneB; ++j) {
+        for (int j = 0; j < E; ++j) {
             const int e = lane + 64 * j;
             v[j] = e < n ? c[e].v : -INFINITY;
             idx[j] = e < n ? c[e].i : INT_MAX;
         }
-        wave_select<kMaxPerLaneB>(v, idx, k, best + wave * k);
+        wave_select<E>(v, idx, k, best + wave * k);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < K1 * k; e += blockDim.x) {
@@ -154,7 +245,12 @@ extern "C" mdt_status mdt_topk_tree_expand(void* stream, int B, int K, int V, in
     MDT_LAUNCH("topk_slices", topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);
     st = mdt_launched("topk_slices");
     if (st != MDT_OK) return st;
-    MDT_LAUNCH("topk_merge_expand", topk_merge_expand, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns,
-               tree->parent, tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
+    // candidates per lane in the merge: 1, 2, 4 or 8
+    const int per_lane = (ns * k_cfg + 63) / 64;
+    auto kern = per_lane <= 1 ? topk_merge_expand<1>
+              : per_lane <= 2 ? topk_merge_expand<2>
+              : per_lane <= 4 ? topk_merge_expand<4> : topk_merge_expand<kMaxPerLaneB>;
+    MDT_LAUNCH("topk_merge_expand", kern, dim3(B), dim3(64 * K1), 0, s, cand, K1, k_cfg, ns, tree->parent,
+               tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
     return mdt_launched("topk_merge_expand");
 }

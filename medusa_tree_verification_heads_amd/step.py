@@ -6,6 +6,7 @@ workspace once, and ``run()`` enqueues
     medusa_heads -> topk_tree_expand -> tree_attention -> verify_logits
     -> accept_path -> kv_compact
 
+(the last two as the single launch accept_compact unless ``fused_tail=False``)
 with no host synchronisation, so a step can also be captured in a HIP graph.
 The order is the information flow of the summary page ("Medusa: Simple LLM
 Inference Acceleration Framework with Multiple Decoding Heads", section 3.2).
@@ -16,7 +17,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_path, kv_compact, medusa_heads,
+from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path, kv_compact,
+               medusa_heads,
                medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace)
 
@@ -30,8 +32,10 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
 
 class VerifyStep:
     def __init__(self, w, inp: dict, mode: str = "greedy", temperature: float = 0.0, eps: float = 0.09,
-                 delta: float = 0.3, device="cuda", want_logits: bool = False, tree: Tree = None):
+                 delta: float = 0.3, device="cuda", want_logits: bool = False, tree: Tree = None,
+                 fused_tail: bool = True):
         self.w = w
+        self.fused_tail = fused_tail
         self.mode = GREEDY if mode == "greedy" else TYPICAL
         self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
         dev = torch.device(device)
@@ -75,6 +79,11 @@ class VerifyStep:
         x = self.o.view(w.B * self.tree.T, w.d)
         verify_logits(x, t["Wlm"], self.tree, self.tokens, self.temperature, stats=self.stats, edge=self.edge,
                       logits=self.vlogits, want_logits=self.vlogits is not None, ws=self.ws_verify, stream=stream)
+        if self.fused_tail:
+            accept_compact(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta,
+                           self.temperature, self.k_rot, t["v"], self.cache, self.prefix_len, path=self.path,
+                           n_acc=self.n_acc, new_prefix_len=self.new_len, stream=stream)
+            return
         accept_path(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta, self.temperature,
                     path=self.path, n_acc=self.n_acc, stream=stream)
         kv_compact(self.path, self.n_acc, self.k_rot, t["v"], self.cache, self.prefix_len, self.new_len,

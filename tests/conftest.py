@@ -14,8 +14,8 @@ def _ensure_built():
     """Tests load the in-tree libmdt.so; build it once if nothing is built yet."""
     lib = os.path.join(ROOT, "medusa_tree_verification_heads_amd", "libmdt.so")
     if not os.path.exists(lib):
-        from medusa_tree_verification_heads_amd import build as _b
-        _b.build(verbose=False)
+        from __graft_entry__ import _builder
+        _builder().build(verbose=False)
 
 
 _ensure_built()

@@ -168,6 +168,47 @@ def test_stage_topk_from_oracle_logits(name):
     assert np.array_equal(val.cpu().numpy(), np.take_along_axis(l32, ref, axis=2))
 
 
+def _tie_rows(V, rng):
+    """Rows that stress the selection: coarse quantisation (ties at the top), all
+    equal, three values only, -inf entries, the best values packed in one slice,
+    and a row sorted in ascending order."""
+    rows = [np.round(rng.standard_normal(V) * 4) / 4,
+            np.zeros(V),
+            rng.integers(0, 3, V).astype(np.float64),
+            np.where(rng.random(V) < 0.5, -np.inf, rng.standard_normal(V)),
+            np.concatenate([rng.standard_normal(max(V - 100, 0)) - 10, rng.standard_normal(min(V, 100))]),
+            np.arange(V, dtype=np.float64)]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("V,k", [(3001, 10), (32000, 10), (32000, 32), (50001, 16), (37, 32)])
+def test_stage_topk_ties_and_fallback(V, k):
+    """Exact order (value desc, index asc) on tie-heavy rows, including rows where
+    far more elements than the survivor capacity reach the threshold."""
+    import medusa_tree_verification_heads_amd as mdt
+    from oracle import step as ostep
+    note(f"topk ties V={V} k={k}")
+    rng = np.random.default_rng(V * 100 + k)
+    K = 4
+    rows = _tie_rows(V, rng)
+    B = 2
+    logits = np.concatenate([rows, rows[::-1], rows[:-2] * -1.0])[: B * (K + 1)].reshape(B, K + 1, V)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    tree = mdt.Tree.scored(K, min(k, 10), 24).to_device("cuda")
+    pl = torch.tensor([5, 9], dtype=torch.int32).cuda()
+    idx, val, tok, pos = mdt.topk_tree_expand(torch.from_numpy(logits).cuda(), k, tree, pl)
+    torch.cuda.synchronize()
+    idx, val, tok = idx.cpu().numpy(), val.cpu().numpy(), tok.cpu().numpy()
+    for b in range(B):
+        for r in range(K + 1):
+            ref_i, ref_v = ostep.topk(logits[b, r].astype(np.float64), k)
+            assert idx[b, r].tolist() == ref_i.tolist(), (b, r)
+            assert np.array_equal(val[b, r], logits[b, r, ref_i]), (b, r)
+        t = tree.tree
+        for i in range(t.T):
+            assert tok[b, i] == idx[b, t.depth[i], t.rank[i]]
+
+
 @pytest.mark.parametrize("name,run_idx", RUNS)
 def test_stage_verify_accept_from_oracle_x(name, run_idx):
     import medusa_tree_verification_heads_amd as mdt

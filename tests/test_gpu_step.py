@@ -13,12 +13,12 @@ pytestmark = pytest.mark.gpu
 KEYS = ("logits", "topk_idx", "tokens", "pos", "o", "k_rot", "stats", "edge", "path", "n_acc", "new_len", "Kc", "Vc")
 
 
-def _make(name, run_idx=1):
+def _make(name, run_idx=1, fused_tail=True):
     from medusa_tree_verification_heads_amd.step import VerifyStep
     w, inp = case_inputs(name)
     run = w.accept[min(run_idx, len(w.accept) - 1)]
-    note(f"step {name} {run}")
-    return VerifyStep(w, inp, run.mode, run.temperature, run.eps, run.delta)
+    note(f"step {name} {run} fused_tail={fused_tail}")
+    return VerifyStep(w, inp, run.mode, run.temperature, run.eps, run.delta, fused_tail=fused_tail)
 
 
 def _same(a, b):
@@ -34,6 +34,17 @@ def test_repeated_steps_are_bit_identical(name):
     for _ in range(3):
         s.run()
         _same(first, s.outputs())
+
+
+@pytest.mark.parametrize("run_idx", [0, 1])
+@pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged", "33b-mini", "tiny-fp32-T10"])
+def test_fused_tail_matches_separate_calls(name, run_idx):
+    """accept_compact writes exactly what accept_path then kv_compact write."""
+    sep = _make(name, run_idx, fused_tail=False)
+    sep.run()
+    fused = _make(name, run_idx, fused_tail=True)
+    fused.run()
+    _same(sep.outputs(), fused.outputs())
 
 
 @pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged"])

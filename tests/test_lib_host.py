@@ -159,3 +159,12 @@ def test_verify_accept_compact_validation():
     c.layout, c.capacity, c.k, c.v = 0, 1029, 1 << 20, 1 << 20
     assert k(None, 1, 1, 64, 3, 5, P, 5, P, P, P, ctypes.byref(c), P, P) == -2           # row not 16-byte multiple
     assert k(None, 2, 1, 64, 32, 128, P, 5, P, P, P, ctypes.byref(c), P, P) == -3
+    ac = mdt.lib.mdt_accept_compact
+    def fused(dt=1, H=32, Dh=128, mode=1, eps=0.09, stride=5, cache=c, kr=P):
+        return ac(None, dt, 1, H, Dh, ctypes.byref(d), P, P, P, mode, eps, 0.3, 0.7, P, stride, P, kr, P,
+                  ctypes.byref(cache), P, P)
+    assert fused(mode=3) == -6 and fused(eps=0.0) == -6      # the accept_path checks
+    assert fused(stride=4) == -2
+    assert fused(dt=1, H=1, Dh=3) == -2                       # the kv_compact checks
+    assert fused(dt=2) == -3
+    assert fused(kr=None) == -1 and fused(kr=MIS) == -4
