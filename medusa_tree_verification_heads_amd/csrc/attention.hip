@@ -13,7 +13,8 @@
 //     64-key K and V tiles are staged in LDS (V transposed), the next tile already
 //     in flight in registers, and both products run on MFMA 16x16x32 bf16:
 //     S^T = K Q^T, then O^T = V^T P^T, so the probabilities stay in registers
-//     between the two.  Online softmax keeps (max, sum) per query.  One extra
+//     between the two.  Online softmax keeps (max, sum) per query, the max in
+//     log2 units (scores scaled by log2 e, exponentials by exp2).  One extra
 //     workgroup per (sequence, head) rotates the tree keys at their depth
 //     positions (writing k_rot, which is what gets cached) and attends to them
 //     under the ancestor-or-self bitmask.  Rotation angles come from a per-depth
@@ -36,6 +37,8 @@ constexpr int kDh = 128;           // head dim of the MFMA path
 constexpr int kKStride = kDh + 8;  // LDS row stride of K tile (elements)
 constexpr int kVStride = kTile + 4;  // LDS row stride of transposed V tile (elements)
 constexpr int kMinTilesPerSplit = 4;
+constexpr int kMaxSplitPages = 4096;  // page-table entries a workgroup stages in LDS
+constexpr int kMaxTilesPerSplit = (kMaxSplitPages - 2) * 1 / kTile;  // holds for page_size >= 1
 
 struct KV {
     const void* k;
@@ -173,8 +176,12 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even, one v_cvt_pk_bf16_f32), lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float elt(const u32x4& v, int t) {
@@ -182,10 +189,15 @@ __device__ __forceinline__ float elt(const u32x4& v, int t) {
     return __uint_as_float((t & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// cos/sin of pos * theta^(-2m/Dh): the angle is formed and reduced to [-pi, pi] in
-// double precision, then evaluated in single precision.
-__device__ __forceinline__ float2 rope_cs_table_entry(int pos, int m, double theta) {
-    const double a = (double)pos * pow(theta, -2.0 * (double)m / (double)kDh);
+// theta^(-2m/Dh), the rotation frequency of pair m (double precision)
+__device__ __forceinline__ double rope_inv_freq(int m, double theta) {
+    return pow(theta, -2.0 * (double)m / (double)kDh);
+}
+
+// cos/sin of pos * inv_freq: the angle is formed and reduced to [-pi, pi] in double
+// precision, then evaluated in single precision.
+__device__ __forceinline__ float2 rope_cs_table_entry(int pos, double inv_freq) {
+    const double a = (double)pos * inv_freq;
     const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
     float s, c;
     sincosf((float)r, &s, &c);
@@ -225,13 +237,24 @@ struct AttnArgs {
 // Workgroups 0..nsplit-1 attend to prefix key ranges; workgroup nsplit rotates the tree
 // keys (writing k_rot) and attends to them, masked by the ancestor-or-self bitmask.
 // Grid (nsplit + 1, H, B); all partials are merged by attn_combine.
-template <int NWB>
+//
+// Global loads are never issued under a branch and a loaded register is not touched
+// before it is needed: the compiler's load counter is in-order, so either would make
+// a wave wait for every load in flight.  Prefix pieces outside the split or on an
+// unmapped page read the first 16 bytes of q instead (always present) and are zeroed
+// when stored (a validity bit per piece); the pages of a paged cache are looked up in LDS.
+template <int NWB, bool PAGED>
 __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     constexpr int NT = 64 * NWB;
     constexpr int PPT = kTile * (kDh / 8) / NT;  // 16-byte K pieces per thread per tile
+    constexpr int kVItems = (kTile / 2) * (kDh / 8);  // V items: (key pair, 8 dims)
+    constexpr int VPT = kVItems / NT > 0 ? kVItems / NT : 1;
+    static_assert(PPT + 2 * VPT <= 32, "validity bits per slot");
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) bf16_t Vt[kDh * kVStride];
     __shared__ float2 cs[(MDT_MAX_HEADS + 1) * (kDh / 2)];  // cos/sin per (depth, pair)
+    __shared__ double inv_freq[kDh / 2];
+    __shared__ int pages[PAGED ? kMaxSplitPages : 1];        // physical page of each page of the split
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const bool tree_split = split == A.nsplit;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,76 +266,128 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     const float scale = 1.f / sqrtf((float)kDh);
     const bf16_t* Kg = (const bf16_t*)A.cache.k;
     const bf16_t* Vg = (const bf16_t*)A.cache.v;
-    for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
-        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), e % (kDh / 2), A.theta);
+    const int psz = PAGED ? A.cache.page_size : 1;
+    const int pg0 = j_begin / psz;
+
+    // this wave's 16 queries (loaded first, so that waiting for them waits for nothing else):
+    // lane holds query qi, dims 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
+    const int qi = wave * 16 + c16;
+    const bool q_ok = qi < T;
+    const int qc = q_ok ? qi : 0;
+    u32x4 bq[4];
+    uint64_t qa[MDT_MAX_NODES / 64];
+    {
+        const long node = (((long)b * T + qc) * H + h) * kDh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
+#pragma unroll
+        for (int w = 0; w < MDT_MAX_NODES / 64; ++w) qa[w] = A.anc[(long)qc * A.W + min(w, A.W - 1)];
+    }
+    const int dq_raw = A.depth[qc];
+
+    if (PAGED) {
+        const int np = j_end > j_begin ? (j_end - 1) / psz - pg0 + 1 : 0;  // <= kMaxSplitPages (host plan)
+        for (int e = tid; e < np; e += NT) {
+            const int pg = pg0 + e;
+            const int page = pg < A.cache.max_pages ? A.cache.table[(long)b * A.cache.max_pages + pg] : -1;
+            pages[e] = (page >= 0 && page < A.cache.num_pages) ? page : -1;
+        }
+        __syncthreads();
+    }
+    // element offset of prefix key j of this split, or -1 (outside the split, unmapped)
+    auto key_off = [&](int j) -> long {
+        if (j >= j_end) return -1;
+        if (!PAGED) return (((long)b * A.cache.capacity + j) * H + h) * kDh;
+        const int page = pages[j / psz - pg0];
+        return page < 0 ? -1 : (((long)page * psz + j % psz) * H + h) * kDh;
+    };
 
     // prefix tile staging through registers.  K: piece c = tid + NT*p is (key c/16, dims
     // 8*(c%16)..), stored row-major.  V: item c is (key pair c%32, dims 8*(c/32)..); the two
     // keys' values are packed per dimension into one dword, so the transposed LDS writes of
-    // a wave hit consecutive dwords.
-    constexpr int VPT = (kTile / 2) * (kDh / 8) / NT > 0 ? (kTile / 2) * (kDh / 8) / NT : 1;
-    // PF register slots: the PF tiles after the current one are in flight while it runs
+    // a wave hit consecutive dwords.  PF register slots: the PF tiles after the current
+    // one are in flight while it runs.
     constexpr int PF = NWB >= 16 ? 1 : 2;
     u32x4 kr[PF][PPT], va[PF][VPT], vb[PF][VPT];
+    uint32_t valid[PF];
+    const int row_elems = H * kDh;  // elements between consecutive keys of a contiguous cache
     auto load_prefix = [&](int t0, int slot) {
+        uint32_t m = 0;
+        // contiguous cache: the tile's keys are consecutive rows from this base
+        const long tile_base = (((long)b * A.cache.capacity + t0) * H + h) * kDh;
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int c = tid + NT * p;
-            const int j = t0 + (c >> 4), dc = c & 15;
-            kr[slot][p] = u32x4{0, 0, 0, 0};
-            if (j < j_end) {
-                const long off = kv_offset(A.cache, b, j, h, H, kDh);
-                if (off >= 0) kr[slot][p] = *(const u32x4*)(Kg + off + 8 * dc);
-            }
+            const int key = c >> 4;
+            const long off = PAGED ? key_off(t0 + key) : (t0 + key < j_end ? tile_base + key * row_elems : -1);
+            m |= (off >= 0 ? 1u : 0u) << p;
+            kr[slot][p] = *(const u32x4*)(off >= 0 ? Kg + off + 8 * (c & 15) : A.q);
         }
 #pragma unroll
         for (int p = 0; p < VPT; ++p) {
             const int c = tid + NT * p;
-            const int j = t0 + 2 * (c & 31), dc = c >> 5;
-            va[slot][p] = vb[slot][p] = u32x4{0, 0, 0, 0};
-            if (c < (kTile / 2) * (kDh / 8)) {
-                if (j < j_end) {
-                    const long off = kv_offset(A.cache, b, j, h, H, kDh);
-                    if (off >= 0) va[slot][p] = *(const u32x4*)(Vg + off + 8 * dc);
-                }
-                if (j + 1 < j_end) {
-                    const long off = kv_offset(A.cache, b, j + 1, h, H, kDh);
-                    if (off >= 0) vb[slot][p] = *(const u32x4*)(Vg + off + 8 * dc);
-                }
+            const int key = 2 * (c & 31), dc = c >> 5;
+            const bool item = c < kVItems;
+            long oa, ob;
+            if (PAGED) {
+                oa = item ? key_off(t0 + key) : -1;
+                ob = item ? key_off(t0 + key + 1) : -1;
+            } else {
+                oa = item && t0 + key < j_end ? tile_base + key * row_elems : -1;
+                ob = item && t0 + key + 1 < j_end ? tile_base + (key + 1) * row_elems : -1;
             }
+            m |= (oa >= 0 ? 1u : 0u) << (PPT + 2 * p);
+            m |= (ob >= 0 ? 1u : 0u) << (PPT + 2 * p + 1);
+            va[slot][p] = *(const u32x4*)(oa >= 0 ? Vg + oa + 8 * dc : A.q);
+            vb[slot][p] = *(const u32x4*)(ob >= 0 ? Vg + ob + 8 * dc : A.q);
         }
+        valid[slot] = m;
     };
     auto store_k = [&](int key, int dc, const u32x4& kv) { *(u32x4*)(Ks + key * kKStride + 8 * dc) = kv; };
     // keys 2*kp, 2*kp+1, dims 8*dc .. 8*dc+7 into the transposed V tile
     auto store_v_pair = [&](int kp, int dc, const u32x4& v0, const u32x4& v1) {
+        // dim t of the pair: low halves (t even) or high halves (t odd) of word t/2,
+        // key 2kp in the low 16 bits (one byte permute each)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const uint32_t sh = 16 * (t & 1);
-            const uint32_t lo = (v0[t >> 1] >> sh) & 0xffffu, hi = (v1[t >> 1] >> sh) & 0xffffu;
-            ((uint32_t*)(Vt + (8 * dc + t) * kVStride))[kp] = lo | (hi << 16);
+        for (int t = 0; t < 8; ++t)
+            ((uint32_t*)(Vt + (8 * dc + t) * kVStride))[kp] =
+                __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], (t & 1) ? 0x07060302u : 0x05040100u);
+    };
+    auto store_prefix = [&](int slot) {
+        const u32x4 z{0, 0, 0, 0};
+        const uint32_t m = valid[slot];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int c = tid + NT * p;
+            store_k(c >> 4, c & 15, ((m >> p) & 1u) ? kr[slot][p] : z);
+        }
+#pragma unroll
+        for (int p = 0; p < VPT; ++p) {
+            const int c = tid + NT * p;
+            if (c < kVItems)
+                store_v_pair(c & 31, c >> 5, ((m >> (PPT + 2 * p)) & 1u) ? va[slot][p] : z,
+                             ((m >> (PPT + 2 * p + 1)) & 1u) ? vb[slot][p] : z);
         }
     };
 #pragma unroll
-    for (int s = 0; s < PF; ++s)
-        if (j_begin + s * kTile < j_end) load_prefix(j_begin + s * kTile, s);
-    __syncthreads();  // cos/sin table ready
+    for (int s = 0; s < PF; ++s) load_prefix(j_begin + s * kTile, s);
 
-    // this wave's 16 queries, rotated, as the B operand of S^T = K Q^T:
-    // lane holds query qi, dims 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
-    const int qi = wave * 16 + c16;
-    const bool q_ok = qi < T;
-    u32x4 bq[4];
-    uint64_t qa[MDT_MAX_NODES / 64] = {0, 0, 0, 0};
+    if (tid < kDh / 2) inv_freq[tid] = rope_inv_freq(tid, A.theta);
+    __syncthreads();
+    for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
+        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), inv_freq[e % (kDh / 2)]);
+    __syncthreads();  // cos/sin table ready
     {
-        const long node = (((long)b * T + (q_ok ? qi : 0)) * H + h) * kDh;
+        if (!q_ok)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[s] = q_ok ? *(const u32x4*)(A.q + node + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
-        const int dq = q_ok ? min(max(A.depth[qi], 0), A.max_depth) : 0;
+            for (int s = 0; s < 4; ++s) bq[s] = u32x4{0, 0, 0, 0};
+        const int dq = q_ok ? min(max(dq_raw, 0), A.max_depth) : 0;
         const float2* row = cs + dq * (kDh / 2);
         rotate8(bq[0], bq[2], row, 8 * g);
         rotate8(bq[1], bq[3], row, 32 + 8 * g);
-        if (tree_split && q_ok)
-            for (int w = 0; w < A.W; ++w) qa[w] = A.anc[(long)qi * A.W + w];
+#pragma unroll
+        for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
+            if (!(tree_split && q_ok && w < A.W)) qa[w] = 0;
     }
 
     f32x4 oacc[8];
@@ -320,8 +395,11 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;  // of query qi, replicated over g
 
-    // one staged tile: keys base..base+63 (nvalid of them real); tree tiles use the bitmask
-    auto attend_tile = [&](int base, int nvalid, bool tree) {
+    // One staged tile: keys base..base+63, nvalid of them real.  Scores are kept in log2
+    // units (scale * log2 e folded into one multiply), so the softmax uses exp2.  Full
+    // prefix tiles skip the masking; the last prefix tile and tree tiles (bitmask) do not.
+    const float sl2 = scale * 1.4426950408889634f;
+    auto attend_tile = [&](int base, int nvalid, bool masked) {
         f32x4 sacc[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -331,31 +409,42 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
             for (int s = 0; s < 4; ++s) acc = mfma16(*(const u32x4*)(krow + 32 * s), bq[s], acc);
             sacc[kb] = acc;
         }
-        // tiles start at multiples of 64, so a tree tile reads one word of the query's mask row
-        const int wi = base >> 6;
-        const uint64_t qw = !tree ? ~0ull : (wi == 0 ? qa[0] : wi == 1 ? qa[1] : wi == 2 ? qa[2] : qa[3]);
         float tmax = -INFINITY;
+        if (masked) {
+            // tiles start at multiples of 64, so a tree tile reads one word of the query's mask
+            // row; a prefix tile is only cut at nvalid
+            const int wi = base >> 6;
+            const uint64_t qw = !tree_split ? ~0ull : wi == 0 ? qa[0] : wi == 1 ? qa[1] : wi == 2 ? qa[2] : qa[3];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jj = kb * 16 + 4 * g + e;
-                const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
-                const float sv = ok ? sacc[kb][e] * scale : -INFINITY;
-                sacc[kb][e] = sv;
-                tmax = fmaxf(tmax, sv);
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int jj = kb * 16 + 4 * g + e;
+                    const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
+                    const float sv = ok ? sacc[kb][e] * sl2 : -INFINITY;
+                    sacc[kb][e] = sv;
+                    tmax = fmaxf(tmax, sv);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sacc[kb][e] *= sl2;
+                    tmax = fmaxf(tmax, sacc[kb][e]);
+                }
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m_run, tmax);
         const bool live = m_new != -INFINITY;
-        const float corr = live ? expf(m_run - m_new) : 1.f;
+        const float corr = live ? exp2f(m_run - m_new) : 1.f;
         float tsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = live ? expf(sacc[kb][e] - m_new) : 0.f;
+                const float p = live ? exp2f(sacc[kb][e] - m_new) : 0.f;
                 sacc[kb][e] = p;
                 tsum += p;
             }
@@ -384,27 +473,17 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
         }
     };
 
-    // prefix keys of this split
+    // prefix keys of this split, PF tiles per iteration; a tile past the end is staged as
+    // zeros and not attended, and the tile PF ahead is always requested (a dummy past the end)
     for (int t0 = j_begin; t0 < j_end; t0 += PF * kTile) {
 #pragma unroll
         for (int half = 0; half < PF; ++half) {
             const int tt = t0 + half * kTile;
-            if (tt < j_end) {
-                __syncthreads();
-#pragma unroll
-                for (int p = 0; p < PPT; ++p) {
-                    const int c = tid + NT * p;
-                    store_k(c >> 4, c & 15, kr[half][p]);
-                }
-#pragma unroll
-                for (int p = 0; p < VPT; ++p) {
-                    const int c = tid + NT * p;
-                    if (c < (kTile / 2) * (kDh / 8)) store_v_pair(c & 31, c >> 5, va[half][p], vb[half][p]);
-                }
-                __syncthreads();
-                if (tt + PF * kTile < j_end) load_prefix(tt + PF * kTile, half);
-                attend_tile(tt, j_end - tt, false);
-            }
+            __syncthreads();
+            store_prefix(half);
+            __syncthreads();
+            load_prefix(tt + PF * kTile, half);
+            if (tt < j_end) attend_tile(tt, j_end - tt, j_end - tt < kTile);
         }
     }
 
@@ -465,7 +544,7 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
         const long p = pbase + (long)s * Tpad;
         const float ms = part_ml[p * 2];
         if (ms == -INFINITY) continue;
-        const float wgt = expf(ms - M);
+        const float wgt = exp2f(ms - M);  // maxima are in log2 units
         den += part_ml[p * 2 + 1] * wgt;
         na += part_o[p * kDh + lane] * wgt;
         nb += part_o[p * kDh + lane + 64] * wgt;
@@ -490,6 +569,7 @@ Plan plan(int B, int T, int H, int capacity) {
     if (want < 1) want = 1;
     int tps = (int)((tiles + want - 1) / want);
     if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+    if (tps > kMaxTilesPerSplit) tps = kMaxTilesPerSplit;
     p.tiles_per_split = tps;
     p.nsplit = (tiles + tps - 1) / tps;
     // prefix splits plus one tree split
@@ -556,12 +636,11 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
                (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
                tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth};
     const dim3 grid(p.nsplit + 1, H, B);
-    if (p.nwb == 4)
-        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<4>, grid, dim3(256), 0, s, A);
-    else if (p.nwb == 8)
-        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<8>, grid, dim3(512), 0, s, A);
-    else
-        MDT_LAUNCH("attn_tree_mfma", attn_tree_mfma<16>, grid, dim3(1024), 0, s, A);
+    const bool paged = cache->layout == MDT_KV_PAGED;
+    auto kern = p.nwb == 4 ? (paged ? attn_tree_mfma<4, true> : attn_tree_mfma<4, false>)
+              : p.nwb == 8 ? (paged ? attn_tree_mfma<8, true> : attn_tree_mfma<8, false>)
+                           : (paged ? attn_tree_mfma<16, true> : attn_tree_mfma<16, false>);
+    MDT_LAUNCH("attn_tree_mfma", kern, grid, dim3(64 * p.nwb), 0, s, A);
     st = mdt_launched("attn_tree_mfma");
     if (st != MDT_OK) return st;
     MDT_LAUNCH("attn_combine", attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,

@@ -8,7 +8,8 @@
 // HBM stream of K*d*d + (K+1)*d*V weights.  Each output row is a dot product of a
 // contiguous weight row with an activation vector held in LDS as fp32.  A wave
 // owns two rows at a time; each lane loads 16-byte chunks lane, lane+64, ... of
-// both rows, so a wave instruction reads 1 KiB of contiguous weights per row.
+// both rows, so a wave instruction reads 1 KiB of contiguous weights per row, and
+// the loads of the wave's next segment are in flight while it multiplies.
 //
 // Launch 1 streams W1 (-> a_k = SiLU(u) + h, fp32 in the workspace) together with
 // W_lm (-> logits_0), which only needs h; launch 2 streams W2 (-> logits_1..K).
@@ -25,7 +26,7 @@ constexpr int kLdsBytes = 64 * 1024;
 struct GemvSeg {
     const void* W;        // [nrows][d], storage type
     const void* x;        // activation vectors: x + b * x_bstride (elements)
-    const void* resid;    // SiLU epilogue residual (storage type): resid + b * resid_bstride + row
+    const void* resid;    // SiLU epilogue residual: must be x itself (read from LDS)
     float* out;           // out + b * out_bstride + row
     long x_bstride;
     long resid_bstride;
@@ -90,7 +91,11 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
 }
 
 // STAGE only names the launch (1: W1 + LM head, 2: W2) so that profiles separate the two.
-template <typename WT, int NV, int STAGE>
+// The wave walks (row pair, segment) items in order, a segment being SEG chunks of
+// 16 bytes per lane of both rows (64*SEG chunks per row); the next item's loads are
+// issued before the current item's multiply-adds, so every wave keeps 4*SEG loads in
+// flight without gaps between rows.
+template <typename WT, int NV, int STAGE, int SEG>
 __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
     extern __shared__ float xs[];  // [NV][d]
     const int wg = blockIdx.x;
@@ -108,62 +113,82 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
 
     constexpr int VEC = Chunk<WT>::kElems;
     const int nchunk = d / VEC;
+    const int nseg = (nchunk + 64 * SEG - 1) / (64 * SEG);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r0 = (wg - S.wg_begin) * S.rows_per_wg;
     const int r1 = min(S.nrows, r0 + S.rows_per_wg);
+    const int first = r0 + 2 * wave;  // pairs first, first + 8, ...
+    const int npairs = first < r1 ? (r1 - first + 7) / 8 : 0;
+    const int items = npairs * nseg;
     const WT* W = (const WT*)S.W;
 
-    for (int r = r0 + 2 * wave; r < r1; r += 2 * (kThreads / 64)) {
+    uint4 c0[SEG], c1[SEG], n0[SEG], n1[SEG];
+    // Loads are never under a branch (a load under a branch makes the compiler wait for
+    // every load in flight): addresses are clamped, a tail chunk multiplies as zero, and
+    // a dummy item (real == false) makes all lanes read one 16-byte piece.
+    auto load = [&](int it, bool real, uint4 (&p)[SEG], uint4 (&q)[SEG]) {
+        const int pair = it / nseg, sg = it - pair * nseg;
+        const int r = first + 8 * pair;
         const bool two = r + 1 < r1;
         const uint4* w0 = (const uint4*)(W + (size_t)r * d);
         const uint4* w1 = (const uint4*)(W + (size_t)(two ? r + 1 : r) * d);
-        float acc0[NV], acc1[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
-        int c = lane;
-        // four chunks of each row in flight per iteration
-        for (; c + 192 < nchunk; c += 256) {
-            uint4 a[4], b[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                a[u] = ld_stream(w0 + c + 64 * u);
-                b[u] = ld_stream(w1 + c + 64 * u);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const float* xp = xs + v * d + (c + 64 * u) * VEC;
-                    acc0[v] += Chunk<WT>::dot(a[u], xp);
-                    acc1[v] += Chunk<WT>::dot(b[u], xp);
-                }
+        for (int u = 0; u < SEG; ++u) {
+            const int c = real ? min(sg * 64 * SEG + lane + 64 * u, nchunk - 1) : 0;
+            p[u] = ld_stream(w0 + c);
+            q[u] = ld_stream(w1 + c);
         }
-        for (; c < nchunk; c += 64) {
-            const uint4 a = ld_stream(w0 + c);
-            const uint4 b = ld_stream(w1 + c);
+    };
+    float acc0[NV], acc1[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
+    if (items > 0) load(0, true, c0, c1);
+    for (int it = 0; it < items; ++it) {
+        const bool more = it + 1 < items;
+        load(more ? it + 1 : it, more, n0, n1);
+        const int pair = it / nseg, sg = it - pair * nseg;
+#pragma unroll
+        for (int u = 0; u < SEG; ++u) {
+            const int c = sg * 64 * SEG + lane + 64 * u;
+            const bool in = c < nchunk;
+            const int cc = in ? c : nchunk - 1;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const float* xp = xs + v * d + c * VEC;
-                acc0[v] += Chunk<WT>::dot(a, xp);
-                acc1[v] += Chunk<WT>::dot(b, xp);
+                const float* xp = xs + v * d + cc * VEC;
+                const float d0 = Chunk<WT>::dot(c0[u], xp), d1 = Chunk<WT>::dot(c1[u], xp);
+                acc0[v] += in ? d0 : 0.f;
+                acc1[v] += in ? d1 : 0.f;
             }
         }
+        if (sg == nseg - 1) {
+            const int r = first + 8 * pair;
+            const bool two = r + 1 < r1;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            acc0[v] = wave_sum(acc0[v]);
-            acc1[v] = wave_sum(acc1[v]);
-        }
-        if (lane == 0) {
-            for (int v = 0; v < nv; ++v) {
-                const long b = b0 + v;
-                for (int q = 0; q < (two ? 2 : 1); ++q) {
-                    const int row = r + q;
-                    float u = q ? acc1[v] : acc0[v];
-                    if (S.silu) u = u / (1.f + expf(-u)) + Elt<WT>::ld((const WT*)S.resid + b * S.resid_bstride + row);
-                    S.out[b * S.out_bstride + row] = u;
+            for (int v = 0; v < NV; ++v) {
+                acc0[v] = wave_sum(acc0[v]);
+                acc1[v] = wave_sum(acc1[v]);
+            }
+            if (lane == 0) {
+                for (int v = 0; v < nv; ++v) {
+                    const long b = b0 + v;
+                    for (int q = 0; q < (two ? 2 : 1); ++q) {
+                        const int row = r + q;
+                        float u = q ? acc1[v] : acc0[v];
+                        // the residual is the activation itself (h, staged in LDS), so the
+                        // epilogue issues no global load that would wait for the prefetch
+                        if (S.silu) u = u / (1.f + expf(-u)) + xs[v * d + row];
+                        S.out[b * S.out_bstride + row] = u;
+                    }
                 }
             }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < SEG; ++u) {
+            c0[u] = n0[u];
+            c1[u] = n1[u];
         }
     }
 }
@@ -192,15 +217,18 @@ mdt_status launch(GemvLaunch& P, hipStream_t stream) {
     const int d = P.d;
     int nv = 1;
     while (nv * 2 <= 8 && nv * 2 <= P.B && (size_t)(nv * 2) * d * sizeof(float) <= (size_t)kLdsBytes) nv *= 2;
-    const int nwg = plan_segments(P, mdt_num_cus() * 8);
+    // one resident round of workgroups: the kernels hold 3 (SEG 8) or 4 (SEG 4)
+    // workgroups per CU at their register counts, and a workgroup stages its
+    // activations once, so fewer, longer row blocks amortise that and the first load
+    const int nwg = plan_segments(P, mdt_num_cus() * (nv <= 2 ? 3 : 4));
     dim3 grid(nwg, (P.B + nv - 1) / nv);
     const size_t lds = (size_t)nv * d * sizeof(float);
     const char* name = STAGE == 1 ? "heads_gemv_w1_lm" : "heads_gemv_w2";
     switch (nv) {
-        case 1: MDT_LAUNCH(name, (heads_gemv<WT, 1, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        case 2: MDT_LAUNCH(name, (heads_gemv<WT, 2, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        case 4: MDT_LAUNCH(name, (heads_gemv<WT, 4, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
-        default: MDT_LAUNCH(name, (heads_gemv<WT, 8, STAGE>), grid, dim3(kThreads), lds, stream, P); break;
+        case 1: MDT_LAUNCH(name, (heads_gemv<WT, 1, STAGE, 8>), grid, dim3(kThreads), lds, stream, P); break;
+        case 2: MDT_LAUNCH(name, (heads_gemv<WT, 2, STAGE, 8>), grid, dim3(kThreads), lds, stream, P); break;
+        case 4: MDT_LAUNCH(name, (heads_gemv<WT, 4, STAGE, 4>), grid, dim3(kThreads), lds, stream, P); break;
+        default: MDT_LAUNCH(name, (heads_gemv<WT, 8, STAGE, 4>), grid, dim3(kThreads), lds, stream, P); break;
     }
     return mdt_launched(name);
 }

@@ -128,8 +128,9 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_non
 // its 64 weight rows and 64 x rows into LDS with row-contiguous 16-byte loads (each
 // wave instruction covers whole 1 KiB row runs, the pattern HBM streams best), then
 // every wave reads MFMA fragments out of LDS: B = its 16 weight rows, A = the 64 x rows.
-// While chunk c is multiplied, weight rows of chunks c+1, c+2 and x rows of chunk c+1
-// are in flight in registers; two workgroups share a CU's LDS.
+// Two register buffers alternate
+// statically (the loop handles chunks c and c+1), so while chunk c is multiplied the
+// weights of chunks c+1 and c+2 and the x rows of chunk c+1 are in flight.
 template <int KC>
 __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
                                                    int d, int V, float tau, int nblk_n, Part* __restrict__ part,
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     constexpr int kPR = KC / 8;                   // 16-byte pieces per row per chunk
     constexpr int kPPT = 64 * kPR / 256;          // pieces per thread per chunk (per matrix)
     constexpr int kTileBytes = 64 * kStride * 2;  // one 64-row tile
-    static_assert(2 * kTileBytes >= 64 * kZStride * 4, "epilogue tile must fit");
+    static_assert(2 * kTileBytes >= 64 * kZStride * 4, "the logits tile must fit");
+    static_assert(KC % 32 == 0, "k-steps of 32");
     __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
     bf16_t* xs = (bf16_t*)smem;
     bf16_t* ws = (bf16_t*)(smem + kTileBytes);
@@ -149,52 +151,45 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     const int g = lane >> 4, c16 = lane & 15;
     const int nchunks = (d + KC - 1) / KC;
 
-    // weight rows run two chunks ahead (HBM latency), x rows one chunk ahead (L2); x of
-    // chunk c+1 is requested before the weights of chunk c+2, so waiting for it leaves
-    // those weight loads in flight
-    u32x4 wa[kPPT], wb[kPPT], xr[kPPT];
+    // No load is under a branch and no loaded register is touched before its LDS store
+    // (either would make the compiler wait for the loads still in flight): a piece
+    // outside the matrix, or of a chunk past the end, reads element 0 and is replaced
+    // by zero when it is stored.
+    u32x4 wA[kPPT], wB[kPPT], xr[kPPT];
+    auto piece_in = [&](int c, int j, int rows0, int nrows) {
+        const int p = threadIdx.x + 256 * j;
+        const int r = p / kPR, off = 8 * (p % kPR);
+        return c < nchunks && off < d - c * KC && rows0 + r < nrows;
+    };
+    auto piece_at = [&](int c, int j, int rows0) {
+        const int p = threadIdx.x + 256 * j;
+        return (size_t)(rows0 + p / kPR) * d + c * KC + 8 * (p % kPR);
+    };
     auto load_w = [&](int c, u32x4 (&wr)[kPPT]) {
-        const int k0 = c * KC, kc = min(KC, d - k0);
 #pragma unroll
-        for (int j = 0; j < kPPT; ++j) {
-            const int p = threadIdx.x + 256 * j;
-            const int r = p / kPR, off = 8 * (p % kPR);
-            wr[j] = (off < kc && n0 + r < V) ? ld_stream(W + (size_t)(n0 + r) * d + k0 + off) : u32x4{0, 0, 0, 0};
-        }
+        for (int j = 0; j < kPPT; ++j) wr[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
     };
     auto load_x = [&](int c) {
-        const int k0 = c * KC, kc = min(KC, d - k0);
 #pragma unroll
-        for (int j = 0; j < kPPT; ++j) {
-            const int p = threadIdx.x + 256 * j;
-            const int r = p / kPR, off = 8 * (p % kPR);
-            xr[j] = (off < kc && m0 + r < M) ? *(const u32x4*)(x + (size_t)(m0 + r) * d + k0 + off) : u32x4{0, 0, 0, 0};
-        }
+        for (int j = 0; j < kPPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
     };
-    auto store = [&](const u32x4 (&wr)[kPPT]) {
+    auto store = [&](int c, const u32x4 (&wr)[kPPT]) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
             const int p = threadIdx.x + 256 * j;
             const int r = p / kPR, off = 8 * (p % kPR);
-            *(u32x4*)(ws + r * kStride + off) = wr[j];
-            *(u32x4*)(xs + r * kStride + off) = xr[j];
+            const u32x4 z{0, 0, 0, 0};
+            *(u32x4*)(ws + r * kStride + off) = piece_in(c, j, n0, V) ? wr[j] : z;
+            *(u32x4*)(xs + r * kStride + off) = piece_in(c, j, m0, M) ? xr[j] : z;
         }
     };
 
+    // wave w owns weight rows 16w .. 16w+15 of the tile against all 64 x rows
     f32x4 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load_w(0, wa);
-    load_x(0);
-    if (nchunks > 1) load_w(1, wb);
-    store(wa);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPPT; ++j) wa[j] = wb[j];
-    for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) load_x(c + 1);
-        if (c + 2 < nchunks) load_w(c + 2, wb);
-        const int nsteps = min(KC, d - c * KC) / 32;
+    auto compute = [&](int c) {
+        const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
         const bf16_t* wrow = ws + (wave * 16 + c16) * kStride + 8 * g;
 #pragma unroll 4
         for (int s = 0; s < KC / 32; ++s) {
@@ -207,13 +202,27 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
                 }
             }
         }
+    };
+    load_w(0, wA);
+    load_x(0);
+    load_w(1, wB);
+    store(0, wA);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+        // LDS: chunk c; wB: chunk c+1
+        load_x(c + 1);
+        load_w(c + 2, wA);
+        compute(c);
         __syncthreads();
-        if (c + 1 < nchunks) {
-            store(wa);
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < kPPT; ++j) wa[j] = wb[j];
-        }
+        store(c + 1, wB);
+        __syncthreads();
+        // LDS: chunk c+1; wA: chunk c+2
+        load_x(c + 2);
+        load_w(c + 3, wB);
+        compute(c + 1);
+        __syncthreads();
+        store(c + 2, wA);
+        __syncthreads();
     }
     float* zt = (float*)smem;  // [64][kZStride], reuses the tiles
 #pragma unroll
