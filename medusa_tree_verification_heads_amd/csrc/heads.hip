@@ -15,6 +15,8 @@
 // W_lm (-> logits_0), which only needs h; launch 2 streams W2 (-> logits_1..K).
 // Rows of all heads of a launch form one grid; a workgroup owns a contiguous row
 // block of one head.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -25,7 +27,7 @@ constexpr int kLdsBytes = 64 * 1024;
 
 struct GemvSeg {
     const void* W;        // [nrows][d], storage type
-    const void* x;        // activation vectors: x + b * x_bstride (elements)
+    const void* x;        // activations x + b * x_bstride: storage type in launch 1, fp32 in launch 2
     const void* resid;    // SiLU epilogue residual: must be x itself (read from LDS)
     float* out;           // out + b * out_bstride + row
     long x_bstride;
@@ -34,7 +36,6 @@ struct GemvSeg {
     int nrows;
     int rows_per_wg;
     int wg_begin;
-    int x_f32;            // activation stored as fp32 (else storage type)
     int silu;             // epilogue: SiLU(u) + resid
     int pad;
 };
@@ -46,11 +47,6 @@ struct GemvLaunch {
     int B;
     int pad;
 };
-
-template <typename WT>
-__device__ __forceinline__ float load_act(const void* x, long i, bool f32) {
-    return f32 ? ((const float*)x)[i] : Elt<WT>::ld((const WT*)x + i);
-}
 
 // Multiply-add one 16-byte weight chunk with the matching activations.
 template <typename WT> struct Chunk;
@@ -106,11 +102,6 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
     const int b0 = blockIdx.y * NV;
     const int nv = min(NV, P.B - b0);
 
-    for (int v = 0; v < nv; ++v)
-        for (int e = threadIdx.x; e < d; e += kThreads)
-            xs[v * d + e] = load_act<WT>(S.x, (long)(b0 + v) * S.x_bstride + e, S.x_f32 != 0);
-    __syncthreads();
-
     constexpr int VEC = Chunk<WT>::kElems;
     const int nchunk = d / VEC;
     const int nseg = (nchunk + 64 * SEG - 1) / (64 * SEG);
@@ -123,16 +114,17 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
     const int items = npairs * nseg;
     const WT* W = (const WT*)S.W;
 
-    uint4 c0[SEG], c1[SEG], n0[SEG], n1[SEG];
-    // Loads are never under a branch (a load under a branch makes the compiler wait for
-    // every load in flight): addresses are clamped, a tail chunk multiplies as zero, and
-    // a dummy item (real == false) makes all lanes read one 16-byte piece.
+    uint4 a0[SEG], a1[SEG], b0r[SEG], b1r[SEG];  // two static buffers: items it (A) and it+1 (B)
+    // Loads are never under a branch and buffers are never copied (either would make the
+    // compiler wait for every load in flight): addresses are clamped, a tail chunk
+    // multiplies as zero, and a dummy item (real == false) makes all lanes read one piece.
     auto load = [&](int it, bool real, uint4 (&p)[SEG], uint4 (&q)[SEG]) {
-        const int pair = it / nseg, sg = it - pair * nseg;
+        const int itc = real ? it : 0;
+        const int pair = itc / nseg, sg = itc - pair * nseg;
         const int r = first + 8 * pair;
         const bool two = r + 1 < r1;
-        const uint4* w0 = (const uint4*)(W + (size_t)r * d);
-        const uint4* w1 = (const uint4*)(W + (size_t)(two ? r + 1 : r) * d);
+        const uint4* w0 = (const uint4*)(W + (size_t)(real ? r : r0) * d);
+        const uint4* w1 = (const uint4*)(W + (size_t)(real && two ? r + 1 : (real ? r : r0)) * d);
 #pragma unroll
         for (int u = 0; u < SEG; ++u) {
             const int c = real ? min(sg * 64 * SEG + lane + 64 * u, nchunk - 1) : 0;
@@ -143,10 +135,7 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
     float acc0[NV], acc1[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
-    if (items > 0) load(0, true, c0, c1);
-    for (int it = 0; it < items; ++it) {
-        const bool more = it + 1 < items;
-        load(more ? it + 1 : it, more, n0, n1);
+    auto process = [&](int it, const uint4 (&p)[SEG], const uint4 (&q)[SEG]) {
         const int pair = it / nseg, sg = it - pair * nseg;
 #pragma unroll
         for (int u = 0; u < SEG; ++u) {
@@ -156,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const float* xp = xs + v * d + cc * VEC;
-                const float d0 = Chunk<WT>::dot(c0[u], xp), d1 = Chunk<WT>::dot(c1[u], xp);
+                const float d0 = Chunk<WT>::dot(p[u], xp), d1 = Chunk<WT>::dot(q[u], xp);
                 acc0[v] += in ? d0 : 0.f;
                 acc1[v] += in ? d1 : 0.f;
             }
@@ -172,9 +161,9 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
             if (lane == 0) {
                 for (int v = 0; v < nv; ++v) {
                     const long b = b0 + v;
-                    for (int q = 0; q < (two ? 2 : 1); ++q) {
-                        const int row = r + q;
-                        float u = q ? acc1[v] : acc0[v];
+                    for (int q2 = 0; q2 < (two ? 2 : 1); ++q2) {
+                        const int row = r + q2;
+                        float u = q2 ? acc1[v] : acc0[v];
                         // the residual is the activation itself (h, staged in LDS), so the
                         // epilogue issues no global load that would wait for the prefetch
                         if (S.silu) u = u / (1.f + expf(-u)) + xs[v * d + row];
@@ -185,11 +174,52 @@ __global__ __launch_bounds__(kThreads) void heads_gemv(GemvLaunch P) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) acc0[v] = acc1[v] = 0.f;
         }
-#pragma unroll
-        for (int u = 0; u < SEG; ++u) {
-            c0[u] = n0[u];
-            c1[u] = n1[u];
+    };
+
+    // Activations (stage 1: the hidden state in the storage type; stage 2: fp32) go to LDS
+    // as fp32.  The first kXB 16-byte pieces per thread are requested before the first
+    // weight segment, so waiting for them waits for nothing newer and both latencies overlap.
+    using XT = typename std::conditional<STAGE == 1, WT, float>::type;
+    constexpr int XV = 16 / (int)sizeof(XT);  // elements per piece
+    constexpr int kXB = 4;
+    const int npieces = nv * d / XV;
+    auto x_piece = [&](int p) -> const uint4* {
+        const int e0 = p * XV, v = e0 / d, e = e0 - v * d;
+        return (const uint4*)((const XT*)S.x + (long)(b0 + v) * S.x_bstride + e);
+    };
+    auto x_store = [&](int p, const uint4& w) {
+        float* dst = xs + p * XV;
+        if constexpr (sizeof(XT) == 4) {
+            *(float4*)dst = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                        __uint_as_float(w.w));
+        } else {
+            *(float4*)dst = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+            *(float4*)(dst + 4) = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                                              __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u));
         }
+    };
+    uint4 xb[kXB];
+#pragma unroll
+    for (int j = 0; j < kXB; ++j) xb[j] = *x_piece(min((int)threadIdx.x + kThreads * j, npieces - 1));
+    load(0, items > 0, a0, a1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kXB; ++j)
+        if ((int)threadIdx.x + kThreads * j < npieces) x_store(threadIdx.x + kThreads * j, xb[j]);
+    for (int p = threadIdx.x + kThreads * kXB; p < npieces; p += kThreads) x_store(p, *x_piece(p));
+    __syncthreads();
+
+    for (int it = 0; it < items; it += 2) {
+        // A holds item it; B gets it+1 while A is used, then A gets it+2 while B is used.
+        // The scheduling barriers keep the loads ahead of the math that precedes them in
+        // the wait order.
+        load(it + 1, it + 1 < items, b0r, b1r);
+        __builtin_amdgcn_sched_barrier(0);
+        process(it, a0, a1);
+        load(it + 2, it + 2 < items, a0, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + 1 < items) process(it + 1, b0r, b1r);
     }
 }
 
@@ -270,7 +300,6 @@ mdt_status run(hipStream_t stream, int B, int d, int V, int K, const void* h, co
         GemvSeg& S = P2.seg[P2.nseg++];
         S.W = (const WT*)W2 + (size_t)k * V * d;
         S.x = a + (size_t)k * d;
-        S.x_f32 = 1;
         S.x_bstride = (long)K * d;
         S.out = logits + (size_t)(k + 1) * V;
         S.out_bstride = (long)(K + 1) * V;
