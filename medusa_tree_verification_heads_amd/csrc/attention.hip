@@ -23,6 +23,8 @@
 // fp32 path: one wave per (sequence, head, node) walks all allowed keys on VALU.
 #include <math.h>
 
+#include <cmath>
+
 #include "common.h"
 
 namespace {
@@ -36,7 +38,6 @@ constexpr int kTile = 64;          // keys per LDS tile
 constexpr int kDh = 128;           // head dim of the MFMA path
 constexpr int kKStride = kDh + 8;  // LDS row stride of K tile (elements)
 constexpr int kVStride = kTile + 4;  // LDS row stride of transposed V tile (elements)
-constexpr int kMinTilesPerSplit = 4;
 constexpr int kMaxSplitPages = 4096;  // page-table entries a workgroup stages in LDS
 constexpr int kMaxTilesPerSplit = (kMaxSplitPages - 2) * 1 / kTile;  // holds for page_size >= 1
 
@@ -189,11 +190,6 @@ __device__ __forceinline__ float elt(const u32x4& v, int t) {
     return __uint_as_float((t & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// theta^(-2m/Dh), the rotation frequency of pair m (double precision)
-__device__ __forceinline__ double rope_inv_freq(int m, double theta) {
-    return pow(theta, -2.0 * (double)m / (double)kDh);
-}
-
 // cos/sin of pos * inv_freq: the angle is formed and reduced to [-pi, pi] in double
 // precision, then evaluated in single precision.
 __device__ __forceinline__ float2 rope_cs_table_entry(int pos, double inv_freq) {
@@ -231,6 +227,7 @@ struct AttnArgs {
     float* part_ml;
     double theta;
     int T, Tpad, H, W, nsplit, tiles_per_split, max_depth;
+    double inv_freq[kDh / 2];  // theta^(-2m/Dh), computed once on the host
 };
 
 // One (sequence, head, key split) per workgroup; NWB waves, wave w owns queries 16w..16w+15.
@@ -253,7 +250,6 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) bf16_t Vt[kDh * kVStride];
     __shared__ float2 cs[(MDT_MAX_HEADS + 1) * (kDh / 2)];  // cos/sin per (depth, pair)
-    __shared__ double inv_freq[kDh / 2];
     __shared__ int pages[PAGED ? kMaxSplitPages : 1];        // physical page of each page of the split
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const bool tree_split = split == A.nsplit;
@@ -307,7 +303,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     // keys' values are packed per dimension into one dword, so the transposed LDS writes of
     // a wave hit consecutive dwords.  PF register slots: the PF tiles after the current
     // one are in flight while it runs.
-    constexpr int PF = NWB >= 16 ? 1 : 2;
+    constexpr int PF = 1;
     u32x4 kr[PF][PPT], va[PF][VPT], vb[PF][VPT];
     uint32_t valid[PF];
     const int row_elems = H * kDh;  // elements between consecutive keys of a contiguous cache
@@ -372,10 +368,8 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) load_prefix(j_begin + s * kTile, s);
 
-    if (tid < kDh / 2) inv_freq[tid] = rope_inv_freq(tid, A.theta);
-    __syncthreads();
     for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
-        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), inv_freq[e % (kDh / 2)]);
+        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
     __syncthreads();  // cos/sin table ready
     {
         if (!q_ok)
@@ -559,19 +553,36 @@ struct Plan {
     size_t po_bytes, pml_bytes;
 };
 
+// Split choice by a cost model in units of one 64-key tile: a workgroup costs a fixed
+// setup plus its tiles (the tree workgroup about three), and the workgroups run one per
+// CU in rounds of kPlanCUs (the MFMA kernel holds one workgroup per CU).  More splits
+// shorten every workgroup but add rounds and partial-state traffic for the combine.
+// A fixed CU count (MI355X) keeps the plan, and so the workspace size, device-independent.
+constexpr int kPlanCUs = 256;
+constexpr double kSetupTiles = 1.2, kTreeTiles = 3.0, kCombineTilesPerSplit = 0.1;
+
 Plan plan(int B, int T, int H, int capacity) {
     Plan p;
     p.Tpad = (T + 15) / 16 * 16;
     const int waves = p.Tpad / 16;
     p.nwb = waves <= 4 ? 4 : (waves <= 8 ? 8 : 16);
     const int tiles = capacity > 0 ? (capacity + kTile - 1) / kTile : 1;
-    long want = (512 + (long)B * H - 1) / ((long)B * H);
-    if (want < 1) want = 1;
-    int tps = (int)((tiles + want - 1) / want);
-    if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
-    if (tps > kMaxTilesPerSplit) tps = kMaxTilesPerSplit;
-    p.tiles_per_split = tps;
-    p.nsplit = (tiles + tps - 1) / tps;
+    const long bh = (long)B * H;
+    double best = 1e300;
+    int best_tps = tiles < kMaxTilesPerSplit ? tiles : kMaxTilesPerSplit;
+    for (int tps = 1; tps <= tiles && tps <= kMaxTilesPerSplit; ++tps) {
+        const int ns = (tiles + tps - 1) / tps;
+        const long wgs = bh * (ns + 1);
+        const long rounds = (wgs + kPlanCUs - 1) / kPlanCUs;
+        const double per_wg = kSetupTiles + (tps > kTreeTiles ? tps : kTreeTiles);
+        const double cost = rounds * per_wg + kCombineTilesPerSplit * ns * ((bh + kPlanCUs - 1) / kPlanCUs);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_tps = tps;
+        }
+    }
+    p.tiles_per_split = best_tps;
+    p.nsplit = (tiles + best_tps - 1) / best_tps;
     // prefix splits plus one tree split
     p.po_bytes = ((size_t)B * H * (p.nsplit + 1) * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
     p.pml_bytes = (size_t)B * H * (p.nsplit + 1) * p.Tpad * 2 * sizeof(float);
@@ -634,7 +645,8 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     MDT_REQUIRE(ws_bytes >= p.po_bytes + p.pml_bytes, MDT_ERR_WORKSPACE, "workspace too small");
     AttnArgs A{kv, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix_len, tree->depth, tree->anc,
                (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
-               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth};
+               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, {}};
+    for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
     const dim3 grid(p.nsplit + 1, H, B);
     const bool paged = cache->layout == MDT_KV_PAGED;
     auto kern = p.nwb == 4 ? (paged ? attn_tree_mfma<4, true> : attn_tree_mfma<4, false>)
