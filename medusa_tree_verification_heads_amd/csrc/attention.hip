@@ -531,17 +531,37 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const long pbase = ((long)b * H + h) * nsplit * Tpad + i;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(pbase + (long)s * Tpad) * 2]);
-    float den = 0.f, na = 0.f, nb = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const long p = pbase + (long)s * Tpad;
-        const float ms = part_ml[p * 2];
-        if (ms == -INFINITY) continue;
-        const float wgt = exp2f(ms - M);  // maxima are in log2 units
-        den += part_ml[p * 2 + 1] * wgt;
-        na += part_o[p * kDh + lane] * wgt;
-        nb += part_o[p * kDh + lane + 64] * wgt;
+    // splits in batches of 8, all loads of a batch first; running max and sums rescale
+    // between batches (maxima are in log2 units)
+    float M = -INFINITY, den = 0.f, na = 0.f, nb = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float ms[8], ls[8], oa[8], ob[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long pidx = pbase + (long)min(s0 + u, nsplit - 1) * Tpad;
+            ms[u] = part_ml[pidx * 2];
+            ls[u] = part_ml[pidx * 2 + 1];
+            oa[u] = part_o[pidx * kDh + lane];
+            ob[u] = part_o[pidx * kDh + lane + 64];
+        }
+        float bm = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < nsplit) bm = fmaxf(bm, ms[u]);
+        if (bm == -INFINITY) continue;
+        const float r = exp2f(M - bm);  // 0 while M is -inf
+        den *= r;
+        na *= r;
+        nb *= r;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (s0 + u >= nsplit || ms[u] == -INFINITY) continue;
+            const float wgt = exp2f(ms[u] - bm);
+            den += ls[u] * wgt;
+            na += oa[u] * wgt;
+            nb += ob[u] * wgt;
+        }
+        M = bm;
     }
     bf16_t* o = out + (((long)b * T + i) * H + h) * kDh;
     o[lane] = f32_to_bf16(na / den);

@@ -188,10 +188,11 @@ __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, 
         float v[E];
         int idx[E];
 #pragma unroll
-        for (int j = 0; j < E; ++j) {
-            const int e = lane + 64 * j;
-            v[j] = e < n ? c[e].v : -INFINITY;
-            idx[j] = e < n ? c[e].i : INT_MAX;
+        for (int j = 0; j < E; ++j) {  // unconditional loads (clamped), out-of-range entries replaced
+            const Cand q = c[min(lane + 64 * j, n - 1)];
+            const bool in = lane + 64 * j < n;
+            v[j] = in ? q.v : -INFINITY;
+            idx[j] = in ? q.i : INT_MAX;
         }
         wave_select<E>(v, idx, k, best + wave * k);
     }

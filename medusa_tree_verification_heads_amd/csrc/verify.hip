@@ -272,8 +272,17 @@ __global__ __launch_bounds__(64) void verify_merge(const Part* __restrict__ part
                                                    const int32_t* __restrict__ parent, int T, float* __restrict__ edge) {
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
+    // all loads of a batch are issued before the merges (one round trip per 512 partials)
+    const Part* pr = part + (long)row * nblk_n;
     Part p{-INFINITY, INT_MAX, 0.f, 0.f};
-    for (int j = lane; j < nblk_n; j += 64) p = part_merge(p, part[(long)row * nblk_n + j], tau);
+    for (int j0 = 0; j0 < nblk_n; j0 += 64 * 8) {
+        Part q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = pr[min(j0 + lane + 64 * u, nblk_n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + lane + 64 * u < nblk_n) p = part_merge(p, q[u], tau);
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
     if (lane == 0) {
