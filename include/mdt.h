@@ -69,7 +69,7 @@ typedef enum mdt_status {
     MDT_ERR_VALUE = -6,       /* a scalar parameter is out of range */
     MDT_ERR_WORKSPACE = -7,   /* workspace NULL or too small */
     MDT_ERR_HIP = -8,         /* the HIP runtime reported an error */
-    MDT_ERR_UNSUPPORTED = -9, /* valid request this build does not implement */
+    MDT_ERR_UNSUPPORTED = -9, /* valid request the library does not implement */
     MDT_ERR_ALLOC = -10       /* host allocation failed */
 } mdt_status;
 
