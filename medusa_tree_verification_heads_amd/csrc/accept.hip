@@ -23,7 +23,6 @@
 
 namespace {
 
-constexpr int kWords = MDT_MAX_NODES / 64;
 
 struct AcceptArgs {
     const mdt_row_stats* stats;
@@ -39,37 +38,50 @@ struct AcceptArgs {
     int32_t* n_acc;
 };
 
-// One wave: acceptance of sequence b.  Writes path[b][*] and n_acc[b]; returns the
-// accepted node count (uniform over the wave) and, if lds_path is non-null, leaves
-// the path there as well.
+// One wave: acceptance of sequence b, for trees of NW = ceil(T/64) mask words.  Writes
+// path[b][*] and n_acc[b]; returns the accepted node count (uniform over the wave) and, if
+// lds_path is non-null, leaves the path there as well.  Two rounds of global loads: every
+// per-node value (parent, token, edge logit, depth, mask row) is requested at once, then
+// the parents' statistics; the chosen node's depth and mask row come from other lanes'
+// registers.
+template <int NW>
 __device__ int accept_wave(const AcceptArgs& A, int b, int lane, int32_t* lds_path) {
-    const int T = A.T, W = A.W;
+    const int T = A.T;
     const float ln_eps = logf(A.eps), ln_delta = logf(A.delta);
     const bool onehot_passes = 1.f > fminf(A.eps, A.delta);  // typical at tau = 0, candidate is the argmax
     if (lds_path)
         for (int j = lane; j < A.path_stride; j += 64) lds_path[j] = -1;
-    uint64_t P[kWords];  // passing nodes; the ballot is uniform, so every lane holds the mask
+    int par[NW], tok[NW], dep[NW];
+    float edg[NW];
+    uint64_t an[NW][NW];
 #pragma unroll
-    for (int w = 0; w < kWords; ++w) {
-        P[w] = 0;
-        if (w >= W) continue;
+    for (int w = 0; w < NW; ++w) {
+        const int c = min(w * 64 + lane, T - 1);  // clamped: lanes past T are ignored below
+        par[w] = A.parent[c];
+        tok[w] = A.tokens[(long)b * T + c];
+        edg[w] = A.edge[(long)b * T + c];
+        dep[w] = A.depth[c];
+#pragma unroll
+        for (int x = 0; x < NW; ++x) an[w][x] = A.anc[(long)c * NW + x];
+    }
+    mdt_row_stats st[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) st[w] = A.stats[(long)b * T + min(max(par[w], 0), T - 1)];
+    uint64_t P[NW];  // passing nodes; the ballot is uniform, so every lane holds the mask
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
         const int c = w * 64 + lane;
         bool pass = false;
         if (c == 0) {
             pass = true;
-        } else if (c < T) {
-            const int p = A.parent[c];
-            if (p >= 0 && p < c) {
-                const mdt_row_stats st = A.stats[(long)b * T + p];
-                const int tok = A.tokens[(long)b * T + c];
-                if (A.mode == MDT_ACCEPT_GREEDY) {
-                    pass = tok == st.argmax;
-                } else if (A.tau == 0.f) {
-                    pass = tok == st.argmax && onehot_passes;
-                } else {
-                    const float lp = A.edge[(long)b * T + c] / A.tau - st.logZ;
-                    pass = lp > fminf(ln_eps, ln_delta - st.entropy);
-                }
+        } else if (c < T && par[w] >= 0 && par[w] < c) {
+            if (A.mode == MDT_ACCEPT_GREEDY) {
+                pass = tok[w] == st[w].argmax;
+            } else if (A.tau == 0.f) {
+                pass = tok[w] == st[w].argmax && onehot_passes;
+            } else {
+                const float lp = edg[w] / A.tau - st[w].logZ;
+                pass = lp > fminf(ln_eps, ln_delta - st[w].entropy);
             }
         }
         P[w] = __ballot(pass);
@@ -77,27 +89,40 @@ __device__ int accept_wave(const AcceptArgs& A, int b, int lane, int32_t* lds_pa
     // deepest accepted node, smallest index among equals
     int key = -1;
 #pragma unroll
-    for (int w = 0; w < kWords; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const int c = w * 64 + lane;
-        if (w >= W || c >= T) continue;
-        bool ok = true;
+        bool ok = c < T;
 #pragma unroll
-        for (int x = 0; x < kWords; ++x)
-            if (x < W) ok = ok && ((A.anc[(long)c * W + x] & ~P[x]) == 0);
-        const int dep = A.depth[c];
-        if (ok && dep >= 0 && dep < 256) key = max(key, (dep << 16) | (0xffff - c));
+        for (int x = 0; x < NW; ++x) ok = ok && ((an[w][x] & ~P[x]) == 0);
+        if (ok && dep[w] >= 0 && dep[w] < 256) key = max(key, (dep[w] << 16) | (0xffff - c));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off, 64));
     const int best = 0xffff - (key & 0xffff);  // the root is always accepted, so key >= 0
-    const int nb = A.depth[best] + 1;
+    const int bw = best >> 6, bl = best & 63;
+    int best_dep = 0;
+    uint64_t abest[NW];
+#pragma unroll
+    for (int x = 0; x < NW; ++x) abest[x] = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {  // the chosen node's depth and mask row, from lane bl
+        const int dw = __shfl(dep[w], bl, 64);
+#pragma unroll
+        for (int x = 0; x < NW; ++x) {
+            const uint64_t a = __shfl(an[w][x], bl, 64);
+            if (w == bw) abest[x] = a;
+        }
+        if (w == bw) best_dep = dw;
+    }
+    const int nb = best_dep + 1;
     int32_t* pb = A.path + (long)b * A.path_stride;
     for (int j = lane; j < A.path_stride; j += 64)
         if (j >= nb) pb[j] = -1;
-    for (int w = 0; w < W; ++w) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
         const int c = w * 64 + lane;
-        if (c < T && ((A.anc[(long)best * W + w] >> lane) & 1ull)) {
-            const int dc = A.depth[c];
+        if (c < T && ((abest[w] >> lane) & 1ull)) {
+            const int dc = dep[w];
             if (dc >= 0 && dc < A.path_stride) {
                 pb[dc] = c;
                 if (lds_path) lds_path[dc] = c;
@@ -109,13 +134,15 @@ __device__ int accept_wave(const AcceptArgs& A, int b, int lane, int32_t* lds_pa
     return n;
 }
 
+template <int NW>
 __global__ __launch_bounds__(64) void accept_kernel(AcceptArgs A) {
-    accept_wave(A, blockIdx.x, threadIdx.x, nullptr);
+    accept_wave<NW>(A, blockIdx.x, threadIdx.x, nullptr);
 }
 
 constexpr int kCopyThreads = 1024;
 constexpr int kCopyBatch = 4;  // 16-byte vectors of k and of v a thread loads before it stores
 
+template <int NW>
 __global__ __launch_bounds__(kCopyThreads) void accept_compact_kernel(AcceptArgs A, KvSlots cache,
                                                                       const uint4* __restrict__ k_rot,
                                                                       const uint4* __restrict__ v, int row_vec,
@@ -126,7 +153,7 @@ __global__ __launch_bounds__(kCopyThreads) void accept_compact_kernel(AcceptArgs
     __shared__ int s_n, s_ok;
     const int b = blockIdx.x, tid = threadIdx.x;
     if (tid < 64) {
-        const int n = accept_wave(A, b, tid, s_path);
+        const int n = accept_wave<NW>(A, b, tid, s_path);
         if (tid == 0) s_n = n;
     }
     __syncthreads();
@@ -200,7 +227,9 @@ extern "C" mdt_status mdt_accept_path(void* stream, int B, const mdt_tree_dev* t
     mdt_status st = check_accept(B, tree, stats, edge_logit, tree_tokens, mode, eps, delta, temperature, path,
                                  path_stride, n_acc, &A);
     if (st != MDT_OK) return st;
-    MDT_LAUNCH("accept_kernel", accept_kernel, dim3(B), dim3(64), 0, (hipStream_t)stream, A);
+    auto kern = A.W == 1 ? accept_kernel<1> : A.W == 2 ? accept_kernel<2> : A.W == 3 ? accept_kernel<3>
+                                                                                 : accept_kernel<4>;
+    MDT_LAUNCH("accept_kernel", kern, dim3(B), dim3(64), 0, (hipStream_t)stream, A);
     return mdt_launched("accept_kernel");
 }
 
@@ -219,7 +248,10 @@ extern "C" mdt_status mdt_accept_compact(void* stream, mdt_dtype dt, int B, int 
     st = mdt_check_compact_args(dt, B, tree->T, H, Dh, path_stride, k_rot, v, cache, prefix_len, new_prefix_len, &c,
                                 &row_vec);
     if (st != MDT_OK) return st;
-    MDT_LAUNCH("accept_compact_kernel", accept_compact_kernel, dim3(B), dim3(kCopyThreads), 0, (hipStream_t)stream,
+    auto kern = A.W == 1 ? accept_compact_kernel<1>
+              : A.W == 2 ? accept_compact_kernel<2>
+              : A.W == 3 ? accept_compact_kernel<3> : accept_compact_kernel<4>;
+    MDT_LAUNCH("accept_compact_kernel", kern, dim3(B), dim3(kCopyThreads), 0, (hipStream_t)stream,
                A, c, (const uint4*)k_rot, (const uint4*)v, row_vec, prefix_len, new_prefix_len);
     return mdt_launched("accept_compact_kernel");
 }

@@ -181,6 +181,10 @@ __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, 
     __shared__ Cand best[(MDT_MAX_HEADS + 1) * MDT_MAX_TOPK];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the tree-fill inputs of this thread's first node are requested with the candidates
+    const int i0 = min((int)threadIdx.x, T - 1);
+    const int dep0 = depth[i0], rk0 = rank[i0], par0 = parent[i0];
+    const int L = prefix_len[b];
     {  // the block has exactly K1 waves: wave w merges head row w
         const int row = b * K1 + wave;
         const Cand* c = cand + (size_t)row * nslice * k;
@@ -201,10 +205,11 @@ __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, 
         topk_idx[(size_t)b * K1 * k + e] = best[e].i;
         topk_val[(size_t)b * K1 * k + e] = best[e].v;
     }
-    const int L = prefix_len[b];
     for (int i = threadIdx.x; i < T; i += blockDim.x) {
-        const int dep = depth[i], rk = rank[i];
-        const bool ok = dep >= 0 && dep < K1 && rk >= 0 && rk < k && (i == 0 ? dep == 0 : parent[i] < i);
+        const bool first = i == (int)threadIdx.x;
+        const int dep = first ? dep0 : depth[i], rk = first ? rk0 : rank[i];
+        const int par = first ? par0 : parent[i];
+        const bool ok = dep >= 0 && dep < K1 && rk >= 0 && rk < k && (i == 0 ? dep == 0 : par < i);
         tokens[(size_t)b * T + i] = ok ? best[dep * k + rk].i : -1;
         pos[(size_t)b * T + i] = L + dep;
     }
