@@ -70,11 +70,24 @@ __device__ __forceinline__ Part shfl_xor_part(Part p, int off) {
 
 // Reduce a logits tile zt[MT][kZStride] (rows m0.., cols n0..) to per-row partials,
 // write optional full logits and the edge logits that fall inside the tile.
+// Edge inputs of this thread's first node of the tile's sequences, requested before the
+// weight stream so that the epilogue does not wait for them.
+struct EdgePre {
+    int par, tok;
+};
+
+template <int MT>
+__device__ EdgePre edge_preload(int m0, int M, const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens,
+                                int T) {
+    const int idx = min(m0 / T * T + (int)threadIdx.x, M - 1);
+    return EdgePre{parent[idx % T], tokens[idx]};
+}
+
 template <int MT>
 __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, float tau, int nblk_n,
                               Part* __restrict__ part, float* __restrict__ logits_opt,
                               const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens, int T,
-                              float* __restrict__ edge) {
+                              float* __restrict__ edge, EdgePre pre) {
     constexpr int TPR = 256 / MT;       // threads per row
     constexpr int CPT = kNB / TPR;      // columns per thread
     const int t = threadIdx.x;
@@ -108,11 +121,12 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
     const int first_b = m0 / T, last_b = min(M - 1, m0 + MT - 1) / T;
     for (int idx = first_b * T + t; idx <= last_b * T + T - 1; idx += 256) {
         const int b = idx / T, c = idx % T;
-        if (c == 0) continue;
-        const int pr = parent[c];
+        if (c == 0 || idx >= M) continue;
+        const bool first = idx == first_b * T + t;  // preloaded
+        const int pr = first ? pre.par : parent[c];
         if (pr < 0 || pr >= T) continue;
         const int rr = b * T + pr;
-        const int tok = tokens[idx];
+        const int tok = first ? pre.tok : tokens[idx];
         if (rr >= m0 && rr < m0 + MT && rr < M && tok >= n0 && tok < n0 + ncol) edge[idx] = zt[(rr - m0) * kZStride + tok - n0];
     }
 }
@@ -150,6 +164,7 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int nchunks = (d + KC - 1) / KC;
+    const EdgePre pre = edge_preload<kMB>(m0, M, parent, tokens, T);
 
     // No load is under a branch and no loaded register is touched before its LDS store
     // (either would make the compiler wait for the loads still in flight): a piece
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
 #pragma unroll
         for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZStride + wave * 16 + c16] = acc[mt][e];
     __syncthreads();
-    tile_epilogue<kMB>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge);
+    tile_epilogue<kMB>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
 // fp32 path: grid (ceil(V/64), ceil(M/16)), block 256; x rows staged in LDS as fp32.
@@ -262,7 +277,8 @@ __global__ __launch_bounds__(256) void verify_f32(const float* __restrict__ x, c
 #pragma unroll
     for (int j = 0; j < 4; ++j) zt[(rg * 4 + j) * kZStride + cl] = acc[j];
     __syncthreads();
-    tile_epilogue<16>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge);
+    tile_epilogue<16>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge,
+                      edge_preload<16>(m0, M, parent, tokens, T));
 }
 
 // Merge row partials in block order; grid (M), block 64.  Also writes the edge
