@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxSeg = 2 * MDT_MAX_HEADS + 1;
+constexpr int kRowsPerWg = 16;  // rows per workgroup per activation vector (launch planning)
 constexpr int kLdsBytes = 64 * 1024;
 
 struct GemvSeg {
@@ -247,10 +248,16 @@ mdt_status launch(GemvLaunch& P, hipStream_t stream) {
     const int d = P.d;
     int nv = 1;
     while (nv * 2 <= 8 && nv * 2 <= P.B && (size_t)(nv * 2) * d * sizeof(float) <= (size_t)kLdsBytes) nv *= 2;
-    // one resident round of workgroups: the kernels hold 3 (SEG 8) or 4 (SEG 4)
-    // workgroups per CU at their register counts, and a workgroup stages its
-    // activations once, so fewer, longer row blocks amortise that and the first load
-    const int nwg = plan_segments(P, mdt_num_cus() * (nv <= 2 ? 3 : 4));
+    // Short workgroups of about kRowsPerWg rows (two row pairs per wave): far more
+    // workgroups than resident slots, so the dispatcher refills a CU as soon as one of its
+    // workgroups retires.  With one long block per slot, the SIMD arbiter's preference for
+    // older waves made the first workgroup on every CU finish long before the last, which
+    // then streamed the tail with few loads in flight.
+    long rows_total = 0;
+    for (int q = 0; q < P.nseg; ++q) rows_total += P.seg[q].nrows;
+    // a workgroup stages nv activation vectors, so its row block grows with nv
+    const long rows_per_wg = (long)kRowsPerWg * nv;
+    const int nwg = plan_segments(P, (int)((rows_total + rows_per_wg - 1) / rows_per_wg));
     dim3 grid(nwg, (P.B + nv - 1) / nv);
     const size_t lds = (size_t)nv * d * sizeof(float);
     const char* name = STAGE == 1 ? "heads_gemv_w1_lm" : "heads_gemv_w2";
