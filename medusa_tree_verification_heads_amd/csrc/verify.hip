@@ -34,6 +34,9 @@ constexpr int kZStride = kNB + 1;
 #ifndef MDT_VERIFY_KC
 #define MDT_VERIFY_KC 256        // dims per staged chunk (LDS holds one 64-row tile of x and of W)
 #endif
+#ifndef MDT_VERIFY_NB
+#define MDT_VERIFY_NB 64         // vocabulary columns per MFMA workgroup (4 waves of 16 per 64)
+#endif
 
 struct Part {
     float m;
@@ -68,7 +71,7 @@ __device__ __forceinline__ Part shfl_xor_part(Part p, int off) {
     return q;
 }
 
-// Reduce a logits tile zt[MT][kZStride] (rows m0.., cols n0..) to per-row partials,
+// Reduce a logits tile zt[MT][NB + 1] (rows m0.., cols n0..) to per-row partials,
 // write optional full logits and the edge logits that fall inside the tile.
 // Edge inputs of this thread's first node of the tile's sequences, requested before the
 // weight stream so that the epilogue does not wait for them.
@@ -83,19 +86,20 @@ __device__ EdgePre edge_preload(int m0, int M, const int32_t* __restrict__ paren
     return EdgePre{parent[idx % T], tokens[idx]};
 }
 
-template <int MT>
+template <int MT, int NB, int NT>
 __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, float tau, int nblk_n,
                               Part* __restrict__ part, float* __restrict__ logits_opt,
                               const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens, int T,
                               float* __restrict__ edge, EdgePre pre) {
-    constexpr int TPR = 256 / MT;       // threads per row
-    constexpr int CPT = kNB / TPR;      // columns per thread
+    constexpr int kZS = NB + 1;         // row stride of zt
+    constexpr int TPR = NT / MT;        // threads per row
+    constexpr int CPT = NB / TPR;       // columns per thread
     const int t = threadIdx.x;
     const int r = t / TPR, q = t % TPR;
     const int row = m0 + r;
-    const int ncol = min(kNB, V - n0);
+    const int ncol = min(NB, V - n0);
     Part p{-INFINITY, INT_MAX, 0.f, 0.f};
-    const float* z = zt + r * kZStride;
+    const float* z = zt + r * kZS;
     for (int c = q * CPT; c < q * CPT + CPT; ++c) {
         if (c >= ncol) break;
         if (better(z[c], n0 + c, p.m, p.a)) {
@@ -119,7 +123,7 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
         for (int c = q * CPT; c < q * CPT + CPT && c < ncol; ++c) logits_opt[(long)row * V + n0 + c] = z[c];
     // edges: node c of sequence b reads row b*T + parent(c) at column token(b, c)
     const int first_b = m0 / T, last_b = min(M - 1, m0 + MT - 1) / T;
-    for (int idx = first_b * T + t; idx <= last_b * T + T - 1; idx += 256) {
+    for (int idx = first_b * T + t; idx <= last_b * T + T - 1; idx += NT) {
         const int b = idx / T, c = idx % T;
         if (c == 0 || idx >= M) continue;
         const bool first = idx == first_b * T + t;  // preloaded
@@ -127,7 +131,7 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
         if (pr < 0 || pr >= T) continue;
         const int rr = b * T + pr;
         const int tok = first ? pre.tok : tokens[idx];
-        if (rr >= m0 && rr < m0 + MT && rr < M && tok >= n0 && tok < n0 + ncol) edge[idx] = zt[(rr - m0) * kZStride + tok - n0];
+        if (rr >= m0 && rr < m0 + MT && rr < M && tok >= n0 && tok < n0 + ncol) edge[idx] = zt[(rr - m0) * kZS + tok - n0];
     }
 }
 
@@ -145,22 +149,26 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_non
 // Two register buffers alternate
 // statically (the loop handles chunks c and c+1), so while chunk c is multiplied the
 // weights of chunks c+1 and c+2 and the x rows of chunk c+1 are in flight.
-template <int KC>
-__global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
-                                                   int d, int V, float tau, int nblk_n, Part* __restrict__ part,
-                                                   float* __restrict__ logits_opt, const int32_t* __restrict__ parent,
-                                                   const int32_t* __restrict__ tokens, int T,
-                                                   float* __restrict__ edge) {
+template <int KC, int NB>
+__global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+                                                      int M, int d, int V, float tau, int nblk_n,
+                                                      Part* __restrict__ part, float* __restrict__ logits_opt,
+                                                      const int32_t* __restrict__ parent,
+                                                      const int32_t* __restrict__ tokens, int T,
+                                                      float* __restrict__ edge) {
+    constexpr int NT = 4 * NB;                    // one wave per 16 weight rows
     constexpr int kStride = KC + 8;               // LDS row stride (elements)
     constexpr int kPR = KC / 8;                   // 16-byte pieces per row per chunk
-    constexpr int kPPT = 64 * kPR / 256;          // pieces per thread per chunk (per matrix)
-    constexpr int kTileBytes = 64 * kStride * 2;  // one 64-row tile
-    static_assert(2 * kTileBytes >= 64 * kZStride * 4, "the logits tile must fit");
+    constexpr int kPPT = NB * kPR / NT;           // weight pieces per thread per chunk
+    constexpr int kXPT = 64 * kPR / NT;           // x pieces per thread per chunk
+    constexpr int kXBytes = 64 * kStride * 2;     // the 64-row x tile
+    constexpr int kWBytes = NB * kStride * 2;     // the NB-row weight tile
+    static_assert(kXBytes + kWBytes >= 64 * (NB + 1) * 4, "the logits tile must fit");
     static_assert(KC % 32 == 0, "k-steps of 32");
-    __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char smem[kXBytes + kWBytes];
     bf16_t* xs = (bf16_t*)smem;
-    bf16_t* ws = (bf16_t*)(smem + kTileBytes);
-    const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMB;
+    bf16_t* ws = (bf16_t*)(smem + kXBytes);
+    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int nchunks = (d + KC - 1) / KC;
@@ -170,14 +178,14 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     // (either would make the compiler wait for the loads still in flight): a piece
     // outside the matrix, or of a chunk past the end, reads element 0 and is replaced
     // by zero when it is stored.
-    u32x4 wA[kPPT], wB[kPPT], xr[kPPT];
+    u32x4 wA[kPPT], wB[kPPT], xr[kXPT];
     auto piece_in = [&](int c, int j, int rows0, int nrows) {
-        const int p = threadIdx.x + 256 * j;
+        const int p = threadIdx.x + NT * j;
         const int r = p / kPR, off = 8 * (p % kPR);
         return c < nchunks && off < d - c * KC && rows0 + r < nrows;
     };
     auto piece_at = [&](int c, int j, int rows0) {
-        const int p = threadIdx.x + 256 * j;
+        const int p = threadIdx.x + NT * j;
         return (size_t)(rows0 + p / kPR) * d + c * KC + 8 * (p % kPR);
     };
     auto load_w = [&](int c, u32x4 (&wr)[kPPT]) {
@@ -186,16 +194,19 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
     };
     auto load_x = [&](int c) {
 #pragma unroll
-        for (int j = 0; j < kPPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
+        for (int j = 0; j < kXPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
     };
     auto store = [&](int c, const u32x4 (&wr)[kPPT]) {
+        const u32x4 z{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
-            const int p = threadIdx.x + 256 * j;
-            const int r = p / kPR, off = 8 * (p % kPR);
-            const u32x4 z{0, 0, 0, 0};
-            *(u32x4*)(ws + r * kStride + off) = piece_in(c, j, n0, V) ? wr[j] : z;
-            *(u32x4*)(xs + r * kStride + off) = piece_in(c, j, m0, M) ? xr[j] : z;
+            const int p = threadIdx.x + NT * j;
+            *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wr[j] : z;
+        }
+#pragma unroll
+        for (int j = 0; j < kXPT; ++j) {
+            const int p = threadIdx.x + NT * j;
+            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
         }
     };
 
@@ -239,13 +250,13 @@ __global__ __launch_bounds__(256) void verify_mfma(const bf16_t* __restrict__ x,
         store(c + 2, wA);
         __syncthreads();
     }
-    float* zt = (float*)smem;  // [64][kZStride], reuses the tiles
+    float* zt = (float*)smem;  // [64][NB + 1], reuses the tiles
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZStride + wave * 16 + c16] = acc[mt][e];
+        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (NB + 1) + wave * 16 + c16] = acc[mt][e];
     __syncthreads();
-    tile_epilogue<kMB>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
+    tile_epilogue<kMB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
 // fp32 path: grid (ceil(V/64), ceil(M/16)), block 256; x rows staged in LDS as fp32.
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(256) void verify_f32(const float* __restrict__ x, c
 #pragma unroll
     for (int j = 0; j < 4; ++j) zt[(rg * 4 + j) * kZStride + cl] = acc[j];
     __syncthreads();
-    tile_epilogue<16>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge,
+    tile_epilogue<16, kNB, 256>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge,
                       edge_preload<16>(m0, M, parent, tokens, T));
 }
 
@@ -356,10 +367,12 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     const int M = B * T;
-    const int nblk_n = (V + kNB - 1) / kNB;
+    const int nb_cols = dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
+    const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
     if (dt == MDT_BF16) {
-        MDT_LAUNCH("verify_mfma", verify_mfma<MDT_VERIFY_KC>, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(256), 0, s,
+        auto kern = verify_mfma<MDT_VERIFY_KC, MDT_VERIFY_NB>;
+        MDT_LAUNCH("verify_mfma", kern, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(4 * MDT_VERIFY_NB), 0, s,
                    (const bf16_t*)x,
                            (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
