@@ -6,21 +6,28 @@
 // token) and step 4 (position id = prefix length + depth).
 //
 // Selection is a total order: larger value first, equal values by smaller index.
-// A wave selects its k best elements in k rounds; each round every lane offers
-// its best element that comes after the previous winner, and a DPP row-op
-// reduction picks the winner.
 //
-// Stage A: every workgroup reduces a 2048-element slice of one row to k
-// candidates.  Rounds over all 2048 elements would cost k full scans, so a
-// threshold first discards almost everything: in each wave the k-th largest of
-// the 64 lane maxima (counted with multiplicity) is a value that at least k of the
-// wave's elements reach, so the slice's k best all lie at or above the largest of
-// the four wave thresholds.  The elements that reach it (typically little more
-// than k) are packed into LDS and one wave selects among them.  If more than
-// kCap elements reach it (many equal values), the workgroup falls back to rounds
-// over every element.  Stage B: one workgroup per sequence, one wave per head row
-// merges the slices' candidates and then all threads fill the tree tokens and
-// positions.
+// Rows of up to 32768 logits (every vocabulary of the workloads): one launch,
+// topk_rows, one workgroup per (sequence, head row) with the whole row in
+// registers.  A radix search over the thread maxima gives a threshold that at
+// least k elements reach; the few elements at or above it are ranked directly.
+// The workgroup then writes the tree tokens of the nodes at its own depth, since a
+// node's token depends on its depth's row only.  Heavy ties (more than 1024
+// elements at the threshold) fall back to k selection rounds per wave.
+//
+// Longer rows: two launches.  A wave selects its k best elements in k rounds;
+// each round every lane offers its best element that comes after the previous
+// winner, and a DPP row-op reduction picks the winner.  Stage A: every workgroup
+// reduces a 2048-element slice of one row to k candidates.  Rounds over all 2048
+// elements would cost k full scans, so a threshold first discards almost
+// everything: in each wave the k-th largest of the 64 lane maxima (counted with
+// multiplicity) is a value that at least k of the wave's elements reach, so the
+// slice's k best all lie at or above the largest of the four wave thresholds.
+// The elements that reach it (typically little more than k) are packed into LDS
+// and one wave selects among them.  If more than kCap elements reach it (many
+// equal values), the workgroup falls back to rounds over every element.  Stage
+// B: one workgroup per sequence, one wave per head row merges the slices'
+// candidates and then all threads fill the tree tokens and positions.
 #include <climits>
 
 #include "common.h"
@@ -215,6 +222,301 @@ __global__ void topk_merge_expand(const Cand* __restrict__ cand, int K1, int k, 
     }
 }
 
+// One workgroup per (sequence, head row) when the whole row fits in registers: 1024
+// threads hold 32 logits each (elements tid + 1024 j, so every wave load reads 256
+// contiguous bytes).  A threshold that at least k elements reach comes from the
+// thread maxima: two 8-bit radix passes over their order-preserving keys (LDS
+// histograms, one wave scanning the 256 bins from the top) locate the k-th largest
+// maximum to 16 key bits, and every element at or above that bin's lower bound is a
+// candidate (typically a few more than k).  Each candidate's rank is the number of
+// candidates ahead of it in the total order, so the k best land in place without
+// sequential rounds.  The workgroup then writes the tree tokens of the nodes at its
+// depth (a node's token depends on its own depth's row only) and their positions, so
+// no second launch is needed.  Heavy ties (more than 1024 candidates) fall back to
+// per-wave selection rounds over every element.
+constexpr int kRowThreads = 1024;
+constexpr int kRowPer = 32;
+constexpr int kRowMaxV = kRowThreads * kRowPer;
+constexpr int kRowWaves = kRowThreads / 64;
+
+// Order-preserving map of a float onto uint32 (larger float, larger key); -0 is first
+// made +0 so that equal values get equal keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit key of (value, index): larger key = earlier in (value desc, index asc).
+__device__ __forceinline__ uint64_t cand_key(float v, int i) {
+    return ((uint64_t)order_key(v) << 32) | (uint32_t)(~(uint32_t)i);
+}
+
+// Exclusive prefix sum over the wave of a count below 2^11: bit b of every lane's count
+// contributes 2^b for each lower lane that has it (one ballot and one mbcnt per bit).
+__device__ __forceinline__ int wave_excl_prefix11(int x) {
+    int r = 0;
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) r += lanes_below(__ballot((x >> bit) & 1)) << bit;
+    return r;
+}
+
+// Wave 0: scan 256 bins from the top; the bin where the running count reaches `need`,
+// and how many of the counted items lie strictly above it.
+__device__ __forceinline__ void radix_pick(const int* hist, int need, int lane, int* out_bin, int* out_above) {
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+    const int sl = c[0] + c[1] + c[2] + c[3];
+    int run = wave_excl_prefix11(sl);  // items in bins above this lane's
+    if (run < need && run + sl >= need) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (run + c[j] >= need) {
+                *out_bin = 255 - 4 * lane - j;
+                *out_above = run;
+                break;
+            }
+            run += c[j];
+        }
+    }
+}
+
+// Largest 64-bit value over the wave, uniform (same DPP sequence as wave_argmax_dpp).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#define MDT_MAX64_STEP(CTRL, ROWS)                                                                   \
+    {                                                                                               \
+        const int hi = (int)(x >> 32), lo = (int)(uint32_t)x;                                        \
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false) << 32) | \
+                           (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);    \
+        x = o > x ? o : x;                                                                          \
+    }
+    MDT_MAX64_STEP(0xB1, 0xf)
+    MDT_MAX64_STEP(0x4E, 0xf)
+    MDT_MAX64_STEP(0x141, 0xf)
+    MDT_MAX64_STEP(0x140, 0xf)
+    MDT_MAX64_STEP(0x142, 0xa)
+    MDT_MAX64_STEP(0x143, 0xc)
+#undef MDT_MAX64_STEP
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(x >> 32), 63);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Index of a thread's element j: with 16-byte loads (VEC4) the thread holds runs of four
+// (elements 4(tid + 1024 q) + c, j = 4q + c), otherwise single elements tid + 1024 j.
+// Either way a thread's indices increase with j.
+template <bool VEC4>
+__device__ __forceinline__ int row_elem(int tid, int j) {
+    return VEC4 ? 4 * (tid + kRowThreads * (j >> 2)) + (j & 3) : tid + kRowThreads * j;
+}
+
+// Inverse of order_key.
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// k rounds over a thread's kRowPer elements (element j has index row_elem(tid, j), valid
+// below V; kk holds their order keys): each round every lane offers its best element
+// after the previous winner, and a 64-bit (key, ~index) wave maximum picks the winner.
+// Values come back from the keys (a -0 element reads as +0).
+template <bool VEC4>
+__device__ void wave_select_row(const uint32_t (&kk)[kRowPer], int tid, int V, int k, Cand* out) {
+    uint32_t lk = 0xffffffffu;
+    int li = -1;  // previous winner (key, index); the first round admits everything
+    for (int r = 0; r < k; ++r) {
+        uint32_t bk = 0;
+        int bi = INT_MAX;
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < kRowPer; ++j) {
+            const int e = row_elem<VEC4>(tid, j);
+            const bool after = (kk[j] < lk) | ((kk[j] == lk) & (e > li)) | (r == 0);
+            const bool take = (e < V) & after & (!any | (kk[j] > bk));  // same key: smaller j came first
+            bk = take ? kk[j] : bk;
+            bi = take ? e : bi;
+            any = any | take;
+        }
+        const uint64_t mine = any ? (((uint64_t)bk << 32) | (uint32_t)~(uint32_t)bi) : 0ull;
+        const uint64_t w = wave_max_u64(mine);
+        lk = (uint32_t)(w >> 32);
+        li = (int)~(uint32_t)w;
+        if ((threadIdx.x & 63) == 0) out[r] = Cand{w ? key_value(lk) : -INFINITY, w ? li : INT_MAX};
+    }
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kRowThreads) void topk_rows(const float* __restrict__ logits, int V, int k, int K1,
+                                                         const int32_t* __restrict__ parent,
+                                                         const int32_t* __restrict__ depth,
+                                                         const int32_t* __restrict__ rank, int T,
+                                                         const int32_t* __restrict__ prefix_len,
+                                                         int32_t* __restrict__ topk_idx, float* __restrict__ topk_val,
+                                                         int32_t* __restrict__ tokens, int32_t* __restrict__ pos) {
+    __shared__ Cand surv[kRowThreads + 64];  // candidates, then one discard slot per lane
+    __shared__ Cand wave_best[kRowWaves * MDT_MAX_TOPK];
+    __shared__ Cand best[MDT_MAX_TOPK];
+    __shared__ int hist[2][256];
+    __shared__ int pick[5];  // bin 1, count above it, bin 2, count above it, candidates
+    __shared__ int node[3][MDT_MAX_NODES];  // depth, rank, parent
+    __shared__ int node_L;
+    const int row = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The output pointers are held in vector registers from here on: left to itself the
+    // compiler reloads kernel arguments late to free scalar registers, and such a reload
+    // waits on memory in the middle of the selection.
+    asm volatile("" : "+v"(topk_idx), "+v"(topk_val), "+v"(tokens), "+v"(pos));
+    // The tree inputs of this thread's node (T <= MDT_MAX_NODES) and the prefix length,
+    // used at the end, are requested first and parked in LDS once the logits are in
+    // flight.  The prefix length is read with a vector load through a register offset
+    // (a scalar load would share the counter that every later wait for an LDS result
+    // waits on).
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    const int L = prefix_len[b + vzero];
+    const int i0 = min(tid, T - 1);
+    const int dep0 = depth[i0], rk0 = rank[i0], par0 = parent[i0];
+    // the row through a buffer resource: one 32-bit offset register per load
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(logits + ((size_t)b * K1 + row) * V), (short)0, V * 4, 0x00020000);
+    float v[kRowPer];
+    if constexpr (VEC4) {
+#pragma unroll
+        for (int q = 0; q < kRowPer / 4; ++q) {
+            // four adjacent dword loads, which the compiler merges into one 16-byte load
+            const int off = 4 * min(row_elem<true>(tid, 4 * q), V - 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                v[4 * q + c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * c, 0, 0));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRowPer; ++j)
+            v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * min(row_elem<false>(tid, j), V - 1), 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // unconditional (threads past T rewrite node T-1 with its own values): a store under
+    // a branch would let the compiler sink the loads behind the logits
+    node[0][i0] = dep0;
+    node[1][i0] = rk0;
+    node[2][i0] = par0;
+    node_L = L;
+    if (tid < 512) hist[tid >> 8][tid & 255] = 0;
+    if (tid == 0) pick[4] = 0;
+    // elements past the row become NaN: no comparison selects them and fmaxf skips them
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+        v[j] = row_elem<VEC4>(tid, j) < V ? v[j] : __builtin_nanf("");
+        m = fmaxf(m, v[j]);
+    }
+    const uint32_t km = order_key(m);
+    __syncthreads();
+    atomicAdd(&hist[0][km >> 24], 1);
+    __syncthreads();
+    if (wave == 0) radix_pick(hist[0], k, lane, &pick[0], &pick[1]);
+    __syncthreads();
+    const int b1 = pick[0];
+    if ((int)(km >> 24) == b1) atomicAdd(&hist[1][(km >> 16) & 255], 1);
+    __syncthreads();
+    if (wave == 0) radix_pick(hist[1], k - pick[1], lane, &pick[2], &pick[3]);
+    __syncthreads();
+    const uint32_t thr = ((uint32_t)b1 << 24) | ((uint32_t)pick[2] << 16);
+
+    // the same test as a float comparison: v >= tf exactly when order_key(v) >= thr
+    // (keys at or below that of -inf mean every element)
+    const float tf = (thr & 0x80000000u) ? __uint_as_float(thr & 0x7fffffffu)
+                   : thr <= order_key(-INFINITY) ? -INFINITY : __uint_as_float(~thr);
+    // candidates: only a thread whose maximum passes holds any; it counts them, takes
+    // its slots with one LDS atomic and writes every element (the ones that fail go to
+    // a slot of its own past the list, so no write sits under a branch)
+    if (m >= tf) {
+        uint32_t mask = 0;  // bit j: element j passes (a bit mask keeps the tests in VGPRs)
+#pragma unroll
+        for (int j = 0; j < kRowPer; ++j) mask |= (v[j] >= tf ? 1u : 0u) << j;
+        int at = atomicAdd(&pick[4], (int)__popc(mask));
+        if ((mask & (mask - 1u)) == 0u) {
+            // the usual case, one candidate (the thread's maximum itself), or none (a thread
+            // past the row end when the threshold is -inf)
+            if (mask != 0u && at < kRowThreads) surv[at] = Cand{m, row_elem<VEC4>(tid, __builtin_ctz(mask))};
+        } else {
+            const int trash = kRowThreads + lane;
+#pragma unroll
+            for (int j = 0; j < kRowPer; ++j) {
+                const int in = (int)((mask >> j) & 1u);
+                surv[in && at < kRowThreads ? at : trash] = Cand{v[j], row_elem<VEC4>(tid, j)};
+                at += in;
+            }
+        }
+    }
+    __syncthreads();
+    const int n = pick[4];  // uniform over the workgroup
+    if (n <= 64) {
+        // one wave: lane c holds candidate c; its rank counts the candidates ahead of it
+        if (wave == 0) {
+            const Cand c = surv[min(lane, max(n - 1, 0))];
+            const uint64_t key = lane < n ? cand_key(c.v, c.i) : 0ull;
+            const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+            int r = 0;
+            for (int s2 = 0; s2 < n; ++s2) {
+                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(khi, s2) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane(klo, s2);
+                r += o > key ? 1 : 0;
+            }
+            if (lane < n && r < k) best[r] = c;
+        }
+    } else if (n <= kRowThreads) {
+        if (tid < n) {
+            const Cand c = surv[tid];
+            const uint64_t key = cand_key(c.v, c.i);
+            int r = 0;
+            for (int s2 = 0; s2 < n; ++s2) {
+                const Cand o = surv[s2];
+                r += cand_key(o.v, o.i) > key ? 1 : 0;
+            }
+            if (r < k) best[r] = c;
+        }
+    } else {
+        // many equal values at the threshold: every wave selects among its own elements,
+        // then one wave among the waves' winners
+        uint32_t kk[kRowPer];
+#pragma unroll
+        for (int j = 0; j < kRowPer; ++j) kk[j] = order_key(v[j]);
+        wave_select_row<VEC4>(kk, tid, V, k, wave_best + wave * k);
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int E = kRowWaves * MDT_MAX_TOPK / 64;
+            float mv[E];
+            int mi[E];
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const int c = lane + 64 * j;
+                mv[j] = c < kRowWaves * k ? wave_best[c].v : -INFINITY;
+                mi[j] = c < kRowWaves * k ? wave_best[c].i : INT_MAX;
+            }
+            wave_select<E>(mv, mi, k, best);
+        }
+    }
+    __syncthreads();
+    const size_t o = ((size_t)b * K1 + row) * k;
+    if (tid < k) {
+        const Cand c = best[tid];
+        topk_idx[o + tid] = c.i;
+        // the heavy-tie path selected on keys, which read -0 as +0: take the value itself
+        topk_val[o + tid] = n > kRowThreads ? logits[((size_t)b * K1 + row) * V + c.i] : c.v;
+    }
+    // nodes at this row's depth; row 0 also writes the nodes whose depth is out of range
+    if (tid < T) {
+        const int i = tid;
+        const int dep = node[0][i], rk = node[1][i], par = node[2][i];
+        const bool in_range = dep >= 0 && dep < K1;
+        if (in_range ? dep == row : row == 0) {
+            const bool ok = in_range && rk >= 0 && rk < k && (i == 0 ? dep == 0 : par < i);
+            tokens[(size_t)b * T + i] = ok ? best[rk].i : -1;
+            pos[(size_t)b * T + i] = node_L + dep;
+        }
+    }
+}
+
 int num_slices(int V) { return (V + kSlice - 1) / kSlice; }
 
 }  // namespace
@@ -246,6 +548,12 @@ extern "C" mdt_status mdt_topk_tree_expand(void* stream, int B, int K, int V, in
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     const int K1 = K + 1;
+    if (V <= kRowMaxV) {
+        auto kern = V % 4 == 0 ? topk_rows<true> : topk_rows<false>;
+        MDT_LAUNCH("topk_rows", kern, dim3(K1, B), dim3(kRowThreads), 0, s, logits, V, k_cfg, K1, tree->parent,
+                   tree->depth, tree->rank, tree->T, prefix_len, topk_idx, topk_val, tree_tokens, pos_ids);
+        return mdt_launched("topk_rows");
+    }
     const int ns = num_slices(V);
     Cand* cand = (Cand*)ws;
     MDT_LAUNCH("topk_slices", topk_slices, dim3(ns, B * K1), dim3(256), 0, s, logits, V, k_cfg, ns, cand);

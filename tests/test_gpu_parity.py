@@ -181,7 +181,7 @@ def _tie_rows(V, rng):
     return np.stack(rows).astype(np.float32)
 
 
-@pytest.mark.parametrize("V,k", [(3001, 10), (32000, 10), (32000, 32), (50001, 16), (37, 32)])
+@pytest.mark.parametrize("V,k", [(3001, 10), (32000, 10), (32000, 32), (32768, 32), (32769, 10), (50001, 16), (37, 32)])
 def test_stage_topk_ties_and_fallback(V, k):
     """Exact order (value desc, index asc) on tie-heavy rows, including rows where
     far more elements than the survivor capacity reach the threshold."""
