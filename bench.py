@@ -12,7 +12,10 @@ the roofline object uses the dominant kernel's (the W2 head GEMV stream).  The
 timed region is K replays of a HIP graph that holds the whole step, between two
 torch.cuda.synchronize() calls (the events add dispatch gaps, so they stay out
 of it).  The CPU oracle is timed on the host on whole steps of the same
-workload for about 10 s.  One JSON line goes to stdout.
+workload for about 10 s.  A report of chained steps (``decode_loop``: each step
+starts from the previous step's last accepted node, replayed as one graph) gives
+the time per chained step and the synthetic acceptance; it is context, not the
+metric.  One JSON line goes to stdout.
 """
 
 from __future__ import annotations
@@ -29,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+LOOP_STEPS = 8           # chained steps of the decode-loop report
 METRIC = "Medusa verify-steps/s + achieved HBM GB/s vs peak, 7B-shape 64-node tree"
 
 
@@ -91,6 +95,42 @@ def cpu_baseline(w, inp, mode, tau, eps, delta):
                       f"{len(os.sched_getaffinity(0))} affinity cores"}
 
 
+def decode_loop_report(w, inp, seed, step, mode, tau, eps, delta, replays):
+    """LOOP_STEPS chained steps (the next step starts from the last accepted node), replayed as
+    one HIP graph: time per chained step and the synthetic acceptance (tokens per step)."""
+    import numpy as np
+    import torch
+    from medusa_tree_verification_heads_amd.step import DecodeLoop
+    from workloads import step_qkv
+    qkv = [step_qkv(w, seed, s) for s in range(LOOP_STEPS)]
+    loop = DecodeLoop(w, inp, qkv, mode, tau, eps, delta, step=step)
+    loop.run()
+    torch.cuda.synchronize()
+    n_acc = loop.n_acc.cpu().numpy()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        loop.run()
+    reps = max(1, replays // LOOP_STEPS)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / (reps * LOOP_STEPS)
+    mean_acc = float(n_acc.mean())
+    return {"steps": LOOP_STEPS, "us_per_step": round(us, 2), "mean_accepted_per_step": round(mean_acc, 3),
+            "accepted_tokens_per_s": round(1e6 / us * mean_acc * w.B, 1),
+            "n_acc_per_step": n_acc[:, 0].tolist(),
+            "note": "synthetic random weights: the acceptance is not that of a trained model"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +140,7 @@ def main():
     ap.add_argument("--mode", default="typical", choices=["typical", "greedy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the chained-step (decode loop) report")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -138,7 +179,7 @@ def main():
     tau = run.temperature if run else (0.7 if args.mode == "typical" else 0.0)
     eps, delta = (run.eps, run.delta) if run else (0.09, 0.3)
     t0 = time.perf_counter()
-    inp = make_inputs(w, seed)
+    inp = make_inputs(w, seed, steps=LOOP_STEPS)   # cache room for the chained-step report
     log(f"inputs for {name} (seed {seed}) drawn in {time.perf_counter() - t0:.1f}s")
     step = VerifyStep(w, inp, args.mode, tau, eps, delta)
     T = step.tree.T
@@ -189,6 +230,11 @@ def main():
         timing = "HIP-graph replay of the six calls"
     log(f"timed {args.steps} steps ({timing}): {ms_per_step * 1e3:.1f} us/step")
 
+    loop_rep = None
+    if not args.no_graph and not args.no_loop:
+        loop_rep = decode_loop_report(w, inp, seed, step, args.mode, tau, eps, delta, args.steps)
+        log(f"decode loop: {loop_rep}")
+
     lens = inp["prefix_len"]
     ab = algorithmic_bytes(w, T, lens)
     dom = "heads_gemv_w2"
@@ -226,6 +272,7 @@ def main():
         "eager_ms_per_step": round(eager_ms, 5),
         "n_acc": step.n_acc.cpu().tolist()[:8],
         "roofline": roofline,
+        "decode_loop": loop_rep,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -10,6 +10,7 @@
  *   mdt_accept_path       greedy or typical acceptance -> longest accepted path
  *   mdt_kv_compact        append the accepted path's keys/values to the cache
  *   mdt_accept_compact    the last two in one launch (same results)
+ *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
  *
  * The pages this follows are the Medusa pages: "Medusa: Simple LLM Inference
  * Acceleration Framework with Multiple Decoding Heads" (summary page, section 3.2
@@ -369,6 +370,26 @@ mdt_status mdt_accept_compact(void* stream, mdt_dtype dt, int B, int H, int Dh, 
                               int mode, float eps, float delta, float temperature, int32_t* path, int path_stride,
                               int32_t* n_acc, const void* k_rot, const void* v, const mdt_kv_cache* cache,
                               const int32_t* prefix_len, int32_t* new_prefix_len);
+
+/*
+ * Hidden state of the next step: h_next[b] = x[b][path[b][n_acc[b] - 1]], the node
+ * output of sequence b's deepest accepted node.  The summary page, section 3.2, has the
+ * next iteration continue from the last accepted token, whose hidden state feeds the
+ * heads and whose LM-head row gives the next root; with x the node outputs that
+ * mdt_verify_logits consumed, this row is exactly that hidden state.
+ *  dt           MDT_BF16 or MDT_F32: storage type of x and h_next
+ *  B, T, d      sequences, tree nodes (1..MDT_MAX_NODES), hidden size; d * element size
+ *               must be a multiple of 16 bytes
+ *  x            device [B][T][d] node outputs (the tree-attention output viewed as rows)
+ *  path, path_stride, n_acc
+ *               device, as written by mdt_accept_path / mdt_accept_compact
+ *  h_next       device [B][d] (output; must not overlap x)
+ * A sequence whose n_acc is outside 1..path_stride or whose last path node is outside
+ * 0..T-1 gets a row of zeros.
+ * Errors: MDT_ERR_DTYPE, MDT_ERR_SHAPE, MDT_ERR_NULL, MDT_ERR_ALIGN.
+ */
+mdt_status mdt_next_state(void* stream, mdt_dtype dt, int B, int T, int d, const void* x, const int32_t* path,
+                          int path_stride, const int32_t* n_acc, void* h_next);
 
 /* ------------------------------------------------------------------------- */
 /* Misc                                                                       */

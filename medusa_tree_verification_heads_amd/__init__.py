@@ -6,7 +6,8 @@ device pointers and the current torch stream to the C ABI declared in
 ``include/mdt.h``.  The functions carry the C names without the ``mdt_`` prefix:
 
     medusa_heads, topk_tree_expand, tree_attention, verify_logits,
-    accept_path, kv_compact, accept_compact (the last two in one launch)
+    accept_path, kv_compact, accept_compact (the last two in one launch),
+    next_state (the hidden state a following step starts from)
 
 plus the static tree helpers (``Tree``) and workspace queries.  Importing this
 module without a built ``libmdt.so`` raises ImportError: there is no fallback.
@@ -89,6 +90,8 @@ _SIGS = [
     ("mdt_accept_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
                                    c_void_p, c_int, c_float, c_float, c_float, c_void_p, c_int, c_void_p, c_void_p,
                                    c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
+    ("mdt_next_state", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                               c_void_p]),
 ]
 
 EXPORTED = [name for name, _, _ in _SIGS]
@@ -388,6 +391,15 @@ def kv_compact(path, n_acc, k_rot, v, cache: KVCache, prefix_len, new_prefix_len
                               _ptr(n_acc), _ptr(k_rot), _ptr(v), ctypes.byref(cache.desc), _ptr(prefix_len),
                               _ptr(new_prefix_len)), "kv_compact")
     return new_prefix_len
+
+
+def next_state(x, path, n_acc, out=None, stream=None):
+    """Row of x [B][T][d] at each sequence's deepest accepted node -> [B][d]."""
+    B, T, d = x.shape
+    out = torch.empty((B, d), dtype=x.dtype, device=x.device) if out is None else out
+    _check(lib.mdt_next_state(_stream(stream), _dtype_code(x), B, T, d, _ptr(x), _ptr(path), path.shape[1],
+                              _ptr(n_acc), _ptr(out)), "next_state")
+    return out
 
 
 def accept_compact(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps, delta, temperature, k_rot, v,

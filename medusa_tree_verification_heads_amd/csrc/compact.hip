@@ -10,6 +10,11 @@
 // with 16-byte vector moves.  Every workgroup of a sequence first validates the
 // whole sequence (path nodes, length, destination slots, pages), so either the
 // full path is written or nothing of it.
+//
+// mdt_next_state: the node output of a sequence's deepest accepted node becomes the
+// hidden state the next step starts from (summary page, section 3.2: the next
+// iteration continues from the last accepted token).  One workgroup per sequence
+// copies that row with 16-byte moves.
 #include "kv_slot.h"
 
 namespace {
@@ -39,6 +44,18 @@ __global__ __launch_bounds__(256) void compact_kernel(KvSlots cache, const int32
         K[dst + e] = k_rot[src + e];
         Vv[dst + e] = v[src + e];
     }
+}
+
+__global__ __launch_bounds__(256) void next_state_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ path,
+                                                           int path_stride, const int32_t* __restrict__ n_acc, int T,
+                                                           int row_vec, uint4* __restrict__ h_next) {
+    const int b = blockIdx.x;
+    const int n = n_acc[b];
+    const int node = path[(long)b * path_stride + min(max(n - 1, 0), path_stride - 1)];
+    const bool ok = n >= 1 && n <= path_stride && node >= 0 && node < T;
+    const long src = ((long)b * T + (ok ? node : 0)) * row_vec;
+    uint4* dst = h_next + (long)b * row_vec;
+    for (int e = threadIdx.x; e < row_vec; e += blockDim.x) dst[e] = ok ? x[src + e] : make_uint4(0, 0, 0, 0);
 }
 
 }  // namespace
@@ -85,4 +102,19 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
     MDT_LAUNCH("compact_kernel", compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path,
                path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
     return mdt_launched("compact_kernel");
+}
+
+extern "C" mdt_status mdt_next_state(void* stream, mdt_dtype dt, int B, int T, int d, const void* x,
+                                     const int32_t* path, int path_stride, const int32_t* n_acc, void* h_next) {
+    MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    MDT_REQUIRE(B >= 1 && B <= 65535 && T >= 1 && T <= MDT_MAX_NODES && d >= 1, MDT_ERR_SHAPE,
+                "bad shape B=%d T=%d d=%d", B, T, d);
+    MDT_REQUIRE(path_stride >= 1 && path_stride <= MDT_MAX_NODES, MDT_ERR_SHAPE, "path_stride out of range");
+    const size_t row_bytes = (size_t)d * (dt == MDT_BF16 ? 2 : 4);
+    MDT_REQUIRE(row_bytes % 16 == 0, MDT_ERR_SHAPE, "d*element size must be a multiple of 16 bytes");
+    MDT_REQUIRE(x && path && n_acc && h_next, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(h_next), MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    MDT_LAUNCH("next_state_kernel", next_state_kernel, dim3(B), dim3(256), 0, (hipStream_t)stream, (const uint4*)x,
+               path, path_stride, n_acc, T, (int)(row_bytes / 16), (uint4*)h_next);
+    return mdt_launched("next_state_kernel");
 }

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path, kv_compact,
-               medusa_heads,
+               medusa_heads, next_state,
                medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace)
 
@@ -69,25 +69,34 @@ class VerifyStep:
         self.ws_attn = new_workspace(tree_attention_workspace(dt, B, T, H, Dh, self.cache.desc.capacity), dev)
         self.ws_verify = new_workspace(verify_logits_workspace(dt, B, T, d, V), dev)
 
-    def run(self, stream=None):
+    def run(self, stream=None, h=None, qkv=None, prefix_len=None, new_prefix_len=None, tokens=None, path=None,
+            n_acc=None):
+        """Enqueue one step.  The keyword arguments replace the step's own input or output
+        tensors for this call (a chain of steps passes each step's own)."""
         t, w = self.t, self.w
-        medusa_heads(t["h"], t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
-        topk_tree_expand(self.logits, w.k_cfg, self.tree, self.prefix_len, self.topk_idx, self.topk_val, self.tokens,
+        h = t["h"] if h is None else h
+        q, k, v = (t["q"], t["k"], t["v"]) if qkv is None else qkv
+        prefix_len = self.prefix_len if prefix_len is None else prefix_len
+        new_len = self.new_len if new_prefix_len is None else new_prefix_len
+        tokens = self.tokens if tokens is None else tokens
+        path = self.path if path is None else path
+        n_acc = self.n_acc if n_acc is None else n_acc
+        medusa_heads(h, t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
+        topk_tree_expand(self.logits, w.k_cfg, self.tree, prefix_len, self.topk_idx, self.topk_val, tokens,
                          self.pos, ws=self.ws_topk, stream=stream)
-        tree_attention(t["q"], t["k"], t["v"], self.cache, self.prefix_len, self.tree, w.rope_theta, out=self.o,
+        tree_attention(q, k, v, self.cache, prefix_len, self.tree, w.rope_theta, out=self.o,
                        k_rot=self.k_rot, ws=self.ws_attn, stream=stream)
         x = self.o.view(w.B * self.tree.T, w.d)
-        verify_logits(x, t["Wlm"], self.tree, self.tokens, self.temperature, stats=self.stats, edge=self.edge,
+        verify_logits(x, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats, edge=self.edge,
                       logits=self.vlogits, want_logits=self.vlogits is not None, ws=self.ws_verify, stream=stream)
         if self.fused_tail:
-            accept_compact(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta,
-                           self.temperature, self.k_rot, t["v"], self.cache, self.prefix_len, path=self.path,
-                           n_acc=self.n_acc, new_prefix_len=self.new_len, stream=stream)
+            accept_compact(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta,
+                           self.temperature, self.k_rot, v, self.cache, prefix_len, path=path,
+                           n_acc=n_acc, new_prefix_len=new_len, stream=stream)
             return
-        accept_path(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta, self.temperature,
-                    path=self.path, n_acc=self.n_acc, stream=stream)
-        kv_compact(self.path, self.n_acc, self.k_rot, t["v"], self.cache, self.prefix_len, self.new_len,
-                   stream=stream)
+        accept_path(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta, self.temperature,
+                    path=path, n_acc=n_acc, stream=stream)
+        kv_compact(path, n_acc, self.k_rot, v, self.cache, prefix_len, new_len, stream=stream)
 
     def outputs(self) -> dict:
         """Copies of every output on the host (synchronises)."""
@@ -105,3 +114,43 @@ class VerifyStep:
                     stats=f(self.stats).view(np.int32), edge=f(self.edge), vlogits=f(self.vlogits),
                     path=f(self.path), n_acc=f(self.n_acc), new_len=f(self.new_len),
                     Kc=f(self.t["Kc"]), Vc=f(self.t["Vc"]))
+
+
+class DecodeLoop:
+    """Chained steps on one stream (multi-step decoding).
+
+    Step s+1 starts from step s: its hidden state is the node output of each
+    sequence's deepest accepted node (``next_state``), its prefix length is step s's
+    new length, and the cache already holds step s's accepted keys and values.  The
+    tree's q/k/v inputs of every step are given (``qkv_steps``).  Every step reads
+    and writes its own prefix-length, hidden-state, token, path and n_acc tensors,
+    so ``run()`` can be repeated (or replayed as a graph) from the same start.
+    """
+
+    def __init__(self, w, inp: dict, qkv_steps, mode: str = "greedy", temperature: float = 0.0, eps: float = 0.09,
+                 delta: float = 0.3, device="cuda", fused_tail: bool = True, want_logits: bool = False,
+                 step: VerifyStep = None):
+        # an existing step (same inputs) can be reused: the chain only adds its own state tensors
+        self.step = step or VerifyStep(w, inp, mode, temperature, eps, delta, device, want_logits=want_logits,
+                                       fused_tail=fused_tail)
+        st = self.step
+        self.S = len(qkv_steps)
+        dev = st.dev
+        self.qkv = [tuple(to_device(q[n], dev) for n in ("q", "k", "v")) for q in qkv_steps]
+        S, B, T = self.S, w.B, st.tree.T
+        self.h = [st.t["h"]] + [torch.empty_like(st.t["h"]) for _ in range(S)]
+        self.lens = [st.prefix_len] + [torch.empty_like(st.prefix_len) for _ in range(S)]
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tokens = torch.empty((S, B, T), **i32)
+        self.paths = torch.empty((S, B, st.path.shape[1]), **i32)
+        self.n_acc = torch.empty((S, B), **i32)
+
+    def run_step(self, s: int, stream=None):
+        st, w = self.step, self.step.w
+        st.run(stream, h=self.h[s], qkv=self.qkv[s], prefix_len=self.lens[s], new_prefix_len=self.lens[s + 1],
+               tokens=self.tokens[s], path=self.paths[s], n_acc=self.n_acc[s])
+        next_state(st.o.view(w.B, st.tree.T, w.d), self.paths[s], self.n_acc[s], out=self.h[s + 1], stream=stream)
+
+    def run(self, stream=None):
+        for s in range(self.S):
+            self.run_step(s, stream)

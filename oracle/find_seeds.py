@@ -7,6 +7,11 @@ run of the workload.  Only this package (``oracle``) and the input generator are
 used.
 
     python -m oracle.find_seeds [name ...]
+    python -m oracle.find_seeds --loop S [name ...]   # S chained steps ("name@loopS" entries)
+
+Chained steps start from attention outputs, whose scale shrinks with the prefix
+length, so their logits are close together and only the small cases have loop
+seeds with every margin >= MIN_MARGIN.
 """
 
 from __future__ import annotations
@@ -18,7 +23,7 @@ import time
 
 import numpy as np
 
-from workloads import make_inputs
+from workloads import make_inputs, step_qkv
 from workloads.configs import PARITY_CASES, WORKLOADS
 
 from . import margins, step, tree as otree
@@ -53,23 +58,41 @@ def case_margin(w, seed: int) -> float:
     return m
 
 
-def main(names):
+def loop_margin(w, seed: int, steps: int) -> float:
+    """Smallest decision margin over every step of a chain of ``steps``, for every acceptance run."""
+    inp = make_inputs(w, seed, steps=steps)
+    qkv = [step_qkv(w, seed, s) for s in range(steps)]
+    tree = otree.build_tree(w)
+    m = float("inf")
+    for run in w.accept:
+        res = step.decode_loop(w, inp, qkv, tree, run.mode, run.temperature, run.eps, run.delta)
+        for r in res:
+            m = min(m, margins.step_margin(r, w, tree, run.mode, run.eps, run.delta, run.temperature))
+    return m
+
+
+def main(names, steps=1):
     seeds = json.load(open(OUT)) if os.path.exists(OUT) else {}
     for name in names:
         idx = ORDER.index(name) + 1
         w = PARITY_CASES.get(name) or WORKLOADS[name]
+        key = name if steps == 1 else f"{name}@loop{steps}"
         for attempt in range(100):
-            seed = 1000 * idx + attempt
+            seed = 1000 * idx + attempt + (0 if steps == 1 else 500)
             t0 = time.time()
-            m = case_margin(w, seed)
-            print(f"{name} seed {seed}: margin {m:.3e} ({time.time() - t0:.1f}s)", flush=True)
+            m = case_margin(w, seed) if steps == 1 else loop_margin(w, seed, steps)
+            print(f"{key} seed {seed}: margin {m:.3e} ({time.time() - t0:.1f}s)", flush=True)
             if m >= margins.MIN_MARGIN:
-                seeds[name] = {"seed": seed, "margin": m}
+                seeds[key] = {"seed": seed, "margin": m}
                 break
         else:
-            raise SystemExit(f"no seed found for {name}")
+            raise SystemExit(f"no seed found for {key}")
         json.dump(seeds, open(OUT, "w"), indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ORDER)
+    args = sys.argv[1:]
+    n_steps = 1
+    if args[:1] == ["--loop"]:
+        n_steps, args = int(args[1]), args[2:]
+    main(args or ORDER, n_steps)

@@ -310,3 +310,31 @@ def step(w, inp: dict, tree: OracleTree, mode: str, tau: float, eps=0.09, delta=
     return dict(logits=logits, a=a, topk_idx=tk_idx, topk_val=tk_val, tokens=tokens, pos=pos,
                 o=o, k_rot=k_rot, x=x, z=z, stats=stats, edge=edge, paths=paths, n_acc=n_acc,
                 K_new=Kn, V_new=Vn, new_len=new_len)
+
+
+# ----------------------------------------------------------------------------
+# chained steps (multi-step decoding)
+# ----------------------------------------------------------------------------
+
+def decode_loop(w, inp: dict, qkv_steps, tree: OracleTree, mode: str, tau: float, eps=0.09, delta=0.3):
+    """Chain one step per entry of ``qkv_steps`` (the tree's q/k/v inputs of that step).
+
+    Summary page, section 3.2: after acceptance the next iteration continues from
+    the last accepted token.  Step s+1 starts from step s's result: its hidden state
+    h is the node output of each sequence's deepest accepted node (whose LM-head
+    row is that node's verifier row, so the next root is that row's argmax), its
+    cache is the compacted one and its prefix length is the new length.  Weights
+    stay the same.  Returns the list of step results.
+    """
+    state = {k: v for k, v in inp.items() if k not in ("q", "k", "v")}
+    results = []
+    for qkv in qkv_steps:
+        cur = dict(state)
+        cur.update(qkv)
+        r = step(w, cur, tree, mode, tau, eps, delta)
+        results.append(r)
+        B = w.B
+        state["h"] = np.stack([r["o"][b, r["paths"][b][-1]].reshape(w.d) for b in range(B)])
+        state["Kc"], state["Vc"] = r["K_new"], r["V_new"]
+        state["prefix_len"] = np.asarray(r["new_len"], dtype=np.int32)
+    return results

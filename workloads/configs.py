@@ -66,9 +66,9 @@ class Workload:
     def max_prefix(self) -> int:
         return self.L_range[1] if self.L_range else self.L
 
-    def cache_capacity(self) -> int:
-        """Slots per sequence: the prefix plus room for one accepted path (K+1 tokens)."""
-        return self.max_prefix() + self.K + 1
+    def cache_capacity(self, steps: int = 1) -> int:
+        """Slots per sequence: the prefix plus room for one accepted path (K+1 tokens) per step."""
+        return self.max_prefix() + steps * (self.K + 1)
 
 
 TYPICAL_07 = AcceptRun("typical", 0.7, 0.09, 0.3)

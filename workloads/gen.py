@@ -87,11 +87,12 @@ def prefix_lengths(w: Workload, seed: int) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=w.B, dtype=np.int64).astype(np.int32)
 
 
-def page_layout(w: Workload, seed: int, lens: np.ndarray):
-    """(page_table [B][max_pages] int32, number of physical pages)."""
+def page_layout(w: Workload, seed: int, lens: np.ndarray, steps: int = 1):
+    """(page_table [B][max_pages] int32, number of physical pages); room for ``steps`` paths."""
     ps = w.page_size
-    need = [(int(L) + w.K + 1 + ps - 1) // ps for L in lens]
-    max_pages = (w.max_prefix() + w.K + 1 + ps - 1) // ps
+    room = steps * (w.K + 1)
+    need = [(int(L) + room + ps - 1) // ps for L in lens]
+    max_pages = (w.max_prefix() + room + ps - 1) // ps
     total = int(sum(need))
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TID_PAGES])))
     perm = rng.permutation(total).astype(np.int32)
@@ -103,14 +104,14 @@ def page_layout(w: Workload, seed: int, lens: np.ndarray):
     return table, total
 
 
-def _cache(w: Workload, seed: int, tid: int, lens: np.ndarray, std: float, bf16: bool, table):
+def _cache(w: Workload, seed: int, tid: int, lens: np.ndarray, std: float, bf16: bool, table, steps: int = 1):
     """Prefix KV cache: contiguous [B][cap][H][Dh] or paged pool [P][page][H][Dh]."""
     row = w.H * w.Dh
     total = int(lens.sum())
     vals = normal_stream(seed, tid, total * row, std, bf16).reshape(total, row)
     dt = vals.dtype
     if not w.paged:
-        cap = w.cache_capacity()
+        cap = w.cache_capacity(steps)
         out = np.zeros((w.B, cap, w.H, w.Dh), dtype=dt)
         off = 0
         for b, L in enumerate(lens):
@@ -133,13 +134,15 @@ def _cache(w: Workload, seed: int, tid: int, lens: np.ndarray, std: float, bf16:
 ALL_PARTS = ("h", "W1", "W2", "Wlm", "kv", "qkv")
 
 
-def make_inputs(w: Workload, seed: int, parts=ALL_PARTS) -> dict:
-    """Draw the inputs of one step.
+def make_inputs(w: Workload, seed: int, parts=ALL_PARTS, steps: int = 1) -> dict:
+    """Draw the inputs of one step (with ``steps`` > 1: of the first of that many chained steps).
 
     Returns a dict with (depending on ``parts``): ``h`` [B][d], ``W1`` [K][d][d],
     ``W2`` [K][V][d], ``Wlm`` [V][d], ``Kc``/``Vc`` (cache), ``q``/``k``/``v``
     [B][T][H][Dh], ``prefix_len`` [B] int32, ``page_table`` (paged only).
-    bf16 tensors are uint16 bit patterns; fp32 tensors are float32.
+    bf16 tensors are uint16 bit patterns; fp32 tensors are float32.  ``steps``
+    only sizes the cache: room for one accepted path (K+1 slots) per step.  The
+    values drawn do not depend on it, except for a paged cache's page table.
     """
     bf16 = w.dtype == "bf16"
     std = float(w.d) ** -0.25
@@ -149,7 +152,7 @@ def make_inputs(w: Workload, seed: int, parts=ALL_PARTS) -> dict:
     out["prefix_len"] = lens
     table = None
     if w.paged:
-        table, _ = page_layout(w, seed, lens)
+        table, _ = page_layout(w, seed, lens, steps)
         out["page_table"] = table
     if "h" in parts:
         out["h"] = normal_stream(seed, TID_H, w.B * w.d, std, bf16).reshape(w.B, w.d)
@@ -160,8 +163,8 @@ def make_inputs(w: Workload, seed: int, parts=ALL_PARTS) -> dict:
     if "Wlm" in parts:
         out["Wlm"] = normal_stream(seed, TID_WLM, w.V * w.d, std, bf16).reshape(w.V, w.d)
     if "kv" in parts:
-        out["Kc"] = _cache(w, seed, TID_KC, lens, std, bf16, table)
-        out["Vc"] = _cache(w, seed, TID_VC, lens, std, bf16, table)
+        out["Kc"] = _cache(w, seed, TID_KC, lens, std, bf16, table, steps)
+        out["Vc"] = _cache(w, seed, TID_VC, lens, std, bf16, table, steps)
     if "qkv" in parts:
         n = w.B * T * w.H * w.Dh
         shp = (w.B, T, w.H, w.Dh)
@@ -169,3 +172,24 @@ def make_inputs(w: Workload, seed: int, parts=ALL_PARTS) -> dict:
         out["k"] = normal_stream(seed, TID_K, n, std, bf16).reshape(shp)
         out["v"] = normal_stream(seed, TID_V, n, std, bf16).reshape(shp)
     return out
+
+
+TID_STEP_QKV = 16  # tensor ids 16, 17, 18 (q, k, v) of step 1; +3 per further step
+
+
+def step_qkv(w: Workload, seed: int, s: int) -> dict:
+    """The tree's q/k/v inputs of step ``s`` of a chain (step 0: those of ``make_inputs``).
+
+    In a full model they would come from the candidate tokens through the layers; here,
+    as for the first step, they are independent seeded draws with the same recipe.
+    """
+    if s == 0:
+        out = make_inputs(w, seed, parts=("qkv",))
+        return {k: out[k] for k in ("q", "k", "v")}
+    bf16 = w.dtype == "bf16"
+    std = float(w.d) ** -0.25
+    T = w.n_nodes
+    n = w.B * T * w.H * w.Dh
+    shp = (w.B, T, w.H, w.Dh)
+    base = TID_STEP_QKV + 3 * (s - 1)
+    return {name: normal_stream(seed, base + i, n, std, bf16).reshape(shp) for i, name in enumerate(("q", "k", "v"))}
