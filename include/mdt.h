@@ -11,6 +11,7 @@
  *   mdt_kv_compact        append the accepted path's keys/values to the cache
  *   mdt_accept_compact    the last two in one launch (same results)
  *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
+ *   mdt_accept_rejection  rejection-sampling acceptance on the tree (a third acceptance rule)
  *
  * The pages this follows are the Medusa pages: "Medusa: Simple LLM Inference
  * Acceleration Framework with Multiple Decoding Heads" (summary page, section 3.2
@@ -370,6 +371,43 @@ mdt_status mdt_accept_compact(void* stream, mdt_dtype dt, int B, int H, int Dh, 
                               int mode, float eps, float delta, float temperature, int32_t* path, int path_stride,
                               int32_t* n_acc, const void* k_rot, const void* v, const mdt_kv_cache* cache,
                               const int32_t* prefix_len, int32_t* new_prefix_len);
+
+/*
+ * Rejection-sampling acceptance on the tree.  "Accelerating LLM Inference with
+ * Speculative Decoding: Notes on Medusa", section 2, and the summary page, section
+ * "Typical Acceptance Scheme" (first paragraph): a candidate x drafted with
+ * probability q(x) is accepted with probability min(1, p(x)/q(x)); after a rejection
+ * the token is drawn from norm(max(0, p - q)).  On the tree: starting at the root
+ * (always accepted), the children of the current node are tried in rank order; p is
+ * the verifier distribution softmax(z/temperature) of the current node, q the
+ * softmax(logits/temperature) of the head whose candidates they are (row depth+1 of
+ * head_logits); child c is accepted iff u_accept[b][c] < min(1, r(x_c)/q(x_c)), r the
+ * current residual (p at first; each rejection replaces r by norm(max(0, r - q))).
+ * An accepted child becomes the current node.  When no child is accepted (or the node
+ * is a leaf) the next token is the first vocabulary entry whose running sum of r
+ * exceeds u_resample[b] times the total; it is -1 if a rejection left r without mass.
+ * The random numbers are inputs, so the call is deterministic.
+ *  B, V, K       sequences, vocabulary (1..32768, else MDT_ERR_UNSUPPORTED), heads
+ *  tree          device tree; tree->max_depth <= K
+ *  vlogits       device f32 [B*T][V]: verifier logits of every node (the logits_opt
+ *                output of mdt_verify_logits)
+ *  head_logits   device f32 [B][K+1][V]: the output of mdt_medusa_heads
+ *  tree_tokens   device int32 [B][T]; a token outside 0..V-1 is never accepted
+ *  temperature   > 0
+ *  u_accept      device f32 [B][T], values in [0, 1) (entry c is used when child c is tried)
+ *  u_resample    device f32 [B], values in [0, 1)
+ *  path          device int32 [B][path_stride] (output), max_depth + 1 <= path_stride <= 1024;
+ *                root..last accepted node, then -1
+ *  n_acc         device int32 [B] (output): accepted node count (>= 1)
+ *  next_token    device int32 [B] (output): the token drawn after the accepted path
+ * The accepted path feeds mdt_kv_compact unchanged.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_TREE, MDT_ERR_VALUE (temperature), MDT_ERR_NULL,
+ * MDT_ERR_UNSUPPORTED (V > 32768).
+ */
+mdt_status mdt_accept_rejection(void* stream, int B, int V, int K, const mdt_tree_dev* tree, const float* vlogits,
+                                const float* head_logits, const int32_t* tree_tokens, float temperature,
+                                const float* u_accept, const float* u_resample, int32_t* path, int path_stride,
+                                int32_t* n_acc, int32_t* next_token);
 
 /*
  * Hidden state of the next step: h_next[b] = x[b][path[b][n_acc[b] - 1]], the node

@@ -7,7 +7,8 @@ device pointers and the current torch stream to the C ABI declared in
 
     medusa_heads, topk_tree_expand, tree_attention, verify_logits,
     accept_path, kv_compact, accept_compact (the last two in one launch),
-    next_state (the hidden state a following step starts from)
+    next_state (the hidden state a following step starts from),
+    accept_rejection (rejection-sampling acceptance)
 
 plus the static tree helpers (``Tree``) and workspace queries.  Importing this
 module without a built ``libmdt.so`` raises ImportError: there is no fallback.
@@ -92,6 +93,8 @@ _SIGS = [
                                    c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
     ("mdt_next_state", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                c_void_p]),
+    ("mdt_accept_rejection", c_int, [c_void_p, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
+                                     c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
 ]
 
 EXPORTED = [name for name, _, _ in _SIGS]
@@ -391,6 +394,22 @@ def kv_compact(path, n_acc, k_rot, v, cache: KVCache, prefix_len, new_prefix_len
                               _ptr(n_acc), _ptr(k_rot), _ptr(v), ctypes.byref(cache.desc), _ptr(prefix_len),
                               _ptr(new_prefix_len)), "kv_compact")
     return new_prefix_len
+
+
+def accept_rejection(vlogits, head_logits, tree_tokens, tree: DeviceTree, temperature, u_accept, u_resample,
+                     path=None, n_acc=None, next_token=None, path_stride=None, stream=None):
+    """Rejection-sampling acceptance; returns (path, n_acc, next_token)."""
+    B, K1, V = head_logits.shape
+    ps = path_stride or tree.tree.max_depth + 1
+    dev = head_logits.device
+    path = torch.empty((B, ps), dtype=torch.int32, device=dev) if path is None else path
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    next_token = torch.empty((B,), dtype=torch.int32, device=dev) if next_token is None else next_token
+    _check(lib.mdt_accept_rejection(_stream(stream), B, V, K1 - 1, ctypes.byref(tree.desc), _ptr(vlogits),
+                                    _ptr(head_logits), _ptr(tree_tokens), float(temperature), _ptr(u_accept),
+                                    _ptr(u_resample), _ptr(path), path.shape[1], _ptr(n_acc), _ptr(next_token)),
+           "accept_rejection")
+    return path, n_acc, next_token
 
 
 def next_state(x, path, n_acc, out=None, stream=None):

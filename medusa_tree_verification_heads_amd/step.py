@@ -10,6 +10,7 @@ workspace once, and ``run()`` enqueues
 with no host synchronisation, so a step can also be captured in a HIP graph.
 The order is the information flow of the summary page ("Medusa: Simple LLM
 Inference Acceleration Framework with Multiple Decoding Heads", section 3.2).
+With mode "rejection" the acceptance is accept_rejection followed by kv_compact.
 """
 
 from __future__ import annotations
@@ -17,8 +18,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path, kv_compact,
-               medusa_heads, next_state,
+from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path,
+               accept_rejection, kv_compact, medusa_heads, next_state,
                medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace)
 
@@ -35,7 +36,12 @@ class VerifyStep:
                  delta: float = 0.3, device="cuda", want_logits: bool = False, tree: Tree = None,
                  fused_tail: bool = True):
         self.w = w
-        self.fused_tail = fused_tail
+        # rejection sampling (mode "rejection") reads full verifier rows and the step's
+        # uniforms (inp["u_accept"], inp["u_resample"]); its acceptance and compaction are
+        # two calls
+        self.rejection = mode == "rejection"
+        want_logits = want_logits or self.rejection
+        self.fused_tail = fused_tail and not self.rejection
         self.mode = GREEDY if mode == "greedy" else TYPICAL
         self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
         dev = torch.device(device)
@@ -63,6 +69,10 @@ class VerifyStep:
         self.path = torch.empty((B, self.tree.tree.max_depth + 1), **i32)
         self.n_acc = torch.empty((B,), **i32)
         self.new_len = torch.empty((B,), **i32)
+        self.next_token = torch.full((B,), -1, **i32)
+        if self.rejection:
+            self.u_accept = torch.from_numpy(np.ascontiguousarray(inp["u_accept"], dtype=np.float32)).to(dev)
+            self.u_resample = torch.from_numpy(np.ascontiguousarray(inp["u_resample"], dtype=np.float32)).to(dev)
         dt = MDT_BF16 if w.dtype == "bf16" else MDT_F32
         self.ws_heads = new_workspace(medusa_heads_workspace(B, d, K), dev)
         self.ws_topk = new_workspace(topk_workspace(B, K, V, k_cfg), dev)
@@ -89,6 +99,11 @@ class VerifyStep:
         x = self.o.view(w.B * self.tree.T, w.d)
         verify_logits(x, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats, edge=self.edge,
                       logits=self.vlogits, want_logits=self.vlogits is not None, ws=self.ws_verify, stream=stream)
+        if self.rejection:
+            accept_rejection(self.vlogits, self.logits, tokens, self.tree, self.temperature, self.u_accept,
+                             self.u_resample, path=path, n_acc=n_acc, next_token=self.next_token, stream=stream)
+            kv_compact(path, n_acc, self.k_rot, v, self.cache, prefix_len, new_len, stream=stream)
+            return
         if self.fused_tail:
             accept_compact(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta,
                            self.temperature, self.k_rot, v, self.cache, prefix_len, path=path,
@@ -112,7 +127,7 @@ class VerifyStep:
         return dict(logits=f(self.logits), topk_idx=f(self.topk_idx), topk_val=f(self.topk_val),
                     tokens=f(self.tokens), pos=f(self.pos), o=f(self.o), k_rot=f(self.k_rot),
                     stats=f(self.stats).view(np.int32), edge=f(self.edge), vlogits=f(self.vlogits),
-                    path=f(self.path), n_acc=f(self.n_acc), new_len=f(self.new_len),
+                    path=f(self.path), n_acc=f(self.n_acc), new_len=f(self.new_len), next_token=f(self.next_token),
                     Kc=f(self.t["Kc"]), Vc=f(self.t["Vc"]))
 
 

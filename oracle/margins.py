@@ -77,3 +77,23 @@ def step_margin(res: dict, w, tree, mode, eps, delta, tau) -> float:
     m = head_margin(res["logits"], w.k_cfg)
     e = edge_margins(res["z"], res["stats"], res["tokens"], tree, mode, eps, delta, tau)
     return min(m, float(e.min()))
+
+
+def rejection_margins(trace, B: int) -> np.ndarray:
+    """Per sequence, the smallest margin of a rejection-sampling walk (``trace`` from
+    ``step.accept_rejection``): |u - min(1, r/q)| of every tried child (inf when the
+    acceptance probability is 1, since u < 1), and for the final draw the distance of
+    u * total from the running sums around the chosen entry, relative to the total."""
+    m = np.full(B, np.inf)
+    for kind, b, u, val in trace:
+        if kind == "accept":
+            if val < 1.0:
+                m[b] = min(m[b], abs(u - val))
+        else:
+            c = val
+            t = u * c[-1]
+            i = int(np.searchsorted(c, t, side="right"))
+            lo = c[i - 1] if i > 0 else 0.0
+            hi = c[min(i, c.shape[0] - 1)]
+            m[b] = min(m[b], min(t - lo, hi - t) / c[-1])
+    return m

@@ -258,6 +258,77 @@ def accept_path(stats, edge, tokens, tree: OracleTree, mode: str, eps=0.09, delt
     return paths, n_acc
 
 
+def softmax_tau(z: np.ndarray, tau: float) -> np.ndarray:
+    """softmax(z / tau), max-shifted."""
+    y = z / tau
+    e = np.exp(y - y.max())
+    return e / e.sum()
+
+
+def inverse_cdf(r: np.ndarray, u: float) -> int:
+    """Smallest index whose running sum of r exceeds u * sum(r) (u in [0, 1))."""
+    c = np.cumsum(r)
+    return int(min(np.searchsorted(c, u * c[-1], side="right"), r.shape[0] - 1))
+
+
+def accept_rejection(z, head_logits, tokens, tree: OracleTree, tau: float, u_accept, u_resample, trace=None):
+    """Rejection-sampling acceptance on the tree.
+
+    Notes page ("Accelerating LLM Inference with Speculative Decoding: Notes on
+    Medusa"), section 2, and the summary page's "Typical Acceptance Scheme" (first
+    paragraph): a candidate x drafted with probability q(x) is accepted with
+    probability min(1, p(x)/q(x)); on rejection the token is drawn from
+    norm(max(0, p - q)).  On the tree: p is the verifier distribution softmax(z/tau)
+    at the current node, q is the softmax(./tau) of the head whose candidates sit one
+    level down.  Walking from the root, the children of the current node are tried in
+    rank order, child c accepted iff u_accept[b][c] < min(1, r(x_c)/q(x_c)) with r the
+    current residual (p at first); a rejection replaces r by norm(max(0, r - q)) before
+    the next sibling.  An accepted child becomes the current node (r = its p).  When no
+    child is accepted (or the node is a leaf) the next token is drawn from r by the
+    inverse CDF at u_resample[b]; it is -1 when r has no mass left.
+
+    Returns (paths root..last, n_acc, next_token) per sequence.  With ``trace`` (a list),
+    every decision is appended as (b, u, threshold) for the acceptance tests and as
+    (b, u * total, running sums) for the final draw, for margin checks.
+    """
+    B, T = tokens.shape
+    kids = [[c for c in range(1, T) if tree.parent[c] == i] for i in range(T)]
+    paths, n_acc, nxt = [], [], []
+    for b in range(B):
+        cur = 0
+        path = [0]
+        r = softmax_tau(z[b * T], tau)
+        while True:
+            d = tree.depth[cur]
+            acc = None
+            for c in kids[cur]:
+                q = softmax_tau(head_logits[b, d + 1], tau)
+                x = int(tokens[b, c])
+                a = min(1.0, r[x] / q[x])
+                if trace is not None:
+                    trace.append(("accept", b, float(u_accept[b, c]), a))
+                if u_accept[b, c] < a:
+                    acc = c
+                    break
+                r = np.maximum(r - q, 0.0)
+                tot = r.sum()
+                if tot <= 0.0:
+                    r = None
+                    break
+                r = r / tot
+            if acc is None:
+                break
+            cur = acc
+            path.append(cur)
+            r = softmax_tau(z[b * T + cur], tau)
+        paths.append(path)
+        n_acc.append(len(path))
+        nxt.append(-1 if r is None else inverse_cdf(r, float(u_resample[b])))
+        if trace is not None and r is not None:
+            trace.append(("draw", b, float(u_resample[b]), np.cumsum(r)))
+    return paths, n_acc, nxt
+
+
 # ----------------------------------------------------------------------------
 # 6. KV compaction
 # ----------------------------------------------------------------------------

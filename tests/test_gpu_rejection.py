@@ -1,0 +1,158 @@
+"""Rejection-sampling acceptance on the GPU against the oracle.
+
+The kernel is fed float32 verifier and head logits; the oracle runs on the same
+values (as float64) and the same uniforms.  Decisions are compared exactly where
+the oracle's walk has margin: |u - min(1, r/q)| >= 1e-4 for every tried child and,
+for the final draw, u * total at least 2e-5 of the total away from the running
+sums around the chosen entry.  A float32 softmax and running sum differ from float64
+by about 1e-6 of the total (a common scale error cancels against u * total), so both
+margins leave a factor of ten or more.  Uniform draws are taken from the first seed
+whose walks all have that margin.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import margins as om
+from oracle import step as ostep
+from tests.parity_util import case_inputs, note, oracle_shared
+from workloads import uniforms
+
+pytestmark = pytest.mark.gpu
+
+TAU = 0.7
+CASES = ["tiny-fp32-T10", "7b-mini", "7b-B16-mini-paged", "33b-mini"]
+
+
+def _margin_ok(trace, B):
+    m = np.full(B, np.inf)
+    for kind, b, u, val in trace:
+        if kind == "accept":
+            if val < 1.0:
+                m[b] = min(m[b], abs(u - val) / 1e-4)
+        else:
+            c = val
+            t = u * c[-1]
+            i = int(np.searchsorted(c, t, side="right"))
+            lo = c[i - 1] if i > 0 else 0.0
+            hi = c[min(i, c.shape[0] - 1)]
+            m[b] = min(m[b], (min(t - lo, hi - t) / c[-1]) / 2e-5)
+    return bool((m >= 1.0).all())
+
+
+def _inputs(name):
+    w, inp = case_inputs(name)
+    sh = oracle_shared(name)
+    z32 = sh["z"].astype(np.float32)
+    l32 = sh["logits"].astype(np.float32)
+    return w, sh, z32, l32
+
+
+def _run_gpu(w, sh, z32, l32, ua, ur):
+    import medusa_tree_verification_heads_amd as mdt
+    tree = mdt.Tree.for_workload(w).to_device("cuda")
+    path, n_acc, nxt = mdt.accept_rejection(torch.from_numpy(z32).cuda(), torch.from_numpy(l32).cuda(),
+                                            torch.from_numpy(sh["tokens"].astype(np.int32)).cuda(), tree, TAU,
+                                            torch.from_numpy(ua).cuda(), torch.from_numpy(ur).cuda())
+    torch.cuda.synchronize()
+    return path.cpu().numpy(), n_acc.cpu().numpy(), nxt.cpu().numpy()
+
+
+def _check(w, sh, z32, l32, ua, ur):
+    trace = []
+    ref = ostep.accept_rejection(z32.astype(np.float64), l32.astype(np.float64), sh["tokens"], sh["tree"], TAU,
+                                 ua.astype(np.float64), ur.astype(np.float64), trace=trace)
+    path, n_acc, nxt = _run_gpu(w, sh, z32, l32, ua, ur)
+    for b in range(w.B):
+        assert n_acc[b] == ref[1][b], b
+        assert path[b, :n_acc[b]].tolist() == ref[0][b], b
+        assert (path[b, n_acc[b]:] == -1).all(), b
+        assert nxt[b] == ref[2][b], b
+    return ref
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_accept_rejection_matches_oracle(name):
+    w, sh, z32, l32 = _inputs(name)
+    for s in range(60):
+        u = uniforms(w, 7000 + s)
+        trace = []
+        ostep.accept_rejection(z32.astype(np.float64), l32.astype(np.float64), sh["tokens"], sh["tree"], TAU,
+                               u["u_accept"].astype(np.float64), u["u_resample"].astype(np.float64), trace=trace)
+        if _margin_ok(trace, w.B):
+            break
+    else:
+        pytest.fail("no uniform draw with margin")
+    note(f"{name}: uniforms of seed {7000 + s}")
+    ref = _check(w, sh, z32, l32, u["u_accept"], u["u_resample"])
+    note(f"{name}: n_acc {ref[1]}, next {ref[2]}")
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_accept_rejection_all_accepted_and_all_rejected(name):
+    w, sh, z32, l32 = _inputs(name)
+    T = sh["tree"].T
+    # u = 0 accepts every first child (its acceptance probability is positive): the walk
+    # follows rank-0 children down to a leaf, then draws from that leaf's distribution
+    ua0 = np.zeros((w.B, T), dtype=np.float32)
+    for s in range(40):
+        ur = uniforms(w, 8000 + s)["u_resample"]
+        trace = []
+        ostep.accept_rejection(z32.astype(np.float64), l32.astype(np.float64), sh["tokens"], sh["tree"], TAU,
+                               ua0.astype(np.float64), ur.astype(np.float64), trace=trace)
+        if _margin_ok(trace, w.B):
+            break
+    else:
+        pytest.fail("no draw with margin")
+    ref = _check(w, sh, z32, l32, ua0, ur)
+    tree = sh["tree"]
+    for p in ref[0]:
+        assert len(p) >= 2 and all(tree.rank[c] == 0 for c in p[1:])
+        assert not any(tree.parent[c] == p[-1] for c in range(T))  # a leaf
+    # u just below 1 rejects every child of the root: the token comes from the residual
+    ua1 = np.full((w.B, T), np.float32(1.0) - np.float32(2 ** -24), dtype=np.float32)
+    for s in range(40):
+        ur = uniforms(w, 9000 + s)["u_resample"]
+        trace = []
+        ostep.accept_rejection(z32.astype(np.float64), l32.astype(np.float64), sh["tokens"], sh["tree"], TAU,
+                               ua1.astype(np.float64), ur.astype(np.float64), trace=trace)
+        if _margin_ok(trace, w.B):
+            break
+    else:
+        pytest.fail("no draw with margin")
+    ref = _check(w, sh, z32, l32, ua1, ur)
+    assert all(n == 1 for n in ref[1])
+
+
+def test_step_with_rejection_acceptance():
+    """The whole step with mode "rejection": the acceptance equals the oracle's walk on the
+    step's own GPU logits, and the compacted cache holds the accepted path."""
+    from medusa_tree_verification_heads_amd.step import VerifyStep
+    name = "7b-mini"
+    w, inp = case_inputs(name)
+    tree = oracle_shared(name)["tree"]
+    for s in range(60):
+        u = uniforms(w, 7100 + s)
+        st_inp = dict(inp)
+        st_inp.update(u)
+        st = VerifyStep(w, st_inp, "rejection", TAU)
+        st.run()
+        g = st.outputs()
+        z = g["vlogits"].astype(np.float64)
+        hl = g["logits"].astype(np.float64)
+        trace = []
+        ref = ostep.accept_rejection(z, hl, g["tokens"], tree, TAU, u["u_accept"].astype(np.float64),
+                                     u["u_resample"].astype(np.float64), trace=trace)
+        if _margin_ok(trace, w.B):
+            break
+    else:
+        pytest.fail("no uniform draw with margin")
+    for b in range(w.B):
+        assert g["n_acc"][b] == ref[1][b]
+        assert g["path"][b, :g["n_acc"][b]].tolist() == ref[0][b]
+        assert g["next_token"][b] == ref[2][b]
+        L = int(inp["prefix_len"][b])
+        for j, node in enumerate(ref[0][b]):
+            assert np.array_equal(g["Kc"][b, L + j], g["k_rot"][b, node])
+    assert np.array_equal(g["new_len"], inp["prefix_len"] + g["n_acc"])

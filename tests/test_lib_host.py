@@ -168,3 +168,21 @@ def test_verify_accept_compact_validation():
     assert fused(dt=1, H=1, Dh=3) == -2                       # the kv_compact checks
     assert fused(dt=2) == -3
     assert fused(kr=None) == -1 and fused(kr=MIS) == -4
+
+
+def test_next_state_and_rejection_validation():
+    n = mdt.lib.mdt_next_state
+    assert n(None, 3, 1, 64, 4096, P, P, 5, P, P) == -3          # dtype
+    assert n(None, 1, 1, 64, 4093, P, P, 5, P, P) == -2          # row not a 16-byte multiple
+    assert n(None, 1, 1, 64, 4096, P, P, 0, P, P) == -2          # path_stride
+    assert n(None, 1, 1, 64, 4096, None, P, 5, P, P) == -1
+    assert n(None, 1, 1, 64, 4096, MIS, P, 5, P, P) == -4
+    d = _tree_desc()
+    r = mdt.lib.mdt_accept_rejection
+    def rej(B=1, V=32000, K=4, tau=0.7, stride=5, vl=P):
+        return r(None, B, V, K, ctypes.byref(d), vl, P, P, tau, P, P, P, stride, P, P)
+    assert rej(tau=0.0) == -6 and rej(tau=-1.0) == -6          # temperature must be > 0
+    assert rej(V=40000) == -9                                   # vocabulary beyond one workgroup's registers
+    assert rej(K=3) == -5                                       # tree deeper than K
+    assert rej(stride=4) == -2 and rej(stride=1100) == -2
+    assert rej(vl=None) == -1

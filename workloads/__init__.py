@@ -6,4 +6,4 @@ HIP path read their inputs from here, so neither depends on the other.
 """
 
 from .configs import WORKLOADS, Workload, get_workload, scaled  # noqa: F401
-from .gen import make_inputs, step_qkv, bf16_round_bits, f32_to_bf16_bits  # noqa: F401
+from .gen import make_inputs, step_qkv, uniforms, bf16_round_bits, f32_to_bf16_bits  # noqa: F401

@@ -193,3 +193,15 @@ def step_qkv(w: Workload, seed: int, s: int) -> dict:
     shp = (w.B, T, w.H, w.Dh)
     base = TID_STEP_QKV + 3 * (s - 1)
     return {name: normal_stream(seed, base + i, n, std, bf16).reshape(shp) for i, name in enumerate(("q", "k", "v"))}
+
+
+TID_UNIFORM = 40  # + step index
+
+
+def uniforms(w: Workload, seed: int, s: int = 0) -> dict:
+    """Uniform random numbers in [0, 1) (float32) for rejection-sampling acceptance of step
+    ``s``: ``u_accept`` [B][T] (one per tree node) and ``u_resample`` [B]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TID_UNIFORM + s])))
+    T = w.n_nodes
+    return {"u_accept": rng.random((w.B, T), dtype=np.float32),
+            "u_resample": rng.random(w.B, dtype=np.float32)}
