@@ -152,6 +152,29 @@ mdt_status mdt_tree_build_cartesian(int K, const int* s, mdt_tree_host* out);
 mdt_status mdt_tree_build_scored(int K, int k_cfg, int T, double a0, double rho, double gamma,
                                  int rank_base, int depth_base, mdt_tree_host* out);
 
+/*
+ * Sparse tree from a calibrated accuracy table: acc[j][r] (host, [K][k_cfg], values in
+ * [0, 1]) is the accuracy of the rank-r candidate of head j+1 -- the top-(r+1) accuracy
+ * minus the top-r accuracy (summary page, section "Optimized Tree Construction", step
+ * 1).  Under the pages' independence assumption (step 2) a path's score is the product
+ * of its nodes' accuracies; the tree keeps the T-1 best rank paths by the greedy frontier
+ * of steps 3-4 ("Notes on Medusa", section 4), which maximises the expected acceptance
+ * length among trees of T nodes.  Products are formed in path order in double precision;
+ * ties go to the smaller depth, then to the lexicographically smaller rank path.
+ * Host-only.  Errors: MDT_ERR_NULL, MDT_ERR_SHAPE (as mdt_tree_build_scored),
+ * MDT_ERR_VALUE (an accuracy outside [0, 1]), MDT_ERR_ALLOC.
+ */
+mdt_status mdt_tree_build_table(int K, int k_cfg, int T, const double* acc, mdt_tree_host* out);
+
+/*
+ * Expected acceptance length of a tree under an accuracy table (as above): the sum over
+ * the non-root nodes of the product of the accuracies on their root paths ("Notes on
+ * Medusa", section 4: E[L] = sum_m P(L >= m)).  Host-only; *out in double precision.
+ * Errors: MDT_ERR_NULL, MDT_ERR_TREE (an inconsistent tree), MDT_ERR_SHAPE (K, k_cfg out
+ * of range or not covering the tree's depth and ranks).
+ */
+mdt_status mdt_tree_expected_length(const mdt_tree_host* tree, int K, int k_cfg, const double* acc, double* out);
+
 /* Release the arrays of a host tree (safe on a zeroed struct). */
 void mdt_tree_free(mdt_tree_host* tree);
 

@@ -66,6 +66,9 @@ _SIGS = [
     ("mdt_tree_build_cartesian", c_int, [c_int, ctypes.POINTER(c_int), ctypes.POINTER(TreeHost)]),
     ("mdt_tree_build_scored", c_int, [c_int, c_int, c_int, c_double, c_double, c_double, c_int, c_int,
                                       ctypes.POINTER(TreeHost)]),
+    ("mdt_tree_build_table", c_int, [c_int, c_int, c_int, ctypes.POINTER(c_double), ctypes.POINTER(TreeHost)]),
+    ("mdt_tree_expected_length", c_int, [ctypes.POINTER(TreeHost), c_int, c_int, ctypes.POINTER(c_double),
+                                         ctypes.POINTER(c_double)]),
     ("mdt_tree_free", None, [ctypes.POINTER(TreeHost)]),
     ("mdt_tree_image_bytes", c_size, [c_int]),
     ("mdt_tree_pack", c_int, [ctypes.POINTER(TreeHost), c_void_p, c_size]),
@@ -209,6 +212,25 @@ class Tree:
         _check(lib.mdt_tree_build_scored(K, k_cfg, T, a0, rho, gamma, rank_base, depth_base, ctypes.byref(h)),
                "tree_build_scored")
         return cls(h)
+
+    @classmethod
+    def from_table(cls, acc, T: int) -> "Tree":
+        """Sparse tree of T nodes from an accuracy table acc [K][k] (rank-r accuracy of head j+1)."""
+        a = np.ascontiguousarray(acc, dtype=np.float64)
+        K, k = a.shape
+        h = TreeHost()
+        _check(lib.mdt_tree_build_table(K, k, T, a.ctypes.data_as(ctypes.POINTER(c_double)), ctypes.byref(h)),
+               "tree_build_table")
+        return cls(h)
+
+    def expected_length(self, acc) -> float:
+        """E[L] of this tree under an accuracy table acc [K][k]."""
+        a = np.ascontiguousarray(acc, dtype=np.float64)
+        out = c_double()
+        _check(lib.mdt_tree_expected_length(ctypes.byref(self._host), a.shape[0], a.shape[1],
+                                            a.ctypes.data_as(ctypes.POINTER(c_double)), ctypes.byref(out)),
+               "tree_expected_length")
+        return out.value
 
     @classmethod
     def for_workload(cls, w) -> "Tree":

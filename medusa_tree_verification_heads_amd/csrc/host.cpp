@@ -261,6 +261,71 @@ mdt_status mdt_tree_build_scored(int K, int k_cfg, int T, double a0, double rho,
     return pack_tree(chosen, out);
 }
 
+// Path score from an accuracy table: the product of acc[j][r_j] over the path, multiplied
+// in path order in double precision (equal paths give bitwise equal products).
+static double table_score(const std::vector<int>& p, const double* acc, int k_cfg) {
+    double s = 1.0;
+    for (size_t j = 0; j < p.size(); ++j) s *= acc[j * k_cfg + p[j]];
+    return s;
+}
+
+mdt_status mdt_tree_build_table(int K, int k_cfg, int T, const double* acc, mdt_tree_host* out) {
+    MDT_REQUIRE(out && acc, MDT_ERR_NULL, "out or acc is NULL");
+    MDT_REQUIRE(K >= 1 && K <= MDT_MAX_HEADS, MDT_ERR_SHAPE, "K=%d out of range 1..%d", K, MDT_MAX_HEADS);
+    MDT_REQUIRE(k_cfg >= 1 && k_cfg <= MDT_MAX_TOPK, MDT_ERR_SHAPE, "k_cfg=%d out of range", k_cfg);
+    MDT_REQUIRE(T >= 1 && T <= MDT_MAX_NODES, MDT_ERR_SHAPE, "T=%d out of range 1..%d", T, MDT_MAX_NODES);
+    for (int i = 0; i < K * k_cfg; ++i)
+        MDT_REQUIRE(acc[i] >= 0.0 && acc[i] <= 1.0, MDT_ERR_VALUE, "accuracy %d is not in [0, 1]", i);
+    double cands = 0, lvl = 1;
+    for (int j = 0; j < K; ++j) {
+        lvl *= k_cfg;
+        cands += lvl;
+    }
+    MDT_REQUIRE(T - 1 <= cands, MDT_ERR_SHAPE, "T=%d exceeds the %g candidate nodes", T, cands);
+    // A child's product never exceeds its parent's (accuracies <= 1) and ties go to the
+    // smaller depth, so the greedy frontier takes the T-1 best paths and stays closed
+    // under prefixes.
+    std::priority_queue<Cand, std::vector<Cand>, CandWorse> frontier;
+    for (int r = 0; r < k_cfg; ++r) {
+        std::vector<int> p{r};
+        frontier.push(Cand{table_score(p, acc, k_cfg), p});
+    }
+    std::vector<std::vector<int>> chosen(1);
+    while ((int)chosen.size() < T) {
+        Cand best = frontier.top();
+        frontier.pop();
+        chosen.push_back(best.path);
+        if ((int)best.path.size() < K)
+            for (int r = 0; r < k_cfg; ++r) {
+                std::vector<int> c = best.path;
+                c.push_back(r);
+                frontier.push(Cand{table_score(c, acc, k_cfg), c});
+            }
+    }
+    return pack_tree(chosen, out);
+}
+
+mdt_status mdt_tree_expected_length(const mdt_tree_host* t, int K, int k_cfg, const double* acc, double* out) {
+    MDT_REQUIRE(t && acc && out, MDT_ERR_NULL, "tree, acc or out is NULL");
+    MDT_REQUIRE(t->T >= 1 && t->T <= MDT_MAX_NODES && t->parent && t->depth && t->rank, MDT_ERR_TREE,
+                "invalid host tree");
+    MDT_REQUIRE(K >= 1 && K <= MDT_MAX_HEADS && k_cfg >= 1 && k_cfg <= MDT_MAX_TOPK, MDT_ERR_SHAPE,
+                "K or k_cfg out of range");
+    MDT_REQUIRE(t->max_depth <= K && t->max_rank < k_cfg, MDT_ERR_SHAPE, "the table does not cover the tree");
+    // E[L] = sum over the non-root nodes of their path products ("Notes on Medusa",
+    // section 4); each node's product is its parent's times its own accuracy.
+    std::vector<double> prod(t->T, 1.0);
+    double e = 0.0;
+    for (int i = 1; i < t->T; ++i) {
+        const int p = t->parent[i], d = t->depth[i], r = t->rank[i];
+        MDT_REQUIRE(p >= 0 && p < i && d >= 1 && d <= K && r >= 0 && r < k_cfg, MDT_ERR_TREE, "invalid node %d", i);
+        prod[i] = prod[p] * acc[(d - 1) * k_cfg + r];
+        e += prod[i];
+    }
+    *out = e;
+    return MDT_OK;
+}
+
 void mdt_tree_free(mdt_tree_host* t) {
     if (!t) return;
     std::free(t->parent);

@@ -123,6 +123,60 @@ def expected_accept_length(tree: OracleTree, a0=0.6, rho=0.7, gamma=0.8,
     return sum((path_score(p, a0, rho, gamma, rank_base, depth_base) for p in tree.paths[1:]), Fraction(0))
 
 
+def table_product(path: Path, acc) -> float:
+    """Product of acc[j][r_j] over the path, multiplied in path order in double precision.
+
+    Summary page, "Optimized Tree Construction", step 2 (independence: a path's accuracy
+    is the product of its nodes' accuracies).  The order between paths is decided in
+    double precision, as the library does; expected lengths below are exact.
+    """
+    s = 1.0
+    for j, r in enumerate(path):
+        s *= float(acc[j][r])
+    return s
+
+
+def table_tree_greedy(K: int, k_cfg: int, T: int, acc) -> OracleTree:
+    """Greedy frontier (steps 3-4; "Notes on Medusa", section 4) with table path products."""
+    if T < 1:
+        raise ValueError("T must count the root")
+    chosen: List[Path] = [()]
+    frontier = []
+    for r in range(k_cfg):
+        heapq.heappush(frontier, _order_key((r,), table_product((r,), acc)))
+    while len(chosen) < T:
+        if not frontier:
+            raise ValueError("tree budget exceeds the number of candidate nodes")
+        best = heapq.heappop(frontier)[2]
+        chosen.append(best)
+        if len(best) < K:
+            for r in range(k_cfg):
+                c = best + (r,)
+                heapq.heappush(frontier, _order_key(c, table_product(c, acc)))
+    return _pack(chosen)
+
+
+def table_expected_length(tree: OracleTree, acc) -> Fraction:
+    """E[L] = sum over the non-root nodes of the exact product of their accuracies."""
+    tot = Fraction(0)
+    for p in tree.paths[1:]:
+        s = Fraction(1)
+        for j, r in enumerate(p):
+            s *= Fraction(float(acc[j][r]))
+        tot += s
+    return tot
+
+
+def marginal_accuracy(top_i) -> List[float]:
+    """Accuracy of the rank-i candidate from cumulative top-i accuracies: top-i minus top-(i-1)
+    (summary page, "Optimized Tree Construction", step 1)."""
+    out, prev = [], 0.0
+    for c in top_i:
+        out.append(float(c) - prev)
+        prev = float(c)
+    return out
+
+
 def ancestor_mask(tree: OracleTree):
     """M[i][j] = True iff walking parent pointers from i reaches j (i itself included)."""
     T = tree.T
