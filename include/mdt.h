@@ -12,6 +12,9 @@
  *   mdt_accept_compact    the last two in one launch (same results)
  *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
  *   mdt_accept_rejection  rejection-sampling acceptance on the tree (a third acceptance rule)
+ *   mdt_kv_compact_layers mdt_kv_compact for every layer of a model in one launch
+ *   mdt_embed, mdt_rmsnorm, mdt_linear
+ *                         the decoder-layer pieces of the full verify forward
  *
  * The pages this follows are the Medusa pages: "Medusa: Simple LLM Inference
  * Acceleration Framework with Multiple Decoding Heads" (summary page, section 3.2
@@ -84,6 +87,11 @@ typedef enum mdt_accept_mode {
     MDT_ACCEPT_GREEDY = 0,
     MDT_ACCEPT_TYPICAL = 1
 } mdt_accept_mode;
+
+typedef enum mdt_act {
+    MDT_ACT_NONE = 0,   /* mdt_linear: plain product */
+    MDT_ACT_SWIGLU = 1  /* mdt_linear: SwiGLU of an interleaved gate/up product */
+} mdt_act;
 
 typedef enum mdt_kv_layout {
     MDT_KV_CONTIG = 0,  /* k,v: [B][capacity][H][Dh] */
@@ -451,6 +459,83 @@ mdt_status mdt_accept_rejection(void* stream, int B, int V, int K, const mdt_tre
  */
 mdt_status mdt_next_state(void* stream, mdt_dtype dt, int B, int T, int d, const void* x, const int32_t* path,
                           int path_stride, const int32_t* n_acc, void* h_next);
+
+/*
+ * mdt_kv_compact for a model of n_layers layers in one launch: layer l reads
+ * k_rot + l*k_rot_layer_stride and v + l*v_layer_stride and writes the cache whose
+ * k and v pointers are offset by l*cache_layer_stride (strides in elements, each a
+ * multiple of 16 bytes, and at least one layer when n_layers > 1).  Every layer keeps
+ * the same accepted path (the verify forward of the "Tree Attention" steps runs the
+ * whole backbone on the tree, so each layer holds keys/values for every node).
+ * Layer l's writes are exactly those of mdt_kv_compact on layer l's pointers.
+ * Errors: as mdt_kv_compact, plus MDT_ERR_SHAPE (n_layers outside 1..65535, strides
+ * smaller than one layer) and MDT_ERR_ALIGN (strides).
+ */
+mdt_status mdt_kv_compact_layers(void* stream, mdt_dtype dt, int n_layers, int B, int T, int H, int Dh,
+                                 const int32_t* path, int path_stride, const int32_t* n_acc, const void* k_rot,
+                                 long long k_rot_layer_stride, const void* v, long long v_layer_stride,
+                                 const mdt_kv_cache* cache, long long cache_layer_stride,
+                                 const int32_t* prefix_len, int32_t* new_prefix_len);
+
+/* ------------------------------------------------------------------------- */
+/* 7. Decoder layers of the verify forward (bf16 only)                        */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The summary page (section 3.2 step 4; "Tree Attention" steps 3-5) runs the packed
+ * tree through the whole backbone in one forward pass before the LM head, and
+ * "Notes on Medusa", section 3, feeds the node outputs of that pass to the LM head.
+ * The pages name the backbone (Vicuna, a Llama model) without giving its layer.  These
+ * calls are the pieces of the Llama decoder layer: with M = B*T tree rows,
+ *   x    = embed(tree_tokens)
+ *   per layer:  h = rmsnorm(x, g_attn); q|k|v = h Wqkv^T (three segments);
+ *               o = mdt_tree_attention(q, k, v); x = x + o Wo^T;
+ *               h = rmsnorm(x, g_mlp); a = silu(h Wg^T) * (h Wu^T); x = x + a Wd^T
+ *   xf   = rmsnorm(x, g_final) -> mdt_verify_logits
+ * Every matrix is bf16 and every product accumulates in fp32; each call rounds its
+ * output to bf16 once.
+ */
+
+/*
+ * y[m][:] = E[tokens[m]][:] for m < M (a token outside 0..V-1 gives a zero row).
+ *  tokens  device int32 [M]; E device bf16 [V][d]; y device bf16 [M][d]; d % 8 == 0.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_NULL, MDT_ERR_ALIGN (E, y).
+ */
+mdt_status mdt_embed(void* stream, int M, int d, int V, const int32_t* tokens, const void* E, void* y);
+
+/*
+ * y[m][j] = bf16(x[m][j] * r_m * g[j]), r_m = 1/sqrt(mean_j x[m][j]^2 + eps) (fp32).
+ *  x device bf16 [M][d]; g device bf16 [d]; y device bf16 [M][d] (may equal x); d % 8 == 0.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_VALUE (eps < 0), MDT_ERR_NULL, MDT_ERR_ALIGN.
+ */
+mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g, float eps, void* y);
+
+/*
+ * z = x W^T with x device bf16 [M][K] and W device bf16 [N][K] (fp32 accumulation), then
+ *  act == MDT_ACT_NONE:   y[q][m][j] = bf16(z[m][q*N/nseg + j] (+ residual[m][q*N/nseg + j]))
+ *                         for the nseg column segments q (y is nseg matrices [M][N/nseg]
+ *                         back to back; with nseg == 1 simply [M][N]).  residual is
+ *                         device bf16 [M][N] or NULL (then nseg may be > 1); y may be
+ *                         the residual buffer itself, never x.
+ *  act == MDT_ACT_SWIGLU: W holds gate and up rows interleaved in groups of 16: rows
+ *                         32i..32i+15 are gate rows 16i.., rows 32i+16..32i+31 the up
+ *                         rows 16i..; y device bf16 [M][N/2] with
+ *                         y[m][16i + c] = bf16(silu(z[m][32i + c]) * z[m][32i + 16 + c]),
+ *                         silu(u) = u / (1 + e^-u).  N % 32 == 0, no residual, nseg == 1.
+ *  K % 32 == 0, N % 8 == 0, N/nseg % 8 == 0.
+ *  split   0 = choose; s > 0 cuts the inner dimension into about s slices (at most 64;
+ *          ignored when the output has more than 16384 tiles of 64 x 64)
+ *  ws      device workspace of mdt_linear_workspace(M, N, K, split) bytes (0 bytes, and
+ *          ws may be NULL, when the inner dimension is not cut).  Its first 64 KiB are
+ *          arrival counters: they must be zero when the call starts (allocate the
+ *          workspace zeroed) and every completed call leaves them zero, so calls of any
+ *          shapes may share one workspace as long as they do not run concurrently.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_VALUE (act, split, residual with nseg > 1 or with
+ * SwiGLU), MDT_ERR_NULL, MDT_ERR_ALIGN, MDT_ERR_WORKSPACE.
+ */
+size_t mdt_linear_workspace(int M, int N, int K, int split);
+mdt_status mdt_linear(void* stream, int M, int N, int K, const void* x, const void* W, const void* residual,
+                      int nseg, int act, void* y, int split, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------- */
 /* Misc                                                                       */

@@ -98,6 +98,14 @@ _SIGS = [
                                c_void_p]),
     ("mdt_accept_rejection", c_int, [c_void_p, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
                                      c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("mdt_kv_compact_layers", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
+                                      c_void_p, ctypes.c_longlong, c_void_p, ctypes.c_longlong,
+                                      ctypes.POINTER(KVCacheDesc), ctypes.c_longlong, c_void_p, c_void_p]),
+    ("mdt_embed", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    ("mdt_rmsnorm", c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_float, c_void_p]),
+    ("mdt_linear_workspace", c_size, [c_int, c_int, c_int, c_int]),
+    ("mdt_linear", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p,
+                           c_int, c_void_p, c_size]),
 ]
 
 EXPORTED = [name for name, _, _ in _SIGS]
@@ -459,3 +467,85 @@ def accept_compact(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps, d
                                   ctypes.byref(cache.desc), _ptr(prefix_len), _ptr(new_prefix_len)),
            "accept_compact")
     return path, n_acc, new_prefix_len
+
+
+def kv_compact_layers(path, n_acc, k_rot, v, cache: KVCache, prefix_len, cache_layer_stride: int,
+                      new_prefix_len=None, stream=None):
+    """kv_compact for every layer at once: k_rot and v are [n_layers][B][T][H][Dh] views (any
+    layer stride), ``cache`` describes layer 0 and layer l's rows sit cache_layer_stride
+    elements further on."""
+    n_layers, B, T, H, Dh = k_rot.shape
+    for t in (k_rot, v):
+        assert t.shape == k_rot.shape and t[0].is_contiguous(), "each layer must be a contiguous [B][T][H][Dh]"
+    new_prefix_len = torch.empty_like(prefix_len) if new_prefix_len is None else new_prefix_len
+    _check(lib.mdt_kv_compact_layers(_stream(stream), _dtype_code(k_rot), n_layers, B, T, H, Dh, _ptr(path),
+                                     path.shape[1], _ptr(n_acc), _ptr(k_rot), k_rot.stride(0), _ptr(v), v.stride(0),
+                                     ctypes.byref(cache.desc), int(cache_layer_stride), _ptr(prefix_len),
+                                     _ptr(new_prefix_len)), "kv_compact_layers")
+    return new_prefix_len
+
+
+# ---------------------------------------------------------------------------
+# decoder-layer pieces of the full verify forward (bf16)
+# ---------------------------------------------------------------------------
+
+ACT_NONE, ACT_SWIGLU = 0, 1
+
+
+def _bf16_2d(t, name):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 2-d bfloat16 tensor")
+
+
+def embed(tokens, E, out=None, stream=None):
+    """Rows E[tokens] -> [M][d] (a token outside the vocabulary gives a zero row)."""
+    _bf16_2d(E, "E")
+    M = tokens.numel()
+    V, d = E.shape
+    out = torch.empty((M, d), dtype=E.dtype, device=E.device) if out is None else out
+    _check(lib.mdt_embed(_stream(stream), M, d, V, _ptr(tokens), _ptr(E), _ptr(out)), "embed")
+    return out
+
+
+def rmsnorm(x, g, eps: float, out=None, stream=None):
+    """bf16(x / sqrt(mean(x^2) + eps) * g) row by row."""
+    _bf16_2d(x, "x")
+    M, d = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check(lib.mdt_rmsnorm(_stream(stream), M, d, _ptr(x), _ptr(g), float(eps), _ptr(out)), "rmsnorm")
+    return out
+
+
+def linear_workspace(M, N, K, split=0) -> int:
+    return lib.mdt_linear_workspace(M, N, K, split)
+
+
+def linear(x, W, residual=None, nseg=1, act=ACT_NONE, out=None, split=0, ws=None, stream=None):
+    """x [M][K] times W [N][K] transposed (bf16 in and out, fp32 accumulation).
+
+    act=ACT_NONE: (+ residual [M][N]) -> [M][N], or [nseg][M][N/nseg] column segments.
+    act=ACT_SWIGLU: W holds gate/up rows interleaved by 16 (see interleave_gate_up) -> [M][N/2].
+    ``ws`` must start zeroed (new_workspace does that); the call leaves it so.
+    """
+    _bf16_2d(x, "x")
+    _bf16_2d(W, "W")
+    M, K = x.shape
+    N = W.shape[0]
+    if act == ACT_SWIGLU:
+        shape = (M, N // 2)
+    else:
+        shape = (M, N) if nseg == 1 else (nseg, M, N // nseg)
+    out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    ws, wsb = _ws(linear_workspace(M, N, K, split), x.device, ws)
+    _check(lib.mdt_linear(_stream(stream), M, N, K, _ptr(x), _ptr(W), _ptr(residual), nseg, act, _ptr(out), split,
+                          _ptr(ws), wsb), "linear")
+    return out
+
+
+def interleave_gate_up(Wg: torch.Tensor, Wu: torch.Tensor) -> torch.Tensor:
+    """The [2F][K] weight layout of ACT_SWIGLU: rows 32i..32i+15 = Wg[16i..16i+15],
+    rows 32i+16..32i+31 = Wu[16i..16i+15] (a row permutation of the stacked pair)."""
+    F, K = Wg.shape
+    assert Wu.shape == (F, K) and F % 16 == 0
+    return torch.stack((Wg.reshape(F // 16, 16, K), Wu.reshape(F // 16, 16, K)), dim=1).reshape(2 * F, K).contiguous()
+

@@ -6,8 +6,8 @@
 // path[j] has depth j, so slot prefix_len + j gets exactly the position it was
 // rotated for.
 //
-// Grid (B, path_stride): workgroup (b, j) copies one row of H*Dh keys and values
-// with 16-byte vector moves.  Every workgroup of a sequence first validates the
+// Grid (B, path_stride, layers): workgroup (b, j, l) copies one row of H*Dh keys and
+// values of layer l with 16-byte vector moves.  Every workgroup of a sequence first validates the
 // whole sequence (path nodes, length, destination slots, pages), so either the
 // full path is written or nothing of it.
 //
@@ -19,12 +19,15 @@
 
 namespace {
 
+// blockIdx.z is the layer: layer l reads k_rot + l*k_stride, v + l*v_stride and writes
+// the cache rows at an offset of l*c_stride (all in 16-byte vectors).
 __global__ __launch_bounds__(256) void compact_kernel(KvSlots cache, const int32_t* __restrict__ path, int path_stride,
                                                       const int32_t* __restrict__ n_acc, const uint4* __restrict__ k_rot,
                                                       const uint4* __restrict__ v, int T, int row_vec,
                                                       const int32_t* __restrict__ prefix_len,
-                                                      int32_t* __restrict__ new_len) {
-    const int b = blockIdx.x, j = blockIdx.y;
+                                                      int32_t* __restrict__ new_len, long k_stride, long v_stride,
+                                                      long c_stride) {
+    const int b = blockIdx.x, j = blockIdx.y, l = blockIdx.z;
     const int n = n_acc[b];
     const int L = prefix_len[b];
     bool ok = n >= 1 && n <= path_stride && L >= 0;
@@ -33,13 +36,15 @@ __global__ __launch_bounds__(256) void compact_kernel(KvSlots cache, const int32
         const int node = path[(long)b * path_stride + q];
         ok = node >= 0 && node < T && slot_row(cache, b, L + q) >= 0;
     }
-    if (j == 0 && threadIdx.x == 0) new_len[b] = ok ? L + n : -1;
+    if (j == 0 && l == 0 && threadIdx.x == 0) new_len[b] = ok ? L + n : -1;
     if (!ok || j >= n) return;
     const int node = path[(long)b * path_stride + j];
     const long dst = slot_row(cache, b, L + j) * row_vec;
     const long src = ((long)b * T + node) * row_vec;
-    uint4* K = (uint4*)cache.k;
-    uint4* Vv = (uint4*)cache.v;
+    uint4* K = (uint4*)cache.k + l * c_stride;
+    uint4* Vv = (uint4*)cache.v + l * c_stride;
+    k_rot += l * k_stride;
+    v += l * v_stride;
     for (int e = threadIdx.x; e < row_vec; e += blockDim.x) {
         K[dst + e] = k_rot[src + e];
         Vv[dst + e] = v[src + e];
@@ -100,7 +105,39 @@ extern "C" mdt_status mdt_kv_compact(void* stream, mdt_dtype dt, int B, int T, i
     if (st != MDT_OK) return st;
     MDT_REQUIRE(path && n_acc, MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_LAUNCH("compact_kernel", compact_kernel, dim3(B, path_stride), dim3(256), 0, (hipStream_t)stream, c, path,
-               path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len);
+               path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len, new_prefix_len, 0L,
+               0L, 0L);
+    return mdt_launched("compact_kernel");
+}
+
+extern "C" mdt_status mdt_kv_compact_layers(void* stream, mdt_dtype dt, int n_layers, int B, int T, int H, int Dh,
+                                            const int32_t* path, int path_stride, const int32_t* n_acc,
+                                            const void* k_rot, long long k_rot_layer_stride, const void* v,
+                                            long long v_layer_stride, const mdt_kv_cache* cache,
+                                            long long cache_layer_stride, const int32_t* prefix_len,
+                                            int32_t* new_prefix_len) {
+    KvSlots c;
+    int row_vec = 0;
+    mdt_status st = mdt_check_compact_args(dt, B, T, H, Dh, path_stride, k_rot, v, cache, prefix_len,
+                                           new_prefix_len, &c, &row_vec);
+    if (st != MDT_OK) return st;
+    MDT_REQUIRE(path && n_acc, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(n_layers >= 1 && n_layers <= 65535, MDT_ERR_SHAPE, "n_layers=%d out of range 1..65535", n_layers);
+    const long long elt = dt == MDT_BF16 ? 2 : 4;
+    const long long rows_in = (long long)B * T * row_vec * 16 / elt;  // elements of one layer's k_rot / v
+    const long long rows_c = cache->layout == MDT_KV_PAGED ? (long long)cache->num_pages * cache->page_size
+                                                           : (long long)B * cache->capacity;
+    MDT_REQUIRE(k_rot_layer_stride >= 0 && v_layer_stride >= 0 && cache_layer_stride >= 0 &&
+                    (k_rot_layer_stride * elt) % 16 == 0 && (v_layer_stride * elt) % 16 == 0 &&
+                    (cache_layer_stride * elt) % 16 == 0,
+                MDT_ERR_ALIGN, "layer strides must be non-negative multiples of 16 bytes");
+    MDT_REQUIRE(n_layers == 1 || (k_rot_layer_stride >= rows_in && v_layer_stride >= rows_in &&
+                                  cache_layer_stride >= rows_c * row_vec * 16 / elt),
+                MDT_ERR_SHAPE, "layer strides smaller than one layer");
+    MDT_LAUNCH("compact_kernel", compact_kernel, dim3(B, path_stride, n_layers), dim3(256), 0, (hipStream_t)stream, c,
+               path, path_stride, n_acc, (const uint4*)k_rot, (const uint4*)v, T, row_vec, prefix_len,
+               new_prefix_len, (long)(k_rot_layer_stride * elt / 16), (long)(v_layer_stride * elt / 16),
+               (long)(cache_layer_stride * elt / 16));
     return mdt_launched("compact_kernel");
 }
 

@@ -1,0 +1,283 @@
+// The decoder layers of the verify forward: the backbone pass that the packed tree goes
+// through before the LM head (summary page, section 3.2 step 4 and "Tree Attention"
+// steps 3-5: all candidates are processed by the full model in one forward pass with
+// the tree mask; "Notes on Medusa", section 3).  The pages name the backbone
+// (Vicuna, a Llama model) but not its layer; the layer here is the Llama one:
+// pre-norm RMSNorm, q/k/v projections, tree attention with rotary positions, output
+// projection with residual, RMSNorm, SwiGLU feed-forward with residual.
+//
+//   mdt_embed    x0[m] = E[token[m]]
+//   mdt_rmsnorm  y = x / sqrt(mean(x^2) + eps) * g
+//   mdt_linear   y = x W^T (+ residual), or the SwiGLU of an interleaved gate/up product
+//
+// mdt_linear streams W once: with M <= 64 rows (a 64-node tree) every weight byte is
+// read once and used for 64 rows, so the product is bound by HBM, not by the matrix
+// cores.  Each workgroup multiplies a 64 x 64 tile (mfma_tile).  When the weight has
+// too few 64-row blocks to fill the chip (the d x d output projection: 64 blocks for
+// 256 CUs), the inner dimension is split over blockIdx.z; every split writes its fp32
+// partial tile, and the workgroup that finishes a tile last (a per-tile arrival
+// counter) adds the partials in split order -- the result does not depend on which
+// workgroup is last -- and runs the epilogue.  The counter is reset by that workgroup,
+// so the workspace is zero again after every call.
+#include <math.h>
+
+#include "mfma_tile.h"
+
+namespace {
+
+constexpr int kKC = 256;  // inner-dimension chunk staged in LDS
+constexpr int kNB = 64;   // weight rows per workgroup
+constexpr int kMBL = 64;  // x rows per workgroup
+constexpr int kThreads = 4 * kNB;
+constexpr int kZs = kNB + 1;  // row stride of the fp32 result tile in LDS
+
+enum Epi { kStore = 0, kResidual = 1, kSwiglu = 2 };
+
+struct LinArgs {
+    const bf16_t* x;
+    const bf16_t* W;
+    const bf16_t* res;
+    bf16_t* y;
+    float* part;
+    unsigned* count;
+    int M, N, K, kslice, nsplit, nseg;
+};
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+__device__ __forceinline__ float lo16(uint32_t u) { return bf16_to_f32(u & 0xffffu); }
+__device__ __forceinline__ float hi16(uint32_t u) { return bf16_to_f32(u >> 16); }
+
+// x SiLU(x)-gated: silu(g) * u, silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
+
+// grid (ceil(N/64), ceil(M/64), nsplit), block 256.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB>::kBytes];
+    __shared__ int is_last;
+    static_assert(MfmaTile<kKC, kNB>::kBytes >= kMBL * kZs * 4, "the result tile must fit");
+    const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    const int k0 = s * a.kslice;
+    const int klen = min(a.kslice, a.K - k0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    float* zt = (float*)smem;  // [64][kZs], reuses the operand tiles
+    f32x4 r[4];
+    mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, [&](const f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) r[mt] = acc[mt];
+    });
+    if (a.nsplit > 1) {
+        // Partial tiles keep the MFMA register layout: thread t's 16 values are floats
+        // 16t..16t+15 of its split's 64 x 64 block, so both the store and the read-back
+        // are four 16-byte accesses per thread.  Publish, count the arrival; the last of
+        // the nsplit workgroups of this tile adds all partials in split order.
+        f32x4* part = (f32x4*)(a.part + (size_t)tile * a.nsplit * (kMBL * kNB)) + 4 * threadIdx.x;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) part[(size_t)s * (kMBL * kNB / 4) + mt] = r[mt];
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) is_last = atomicAdd(a.count + tile, 1u) == (unsigned)(a.nsplit - 1);
+        __syncthreads();
+        if (!is_last) return;
+        __threadfence();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) r[mt] = part[mt];
+        for (int q = 1; q < a.nsplit; ++q) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) r[mt] += part[(size_t)q * (kMBL * kNB / 4) + mt];
+        }
+        if (threadIdx.x == 0) a.count[tile] = 0u;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = r[mt][e];
+    __syncthreads();
+
+    if constexpr (EPI == kSwiglu) {
+        // Weight rows 32j..32j+15 are gate rows 16j.., rows 32j+16..32j+31 the matching up
+        // rows: output column 16j + i = silu(gate_i) * up_i.  One thread, eight outputs.
+        const int row = threadIdx.x >> 2, og = threadIdx.x & 3;
+        const int jj = og >> 1, i0 = 8 * (og & 1);
+        const int m = m0 + row;
+        if (m < a.M && n0 + 32 * jj < a.N) {
+            const float* zr = zt + row * kZs + 32 * jj + i0;
+            uint4 o;
+            o.x = pack2(swiglu(zr[0], zr[16]), swiglu(zr[1], zr[17]));
+            o.y = pack2(swiglu(zr[2], zr[18]), swiglu(zr[3], zr[19]));
+            o.z = pack2(swiglu(zr[4], zr[20]), swiglu(zr[5], zr[21]));
+            o.w = pack2(swiglu(zr[6], zr[22]), swiglu(zr[7], zr[23]));
+            const int F = a.N >> 1;
+            *(uint4*)(a.y + (size_t)m * F + (n0 >> 1) + 16 * jj + i0) = o;
+        }
+    } else {
+        // Eight consecutive columns per item; the columns are cut into nseg equal
+        // segments, segment q going to y + q*M*(N/nseg) as its own [M][N/nseg] matrix.
+        const int nsegc = a.N / a.nseg;
+        for (int it = threadIdx.x; it < kMBL * (kNB / 8); it += kThreads) {
+            const int row = it >> 3, c0 = 8 * (it & 7);
+            const int m = m0 + row, n = n0 + c0;
+            if (m >= a.M || n >= a.N) continue;
+            const float* zr = zt + row * kZs + c0;
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = zr[j];
+            if constexpr (EPI == kResidual) {
+                const uint4 r = *(const uint4*)(a.res + (size_t)m * a.N + n);
+                v[0] += lo16(r.x), v[1] += hi16(r.x), v[2] += lo16(r.y), v[3] += hi16(r.y);
+                v[4] += lo16(r.z), v[5] += hi16(r.z), v[6] += lo16(r.w), v[7] += hi16(r.w);
+            }
+            const int q = n / nsegc;
+            uint4 o;
+            o.x = pack2(v[0], v[1]);
+            o.y = pack2(v[2], v[3]);
+            o.z = pack2(v[4], v[5]);
+            o.w = pack2(v[6], v[7]);
+            *(uint4*)(a.y + (size_t)q * a.M * nsegc + (size_t)m * nsegc + (n - q * nsegc)) = o;
+        }
+    }
+}
+
+// One workgroup per row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint4* __restrict__ x, const uint4* __restrict__ g,
+                                                      int nvec, float inv_d, float eps, uint4* __restrict__ y) {
+    __shared__ float red[4];
+    const uint4* xr = x + (size_t)blockIdx.x * nvec;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < nvec; i += 256) {
+        const uint4 q = xr[i];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = lo16(w[j]), b = hi16(w[j]);
+            ss += a * a + b * b;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) * inv_d + eps);
+    uint4* yr = y + (size_t)blockIdx.x * nvec;
+    for (int i = threadIdx.x; i < nvec; i += 256) {
+        const uint4 q = xr[i], gg = g[i];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w}, gw[4] = {gg.x, gg.y, gg.z, gg.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack2(lo16(w[j]) * r * lo16(gw[j]), hi16(w[j]) * r * hi16(gw[j]));
+        yr[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// One workgroup per row; a token outside [0, V) gives a zero row.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens, const uint4* __restrict__ E,
+                                                    int V, int nvec, uint4* __restrict__ y) {
+    const int t = tokens[blockIdx.x];
+    const bool ok = t >= 0 && t < V;
+    const uint4* src = E + (size_t)(ok ? t : 0) * nvec;
+    uint4* dst = y + (size_t)blockIdx.x * nvec;
+    for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+}
+
+// Workspace: a fixed block of per-tile arrival counters, then the fp32 partial tiles.
+// The counter block does not depend on the call's shape, so calls of different shapes
+// can share one workspace: no call's partials ever land on another call's counters.
+constexpr int kMaxSplitTiles = 16384;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * 4;
+
+struct LinPlan {
+    int tiles_n, tiles_m, nsplit, kslice;
+    size_t ws_bytes;
+};
+
+// Split the inner dimension only while the tile count stays within two workgroups per
+// compute unit (the occupancy the 66 KiB of LDS per workgroup allows), and keep every
+// slice at least 512 long.
+LinPlan plan_linear(int M, int N, int K, int split) {
+    LinPlan p;
+    p.tiles_n = (N + kNB - 1) / kNB;
+    p.tiles_m = (M + kMBL - 1) / kMBL;
+    const long tiles = (long)p.tiles_n * p.tiles_m;
+    int s = split;
+    if (s <= 0) {
+        const long slots = 2L * mdt_num_cus();
+        s = 1;
+        while (tiles * (s + 1) <= slots && K / (s + 1) >= 512) ++s;
+    }
+    s = (s < 1 || tiles > kMaxSplitTiles) ? 1 : s;
+    int ks = (K + s - 1) / s;
+    ks = (ks + 31) / 32 * 32;
+    p.kslice = ks;
+    p.nsplit = (K + ks - 1) / ks;
+    p.ws_bytes = p.nsplit > 1 ? kCounterBytes + (size_t)tiles * p.nsplit * kMBL * kNB * 4 : 0;
+    return p;
+}
+
+}  // namespace
+
+extern "C" size_t mdt_linear_workspace(int M, int N, int K, int split) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return plan_linear(M, N, K, split).ws_bytes;
+}
+
+extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* x, const void* W,
+                                 const void* residual, int nseg, int act, void* y, int split, void* ws,
+                                 size_t ws_bytes) {
+    MDT_REQUIRE(M >= 1 && N >= 1 && K >= 1, MDT_ERR_SHAPE, "bad shape M=%d N=%d K=%d", M, N, K);
+    MDT_REQUIRE((M + kMBL - 1) / kMBL <= 65535, MDT_ERR_SHAPE, "M=%d too large", M);
+    MDT_REQUIRE(K % 32 == 0 && N % 8 == 0, MDT_ERR_SHAPE, "K=%d must be a multiple of 32 and N=%d of 8", K, N);
+    MDT_REQUIRE(act == MDT_ACT_NONE || act == MDT_ACT_SWIGLU, MDT_ERR_VALUE, "unknown activation %d", act);
+    MDT_REQUIRE(split >= 0 && split <= 64, MDT_ERR_VALUE, "split=%d out of range 0..64", split);
+    MDT_REQUIRE(x && W && y, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(W) && mdt_aligned16(y) && mdt_aligned16(residual),
+                MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (act == MDT_ACT_SWIGLU) {
+        MDT_REQUIRE(N % 32 == 0, MDT_ERR_SHAPE, "SwiGLU needs N=%d to be a multiple of 32", N);
+        MDT_REQUIRE(!residual && nseg == 1, MDT_ERR_VALUE, "SwiGLU takes no residual and one segment");
+    } else {
+        MDT_REQUIRE(nseg >= 1 && N % nseg == 0 && (N / nseg) % 8 == 0, MDT_ERR_SHAPE,
+                    "nseg=%d must split N=%d into multiples of 8", nseg, N);
+        MDT_REQUIRE(!residual || nseg == 1, MDT_ERR_VALUE, "a residual needs nseg == 1");
+    }
+    const LinPlan p = plan_linear(M, N, K, split);
+    MDT_REQUIRE(p.ws_bytes == 0 || (ws && ws_bytes >= p.ws_bytes && mdt_aligned16(ws)), MDT_ERR_WORKSPACE,
+                "workspace needs %zu bytes", p.ws_bytes);
+    LinArgs a{(const bf16_t*)x, (const bf16_t*)W, (const bf16_t*)residual, (bf16_t*)y,
+              p.nsplit > 1 ? (float*)((char*)ws + kCounterBytes) : nullptr, (unsigned*)ws,
+              M, N, K, p.kslice, p.nsplit, nseg};
+    const dim3 grid(p.tiles_n, p.tiles_m, p.nsplit);
+    if (act == MDT_ACT_SWIGLU) {
+        MDT_LAUNCH("linear_mfma", linear_mfma<kSwiglu>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    } else if (residual) {
+        MDT_LAUNCH("linear_mfma", linear_mfma<kResidual>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    } else {
+        MDT_LAUNCH("linear_mfma", linear_mfma<kStore>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    }
+    return mdt_launched("linear_mfma");
+}
+
+extern "C" mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g, float eps, void* y) {
+    MDT_REQUIRE(M >= 1 && M <= 2147483647 / 2 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE,
+                "bad shape M=%d d=%d (d a multiple of 8)", M, d);
+    MDT_REQUIRE(eps >= 0.f, MDT_ERR_VALUE, "eps must be >= 0");
+    MDT_REQUIRE(x && g && y, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(g) && mdt_aligned16(y), MDT_ERR_ALIGN,
+                "tensor pointers must be 16-byte aligned");
+    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, (const uint4*)x,
+               (const uint4*)g, d / 8, 1.f / (float)d, eps, (uint4*)y);
+    return mdt_launched("rmsnorm_kernel");
+}
+
+extern "C" mdt_status mdt_embed(void* stream, int M, int d, int V, const int32_t* tokens, const void* E, void* y) {
+    MDT_REQUIRE(M >= 1 && M <= 2147483647 / 2 && V >= 1 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE,
+                "bad shape M=%d d=%d V=%d (d a multiple of 8)", M, d, V);
+    MDT_REQUIRE(tokens && E && y, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(E) && mdt_aligned16(y), MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    MDT_LAUNCH("embed_kernel", embed_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, tokens, (const uint4*)E, V,
+               d / 8, (uint4*)y);
+    return mdt_launched("embed_kernel");
+}

@@ -20,13 +20,9 @@
 #include <climits>
 #include <math.h>
 
-#include "common.h"
+#include "mfma_tile.h"
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNB = 64;          // vocabulary columns per workgroup
 constexpr int kMB = 64;          // node rows per workgroup (bf16 path)
@@ -135,20 +131,8 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
     }
 }
 
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
-
-// grid (ceil(V/64), ceil(M/64)), block 256.  Per chunk of KC dims, the workgroup moves
-// its 64 weight rows and 64 x rows into LDS with row-contiguous 16-byte loads (each
-// wave instruction covers whole 1 KiB row runs, the pattern HBM streams best), then
-// every wave reads MFMA fragments out of LDS: B = its 16 weight rows, A = the 64 x rows.
-// Two register buffers alternate
-// statically (the loop handles chunks c and c+1), so while chunk c is multiplied the
-// weights of chunks c+1 and c+2 and the x rows of chunk c+1 are in flight.
+// grid (ceil(V/NB), ceil(M/64)), block 4*NB: the tile of mfma_tile, then the statistics
+// epilogue.
 template <int KC, int NB>
 __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
                                                       int M, int d, int V, float tau, int nblk_n,
@@ -156,105 +140,20 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
                                                       const int32_t* __restrict__ parent,
                                                       const int32_t* __restrict__ tokens, int T,
                                                       float* __restrict__ edge) {
-    constexpr int NT = 4 * NB;                    // one wave per 16 weight rows
-    constexpr int kStride = KC + 8;               // LDS row stride (elements)
-    constexpr int kPR = KC / 8;                   // 16-byte pieces per row per chunk
-    constexpr int kPPT = NB * kPR / NT;           // weight pieces per thread per chunk
-    constexpr int kXPT = 64 * kPR / NT;           // x pieces per thread per chunk
-    constexpr int kXBytes = 64 * kStride * 2;     // the 64-row x tile
-    constexpr int kWBytes = NB * kStride * 2;     // the NB-row weight tile
-    static_assert(kXBytes + kWBytes >= 64 * (NB + 1) * 4, "the logits tile must fit");
-    static_assert(KC % 32 == 0, "k-steps of 32");
-    __shared__ __attribute__((aligned(16))) char smem[kXBytes + kWBytes];
-    bf16_t* xs = (bf16_t*)smem;
-    bf16_t* ws = (bf16_t*)(smem + kXBytes);
+    constexpr int NT = 4 * NB;
+    static_assert(MfmaTile<KC, NB>::kBytes >= 64 * (NB + 1) * 4, "the logits tile must fit");
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB>::kBytes];
     const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int nchunks = (d + KC - 1) / KC;
     const EdgePre pre = edge_preload<kMB>(m0, M, parent, tokens, T);
-
-    // No load is under a branch and no loaded register is touched before its LDS store
-    // (either would make the compiler wait for the loads still in flight): a piece
-    // outside the matrix, or of a chunk past the end, reads element 0 and is replaced
-    // by zero when it is stored.
-    u32x4 wA[kPPT], wB[kPPT], xr[kXPT];
-    auto piece_in = [&](int c, int j, int rows0, int nrows) {
-        const int p = threadIdx.x + NT * j;
-        const int r = p / kPR, off = 8 * (p % kPR);
-        return c < nchunks && off < d - c * KC && rows0 + r < nrows;
-    };
-    auto piece_at = [&](int c, int j, int rows0) {
-        const int p = threadIdx.x + NT * j;
-        return (size_t)(rows0 + p / kPR) * d + c * KC + 8 * (p % kPR);
-    };
-    auto load_w = [&](int c, u32x4 (&wr)[kPPT]) {
-#pragma unroll
-        for (int j = 0; j < kPPT; ++j) wr[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
-    };
-    auto load_x = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < kXPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
-    };
-    auto store = [&](int c, const u32x4 (&wr)[kPPT]) {
-        const u32x4 z{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kPPT; ++j) {
-            const int p = threadIdx.x + NT * j;
-            *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wr[j] : z;
-        }
-#pragma unroll
-        for (int j = 0; j < kXPT; ++j) {
-            const int p = threadIdx.x + NT * j;
-            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
-        }
-    };
-
-    // wave w owns weight rows 16w .. 16w+15 of the tile against all 64 x rows
-    f32x4 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c) {
-        const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
-        const bf16_t* wrow = ws + (wave * 16 + c16) * kStride + 8 * g;
-#pragma unroll 4
-        for (int s = 0; s < KC / 32; ++s) {
-            if (s < nsteps) {
-                const u32x4 b = *(const u32x4*)(wrow + 32 * s);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kStride + 32 * s + 8 * g);
-                    acc[mt] = mfma16(a, b, acc[mt]);
-                }
-            }
-        }
-    };
-    load_w(0, wA);
-    load_x(0);
-    load_w(1, wB);
-    store(0, wA);
-    __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-        // LDS: chunk c; wB: chunk c+1
-        load_x(c + 1);
-        load_w(c + 2, wA);
-        compute(c);
-        __syncthreads();
-        store(c + 1, wB);
-        __syncthreads();
-        // LDS: chunk c+1; wA: chunk c+2
-        load_x(c + 2);
-        load_w(c + 3, wB);
-        compute(c + 1);
-        __syncthreads();
-        store(c + 2, wA);
-        __syncthreads();
-    }
     float* zt = (float*)smem;  // [64][NB + 1], reuses the tiles
+    mfma_tile<KC, NB>(x, W, M, d, d, V, m0, n0, smem, [&](const f32x4 (&acc)[4]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (NB + 1) + wave * 16 + c16] = acc[mt][e];
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (NB + 1) + wave * 16 + c16] = acc[mt][e];
+    });
     __syncthreads();
     tile_epilogue<kMB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }

@@ -1,0 +1,157 @@
+"""The step with the full verify forward: the tree goes through every decoder layer.
+
+The summary page ("Medusa: Simple LLM Inference Acceleration Framework with
+Multiple Decoding Heads", section 3.2 step 4 and "Tree Attention" steps 3-5) runs
+all candidates through the backbone in one forward pass with the tree mask before
+the LM head.  ``VerifyForward.run()`` enqueues, on one stream and with no host
+synchronisation:
+
+    medusa_heads -> topk_tree_expand -> embed
+    -> per layer: rmsnorm -> linear (q|k|v) -> tree_attention -> linear (+x)
+                  -> rmsnorm -> linear (SwiGLU) -> linear (+x)
+    -> rmsnorm -> verify_logits -> accept_path -> kv_compact_layers
+
+Every layer has its own prefix cache (one allocation [layers][B][capacity][H][Dh]);
+every layer's tree keys/values are kept until acceptance, then the accepted path is
+appended to every layer's cache in one launch.
+"""
+
+from __future__ import annotations
+
+from typing import List
+
+import numpy as np
+import torch
+
+from . import (ACT_SWIGLU, GREEDY, TYPICAL, KVCache, Tree, accept_path, embed, interleave_gate_up,
+               kv_compact_layers, linear, linear_workspace, medusa_heads, medusa_heads_workspace, new_workspace,
+               rmsnorm, topk_tree_expand, topk_workspace, tree_attention, tree_attention_workspace, verify_logits,
+               verify_logits_workspace, MDT_BF16)
+from .step import to_device
+
+LAYER_KEYS = ("g_attn", "Wqkv", "Wo", "g_mlp", "Wgu", "Wd")
+
+
+def upload_layer(lw: dict, device) -> dict:
+    """One layer's numpy weights (bf16 patterns) -> the device layout the calls take:
+    q|k|v stacked into one [3d][d] weight, gate/up interleaved by 16 rows."""
+    t = {k: to_device(lw[k], device) for k in ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_mlp", "Wg", "Wu", "Wd")}
+    return {"g_attn": t["g_attn"], "Wqkv": torch.cat((t["Wq"], t["Wk"], t["Wv"])).contiguous(), "Wo": t["Wo"],
+            "g_mlp": t["g_mlp"], "Wgu": interleave_gate_up(t["Wg"], t["Wu"]), "Wd": t["Wd"]}
+
+
+class VerifyForward:
+    """``base``: device tensors h, W1, W2, Wlm (the step's); ``E``, ``g_final``: embedding and
+    final norm gain; ``layers``: per-layer dicts with LAYER_KEYS; ``Kc``/``Vc``: the caches
+    of every layer, [n_layers][B][capacity][H][Dh]; ``prefix_len``: device int32 [B]."""
+
+    def __init__(self, dw, base: dict, E, g_final, layers: List[dict], Kc, Vc, prefix_len, mode="greedy",
+                 temperature=0.0, eps=0.09, delta=0.3, tree: Tree = None, split: int = 0):
+        w = dw.base
+        assert w.dtype == "bf16" and not w.paged, "the full forward runs on bf16 contiguous caches"
+        self.dw, self.w = dw, w
+        self.mode = GREEDY if mode == "greedy" else TYPICAL
+        self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
+        self.base, self.E, self.g_final, self.layers = base, E, g_final, layers
+        self.Kc, self.Vc, self.prefix_len = Kc, Vc, prefix_len
+        self.split = split
+        dev = E.device
+        self.dev = dev
+        nL = len(layers)
+        self.caches = [KVCache(Kc[l], Vc[l]) for l in range(nL)]
+        self.tree = (tree or Tree.for_workload(w)).to_device(dev)
+        B, d, V, K, k_cfg, T, H, Dh, F = w.B, w.d, w.V, w.K, w.k_cfg, self.tree.T, w.H, w.Dh, dw.ffn
+        M = B * T
+        self.M = M
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.logits = torch.empty((B, K + 1, V), **f32)
+        self.topk_idx = torch.empty((B, K + 1, k_cfg), **i32)
+        self.topk_val = torch.empty((B, K + 1, k_cfg), **f32)
+        self.tokens = torch.empty((B, T), **i32)
+        self.pos = torch.empty((B, T), **i32)
+        self.x = torch.empty((M, d), **bf)
+        self.h = torch.empty((M, d), **bf)
+        self.qkv = torch.empty((nL, 3, M, d), **bf)      # per layer: q, k, v segments
+        self.o = torch.empty((M, d), **bf)
+        self.k_rot = torch.empty((nL, B, T, H, Dh), **bf)
+        self.a = torch.empty((M, F), **bf)
+        self.xf = torch.empty((M, d), **bf)
+        self.stats = torch.empty((M, 4), **i32)
+        self.edge = torch.empty((B, T), **f32)
+        self.path = torch.empty((B, self.tree.tree.max_depth + 1), **i32)
+        self.n_acc = torch.empty((B,), **i32)
+        self.new_len = torch.empty((B,), **i32)
+        self.ws_heads = new_workspace(medusa_heads_workspace(B, d, K), dev)
+        self.ws_topk = new_workspace(topk_workspace(B, K, V, k_cfg), dev)
+        self.ws_attn = new_workspace(tree_attention_workspace(MDT_BF16, B, T, H, Dh, self.caches[0].desc.capacity),
+                                     dev) if nL else None
+        self.ws_verify = new_workspace(verify_logits_workspace(MDT_BF16, B, T, d, V), dev)
+        # one linear workspace for all products: they run one after another on one stream
+        # and each leaves its arrival counters at zero
+        need = max(linear_workspace(M, 3 * d, d, split), linear_workspace(M, d, d, split),
+                   linear_workspace(M, 2 * F, d, split), linear_workspace(M, d, F, split))
+        self.ws_lin = new_workspace(need, dev)
+
+    @classmethod
+    def from_numpy(cls, dw, inp: dict, fin: dict, layers_np: List[dict], device="cuda", **kw):
+        dev = torch.device(device)
+        base = {k: to_device(inp[k], dev) for k in ("h", "W1", "W2", "Wlm")}
+        layers = [upload_layer(lw, dev) for lw in layers_np]
+        Kc = torch.stack([to_device(lw["Kc"], dev) for lw in layers_np]) if layers_np else None
+        Vc = torch.stack([to_device(lw["Vc"], dev) for lw in layers_np]) if layers_np else None
+        lens = torch.from_numpy(inp["prefix_len"].astype(np.int32)).to(dev)
+        return cls(dw, base, to_device(fin["E"], dev), to_device(fin["g_final"], dev), layers, Kc, Vc, lens, **kw)
+
+    def layer(self, l: int, stream=None):
+        """Enqueue decoder layer l on the residual stream self.x (updated in place)."""
+        w, lw = self.w, self.layers[l]
+        B, T, H, Dh = w.B, self.tree.T, w.H, w.Dh
+        eps = self.dw.norm_eps
+        ws = self.ws_lin
+        rmsnorm(self.x, lw["g_attn"], eps, out=self.h, stream=stream)
+        qkv = self.qkv[l]
+        linear(self.h, lw["Wqkv"], nseg=3, out=qkv, split=self.split, ws=ws, stream=stream)
+        shp = (B, T, H, Dh)
+        tree_attention(qkv[0].view(shp), qkv[1].view(shp), qkv[2].view(shp), self.caches[l], self.prefix_len,
+                       self.tree, w.rope_theta, out=self.o.view(shp), k_rot=self.k_rot[l], ws=self.ws_attn,
+                       stream=stream)
+        linear(self.o, lw["Wo"], residual=self.x, out=self.x, split=self.split, ws=ws, stream=stream)
+        rmsnorm(self.x, lw["g_mlp"], eps, out=self.h, stream=stream)
+        linear(self.h, lw["Wgu"], act=ACT_SWIGLU, out=self.a, split=self.split, ws=ws, stream=stream)
+        linear(self.a, lw["Wd"], residual=self.x, out=self.x, split=self.split, ws=ws, stream=stream)
+
+    def run(self, stream=None):
+        w, t = self.w, self.base
+        medusa_heads(t["h"], t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
+        topk_tree_expand(self.logits, w.k_cfg, self.tree, self.prefix_len, self.topk_idx, self.topk_val,
+                         self.tokens, self.pos, ws=self.ws_topk, stream=stream)
+        embed(self.tokens.view(-1), self.E, out=self.x, stream=stream)
+        for l in range(len(self.layers)):
+            self.layer(l, stream)
+        rmsnorm(self.x, self.g_final, self.dw.norm_eps, out=self.xf, stream=stream)
+        verify_logits(self.xf, t["Wlm"], self.tree, self.tokens, self.temperature, stats=self.stats,
+                      edge=self.edge, ws=self.ws_verify, stream=stream)
+        accept_path(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta,
+                    self.temperature, path=self.path, n_acc=self.n_acc, stream=stream)
+        if self.layers:
+            B, T, H, Dh = w.B, self.tree.T, w.H, w.Dh
+            v = self.qkv[:, 2].view(len(self.layers), B, T, H, Dh)
+            kv_compact_layers(self.path, self.n_acc, self.k_rot, v, self.caches[0], self.prefix_len,
+                              self.Kc.stride(0), new_prefix_len=self.new_len, stream=stream)
+
+    def outputs(self) -> dict:
+        torch.cuda.synchronize()
+
+        def f(x):
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).cpu().numpy().view(np.uint16)
+            return x.cpu().numpy()
+
+        out = dict(logits=f(self.logits), tokens=f(self.tokens), x_last=f(self.x), xf=f(self.xf),
+                   stats=f(self.stats).view(np.int32), edge=f(self.edge), path=f(self.path), n_acc=f(self.n_acc),
+                   k_rot=f(self.k_rot), v=f(self.qkv[:, 2]))
+        if self.layers:
+            out.update(new_len=f(self.new_len), Kc=f(self.Kc), Vc=f(self.Vc))
+        return out

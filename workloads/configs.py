@@ -130,3 +130,31 @@ PARITY_CASES = {
 
 def get_case(name: str) -> Workload:
     return PARITY_CASES[name] if name in PARITY_CASES else WORKLOADS[name]
+
+
+# ----------------------------------------------------------------------------
+# Full verify forward: the tree through a stack of decoder layers
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DeepWorkload:
+    """A step workload whose tree goes through ``n_layers`` synthetic Llama decoder layers
+    (RMSNorm, q/k/v, tree attention, output projection, RMSNorm, SwiGLU feed-forward of
+    width ``ffn``) and a final RMSNorm before the LM head.  Vicuna-7B has 32 layers of
+    feed-forward width 11008."""
+    name: str
+    base: Workload
+    n_layers: int
+    ffn: int
+    norm_eps: float = 1e-6
+
+
+FORWARD_WORKLOADS = {
+    "7b-T64-L1024-x32": DeepWorkload("7b-T64-L1024-x32", WORKLOADS["7b-T64-L1024"], 32, 11008),
+}
+
+# Parity cases of the forward: the 7B mini with two layers, and two layers at full 7B width.
+FORWARD_CASES = {
+    "7b-mini-x2": DeepWorkload("7b-mini-x2", PARITY_CASES["7b-mini"], 2, 1376),
+    "7b-T64-L1024-x2": DeepWorkload("7b-T64-L1024-x2", WORKLOADS["7b-T64-L1024"], 2, 11008),
+}

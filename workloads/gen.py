@@ -205,3 +205,49 @@ def uniforms(w: Workload, seed: int, s: int = 0) -> dict:
     T = w.n_nodes
     return {"u_accept": rng.random((w.B, T), dtype=np.float32),
             "u_resample": rng.random(w.B, dtype=np.float32)}
+
+
+# ----------------------------------------------------------------------------
+# full verify forward: decoder-layer weights and per-layer caches
+# ----------------------------------------------------------------------------
+
+TID_EMBED, TID_GFINAL = 900, 901
+TID_LAYER = 1000  # + 16 * layer + j
+LAYER_TENSORS = ("g_attn", "Wq", "Wk", "Wv", "Wo", "g_mlp", "Wg", "Wu", "Wd", "Kc", "Vc")
+
+
+def _gain(seed: int, tid: int, n: int) -> np.ndarray:
+    """Norm gains 1 + N(0, 0.1^2) as bf16 patterns."""
+    z = normal_stream(seed, tid, n, 0.1, False)
+    return f32_to_bf16_bits(z + np.float32(1.0))
+
+
+def forward_inputs(dw, seed: int) -> dict:
+    """The tensors the full forward adds to a step: ``E`` [V][d] (N(0, 1)) and ``g_final`` [d]."""
+    w = dw.base
+    return {"E": normal_stream(seed, TID_EMBED, w.V * w.d, 1.0, True).reshape(w.V, w.d),
+            "g_final": _gain(seed, TID_GFINAL, w.d)}
+
+
+def layer_inputs(dw, seed: int, layer: int, steps: int = 1) -> dict:
+    """Layer ``layer``'s weights (bf16 patterns, [out][in]) and its prefix cache.
+
+    Projection weights are N(0, 1/fan_in) so that each product keeps unit scale; gains
+    are 1 + N(0, 0.1^2); the cache holds N(0, 1) keys/values (the scale of the tree's
+    own keys and values) below each prefix length, zeros elsewhere.
+    """
+    w = dw.base
+    d, F = w.d, dw.ffn
+    tid = {n: TID_LAYER + 16 * layer + j for j, n in enumerate(LAYER_TENSORS)}
+    sd, sf = float(d) ** -0.5, float(F) ** -0.5
+    out = {"g_attn": _gain(seed, tid["g_attn"], d), "g_mlp": _gain(seed, tid["g_mlp"], d)}
+    for n in ("Wq", "Wk", "Wv", "Wo"):
+        out[n] = normal_stream(seed, tid[n], d * d, sd, True).reshape(d, d)
+    out["Wg"] = normal_stream(seed, tid["Wg"], F * d, sd, True).reshape(F, d)
+    out["Wu"] = normal_stream(seed, tid["Wu"], F * d, sd, True).reshape(F, d)
+    out["Wd"] = normal_stream(seed, tid["Wd"], d * F, sf, True).reshape(d, F)
+    lens = prefix_lengths(w, seed)
+    table = page_layout(w, seed, lens, steps)[0] if w.paged else None
+    out["Kc"] = _cache(w, seed, tid["Kc"], lens, 1.0, True, table, steps)
+    out["Vc"] = _cache(w, seed, tid["Vc"], lens, 1.0, True, table, steps)
+    return out
