@@ -14,8 +14,10 @@ torch.cuda.synchronize() calls (the events add dispatch gaps, so they stay out
 of it).  The CPU oracle is timed on the host on whole steps of the same
 workload for about 10 s.  A report of chained steps (``decode_loop``: each step
 starts from the previous step's last accepted node, replayed as one graph) gives
-the time per chained step and the synthetic acceptance; it is context, not the
-metric.  One JSON line goes to stdout.
+the time per chained step and the synthetic acceptance; a report of the full
+verify forward (``full_depth``: the tree through all 32 decoder layers of the
+7B-shaped model before the LM head, one graph) gives its time per step and HBM
+fraction.  Both are context, not the metric.  One JSON line goes to stdout.
 """
 
 from __future__ import annotations
@@ -131,6 +133,101 @@ def decode_loop_report(w, inp, seed, step, mode, tau, eps, delta, replays):
             "note": "synthetic random weights: the acceptance is not that of a trained model"}
 
 
+def forward_bytes(dw, T, lens):
+    """Bytes the full-forward step must move: the step's heads, top-k and LM-head bytes,
+    every layer's weights once, every layer's prefix KV once, the embedding rows, and the
+    layer activations (each written once and read once per use)."""
+    w = dw.base
+    ab = algorithmic_bytes(w, T, lens)
+    e, B, d, F, M, nL = w.elt_bytes, w.B, w.d, dw.ffn, w.B * T, dw.n_layers
+    layer_w = e * (3 * d * d + d * d + 2 * F * d + d * F + 2 * d)
+    kv = e * 2 * int(sum(int(x) for x in lens)) * w.H * w.Dh
+    # per layer: h (w+r), q|k|v (w+r), k_rot (w), o (w+r), x (r+w twice), a (w+r), fp32 slices (w+r)
+    act = e * M * (2 * d + 6 * d + d + 2 * d + 4 * d + 2 * F)
+    total = (ab["heads_gemv_w1_lm"] + ab["heads_gemv_w2"] + ab["topk"] + ab["verify_mfma"] + e * M * d
+             + nL * (layer_w + kv + act + 2 * 2 * e * B * (w.K + 1) * d))
+    return {"layer_weights": nL * layer_w, "prefix_kv": nL * kv, "total": total}
+
+
+def full_depth_report(w, seed, step, mode, tau, eps, delta, replays):
+    """The step with the full verify forward: the tree through every decoder layer of the
+    7B-shaped model (32 layers, feed-forward 11008) before the LM head.  Layer weights,
+    embedding and per-layer caches are drawn on the GPU with a seeded torch generator
+    (13 GB); the heads and LM head are the step's own.  Replayed as one HIP graph."""
+    import numpy as np
+    import torch
+    import medusa_tree_verification_heads_amd as mdt
+    from medusa_tree_verification_heads_amd.forward import VerifyForward
+    from workloads.configs import FORWARD_WORKLOADS
+    dw = next((f for f in FORWARD_WORKLOADS.values() if f.base.name == w.name), None)
+    if dw is None:
+        return None
+    dev = step.dev
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    d, F, nL = w.d, dw.ffn, dw.n_layers
+
+    def rn(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    def gain():
+        return (1 + torch.randn((d,), generator=gen, device=dev) * 0.1).to(torch.bfloat16)
+
+    layers = [{"g_attn": gain(), "Wqkv": rn((3 * d, d), d ** -0.5), "Wo": rn((d, d), d ** -0.5), "g_mlp": gain(),
+               "Wgu": rn((2 * F, d), d ** -0.5), "Wd": rn((d, F), F ** -0.5)} for _ in range(nL)]
+    cap = w.cache_capacity(1)
+    lens = step.prefix_len
+    Kc = torch.zeros((nL, w.B, cap, w.H, w.Dh), dtype=torch.bfloat16, device=dev)
+    Vc = torch.zeros_like(Kc)
+    for b in range(w.B):
+        L = int(lens[b])
+        Kc[:, b, :L] = rn((nL, L, w.H, w.Dh), 1.0)
+        Vc[:, b, :L] = rn((nL, L, w.H, w.Dh), 1.0)
+    f = VerifyForward(dw, step.t, rn((w.V, d), 1.0), gain(), layers, Kc, Vc, lens, mode, tau, eps, delta,
+                      tree=None)
+    for _ in range(2):
+        f.run()
+    torch.cuda.synchronize()
+    timer = mdt.KernelTimer(16 * nL + 16)
+    with timer:
+        f.run()
+    torch.cuda.synchronize()
+    per = {}
+    for k, ms in timer.durations_ms():
+        per[k] = per.get(k, 0.0) + 1e3 * ms
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        f.run()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(3, replays // 20)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / reps
+    fb = forward_bytes(dw, f.tree.T, [int(x) for x in lens.cpu()])
+    gbps = fb["total"] / (us * 1e-6) / 1e9
+    lin = fb["layer_weights"] / (per.get("linear_mfma", 0) * 1e-6) / 1e9 if per.get("linear_mfma") else None
+    rep = {"workload": dw.name, "layers": nL, "ffn": F, "us_per_step": round(us, 1),
+           "steps_per_s": round(1e6 / us, 2), "tree_tokens_per_s": round(1e6 / us * f.M, 1),
+           "algorithmic_bytes": fb["total"], "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "linear_weight_GBps": round(lin, 1) if lin else None, "splits": [f.split_o, f.split_d],
+           "per_kernel_us_per_step": {k: round(v, 1) for k, v in per.items()},
+           "n_acc": f.n_acc.cpu().tolist()[:8],
+           "weights": "drawn on the GPU with a seeded torch generator (13 GB), random: acceptance is not a "
+                      "trained model's"}
+    del f, layers, Kc, Vc
+    torch.cuda.empty_cache()
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +238,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-loop", action="store_true", help="skip the chained-step (decode loop) report")
+    ap.add_argument("--no-full-depth", action="store_true", help="skip the full verify forward report")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -235,6 +333,11 @@ def main():
         loop_rep = decode_loop_report(w, inp, seed, step, args.mode, tau, eps, delta, args.steps)
         log(f"decode loop: {loop_rep}")
 
+    full_rep = None
+    if not args.no_graph and not args.no_full_depth:
+        full_rep = full_depth_report(w, seed, step, args.mode, tau, eps, delta, args.steps)
+        log(f"full verify forward: {full_rep}")
+
     lens = inp["prefix_len"]
     ab = algorithmic_bytes(w, T, lens)
     dom = "heads_gemv_w2"
@@ -273,6 +376,7 @@ def main():
         "n_acc": step.n_acc.cpu().tolist()[:8],
         "roofline": roofline,
         "decode_loop": loop_rep,
+        "full_depth": full_rep,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

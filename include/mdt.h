@@ -13,7 +13,7 @@
  *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
  *   mdt_accept_rejection  rejection-sampling acceptance on the tree (a third acceptance rule)
  *   mdt_kv_compact_layers mdt_kv_compact for every layer of a model in one launch
- *   mdt_embed, mdt_rmsnorm, mdt_linear
+ *   mdt_embed, mdt_rmsnorm, mdt_add_rmsnorm, mdt_linear, mdt_linear_split
  *                         the decoder-layer pieces of the full verify forward
  *
  * The pages this follows are the Medusa pages: "Medusa: Simple LLM Inference
@@ -491,6 +491,8 @@ mdt_status mdt_kv_compact_layers(void* stream, mdt_dtype dt, int n_layers, int B
  *   per layer:  h = rmsnorm(x, g_attn); q|k|v = h Wqkv^T (three segments);
  *               o = mdt_tree_attention(q, k, v); x = x + o Wo^T;
  *               h = rmsnorm(x, g_mlp); a = silu(h Wg^T) * (h Wu^T); x = x + a Wd^T
+ * (the products with few output columns as mdt_linear_split, their residual add fused
+ * into the next RMSNorm by mdt_add_rmsnorm)
  *   xf   = rmsnorm(x, g_final) -> mdt_verify_logits
  * Every matrix is bf16 and every product accumulates in fp32; each call rounds its
  * output to bf16 once.
@@ -511,6 +513,18 @@ mdt_status mdt_embed(void* stream, int M, int d, int V, const int32_t* tokens, c
 mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g, float eps, void* y);
 
 /*
+ * The residual add that closes a split product, then the next RMSNorm:
+ *   x[m][j] = bf16(x[m][j] + part[0][m][j] + ... + part[nparts-1][m][j])  (fp32 sum, in order)
+ *   y[m][j] = bf16(x[m][j] * r_m * g[j])  with r_m of the updated row, as mdt_rmsnorm.
+ *  part  device f32 [nparts][M][d] (1 <= nparts <= 64), e.g. from mdt_linear_split; must
+ *        not overlap x
+ *  x     device bf16 [M][d], read and written; y device bf16 [M][d], not x.
+ * Errors: as mdt_rmsnorm, plus MDT_ERR_VALUE (nparts, overlap).
+ */
+mdt_status mdt_add_rmsnorm(void* stream, int M, int d, int nparts, const float* part, void* x, const void* g,
+                           float eps, void* y);
+
+/*
  * z = x W^T with x device bf16 [M][K] and W device bf16 [N][K] (fp32 accumulation), then
  *  act == MDT_ACT_NONE:   y[q][m][j] = bf16(z[m][q*N/nseg + j] (+ residual[m][q*N/nseg + j]))
  *                         for the nseg column segments q (y is nseg matrices [M][N/nseg]
@@ -523,19 +537,24 @@ mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g,
  *                         y[m][16i + c] = bf16(silu(z[m][32i + c]) * z[m][32i + 16 + c]),
  *                         silu(u) = u / (1 + e^-u).  N % 32 == 0, no residual, nseg == 1.
  *  K % 32 == 0, N % 8 == 0, N/nseg % 8 == 0.
- *  split   0 = choose; s > 0 cuts the inner dimension into about s slices (at most 64;
- *          ignored when the output has more than 16384 tiles of 64 x 64)
- *  ws      device workspace of mdt_linear_workspace(M, N, K, split) bytes (0 bytes, and
- *          ws may be NULL, when the inner dimension is not cut).  Its first 64 KiB are
- *          arrival counters: they must be zero when the call starts (allocate the
- *          workspace zeroed) and every completed call leaves them zero, so calls of any
- *          shapes may share one workspace as long as they do not run concurrently.
- * Errors: MDT_ERR_SHAPE, MDT_ERR_VALUE (act, split, residual with nseg > 1 or with
- * SwiGLU), MDT_ERR_NULL, MDT_ERR_ALIGN, MDT_ERR_WORKSPACE.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_VALUE (act, residual with nseg > 1 or with SwiGLU),
+ * MDT_ERR_NULL, MDT_ERR_ALIGN.
  */
-size_t mdt_linear_workspace(int M, int N, int K, int split);
 mdt_status mdt_linear(void* stream, int M, int N, int K, const void* x, const void* W, const void* residual,
-                      int nseg, int act, void* y, int split, void* ws, size_t ws_bytes);
+                      int nseg, int act, void* y);
+
+/*
+ * The inner dimension cut into nsplit slices of ks = ceil(K/nsplit) rounded up to a
+ * multiple of 32 (the last slice shorter): part[s][m][n] = sum over k in slice s of
+ * x[m][k] W[n][k], fp32, no rounding.  A product whose output has too few 64 x 64
+ * tiles to fill the GPU runs on nsplit times as many workgroups this way; the slices
+ * are added by mdt_add_rmsnorm.
+ *  x, W as mdt_linear; part device f32 [nsplit][M][N]; 1 <= nsplit <= 64, nsplit*32 <= K
+ *  and the rounding of ks must leave exactly nsplit slices.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_VALUE (nsplit), MDT_ERR_NULL, MDT_ERR_ALIGN.
+ */
+mdt_status mdt_linear_split(void* stream, int M, int N, int K, const void* x, const void* W, int nsplit,
+                            float* part);
 
 /* ------------------------------------------------------------------------- */
 /* Misc                                                                       */

@@ -103,9 +103,9 @@ _SIGS = [
                                       ctypes.POINTER(KVCacheDesc), ctypes.c_longlong, c_void_p, c_void_p]),
     ("mdt_embed", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     ("mdt_rmsnorm", c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_float, c_void_p]),
-    ("mdt_linear_workspace", c_size, [c_int, c_int, c_int, c_int]),
-    ("mdt_linear", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p,
-                           c_int, c_void_p, c_size]),
+    ("mdt_add_rmsnorm", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
+    ("mdt_linear", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    ("mdt_linear_split", c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p]),
 ]
 
 EXPORTED = [name for name, _, _ in _SIGS]
@@ -516,16 +516,24 @@ def rmsnorm(x, g, eps: float, out=None, stream=None):
     return out
 
 
-def linear_workspace(M, N, K, split=0) -> int:
-    return lib.mdt_linear_workspace(M, N, K, split)
+def add_rmsnorm(part, x, g, eps: float, out=None, stream=None):
+    """x += part[0] + ... + part[n-1] (fp32 sum, one bf16 rounding), in place; returns
+    rmsnorm(x) * g (bf16).  part: fp32 [n][M][d]."""
+    _bf16_2d(x, "x")
+    M, d = x.shape
+    n = part.shape[0]
+    assert part.dtype == torch.float32 and part.shape == (n, M, d) and part.is_contiguous()
+    out = torch.empty_like(x) if out is None else out
+    _check(lib.mdt_add_rmsnorm(_stream(stream), M, d, n, _ptr(part), _ptr(x), _ptr(g), float(eps), _ptr(out)),
+           "add_rmsnorm")
+    return out
 
 
-def linear(x, W, residual=None, nseg=1, act=ACT_NONE, out=None, split=0, ws=None, stream=None):
+def linear(x, W, residual=None, nseg=1, act=ACT_NONE, out=None, stream=None):
     """x [M][K] times W [N][K] transposed (bf16 in and out, fp32 accumulation).
 
     act=ACT_NONE: (+ residual [M][N]) -> [M][N], or [nseg][M][N/nseg] column segments.
     act=ACT_SWIGLU: W holds gate/up rows interleaved by 16 (see interleave_gate_up) -> [M][N/2].
-    ``ws`` must start zeroed (new_workspace does that); the call leaves it so.
     """
     _bf16_2d(x, "x")
     _bf16_2d(W, "W")
@@ -536,10 +544,38 @@ def linear(x, W, residual=None, nseg=1, act=ACT_NONE, out=None, split=0, ws=None
     else:
         shape = (M, N) if nseg == 1 else (nseg, M, N // nseg)
     out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
-    ws, wsb = _ws(linear_workspace(M, N, K, split), x.device, ws)
-    _check(lib.mdt_linear(_stream(stream), M, N, K, _ptr(x), _ptr(W), _ptr(residual), nseg, act, _ptr(out), split,
-                          _ptr(ws), wsb), "linear")
+    _check(lib.mdt_linear(_stream(stream), M, N, K, _ptr(x), _ptr(W), _ptr(residual), nseg, act, _ptr(out)),
+           "linear")
     return out
+
+
+def linear_split(x, W, nsplit: int, out=None, stream=None):
+    """fp32 products of nsplit slices of the inner dimension -> [nsplit][M][N]."""
+    _bf16_2d(x, "x")
+    _bf16_2d(W, "W")
+    M, K = x.shape
+    N = W.shape[0]
+    out = torch.empty((nsplit, M, N), dtype=torch.float32, device=x.device) if out is None else out
+    _check(lib.mdt_linear_split(_stream(stream), M, N, K, _ptr(x), _ptr(W), int(nsplit), _ptr(out)), "linear_split")
+    return out
+
+
+def auto_split(M: int, N: int, K: int, device=None) -> int:
+    """Slices for a product whose 64 x 64 output tiles are too few to fill the GPU: grow
+    while the workgroups stay within two per compute unit and slices stay >= 512 long."""
+    cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
+    tiles = -(-N // 64) * -(-M // 64)
+    s = 1
+    while tiles * (s + 1) <= 2 * cus and K // (s + 1) >= 512:
+        s += 1
+
+    def slices(n):  # slices left after rounding each to a multiple of 32
+        ks = -(-(-(-K // n)) // 32) * 32
+        return -(-K // ks)
+
+    while s > 1 and slices(s) != s:
+        s -= 1
+    return s
 
 
 def interleave_gate_up(Wg: torch.Tensor, Wu: torch.Tensor) -> torch.Tensor:

@@ -6,19 +6,20 @@
 // pre-norm RMSNorm, q/k/v projections, tree attention with rotary positions, output
 // projection with residual, RMSNorm, SwiGLU feed-forward with residual.
 //
-//   mdt_embed    x0[m] = E[token[m]]
-//   mdt_rmsnorm  y = x / sqrt(mean(x^2) + eps) * g
-//   mdt_linear   y = x W^T (+ residual), or the SwiGLU of an interleaved gate/up product
+//   mdt_embed        x0[m] = E[token[m]]
+//   mdt_rmsnorm      h = x / sqrt(mean(x^2) + eps) * g
+//   mdt_add_rmsnorm  x += sum of fp32 partial products; h = rmsnorm(x) * g
+//   mdt_linear       y = x W^T (+ residual), q|k|v segments, or the SwiGLU of an
+//                    interleaved gate/up product
+//   mdt_linear_split the products of nsplit slices of the inner dimension, in fp32
 //
-// mdt_linear streams W once: with M <= 64 rows (a 64-node tree) every weight byte is
-// read once and used for 64 rows, so the product is bound by HBM, not by the matrix
-// cores.  Each workgroup multiplies a 64 x 64 tile (mfma_tile).  When the weight has
-// too few 64-row blocks to fill the chip (the d x d output projection: 64 blocks for
-// 256 CUs), the inner dimension is split over blockIdx.z; every split writes its fp32
-// partial tile, and the workgroup that finishes a tile last (a per-tile arrival
-// counter) adds the partials in split order -- the result does not depend on which
-// workgroup is last -- and runs the epilogue.  The counter is reset by that workgroup,
-// so the workspace is zero again after every call.
+// The linear calls stream W once: with M <= 64 rows (a 64-node tree) every weight byte
+// is read once and used for 64 rows, so a product is bound by HBM, not by the matrix
+// cores.  Each workgroup multiplies a 64 x 64 tile (mfma_tile).  A weight with few
+// 64-row blocks (the d x d output projection: 64 blocks for 256 CUs) has its inner
+// dimension cut into slices on more workgroups; their fp32 partial tiles are added
+// by the next call, which reads whole rows anyway (mdt_add_rmsnorm: the residual add
+// and the following RMSNorm), so no workgroup waits for another.
 #include <math.h>
 
 #include "mfma_tile.h"
@@ -31,16 +32,15 @@ constexpr int kMBL = 64;  // x rows per workgroup
 constexpr int kThreads = 4 * kNB;
 constexpr int kZs = kNB + 1;  // row stride of the fp32 result tile in LDS
 
-enum Epi { kStore = 0, kResidual = 1, kSwiglu = 2 };
+enum Epi { kStore = 0, kResidual = 1, kSwiglu = 2, kPartial = 3 };
 
 struct LinArgs {
     const bf16_t* x;
     const bf16_t* W;
     const bf16_t* res;
     bf16_t* y;
-    float* part;
-    unsigned* count;
-    int M, N, K, kslice, nsplit, nseg;
+    float* part;  // kPartial: [nsplit][M][N]
+    int M, N, K, kslice, nseg;
 };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -53,51 +53,37 @@ __device__ __forceinline__ float hi16(uint32_t u) { return bf16_to_f32(u >> 16);
 // x SiLU(x)-gated: silu(g) * u, silu(g) = g / (1 + e^-g).
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
-// grid (ceil(N/64), ceil(M/64), nsplit), block 256.
+// grid (ceil(N/64), ceil(M/64), nsplit), block 256; blockIdx.z > 0 only for kPartial.
 template <int EPI>
 __global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB>::kBytes];
-    __shared__ int is_last;
     static_assert(MfmaTile<kKC, kNB>::kBytes >= kMBL * kZs * 4, "the result tile must fit");
     const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
-    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
     const int k0 = s * a.kslice;
     const int klen = min(a.kslice, a.K - k0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     float* zt = (float*)smem;  // [64][kZs], reuses the operand tiles
-    f32x4 r[4];
     mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, [&](const f32x4 (&acc)[4]) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) r[mt] = acc[mt];
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
     });
-    if (a.nsplit > 1) {
-        // Partial tiles keep the MFMA register layout: thread t's 16 values are floats
-        // 16t..16t+15 of its split's 64 x 64 block, so both the store and the read-back
-        // are four 16-byte accesses per thread.  Publish, count the arrival; the last of
-        // the nsplit workgroups of this tile adds all partials in split order.
-        f32x4* part = (f32x4*)(a.part + (size_t)tile * a.nsplit * (kMBL * kNB)) + 4 * threadIdx.x;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) part[(size_t)s * (kMBL * kNB / 4) + mt] = r[mt];
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) is_last = atomicAdd(a.count + tile, 1u) == (unsigned)(a.nsplit - 1);
-        __syncthreads();
-        if (!is_last) return;
-        __threadfence();
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) r[mt] = part[mt];
-        for (int q = 1; q < a.nsplit; ++q) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) r[mt] += part[(size_t)q * (kMBL * kNB / 4) + mt];
-        }
-        if (threadIdx.x == 0) a.count[tile] = 0u;
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = r[mt][e];
     __syncthreads();
+
+    if constexpr (EPI == kPartial) {
+        // four consecutive columns per item, 16-byte stores
+        float* ps = a.part + (size_t)s * a.M * a.N;
+        for (int it = threadIdx.x; it < kMBL * (kNB / 4); it += kThreads) {
+            const int row = it >> 4, c0 = 4 * (it & 15);
+            const int m = m0 + row, n = n0 + c0;
+            if (m >= a.M || n >= a.N) continue;
+            const float* zr = zt + row * kZs + c0;
+            *(float4*)(ps + (size_t)m * a.N + n) = make_float4(zr[0], zr[1], zr[2], zr[3]);
+        }
+        return;
+    }
 
     if constexpr (EPI == kSwiglu) {
         // Weight rows 32j..32j+15 are gate rows 16j.., rows 32j+16..32j+31 the matching up
@@ -143,14 +129,35 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
     }
 }
 
-// One workgroup per row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint4* __restrict__ x, const uint4* __restrict__ g,
+// One workgroup per row.  With nparts > 0 the row first becomes
+// x + part[0] + ... + part[nparts-1] (fp32, in that order), rounded once to bf16 and
+// written back; the norm is taken of the stored row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(uint4* __restrict__ x, const float4* __restrict__ part,
+                                                      int nparts, long part_stride, const uint4* __restrict__ g,
                                                       int nvec, float inv_d, float eps, uint4* __restrict__ y) {
     __shared__ float red[4];
-    const uint4* xr = x + (size_t)blockIdx.x * nvec;
+    uint4* xr = x + (size_t)blockIdx.x * nvec;
     float ss = 0.f;
     for (int i = threadIdx.x; i < nvec; i += 256) {
-        const uint4 q = xr[i];
+        uint4 q = xr[i];
+        if (nparts > 0) {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[2 * j] = lo16(w[j]), v[2 * j + 1] = hi16(w[j]);
+            const float4* pr = part + ((size_t)blockIdx.x * nvec + i) * 2;
+            float4 sa = pr[0], sb = pr[1];
+            for (int p = 1; p < nparts; ++p) {
+                const float4 ta = pr[p * part_stride], tb = pr[p * part_stride + 1];
+                sa.x += ta.x, sa.y += ta.y, sa.z += ta.z, sa.w += ta.w;
+                sb.x += tb.x, sb.y += tb.y, sb.z += tb.z, sb.w += tb.w;
+            }
+            q.x = pack2(v[0] + sa.x, v[1] + sa.y);
+            q.y = pack2(v[2] + sa.z, v[3] + sa.w);
+            q.z = pack2(v[4] + sb.x, v[5] + sb.y);
+            q.w = pack2(v[6] + sb.z, v[7] + sb.w);
+            xr[i] = q;
+        }
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -183,58 +190,42 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
 }
 
-// Workspace: a fixed block of per-tile arrival counters, then the fp32 partial tiles.
-// The counter block does not depend on the call's shape, so calls of different shapes
-// can share one workspace: no call's partials ever land on another call's counters.
-constexpr int kMaxSplitTiles = 16384;
-constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * 4;
+int kslice_for(int K, int nsplit) {
+    int ks = (K + nsplit - 1) / nsplit;
+    return (ks + 31) / 32 * 32;
+}
 
-struct LinPlan {
-    int tiles_n, tiles_m, nsplit, kslice;
-    size_t ws_bytes;
-};
+mdt_status check_linear(int M, int N, int K, const void* x, const void* W, const void* y) {
+    MDT_REQUIRE(M >= 1 && N >= 1 && K >= 1, MDT_ERR_SHAPE, "bad shape M=%d N=%d K=%d", M, N, K);
+    MDT_REQUIRE((M + kMBL - 1) / kMBL <= 65535, MDT_ERR_SHAPE, "M=%d too large", M);
+    MDT_REQUIRE(K % 32 == 0 && N % 8 == 0, MDT_ERR_SHAPE, "K=%d must be a multiple of 32 and N=%d of 8", K, N);
+    MDT_REQUIRE(x && W && y, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(W) && mdt_aligned16(y), MDT_ERR_ALIGN,
+                "tensor pointers must be 16-byte aligned");
+    return MDT_OK;
+}
 
-// Split the inner dimension only while the tile count stays within two workgroups per
-// compute unit (the occupancy the 66 KiB of LDS per workgroup allows), and keep every
-// slice at least 512 long.
-LinPlan plan_linear(int M, int N, int K, int split) {
-    LinPlan p;
-    p.tiles_n = (N + kNB - 1) / kNB;
-    p.tiles_m = (M + kMBL - 1) / kMBL;
-    const long tiles = (long)p.tiles_n * p.tiles_m;
-    int s = split;
-    if (s <= 0) {
-        const long slots = 2L * mdt_num_cus();
-        s = 1;
-        while (tiles * (s + 1) <= slots && K / (s + 1) >= 512) ++s;
-    }
-    s = (s < 1 || tiles > kMaxSplitTiles) ? 1 : s;
-    int ks = (K + s - 1) / s;
-    ks = (ks + 31) / 32 * 32;
-    p.kslice = ks;
-    p.nsplit = (K + ks - 1) / ks;
-    p.ws_bytes = p.nsplit > 1 ? kCounterBytes + (size_t)tiles * p.nsplit * kMBL * kNB * 4 : 0;
-    return p;
+mdt_status launch_rmsnorm(void* stream, int M, int d, void* x, const float* part, int nparts, const void* g,
+                          float eps, void* y) {
+    MDT_REQUIRE(M >= 1 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE, "bad shape M=%d d=%d (d a multiple of 8)", M, d);
+    MDT_REQUIRE(eps >= 0.f, MDT_ERR_VALUE, "eps must be >= 0");
+    MDT_REQUIRE(nparts >= 0 && nparts <= 64, MDT_ERR_VALUE, "nparts=%d out of range 0..64", nparts);
+    MDT_REQUIRE(x && g && y && (nparts == 0 || part), MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(g) && mdt_aligned16(y) && mdt_aligned16(part), MDT_ERR_ALIGN,
+                "tensor pointers must be 16-byte aligned");
+    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, (uint4*)x,
+               (const float4*)part, nparts, (long)M * d / 4, (const uint4*)g, d / 8, 1.f / (float)d, eps, (uint4*)y);
+    return mdt_launched("rmsnorm_kernel");
 }
 
 }  // namespace
 
-extern "C" size_t mdt_linear_workspace(int M, int N, int K, int split) {
-    if (M < 1 || N < 1 || K < 1) return 0;
-    return plan_linear(M, N, K, split).ws_bytes;
-}
-
 extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* x, const void* W,
-                                 const void* residual, int nseg, int act, void* y, int split, void* ws,
-                                 size_t ws_bytes) {
-    MDT_REQUIRE(M >= 1 && N >= 1 && K >= 1, MDT_ERR_SHAPE, "bad shape M=%d N=%d K=%d", M, N, K);
-    MDT_REQUIRE((M + kMBL - 1) / kMBL <= 65535, MDT_ERR_SHAPE, "M=%d too large", M);
-    MDT_REQUIRE(K % 32 == 0 && N % 8 == 0, MDT_ERR_SHAPE, "K=%d must be a multiple of 32 and N=%d of 8", K, N);
+                                 const void* residual, int nseg, int act, void* y) {
+    mdt_status st = check_linear(M, N, K, x, W, y);
+    if (st != MDT_OK) return st;
     MDT_REQUIRE(act == MDT_ACT_NONE || act == MDT_ACT_SWIGLU, MDT_ERR_VALUE, "unknown activation %d", act);
-    MDT_REQUIRE(split >= 0 && split <= 64, MDT_ERR_VALUE, "split=%d out of range 0..64", split);
-    MDT_REQUIRE(x && W && y, MDT_ERR_NULL, "a tensor pointer is NULL");
-    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(W) && mdt_aligned16(y) && mdt_aligned16(residual),
-                MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    MDT_REQUIRE(mdt_aligned16(residual), MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     if (act == MDT_ACT_SWIGLU) {
         MDT_REQUIRE(N % 32 == 0, MDT_ERR_SHAPE, "SwiGLU needs N=%d to be a multiple of 32", N);
         MDT_REQUIRE(!residual && nseg == 1, MDT_ERR_VALUE, "SwiGLU takes no residual and one segment");
@@ -243,13 +234,8 @@ extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* 
                     "nseg=%d must split N=%d into multiples of 8", nseg, N);
         MDT_REQUIRE(!residual || nseg == 1, MDT_ERR_VALUE, "a residual needs nseg == 1");
     }
-    const LinPlan p = plan_linear(M, N, K, split);
-    MDT_REQUIRE(p.ws_bytes == 0 || (ws && ws_bytes >= p.ws_bytes && mdt_aligned16(ws)), MDT_ERR_WORKSPACE,
-                "workspace needs %zu bytes", p.ws_bytes);
-    LinArgs a{(const bf16_t*)x, (const bf16_t*)W, (const bf16_t*)residual, (bf16_t*)y,
-              p.nsplit > 1 ? (float*)((char*)ws + kCounterBytes) : nullptr, (unsigned*)ws,
-              M, N, K, p.kslice, p.nsplit, nseg};
-    const dim3 grid(p.tiles_n, p.tiles_m, p.nsplit);
+    LinArgs a{(const bf16_t*)x, (const bf16_t*)W, (const bf16_t*)residual, (bf16_t*)y, nullptr, M, N, K, K, nseg};
+    const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, 1);
     if (act == MDT_ACT_SWIGLU) {
         MDT_LAUNCH("linear_mfma", linear_mfma<kSwiglu>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
     } else if (residual) {
@@ -260,20 +246,35 @@ extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* 
     return mdt_launched("linear_mfma");
 }
 
+extern "C" mdt_status mdt_linear_split(void* stream, int M, int N, int K, const void* x, const void* W, int nsplit,
+                                       float* part) {
+    mdt_status st = check_linear(M, N, K, x, W, part);
+    if (st != MDT_OK) return st;
+    MDT_REQUIRE(nsplit >= 1 && nsplit <= 64 && nsplit * 32 <= K, MDT_ERR_VALUE,
+                "nsplit=%d out of range 1..min(64, K/32)", nsplit);
+    const int ks = kslice_for(K, nsplit);
+    MDT_REQUIRE((K + ks - 1) / ks == nsplit, MDT_ERR_VALUE, "K=%d cannot be cut into %d slices of 32-multiples", K,
+                nsplit);
+    LinArgs a{(const bf16_t*)x, (const bf16_t*)W, nullptr, nullptr, part, M, N, K, ks, 1};
+    const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, nsplit);
+    MDT_LAUNCH("linear_mfma", linear_mfma<kPartial>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    return mdt_launched("linear_mfma");
+}
+
 extern "C" mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g, float eps, void* y) {
-    MDT_REQUIRE(M >= 1 && M <= 2147483647 / 2 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE,
-                "bad shape M=%d d=%d (d a multiple of 8)", M, d);
-    MDT_REQUIRE(eps >= 0.f, MDT_ERR_VALUE, "eps must be >= 0");
-    MDT_REQUIRE(x && g && y, MDT_ERR_NULL, "a tensor pointer is NULL");
-    MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(g) && mdt_aligned16(y), MDT_ERR_ALIGN,
-                "tensor pointers must be 16-byte aligned");
-    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, (const uint4*)x,
-               (const uint4*)g, d / 8, 1.f / (float)d, eps, (uint4*)y);
-    return mdt_launched("rmsnorm_kernel");
+    return launch_rmsnorm(stream, M, d, (void*)x, nullptr, 0, g, eps, y);
+}
+
+extern "C" mdt_status mdt_add_rmsnorm(void* stream, int M, int d, int nparts, const float* part, void* x,
+                                      const void* g, float eps, void* y) {
+    MDT_REQUIRE(nparts >= 1, MDT_ERR_VALUE, "nparts=%d must be >= 1", nparts);
+    MDT_REQUIRE(!part || (part + (size_t)nparts * M * d <= (const float*)x || (const float*)x + (size_t)M * d / 2 <= part),
+                MDT_ERR_VALUE, "part must not overlap x");
+    return launch_rmsnorm(stream, M, d, x, part, nparts, g, eps, y);
 }
 
 extern "C" mdt_status mdt_embed(void* stream, int M, int d, int V, const int32_t* tokens, const void* E, void* y) {
-    MDT_REQUIRE(M >= 1 && M <= 2147483647 / 2 && V >= 1 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE,
+    MDT_REQUIRE(M >= 1 && V >= 1 && d >= 8 && d % 8 == 0, MDT_ERR_SHAPE,
                 "bad shape M=%d d=%d V=%d (d a multiple of 8)", M, d, V);
     MDT_REQUIRE(tokens && E && y, MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_REQUIRE(mdt_aligned16(E) && mdt_aligned16(y), MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");

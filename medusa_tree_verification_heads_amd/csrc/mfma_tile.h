@@ -71,11 +71,11 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) wr[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
     };
-    auto load_x = [&](int c) {
+    auto load_x = [&](int c, u32x4 (&xb)[kXPT]) {
 #pragma unroll
-        for (int j = 0; j < kXPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
+        for (int j = 0; j < kXPT; ++j) xb[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
     };
-    auto store = [&](int c, const u32x4 (&wr)[kPPT]) {
+    auto store = [&](int c, const u32x4 (&wr)[kPPT], const u32x4 (&xb)[kXPT]) {
         const u32x4 z{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) {
@@ -85,7 +85,7 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
 #pragma unroll
         for (int j = 0; j < kXPT; ++j) {
             const int p = threadIdx.x + NT * j;
-            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
+            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xb[j] : z;
         }
     };
 
@@ -108,25 +108,26 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
         }
     };
     load_w(0, wA);
-    load_x(0);
+    load_x(0, xr);
     load_w(1, wB);
-    store(0, wA);
+    store(0, wA, xr);
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
         // LDS: chunk c; wB: chunk c+1
-        load_x(c + 1);
+        load_x(c + 1, xr);
         load_w(c + 2, wA);
         compute(c);
         __syncthreads();
-        store(c + 1, wB);
+        store(c + 1, wB, xr);
         __syncthreads();
         // LDS: chunk c+1; wA: chunk c+2
-        load_x(c + 2);
+        load_x(c + 2, xr);
         load_w(c + 3, wB);
         compute(c + 1);
         __syncthreads();
-        store(c + 2, wA);
+        store(c + 2, wA, xr);
         __syncthreads();
     }
     epi(acc);
 }
+

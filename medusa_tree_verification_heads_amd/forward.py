@@ -7,9 +7,16 @@ the LM head.  ``VerifyForward.run()`` enqueues, on one stream and with no host
 synchronisation:
 
     medusa_heads -> topk_tree_expand -> embed
-    -> per layer: rmsnorm -> linear (q|k|v) -> tree_attention -> linear (+x)
-                  -> rmsnorm -> linear (SwiGLU) -> linear (+x)
-    -> rmsnorm -> verify_logits -> accept_path -> kv_compact_layers
+    -> rmsnorm -> per layer: linear (q|k|v) -> tree_attention
+                             -> linear_split (o Wo^T) -> add_rmsnorm (x += ., h = norm)
+                             -> linear (SwiGLU) -> linear_split (a Wd^T)
+                             -> add_rmsnorm (x += ., h = next layer's norm, or the final one)
+    -> verify_logits -> accept_path -> kv_compact_layers
+
+The output and down projections have only d output columns (64 tiles of 64 at 7B), so
+their inner dimension is cut into slices (linear_split) whose fp32 products the
+following add_rmsnorm sums into the residual stream; with one slice they are a plain
+linear with the residual in its epilogue followed by rmsnorm.
 
 Every layer has its own prefix cache (one allocation [layers][B][capacity][H][Dh]);
 every layer's tree keys/values are kept until acceptance, then the accepted path is
@@ -23,10 +30,10 @@ from typing import List
 import numpy as np
 import torch
 
-from . import (ACT_SWIGLU, GREEDY, TYPICAL, KVCache, Tree, accept_path, embed, interleave_gate_up,
-               kv_compact_layers, linear, linear_workspace, medusa_heads, medusa_heads_workspace, new_workspace,
-               rmsnorm, topk_tree_expand, topk_workspace, tree_attention, tree_attention_workspace, verify_logits,
-               verify_logits_workspace, MDT_BF16)
+from . import (ACT_SWIGLU, GREEDY, TYPICAL, KVCache, Tree, accept_path, add_rmsnorm, auto_split, embed,
+               interleave_gate_up, kv_compact_layers, linear, linear_split, medusa_heads, medusa_heads_workspace,
+               new_workspace, rmsnorm, topk_tree_expand, topk_workspace, tree_attention, tree_attention_workspace,
+               verify_logits, verify_logits_workspace, MDT_BF16)
 from .step import to_device
 
 LAYER_KEYS = ("g_attn", "Wqkv", "Wo", "g_mlp", "Wgu", "Wd")
@@ -46,7 +53,7 @@ class VerifyForward:
     of every layer, [n_layers][B][capacity][H][Dh]; ``prefix_len``: device int32 [B]."""
 
     def __init__(self, dw, base: dict, E, g_final, layers: List[dict], Kc, Vc, prefix_len, mode="greedy",
-                 temperature=0.0, eps=0.09, delta=0.3, tree: Tree = None, split: int = 0):
+                 temperature=0.0, eps=0.09, delta=0.3, tree: Tree = None, splits=None):
         w = dw.base
         assert w.dtype == "bf16" and not w.paged, "the full forward runs on bf16 contiguous caches"
         self.dw, self.w = dw, w
@@ -54,7 +61,6 @@ class VerifyForward:
         self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
         self.base, self.E, self.g_final, self.layers = base, E, g_final, layers
         self.Kc, self.Vc, self.prefix_len = Kc, Vc, prefix_len
-        self.split = split
         dev = E.device
         self.dev = dev
         nL = len(layers)
@@ -88,11 +94,9 @@ class VerifyForward:
         self.ws_attn = new_workspace(tree_attention_workspace(MDT_BF16, B, T, H, Dh, self.caches[0].desc.capacity),
                                      dev) if nL else None
         self.ws_verify = new_workspace(verify_logits_workspace(MDT_BF16, B, T, d, V), dev)
-        # one linear workspace for all products: they run one after another on one stream
-        # and each leaves its arrival counters at zero
-        need = max(linear_workspace(M, 3 * d, d, split), linear_workspace(M, d, d, split),
-                   linear_workspace(M, 2 * F, d, split), linear_workspace(M, d, F, split))
-        self.ws_lin = new_workspace(need, dev)
+        # slices of the output (o Wo^T) and down (a Wd^T) projections
+        self.split_o, self.split_d = splits or (auto_split(M, d, d, dev), auto_split(M, d, F, dev))
+        self.part = torch.empty((max(self.split_o, self.split_d), M, d), **f32)
 
     @classmethod
     def from_numpy(cls, dw, inp: dict, fin: dict, layers_np: List[dict], device="cuda", **kw):
@@ -104,23 +108,34 @@ class VerifyForward:
         lens = torch.from_numpy(inp["prefix_len"].astype(np.int32)).to(dev)
         return cls(dw, base, to_device(fin["E"], dev), to_device(fin["g_final"], dev), layers, Kc, Vc, lens, **kw)
 
+    def _close(self, a, W, nsplit, g, out, stream):
+        """x += a W^T, then out = rmsnorm(x) * g."""
+        eps = self.dw.norm_eps
+        if nsplit > 1:
+            part = self.part[:nsplit]
+            linear_split(a, W, nsplit, out=part, stream=stream)
+            add_rmsnorm(part, self.x, g, eps, out=out, stream=stream)
+        else:
+            linear(a, W, residual=self.x, out=self.x, stream=stream)
+            rmsnorm(self.x, g, eps, out=out, stream=stream)
+
     def layer(self, l: int, stream=None):
-        """Enqueue decoder layer l on the residual stream self.x (updated in place)."""
+        """Enqueue decoder layer l: self.h holds rmsnorm(x) * g_attn of this layer on entry;
+        on exit self.x is the new residual stream and self.h (or, after the last layer,
+        self.xf) its norm for what follows."""
         w, lw = self.w, self.layers[l]
         B, T, H, Dh = w.B, self.tree.T, w.H, w.Dh
-        eps = self.dw.norm_eps
-        ws = self.ws_lin
-        rmsnorm(self.x, lw["g_attn"], eps, out=self.h, stream=stream)
         qkv = self.qkv[l]
-        linear(self.h, lw["Wqkv"], nseg=3, out=qkv, split=self.split, ws=ws, stream=stream)
+        linear(self.h, lw["Wqkv"], nseg=3, out=qkv, stream=stream)
         shp = (B, T, H, Dh)
         tree_attention(qkv[0].view(shp), qkv[1].view(shp), qkv[2].view(shp), self.caches[l], self.prefix_len,
                        self.tree, w.rope_theta, out=self.o.view(shp), k_rot=self.k_rot[l], ws=self.ws_attn,
                        stream=stream)
-        linear(self.o, lw["Wo"], residual=self.x, out=self.x, split=self.split, ws=ws, stream=stream)
-        rmsnorm(self.x, lw["g_mlp"], eps, out=self.h, stream=stream)
-        linear(self.h, lw["Wgu"], act=ACT_SWIGLU, out=self.a, split=self.split, ws=ws, stream=stream)
-        linear(self.a, lw["Wd"], residual=self.x, out=self.x, split=self.split, ws=ws, stream=stream)
+        self._close(self.o, lw["Wo"], self.split_o, lw["g_mlp"], self.h, stream)
+        linear(self.h, lw["Wgu"], act=ACT_SWIGLU, out=self.a, stream=stream)
+        last = l + 1 == len(self.layers)
+        self._close(self.a, lw["Wd"], self.split_d, self.g_final if last else self.layers[l + 1]["g_attn"],
+                    self.xf if last else self.h, stream)
 
     def run(self, stream=None):
         w, t = self.w, self.base
@@ -128,9 +143,10 @@ class VerifyForward:
         topk_tree_expand(self.logits, w.k_cfg, self.tree, self.prefix_len, self.topk_idx, self.topk_val,
                          self.tokens, self.pos, ws=self.ws_topk, stream=stream)
         embed(self.tokens.view(-1), self.E, out=self.x, stream=stream)
+        g0 = self.layers[0]["g_attn"] if self.layers else self.g_final
+        rmsnorm(self.x, g0, self.dw.norm_eps, out=self.h if self.layers else self.xf, stream=stream)
         for l in range(len(self.layers)):
             self.layer(l, stream)
-        rmsnorm(self.x, self.g_final, self.dw.norm_eps, out=self.xf, stream=stream)
         verify_logits(self.xf, t["Wlm"], self.tree, self.tokens, self.temperature, stats=self.stats,
                       edge=self.edge, ws=self.ws_verify, stream=stream)
         accept_path(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta,

@@ -1,9 +1,9 @@
 """GPU parity of the full verify forward and of its layer calls against the oracle.
 
-Layer calls (embed, rmsnorm, linear in its three forms, with and without a split
-inner dimension): each output element within one bf16 unit of the float64 oracle
-(both round once; they can differ only where the fp32 and fp64 sums straddle a
-rounding boundary), at shapes with ragged row/column tails.
+Layer calls (embed, rmsnorm, linear in its three forms, the split product and its
+closing add_rmsnorm): each output element within one bf16 unit of the float64 oracle
+plus the fp32 arithmetic's own error bound (both round once; they can differ only
+where the two sums straddle a rounding boundary), at shapes with ragged tails.
 
 The forward (two layers: the 7B mini and full 7B width): tree tokens, path, n_acc
 and new lengths bit-exact (every decision's oracle margin is checked to exceed twice
@@ -74,47 +74,51 @@ LIN_SHAPES = [(64, 192, 256), (37, 200, 320), (130, 96, 1376), (64, 512, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", LIN_SHAPES)
-@pytest.mark.parametrize("split", [1, 0, 5])
-def test_linear_plain_and_residual(M, N, K, split):
+def test_linear_plain_and_residual(M, N, K):
     import medusa_tree_verification_heads_amd as mdt
-    note(f"linear M={M} N={N} K={K} split={split}")
-    rng = np.random.default_rng(M * 1000 + N + K + split)
+    note(f"linear M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 1000 + N + K)
     x = _rand_bf16(rng, (M, K))
     W = _rand_bf16(rng, (N, K), K ** -0.5)
     r = _rand_bf16(rng, (M, N))
     xd, Wd, rd = _dev(_to_bits(x)), _dev(_to_bits(W)), _dev(_to_bits(r))
-    ws = mdt.new_workspace(mdt.linear_workspace(M, N, K, split), "cuda")
-    y = mdt.linear(xd, Wd, split=split, ws=ws)
+    y = mdt.linear(xd, Wd)
     bound = _dot_err(x, W, K)
     assert _bad(_bits(y), ofw.linear(x, _to_bits(W)), bound) == 0
     # in place on the residual
-    mdt.linear(xd, Wd, residual=rd, out=rd, split=split, ws=ws)
+    mdt.linear(xd, Wd, residual=rd, out=rd)
     assert _bad(_bits(rd), ofw.linear(x, _to_bits(W), r), bound) == 0
-    # the arrival counters are back at zero; a repeat is bit-identical
-    y2 = mdt.linear(xd, Wd, split=split, ws=ws)
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    assert int(ws[:65536].count_nonzero()) == 0
 
 
-def test_linear_shared_workspace_across_shapes():
-    """A workspace shared by split products of different tile counts (a wide one, then a
-    narrow one whose partials would start right after a shape-sized counter block, then
-    the wide one again) gives the same results as separate workspaces."""
+@pytest.mark.parametrize("M,N,K,nsplit", [(64, 512, 4096, 8), (37, 200, 1376, 2), (130, 96, 1024, 3),
+                                          (64, 4096, 11008, 8)])
+def test_linear_split_and_add_rmsnorm(M, N, K, nsplit):
+    """The slices' fp32 products add up to the product (each within the fp32 dot-product
+    bound), and add_rmsnorm closes them into the residual and normalises the new row."""
     import medusa_tree_verification_heads_amd as mdt
-    rng = np.random.default_rng(99)
-    K = 2048
-    x = _dev(_to_bits(_rand_bf16(rng, (64, K))))
-    Wa = _dev(_to_bits(_rand_bf16(rng, (64 * 96, K), K ** -0.5)))
-    Wb = _dev(_to_bits(_rand_bf16(rng, (64 * 8, K), K ** -0.5)))
-    need = max(mdt.linear_workspace(64, Wa.shape[0], K, 4), mdt.linear_workspace(64, Wb.shape[0], K, 4))
-    ws = mdt.new_workspace(need, "cuda")
-    ya1 = mdt.linear(x, Wa, split=4, ws=ws)
-    yb = mdt.linear(x, Wb, split=4, ws=ws)
-    ya2 = mdt.linear(x, Wa, split=4, ws=ws)
-    yb_alone = mdt.linear(x, Wb, split=4)
-    assert torch.equal(ya1.view(torch.int16), ya2.view(torch.int16))
-    assert torch.equal(yb.view(torch.int16), yb_alone.view(torch.int16))
-    assert int(ws[:65536].count_nonzero()) == 0
+    note(f"linear_split M={M} N={N} K={K} nsplit={nsplit}")
+    rng = np.random.default_rng(N + K + nsplit)
+    x = _rand_bf16(rng, (M, K))
+    W = _rand_bf16(rng, (N, K), K ** -0.5)
+    r = _rand_bf16(rng, (M, N))
+    g = ostep.round_bf16(1 + 0.1 * rng.standard_normal(N))
+    part = mdt.linear_split(_dev(_to_bits(x)), _dev(_to_bits(W)), nsplit)
+    ks = -(-(-(-K // nsplit)) // 32) * 32
+    bound = _dot_err(x, W, K)
+    p = part.cpu().numpy().astype(np.float64)
+    for s_ in range(nsplit):
+        sl = slice(s_ * ks, min(K, (s_ + 1) * ks))
+        assert np.all(np.abs(p[s_] - x[:, sl] @ W[:, sl].T) <= bound + 1e-30)
+    xr = _dev(_to_bits(r))
+    h = mdt.add_rmsnorm(part, xr, _dev(_to_bits(g)), 1e-6)
+    x_new = ofw.linear(x, _to_bits(W), r)
+    assert _bad(_bits(xr), x_new, bound) == 0
+    # the norm is of the row as stored: where an element of x was rounded one unit apart
+    # from the oracle's, the normalised element moves by that difference times r * g
+    ref_h = ofw.rmsnorm(x_new, g, 1e-6)
+    dx = np.abs(ostep.to_f64(_bits(xr)) - x_new)
+    rr = 1.0 / np.sqrt(np.mean(x_new * x_new, axis=1, keepdims=True) + 1e-6)
+    assert _bad(_bits(h), ref_h, (N + 8) * 2.0 ** -24 * np.abs(ref_h) + 1.01 * dx * rr * np.abs(g)) == 0
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 3 * 192, 256), (37, 3 * 512, 512)])
@@ -133,16 +137,15 @@ def test_linear_segments(M, N, K):
 
 
 @pytest.mark.parametrize("M,F,K", [(64, 1376, 512), (37, 48, 256), (64, 11008 // 4, 4096)])
-@pytest.mark.parametrize("split", [1, 0])
-def test_linear_swiglu(M, F, K, split):
+def test_linear_swiglu(M, F, K):
     import medusa_tree_verification_heads_amd as mdt
-    note(f"swiglu M={M} F={F} K={K} split={split}")
+    note(f"swiglu M={M} F={F} K={K}")
     rng = np.random.default_rng(F + K + M)
     h = _rand_bf16(rng, (M, K))
     Wg = _rand_bf16(rng, (F, K), K ** -0.5)
     Wu = _rand_bf16(rng, (F, K), K ** -0.5)
     W = mdt.interleave_gate_up(_dev(_to_bits(Wg)), _dev(_to_bits(Wu)))
-    a = mdt.linear(_dev(_to_bits(h)), W, act=mdt.ACT_SWIGLU, split=split)
+    a = mdt.linear(_dev(_to_bits(h)), W, act=mdt.ACT_SWIGLU)
     zg, zu = h @ Wg.T, h @ Wu.T
     ref = ostep.round_bf16(ofw.swiglu(zg, zu))
     # first-order propagation of the dot-product bounds through silu(g) * u
