@@ -131,3 +131,4 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
     epi(acc);
 }
 
+
