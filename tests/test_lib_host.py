@@ -186,3 +186,47 @@ def test_next_state_and_rejection_validation():
     assert rej(K=3) == -5                                       # tree deeper than K
     assert rej(stride=4) == -2 and rej(stride=1100) == -2
     assert rej(vl=None) == -1
+
+
+def test_layer_calls_validation():
+    """Argument errors of the decoder-layer calls come back before anything is launched."""
+    L = mdt.lib
+    lin = lambda M=64, N=4096, K=4096, x=P, W=P, res=None, nseg=1, act=0, y=P: \
+        L.mdt_linear(None, M, N, K, x, W, res, nseg, act, y)
+    assert lin(K=4008) == -2                      # K not a multiple of 32
+    assert lin(N=4095) == -2                      # N not a multiple of 8
+    assert lin(M=0) == -2
+    assert lin(act=2) == -6                       # unknown activation
+    assert lin(x=None) == -1
+    assert lin(W=MIS) == -4
+    assert lin(act=1, N=4112) == -2               # SwiGLU needs N % 32 == 0
+    assert lin(act=1, res=P) == -6                # SwiGLU takes no residual
+    assert lin(nseg=3, N=4096) == -2              # segments must divide N into multiples of 8
+    assert lin(nseg=2, res=P) == -6               # residual needs one segment
+    sp = lambda K=4096, n=8, x=P, part=P: L.mdt_linear_split(None, 64, 4096, K, x, P, n, part)
+    assert sp(n=0) == -6 and sp(n=65) == -6
+    assert sp(K=64, n=3) == -6                    # more slices than 32-wide k-steps
+    assert sp(K=4096, n=33) == -6                 # rounding to 32-multiples leaves 32 slices
+    assert sp(part=None) == -1
+    rn = L.mdt_rmsnorm
+    assert rn(None, 64, 4100, P, P, 1e-6, P) == -2
+    assert rn(None, 64, 4096, P, P, -1.0, P) == -6
+    assert rn(None, 64, 4096, None, P, 1e-6, P) == -1
+    arn = L.mdt_add_rmsnorm
+    assert arn(None, 64, 4096, 0, P, P, P, 1e-6, P) == -6   # at least one slice
+    assert arn(None, 64, 4096, 2, P, P, P, 1e-6, P) == -6   # slices overlapping x
+    em = L.mdt_embed
+    assert em(None, 64, 4096, 0, P, P, P) == -2
+    assert em(None, 64, 4096, 32000, None, P, P) == -1
+    assert em(None, 64, 4096, 32000, P, MIS, P) == -4
+
+
+def test_compact_layers_validation():
+    c = mdt.KVCacheDesc()
+    c.layout, c.capacity, c.k, c.v = 0, 1029, 1 << 20, 1 << 20
+    f = lambda n=2, ks=64 * 4096, vs=64 * 4096, cs=1029 * 4096: mdt.lib.mdt_kv_compact_layers(
+        None, 1, n, 1, 64, 32, 128, P, 5, P, P, ks, P, vs, ctypes.byref(c), cs, P, P)
+    assert f(n=0) == -2
+    assert f(ks=64 * 4096 - 8) == -2              # stride smaller than one layer
+    assert f(cs=1029 * 4096 - 8) == -2
+    assert f(vs=-8) == -4 and f(ks=3) == -4       # negative or not a 16-byte multiple
