@@ -13,11 +13,14 @@
 //
 // Launch 1 streams W1 (-> a_k = SiLU(u) + h, fp32 in the workspace) together with
 // W_lm (-> logits_0), which only needs h; launch 2 streams W2 (-> logits_1..K).
+// Batches of 4 or more bf16 sequences take the matrix-core path instead
+// (heads_mfma.hip), where each weight byte serves every sequence.
 // Rows of all heads of a launch form one grid; a workgroup owns a contiguous row
 // block of one head.
 #include <type_traits>
 
 #include "common.h"
+#include "heads_mfma.h"
 
 namespace {
 
@@ -339,6 +342,7 @@ extern "C" mdt_status mdt_medusa_heads(void* stream, mdt_dtype dt, int B, int d,
                 ws_bytes, mdt_medusa_heads_workspace(B, d, K));
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
+    if (dt == MDT_BF16 && mdt_heads_mfma_applies(B, d)) return mdt_heads_mfma(s, B, d, V, K, h, W1, W2, Wlm, logits, ws);
     if (dt == MDT_BF16) return run<bf16_t>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
     return run<float>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
 }

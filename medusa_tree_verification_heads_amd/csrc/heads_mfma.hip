@@ -1,0 +1,121 @@
+// The heads of a batch of sequences on the matrix cores (bf16, B >= 4).
+//
+// Same arithmetic as the GEMV path of mdt_medusa_heads (summary page, "MEDUSA Heads":
+// logits_k = W2_k (SiLU(W1_k h) + h), the LM head logits_0 = W_lm h), but every weight
+// byte now serves B sequences: a GEMV that keeps up to 8 activation vectors in LDS
+// re-streams the weights once per 8 sequences and spends B multiply-adds per weight
+// element on the vector ALUs, while the 64 x 64 MFMA tile (mfma_tile.h) reads each
+// weight row once for all B rows of h.
+//
+// Launch 1 streams the rows of W1_0..W1_{K-1} (stacked, K*d rows) and of W_lm: the W1
+// epilogue forms a = SiLU(u) + h in fp32 and stores it as two bf16 rows, a_hi = bf16(a)
+// and a_lo = bf16(a - a_hi), so that launch 2 can multiply a with bf16 operands and
+// still keep about 16 significant bits of a (a_hi + a_lo); the W_lm epilogue writes
+// logits_0.  Launch 2 streams W2_k against the 2B rows [a_hi; a_lo] of head k and adds
+// the two halves of each product in its epilogue.
+#include <math.h>
+
+#include "heads_mfma.h"
+#include "mfma_tile.h"
+
+namespace {
+
+constexpr int kKC = 256;
+constexpr int kNB = 64;
+constexpr int kThreads = 4 * kNB;
+
+struct HeadsArgs {
+    const bf16_t* h;    // [B][d]
+    const bf16_t* W1;   // [K][d][d]
+    const bf16_t* W2;   // [K][V][d]
+    const bf16_t* Wlm;  // [V][d]
+    float* logits;      // [B][K+1][V]
+    bf16_t* ahl;        // [K][2B][d]: rows 0..B-1 a_hi, rows B..2B-1 a_lo
+    int B, d, V, K, w1_tiles;
+};
+
+// grid (K*d/64 + ceil(V/64)): W1 tiles first, then W_lm tiles.
+template <int MT>
+__global__ __launch_bounds__(kThreads) void heads_mfma_w1_lm(HeadsArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB, MT>::kBytes];
+    static_assert(MfmaTile<kKC, kNB, MT>::kBytes >= 16 * MT * (kNB + 1) * 4, "the result tile must fit");
+    const bool w1 = (int)blockIdx.x < a.w1_tiles;
+    const int n0 = (w1 ? blockIdx.x : blockIdx.x - a.w1_tiles) * kNB;
+    const int nrows = w1 ? a.K * a.d : a.V;
+    const bf16_t* W = w1 ? a.W1 : a.Wlm;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    float* zt = (float*)smem;  // [16*MT][kNB + 1]
+    mfma_tile<kKC, kNB, MT>(a.h, W, a.B, a.d, a.d, nrows, 0, n0, smem, [&](const f32x4 (&acc)[MT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (kNB + 1) + wave * 16 + c16] = acc[mt][e];
+    });
+    __syncthreads();
+    for (int it = threadIdx.x; it < a.B * kNB; it += kThreads) {
+        const int b = it / kNB, c = it % kNB;
+        const float u = zt[b * (kNB + 1) + c];
+        if (w1) {
+            const int k = n0 / a.d, j = n0 % a.d + c;  // a 64-row tile lies in one head (d % 64 == 0)
+            const float v = u / (1.f + __expf(-u)) + bf16_to_f32(a.h[(size_t)b * a.d + j]);
+            const bf16_t hi = f32_to_bf16(v);
+            const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+            bf16_t* row = a.ahl + ((size_t)k * 2 * a.B + b) * a.d + j;
+            row[0] = hi;
+            row[(size_t)a.B * a.d] = lo;
+        } else if (n0 + c < a.V) {
+            a.logits[(size_t)b * (a.K + 1) * a.V + n0 + c] = u;
+        }
+    }
+}
+
+// grid (ceil(V/64), K).
+template <int MT>
+__global__ __launch_bounds__(kThreads) void heads_mfma_w2(HeadsArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB, MT>::kBytes];
+    static_assert(MfmaTile<kKC, kNB, MT>::kBytes >= 16 * MT * (kNB + 1) * 4, "the result tile must fit");
+    const int n0 = blockIdx.x * kNB, k = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    float* zt = (float*)smem;
+    const bf16_t* x = a.ahl + (size_t)k * 2 * a.B * a.d;
+    const bf16_t* W = a.W2 + (size_t)k * a.V * a.d;
+    mfma_tile<kKC, kNB, MT>(x, W, 2 * a.B, a.d, a.d, a.V, 0, n0, smem, [&](const f32x4 (&acc)[MT]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (kNB + 1) + wave * 16 + c16] = acc[mt][e];
+    });
+    __syncthreads();
+    for (int it = threadIdx.x; it < a.B * kNB; it += kThreads) {
+        const int b = it / kNB, c = it % kNB;
+        if (n0 + c < a.V)
+            a.logits[((size_t)b * (a.K + 1) + k + 1) * a.V + n0 + c] =
+                zt[b * (kNB + 1) + c] + zt[(a.B + b) * (kNB + 1) + c];
+    }
+}
+
+template <int MT1, int MT2>
+mdt_status launch_pair(const HeadsArgs& a, hipStream_t s) {
+    const int lm_tiles = (a.V + kNB - 1) / kNB;
+    MDT_LAUNCH("heads_mfma_w1_lm", heads_mfma_w1_lm<MT1>, dim3(a.w1_tiles + lm_tiles), dim3(kThreads), 0, s, a);
+    mdt_status st = mdt_launched("heads_mfma_w1_lm");
+    if (st != MDT_OK) return st;
+    MDT_LAUNCH("heads_mfma_w2", heads_mfma_w2<MT2>, dim3(lm_tiles, a.K), dim3(kThreads), 0, s, a);
+    return mdt_launched("heads_mfma_w2");
+}
+
+}  // namespace
+
+bool mdt_heads_mfma_applies(int B, int d) { return B >= kHeadsMfmaMinB && B <= 32 && d % 64 == 0; }
+
+mdt_status mdt_heads_mfma(hipStream_t s, int B, int d, int V, int K, const void* h, const void* W1, const void* W2,
+                          const void* Wlm, float* logits, void* ws) {
+    HeadsArgs a{(const bf16_t*)h, (const bf16_t*)W1, (const bf16_t*)W2, (const bf16_t*)Wlm, logits, (bf16_t*)ws,
+                B, d, V, K, K * d / kNB};
+    // 16-row m-tiles: B rows of h in launch 1, 2B rows of [a_hi; a_lo] in launch 2
+    if (B <= 8) return launch_pair<1, 1>(a, s);
+    if (B <= 16) return launch_pair<1, 2>(a, s);
+    return launch_pair<2, 4>(a, s);
+}

@@ -23,32 +23,34 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 
-template <int KC, int NB>
+template <int KC, int NB, int MT = 4>
 struct MfmaTile {
     static constexpr int NT = 4 * NB;                  // one wave per 16 weight rows
     static constexpr int kStride = KC + 8;             // LDS row stride (elements)
-    static constexpr int kXBytes = 64 * kStride * 2;   // the 64-row x tile
+    static constexpr int kXBytes = 16 * MT * kStride * 2;  // the 16*MT-row x tile
     static constexpr int kWBytes = NB * kStride * 2;   // the NB-row weight tile
     static constexpr int kBytes = kXBytes + kWBytes;
 };
 
 // Multiplies the tile (x rows m0.., weight rows n0..; x is [M][ld], W is [V][ld], the
 // product runs over the first d columns of both) and hands
-// the fp32 accumulators to epi(acc): wave w owns weight rows 16w..16w+15 against all 64
-// x rows, acc[mt] holding x rows 16mt..16mt+15 in the 16x16 MFMA output layout (lane l:
-// column 16w + l%16, rows 16mt + 4(l/16) + e).  `smem` holds MfmaTile<KC, NB>::kBytes
-// bytes; rows of x past M and of W past V read as zero.  d and ld must be multiples of 8.
-template <int KC, int NB, typename Epi>
+// the fp32 accumulators to epi(acc): wave w owns weight rows 16w..16w+15 against all
+// 16*MT x rows, acc[mt] holding x rows 16mt..16mt+15 in the 16x16 MFMA output layout
+// (lane l: column 16w + l%16, rows 16mt + 4(l/16) + e).  `smem` holds
+// MfmaTile<KC, NB, MT>::kBytes bytes; rows of x past M and of W past V read as zero.
+// d must be a multiple of 32 and ld of 8.
+template <int KC, int NB, int MT = 4, typename Epi>
 __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M, int d,
                                           int ld, int V, int m0, int n0, char* smem, Epi&& epi) {
-    constexpr int NT = MfmaTile<KC, NB>::NT;
-    constexpr int kStride = MfmaTile<KC, NB>::kStride;
+    constexpr int NT = MfmaTile<KC, NB, MT>::NT;
+    constexpr int kStride = MfmaTile<KC, NB, MT>::kStride;
     constexpr int kPR = KC / 8;                   // 16-byte pieces per row per chunk
     constexpr int kPPT = NB * kPR / NT;           // weight pieces per thread per chunk
-    constexpr int kXPT = 64 * kPR / NT;           // x pieces per thread per chunk
+    constexpr int kXPT = 16 * MT * kPR / NT;      // x pieces per thread per chunk
     static_assert(KC % 32 == 0, "k-steps of 32");
+    static_assert(16 * MT * kPR % NT == 0, "x pieces must divide among the threads");
     bf16_t* xs = (bf16_t*)smem;
-    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, NB>::kXBytes);
+    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, NB, MT>::kXBytes);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int nchunks = (d + KC - 1) / KC;
@@ -89,9 +91,9 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
         }
     };
 
-    f32x4 acc[4];
+    f32x4 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int c) {
         const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
         const bf16_t* wrow = ws + (wave * 16 + c16) * kStride + 8 * g;
@@ -100,7 +102,7 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
             if (s < nsteps) {
                 const u32x4 b = *(const u32x4*)(wrow + 32 * s);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
+                for (int mt = 0; mt < MT; ++mt) {
                     const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kStride + 32 * s + 8 * g);
                     acc[mt] = mfma16(a, b, acc[mt]);
                 }
