@@ -131,9 +131,12 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
     }
 }
 
-// grid (ceil(V/NB), ceil(M/64)), block 4*NB: the tile of mfma_tile, then the statistics
-// epilogue.
-template <int KC, int NB>
+// grid (ceil(V/NB), ceil(M/(16*MT))), block 4*NB: the tile of mfma_tile (16*MT node rows),
+// then the statistics epilogue.  MT = 4 (64 rows) is used for every M: with 256 rows per
+// workgroup (MT = 16, 128-dim chunks) the batched shapes ran slower (one wave per SIMD
+// at 284 registers), the repeated weight streams being served largely from the
+// last-level cache.
+template <int KC, int NB, int MT = 4>
 __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
                                                       int M, int d, int V, float tau, int nblk_n,
                                                       Part* __restrict__ part, float* __restrict__ logits_opt,
@@ -141,21 +144,22 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
                                                       const int32_t* __restrict__ tokens, int T,
                                                       float* __restrict__ edge) {
     constexpr int NT = 4 * NB;
-    static_assert(MfmaTile<KC, NB>::kBytes >= 64 * (NB + 1) * 4, "the logits tile must fit");
-    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB>::kBytes];
-    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMB;
+    constexpr int MB = 16 * MT;
+    static_assert(MfmaTile<KC, NB, MT>::kBytes >= MB * (NB + 1) * 4, "the logits tile must fit");
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB, MT>::kBytes];
+    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const EdgePre pre = edge_preload<kMB>(m0, M, parent, tokens, T);
-    float* zt = (float*)smem;  // [64][NB + 1], reuses the tiles
-    mfma_tile<KC, NB>(x, W, M, d, d, V, m0, n0, smem, [&](const f32x4 (&acc)[4]) {
+    const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
+    float* zt = (float*)smem;  // [MB][NB + 1], reuses the tiles
+    mfma_tile<KC, NB, MT>(x, W, M, d, d, V, m0, n0, smem, [&](const f32x4 (&acc)[MT]) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (NB + 1) + wave * 16 + c16] = acc[mt][e];
     });
     __syncthreads();
-    tile_epilogue<kMB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
+    tile_epilogue<MB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
 // fp32 path: grid (ceil(V/64), ceil(M/16)), block 256; x rows staged in LDS as fp32.
