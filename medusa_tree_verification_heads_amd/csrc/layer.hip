@@ -129,16 +129,20 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
     }
 }
 
-// One workgroup per row.  With nparts > 0 the row first becomes
-// x + part[0] + ... + part[nparts-1] (fp32, in that order), rounded once to bf16 and
-// written back; the norm is taken of the stored row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(uint4* __restrict__ x, const float4* __restrict__ part,
-                                                      int nparts, long part_stride, const uint4* __restrict__ g,
-                                                      int nvec, float inv_d, float eps, uint4* __restrict__ y) {
-    __shared__ float red[4];
+// One workgroup of kNormThreads per row (a row of d = 4096 is 512 16-byte pieces: one
+// per thread, so every slice load of the row is in flight at once).  With nparts > 0
+// the row first becomes x + part[0] + ... + part[nparts-1] (fp32, in that order),
+// rounded once to bf16 and written back; the norm is taken of the stored row.
+constexpr int kNormThreads = 512;
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint4* __restrict__ x, const float4* __restrict__ part,
+                                                               int nparts, long part_stride,
+                                                               const uint4* __restrict__ g, int nvec, float inv_d,
+                                                               float eps, uint4* __restrict__ y) {
+    __shared__ float red[kNormThreads / 64];
     uint4* xr = x + (size_t)blockIdx.x * nvec;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < nvec; i += 256) {
+    for (int i = threadIdx.x; i < nvec; i += kNormThreads) {
         uint4 q = xr[i];
         if (nparts > 0) {
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -168,9 +172,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(uint4* __restrict__ x, con
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) * inv_d + eps);
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+    const float r = rsqrtf(tot * inv_d + eps);
     uint4* yr = y + (size_t)blockIdx.x * nvec;
-    for (int i = threadIdx.x; i < nvec; i += 256) {
+    for (int i = threadIdx.x; i < nvec; i += kNormThreads) {
         const uint4 q = xr[i], gg = g[i];
         const uint32_t w[4] = {q.x, q.y, q.z, q.w}, gw[4] = {gg.x, gg.y, gg.z, gg.w};
         uint32_t o[4];
@@ -213,7 +220,7 @@ mdt_status launch_rmsnorm(void* stream, int M, int d, void* x, const float* part
     MDT_REQUIRE(x && g && y && (nparts == 0 || part), MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(g) && mdt_aligned16(y) && mdt_aligned16(part), MDT_ERR_ALIGN,
                 "tensor pointers must be 16-byte aligned");
-    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, (uint4*)x,
+    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(kNormThreads), 0, (hipStream_t)stream, (uint4*)x,
                (const float4*)part, nparts, (long)M * d / 4, (const uint4*)g, d / 8, 1.f / (float)d, eps, (uint4*)y);
     return mdt_launched("rmsnorm_kernel");
 }

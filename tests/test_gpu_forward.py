@@ -308,3 +308,36 @@ def test_compact_layers_planted_paths():
         keep[L:L + len(path)] = False
         assert torch.equal(f.Kc[l, 0, keep].view(torch.int16), K0[l, 0, keep].view(torch.int16))
         assert torch.equal(f.Vc[l, 0, keep].view(torch.int16), V0[l, 0, keep].view(torch.int16))
+
+
+def test_forward_graph_replay_matches_eager():
+    """The whole forward captured as one HIP graph gives the eager outputs on every replay,
+    with eager runs in between (compaction rewrites the same rows: the prefix length
+    input is not advanced)."""
+    from medusa_tree_verification_heads_amd.forward import VerifyForward
+    dw, inp, fin, layers = _inputs("7b-mini-x2")
+    f = VerifyForward.from_numpy(dw, inp, fin, layers, mode="typical", temperature=0.7)
+    f.run()
+    eager = f.outputs()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        f.run()
+
+    def same(a, b):
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        same(eager, f.outputs())
+        f.run()
+        torch.cuda.synchronize()
+        same(eager, f.outputs())
+
