@@ -153,8 +153,10 @@ FORWARD_WORKLOADS = {
     "7b-T64-L1024-x32": DeepWorkload("7b-T64-L1024-x32", WORKLOADS["7b-T64-L1024"], 32, 11008),
 }
 
-# Parity cases of the forward: the 7B mini with two layers, and two layers at full 7B width.
+# Parity cases of the forward: the 7B mini with two layers (also with two sequences), and
+# two layers at full 7B width.
 FORWARD_CASES = {
     "7b-mini-x2": DeepWorkload("7b-mini-x2", PARITY_CASES["7b-mini"], 2, 1376),
+    "7b-mini-B2-x2": DeepWorkload("7b-mini-B2-x2", scaled(PARITY_CASES["7b-mini"], name="7b-mini-B2", B=2), 2, 1376),
     "7b-T64-L1024-x2": DeepWorkload("7b-T64-L1024-x2", WORKLOADS["7b-T64-L1024"], 2, 11008),
 }
