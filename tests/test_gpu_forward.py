@@ -345,3 +345,59 @@ def test_forward_graph_replay_matches_eager():
         torch.cuda.synchronize()
         same(eager, f.outputs())
 
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 32), (1, 96, 64), (17, 40, 96), (65, 8, 32)])
+def test_linear_smallest_shapes(M, N, K):
+    """Single rows, a single 8-column group, a single 32-wide k-step, a second row tile."""
+    import medusa_tree_verification_heads_amd as mdt
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = _rand_bf16(rng, (M, K))
+    W = _rand_bf16(rng, (N, K), K ** -0.5)
+    r = _rand_bf16(rng, (M, N))
+    xd, Wd, rd = _dev(_to_bits(x)), _dev(_to_bits(W)), _dev(_to_bits(r))
+    bound = _dot_err(x, W, K)
+    assert _bad(_bits(mdt.linear(xd, Wd)), ofw.linear(x, _to_bits(W)), bound) == 0
+    mdt.linear(xd, Wd, residual=rd, out=rd)
+    assert _bad(_bits(rd), ofw.linear(x, _to_bits(W), r), bound) == 0
+    if N % 32 == 0:
+        F = N // 2
+        Wg, Wu = W[0::2][:F], W[1::2][:F]
+        a = mdt.linear(xd, mdt.interleave_gate_up(_dev(_to_bits(Wg)), _dev(_to_bits(Wu))), act=mdt.ACT_SWIGLU)
+        zg, zu = x @ Wg.T, x @ Wu.T
+        ref = ostep.round_bf16(ofw.swiglu(zg, zu))
+        b2 = 1.1 * _dot_err(x, Wg, K) * np.abs(zu) + np.abs(ofw.swiglu(zg, np.ones_like(zg))) * _dot_err(x, Wu, K)
+        assert _bad(_bits(a), ref, b2 + 1e-6 * np.abs(ref)) == 0
+    if K >= 64:
+        part = mdt.linear_split(xd, Wd, 2)
+        assert np.allclose(part.sum(0).cpu().numpy(), x @ W.T, rtol=0, atol=float(bound.max()) * 2 + 1e-6)
+
+
+def test_compact_layers_paged():
+    """Layered compaction into a paged pool: layer l's pool sits cache_layer_stride
+    elements after layer 0's; the page table is shared."""
+    import medusa_tree_verification_heads_amd as mdt
+    B, T, H, Dh, nL, page, npages = 2, 10, 2, 128, 3, 16, 12
+    rng = np.random.default_rng(5)
+    k_rot = torch.from_numpy(rng.standard_normal((nL, B, T, H, Dh)).astype(np.float32)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(rng.standard_normal((nL, B, T, H, Dh)).astype(np.float32)).to(torch.bfloat16).cuda()
+    Kp = torch.zeros((nL, npages, page, H, Dh), dtype=torch.bfloat16, device="cuda")
+    Vp = torch.zeros_like(Kp)
+    table = torch.tensor([[3, 7, 1, -1], [0, 9, 4, 11]], dtype=torch.int32, device="cuda")
+    cache = mdt.KVCache(Kp[0], Vp[0], table, page)
+    lens = torch.tensor([14, 30], dtype=torch.int32, device="cuda")
+    path = torch.tensor([[0, 2, 7, -1], [0, 1, -1, -1]], dtype=torch.int32, device="cuda")
+    n = torch.tensor([3, 2], dtype=torch.int32, device="cuda")
+    new_len = mdt.kv_compact_layers(path, n, k_rot, v, cache, lens, Kp.stride(0))
+    torch.cuda.synchronize()
+    assert new_len.cpu().tolist() == [17, 32]
+    tb = table.cpu().numpy()
+    for l in range(nL):
+        for b, L in enumerate([14, 30]):
+            for j, node in enumerate(path[b, :int(n[b])].cpu().tolist()):
+                slot = L + j
+                pg, off = tb[b, slot // page], slot % page
+                assert torch.equal(Kp[l, pg, off].view(torch.int16), k_rot[l, b, node].view(torch.int16))
+                assert torch.equal(Vp[l, pg, off].view(torch.int16), v[l, b, node].view(torch.int16))
+    written = sum(int(n[b]) for b in range(B)) * nL
+    assert int((Kp.view(torch.int16) != 0).any(dim=-1).any(dim=-1).sum()) == written
