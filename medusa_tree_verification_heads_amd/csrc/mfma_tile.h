@@ -134,3 +134,105 @@ __device__ __forceinline__ void mfma_tile(const bf16_t* __restrict__ x, const bf
 }
 
 
+
+// A 128 x 128 tile for products with many x rows (compute-bound when both sides are
+// large): 4 waves in a 2 x 2 grid, wave (wm, wn) = (w / 2, w % 2) multiplying x rows
+// 64 wm .. +64 against weight rows 64 wn .. +64, i.e. 4 x 4 MFMA 16x16 fragments, so
+// every fragment read from LDS feeds four products (the 64 x 64 tile's waves read all
+// 64 x rows for 16 weight rows: 1.25 reads per product).  Same staging as mfma_tile:
+// row-contiguous 16-byte loads, two register buffers, pieces outside the matrices
+// zeroed in LDS.  acc[nt][mt]: weight rows 64 wn + 16 nt + l%16, x rows
+// 64 wm + 16 mt + 4(l/16) + e.  LDS: MfmaTile128<KC>::kBytes.
+template <int KC>
+struct MfmaTile128 {
+    static constexpr int kStride = KC + 8;
+    static constexpr int kXBytes = 128 * kStride * 2;
+    static constexpr int kBytes = 2 * kXBytes;
+};
+
+template <int KC, typename Epi>
+__device__ __forceinline__ void mfma_tile128(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
+                                             int d, int ld, int V, int m0, int n0, char* smem, Epi&& epi) {
+    constexpr int NT = 256;
+    constexpr int kStride = MfmaTile128<KC>::kStride;
+    constexpr int kPR = KC / 8;
+    constexpr int kPT = 128 * kPR / NT;  // pieces per thread per chunk, each operand
+    static_assert(KC % 32 == 0 && 128 * kPR % NT == 0, "chunk shape");
+    bf16_t* xs = (bf16_t*)smem;
+    bf16_t* ws = (bf16_t*)(smem + MfmaTile128<KC>::kXBytes);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nchunks = (d + KC - 1) / KC;
+
+    u32x4 wA[kPT], wB[kPT], xr[kPT];
+    auto piece_in = [&](int c, int j, int rows0, int nrows) {
+        const int p = threadIdx.x + NT * j;
+        return c < nchunks && 8 * (p % kPR) < d - c * KC && rows0 + p / kPR < nrows;
+    };
+    auto piece_at = [&](int c, int j, int rows0) {
+        const int p = threadIdx.x + NT * j;
+        return (size_t)(rows0 + p / kPR) * ld + c * KC + 8 * (p % kPR);
+    };
+    auto load_w = [&](int c, u32x4 (&wr)[kPT]) {
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) wr[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
+    };
+    auto load_x = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
+    };
+    auto store = [&](int c, const u32x4 (&wr)[kPT]) {
+        const u32x4 z{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) {
+            const int p = threadIdx.x + NT * j;
+            *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wr[j] : z;
+            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c) {
+        const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
+#pragma unroll
+        for (int s = 0; s < KC / 32; ++s) {
+            if (s < nsteps) {
+                u32x4 a[4], b[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    a[mt] = *(const u32x4*)(xs + (64 * wm + 16 * mt + c16) * kStride + 32 * s + 8 * g);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    b[nt] = *(const u32x4*)(ws + (64 * wn + 16 * nt + c16) * kStride + 32 * s + 8 * g);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mfma16(a[mt], b[nt], acc[nt][mt]);
+            }
+        }
+    };
+    load_w(0, wA);
+    load_x(0);
+    load_w(1, wB);
+    store(0, wA);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+        load_x(c + 1);
+        load_w(c + 2, wA);
+        compute(c);
+        __syncthreads();
+        store(c + 1, wB);
+        __syncthreads();
+        load_x(c + 2);
+        load_w(c + 3, wB);
+        compute(c + 1);
+        __syncthreads();
+        store(c + 2, wA);
+        __syncthreads();
+    }
+    epi(acc);
+}

@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kNB = 64;          // vocabulary columns per workgroup
 constexpr int kMB = 64;          // node rows per workgroup (bf16 path)
+constexpr int kBigRows = 256;    // from this many node rows on: 128 x 128 tiles
 constexpr int kZStride = kNB + 1;
 #ifndef MDT_VERIFY_KC
 #define MDT_VERIFY_KC 256        // dims per staged chunk (LDS holds one 64-row tile of x and of W)
@@ -114,7 +115,7 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
-    if (q == 0 && row < M) part[(long)row * nblk_n + blockIdx.x] = p;
+    if (q == 0 && row < M) part[(long)row * nblk_n + n0 / NB] = p;
     if (logits_opt && row < M)
         for (int c = q * CPT; c < q * CPT + CPT && c < ncol; ++c) logits_opt[(long)row * V + n0 + c] = z[c];
     // edges: node c of sequence b reads row b*T + parent(c) at column token(b, c)
@@ -136,7 +137,7 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
 // workgroup (MT = 16, 128-dim chunks) the batched shapes ran slower (one wave per SIMD
 // at 284 registers), the repeated weight streams being served largely from the
 // last-level cache.
-template <int KC, int NB, int MT = 4>
+template <int KC, int NB, int MT = 4, bool MMAJOR = false>
 __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
                                                       int M, int d, int V, float tau, int nblk_n,
                                                       Part* __restrict__ part, float* __restrict__ logits_opt,
@@ -147,7 +148,9 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
     constexpr int MB = 16 * MT;
     static_assert(MfmaTile<KC, NB, MT>::kBytes >= MB * (NB + 1) * 4, "the logits tile must fit");
     __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB, MT>::kBytes];
-    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * MB;
+    // MMAJOR: blockIdx.x walks the node-row blocks, so the workgroups that read one block
+    // of weight rows are dispatched together and share it through the caches
+    const int n0 = (MMAJOR ? blockIdx.y : blockIdx.x) * NB, m0 = (MMAJOR ? blockIdx.x : blockIdx.y) * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
@@ -160,6 +163,37 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
     });
     __syncthreads();
     tile_epilogue<MB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
+}
+
+// Many node rows (batches, 256-node trees): 128 x 128 tiles (mfma_tile128), grid
+// (ceil(M/128), ceil(V/128)) row-block-major, partials per 128 vocabulary columns.
+template <int KC>
+__global__ __launch_bounds__(256) void verify_mfma128(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+                                                      int M, int d, int V, float tau, int nblk_n,
+                                                      Part* __restrict__ part, float* __restrict__ logits_opt,
+                                                      const int32_t* __restrict__ parent,
+                                                      const int32_t* __restrict__ tokens, int T,
+                                                      float* __restrict__ edge) {
+    constexpr int kZ = 128 + 1;
+    constexpr int kLds = MfmaTile128<KC>::kBytes > 128 * kZ * 4 ? MfmaTile128<KC>::kBytes : 128 * kZ * 4;
+    __shared__ __attribute__((aligned(16))) char smem[kLds];
+    const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 128;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    const EdgePre pre = edge_preload<128>(m0, M, parent, tokens, T);
+    float* zt = (float*)smem;  // [128][129], reuses the tiles
+    mfma_tile128<KC>(x, W, M, d, d, V, m0, n0, smem, [&](const f32x4 (&acc)[4][4]) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    zt[(64 * wm + 16 * mt + 4 * g + e) * kZ + 64 * wn + 16 * nt + c16] = acc[nt][mt][e];
+    });
+    __syncthreads();
+    tile_epilogue<128, 128, 256>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
 // fp32 path: grid (ceil(V/64), ceil(M/16)), block 256; x rows staged in LDS as fp32.
@@ -270,10 +304,22 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     const int M = B * T;
-    const int nb_cols = dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
+    const bool big = dt == MDT_BF16 && M >= kBigRows;
+    const int nb_cols = big ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
-    if (dt == MDT_BF16) {
+    if (big) {
+        auto kern = verify_mfma128<64>;
+        MDT_LAUNCH("verify_mfma", kern, dim3((M + 127) / 128, nblk_n), dim3(256), 0, s, (const bf16_t*)x,
+                   (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
+                   edge_logit);
+    } else if (dt == MDT_BF16 && M > kMB) {
+        // several node-row blocks: row-block-major grid (each weight block streamed once)
+        auto kern = verify_mfma<MDT_VERIFY_KC, MDT_VERIFY_NB, 4, true>;
+        MDT_LAUNCH("verify_mfma", kern, dim3((M + kMB - 1) / kMB, nblk_n), dim3(4 * MDT_VERIFY_NB), 0, s,
+                   (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt,
+                   tree->parent, tree_tokens, T, edge_logit);
+    } else if (dt == MDT_BF16) {
         auto kern = verify_mfma<MDT_VERIFY_KC, MDT_VERIFY_NB>;
         MDT_LAUNCH("verify_mfma", kern, dim3(nblk_n, (M + kMB - 1) / kMB), dim3(4 * MDT_VERIFY_NB), 0, s,
                    (const bf16_t*)x,
