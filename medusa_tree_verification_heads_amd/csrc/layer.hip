@@ -53,29 +53,37 @@ __device__ __forceinline__ float hi16(uint32_t u) { return bf16_to_f32(u >> 16);
 // x SiLU(x)-gated: silu(g) * u, silu(g) = g / (1 + e^-g).
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
-// grid (ceil(N/64), ceil(M/64), nsplit), block 256; blockIdx.z > 0 only for kPartial.
-template <int EPI>
-__global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
+// grid (ceil(N/64), ceil(M/64), nsplit), block 256 (K2: 512, the tile on 8 waves that
+// split each chunk's k-steps, for grids of at most one workgroup per CU); blockIdx.z > 0
+// only for kPartial.
+template <int EPI, bool K2 = false>
+__global__ __launch_bounds__(K2 ? 2 * kThreads : kThreads) void linear_mfma(LinArgs a) {
+    constexpr int NTH = K2 ? 2 * kThreads : kThreads;
+    constexpr int kZOff = K2 ? 16384 : 0;  // K2: the halves' reduction buffer comes first
     __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB>::kBytes];
-    static_assert(MfmaTile<kKC, kNB>::kBytes >= kMBL * kZs * 4, "the result tile must fit");
+    static_assert(MfmaTile<kKC, kNB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
     const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
     const int k0 = s * a.kslice;
     const int klen = min(a.kslice, a.K - k0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    float* zt = (float*)smem;  // [64][kZs], reuses the operand tiles
-    mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, [&](const f32x4 (&acc)[4]) {
+    float* zt = (float*)(smem + kZOff);  // [64][kZs], reuses the operand tiles
+    auto to_lds = [&](const f32x4 (&acc)[4]) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
-    });
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + (wave & 3) * 16 + c16] = acc[mt][e];
+    };
+    if constexpr (K2)
+        mfma_tile_k2<kKC>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
+    else
+        mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
     __syncthreads();
 
     if constexpr (EPI == kPartial) {
         // four consecutive columns per item, 16-byte stores
         float* ps = a.part + (size_t)s * a.M * a.N;
-        for (int it = threadIdx.x; it < kMBL * (kNB / 4); it += kThreads) {
+        for (int it = threadIdx.x; it < kMBL * (kNB / 4); it += NTH) {
             const int row = it >> 4, c0 = 4 * (it & 15);
             const int m = m0 + row, n = n0 + c0;
             if (m >= a.M || n >= a.N) continue;
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
         const int row = threadIdx.x >> 2, og = threadIdx.x & 3;
         const int jj = og >> 1, i0 = 8 * (og & 1);
         const int m = m0 + row;
-        if (m < a.M && n0 + 32 * jj < a.N) {
+        if (row < kMBL && m < a.M && n0 + 32 * jj < a.N) {
             const float* zr = zt + row * kZs + 32 * jj + i0;
             uint4 o;
             o.x = pack2(swiglu(zr[0], zr[16]), swiglu(zr[1], zr[17]));
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(LinArgs a) {
         // Eight consecutive columns per item; the columns are cut into nseg equal
         // segments, segment q going to y + q*M*(N/nseg) as its own [M][N/nseg] matrix.
         const int nsegc = a.N / a.nseg;
-        for (int it = threadIdx.x; it < kMBL * (kNB / 8); it += kThreads) {
+        for (int it = threadIdx.x; it < kMBL * (kNB / 8); it += NTH) {
             const int row = it >> 3, c0 = 8 * (it & 7);
             const int m = m0 + row, n = n0 + c0;
             if (m >= a.M || n >= a.N) continue;
@@ -243,12 +251,18 @@ extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* 
     }
     LinArgs a{(const bf16_t*)x, (const bf16_t*)W, (const bf16_t*)residual, (bf16_t*)y, nullptr, M, N, K, K, nseg};
     const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, 1);
+    // at most one workgroup per CU: the 8-wave tile hides more latency per SIMD
+    const bool k2 = (long)grid.x * grid.y <= mdt_num_cus();
+    const hipStream_t hs = (hipStream_t)stream;
     if (act == MDT_ACT_SWIGLU) {
-        MDT_LAUNCH("linear_mfma", linear_mfma<kSwiglu>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kSwiglu, true>), grid, dim3(2 * kThreads), 0, hs, a);
+        else MDT_LAUNCH("linear_mfma", linear_mfma<kSwiglu>, grid, dim3(kThreads), 0, hs, a);
     } else if (residual) {
-        MDT_LAUNCH("linear_mfma", linear_mfma<kResidual>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kResidual, true>), grid, dim3(2 * kThreads), 0, hs, a);
+        else MDT_LAUNCH("linear_mfma", linear_mfma<kResidual>, grid, dim3(kThreads), 0, hs, a);
     } else {
-        MDT_LAUNCH("linear_mfma", linear_mfma<kStore>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kStore, true>), grid, dim3(2 * kThreads), 0, hs, a);
+        else MDT_LAUNCH("linear_mfma", linear_mfma<kStore>, grid, dim3(kThreads), 0, hs, a);
     }
     return mdt_launched("linear_mfma");
 }

@@ -236,3 +236,107 @@ __device__ __forceinline__ void mfma_tile128(const bf16_t* __restrict__ x, const
     }
     epi(acc);
 }
+
+// The 64 x 64 tile on 8 waves: wave w multiplies weight rows 16 (w % 4) .. +16 against all
+// 64 x rows over the k-steps of half w / 4 of every chunk; at the end the second half's
+// accumulators are added to the first's through LDS (at offset 0, 16 KiB) and epi(acc)
+// runs on waves 0-3 only, with the layout of mfma_tile.  For grids of at most one
+// workgroup per CU, where the 4-wave tile leaves each SIMD a single wave to hide every
+// latency.  Block 512 threads; LDS MfmaTile<KC, NB>::kBytes (NB = 64).
+template <int KC, typename Epi>
+__device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
+                                             int d, int ld, int V, int m0, int n0, char* smem, Epi&& epi) {
+    constexpr int NT = 512;
+    constexpr int kStride = MfmaTile<KC, 64>::kStride;
+    constexpr int kPR = KC / 8;
+    constexpr int kPPT = 64 * kPR / NT;
+    constexpr int kXPT = 64 * kPR / NT;
+    constexpr int kS = KC / 32;
+    static_assert(KC % 64 == 0 && 64 * kPR % NT == 0, "chunk shape");
+    bf16_t* xs = (bf16_t*)smem;
+    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, 64>::kXBytes);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int wr = wave & 3, half = wave >> 2;
+    const int nchunks = (d + KC - 1) / KC;
+
+    u32x4 wA[kPPT], wB[kPPT], xr[kXPT];
+    auto piece_in = [&](int c, int j, int rows0, int nrows) {
+        const int p = threadIdx.x + NT * j;
+        return c < nchunks && 8 * (p % kPR) < d - c * KC && rows0 + p / kPR < nrows;
+    };
+    auto piece_at = [&](int c, int j, int rows0) {
+        const int p = threadIdx.x + NT * j;
+        return (size_t)(rows0 + p / kPR) * ld + c * KC + 8 * (p % kPR);
+    };
+    auto load_w = [&](int c, u32x4 (&wv)[kPPT]) {
+#pragma unroll
+        for (int j = 0; j < kPPT; ++j) wv[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
+    };
+    auto load_x = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < kXPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
+    };
+    auto store = [&](int c, const u32x4 (&wv)[kPPT]) {
+        const u32x4 z{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kPPT; ++j) {
+            const int p = threadIdx.x + NT * j;
+            *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wv[j] : z;
+            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
+        }
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c) {
+        const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
+        const bf16_t* wrow = ws + (wr * 16 + c16) * kStride + 8 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < kS / 2; ++s2) {
+            const int s = half * (kS / 2) + s2;
+            if (s < nsteps) {
+                const u32x4 b = *(const u32x4*)(wrow + 32 * s);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kStride + 32 * s + 8 * g);
+                    acc[mt] = mfma16(a, b, acc[mt]);
+                }
+            }
+        }
+    };
+    load_w(0, wA);
+    load_x(0);
+    load_w(1, wB);
+    store(0, wA);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+        load_x(c + 1);
+        load_w(c + 2, wA);
+        compute(c);
+        __syncthreads();
+        store(c + 1, wB);
+        __syncthreads();
+        load_x(c + 2);
+        load_w(c + 3, wB);
+        compute(c + 1);
+        __syncthreads();
+        store(c + 2, wA);
+        __syncthreads();
+    }
+    float* red = (float*)smem;  // [4 waves][4 mt][4 e][64 lanes]
+    if (half == 1) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((wr * 4 + mt) * 4 + e) * 64 + lane] = acc[mt][e];
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mt][e] += red[((wr * 4 + mt) * 4 + e) * 64 + lane];
+        epi(acc);
+    }
+}
