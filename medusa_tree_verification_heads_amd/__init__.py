@@ -562,11 +562,12 @@ def linear_split(x, W, nsplit: int, out=None, stream=None):
 
 def auto_split(M: int, N: int, K: int, device=None) -> int:
     """Slices for a product whose 64 x 64 output tiles are too few to fill the GPU: grow
-    while the workgroups stay within two per compute unit and slices stay >= 512 long."""
+    while the workgroups stay within one per compute unit (where the library runs the
+    tile on 8 waves) and slices stay >= 512 long."""
     cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
     tiles = -(-N // 64) * -(-M // 64)
     s = 1
-    while tiles * (s + 1) <= 2 * cus and K // (s + 1) >= 512:
+    while tiles * (s + 1) <= cus and K // (s + 1) >= 512:
         s += 1
 
     def slices(n):  # slices left after rounding each to a multiple of 32

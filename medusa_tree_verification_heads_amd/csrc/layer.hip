@@ -278,7 +278,10 @@ extern "C" mdt_status mdt_linear_split(void* stream, int M, int N, int K, const 
                 nsplit);
     LinArgs a{(const bf16_t*)x, (const bf16_t*)W, nullptr, nullptr, part, M, N, K, ks, 1};
     const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, nsplit);
-    MDT_LAUNCH("linear_mfma", linear_mfma<kPartial>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    if ((long)grid.x * grid.y * grid.z <= mdt_num_cus())
+        MDT_LAUNCH("linear_mfma", (linear_mfma<kPartial, true>), grid, dim3(2 * kThreads), 0, (hipStream_t)stream, a);
+    else
+        MDT_LAUNCH("linear_mfma", linear_mfma<kPartial>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
     return mdt_launched("linear_mfma");
 }
 

@@ -8,15 +8,16 @@ synchronisation:
 
     medusa_heads -> topk_tree_expand -> embed
     -> rmsnorm -> per layer: linear (q|k|v) -> tree_attention
-                             -> linear_split (o Wo^T) -> add_rmsnorm (x += ., h = norm)
+                             -> linear_split (o Wo^T, slices) -> add_rmsnorm (x += ., h = norm)
                              -> linear (SwiGLU) -> linear_split (a Wd^T)
                              -> add_rmsnorm (x += ., h = next layer's norm, or the final one)
     -> verify_logits -> accept_path -> kv_compact_layers
 
 The output and down projections have only d output columns (64 tiles of 64 at 7B), so
-their inner dimension is cut into slices (linear_split) whose fp32 products the
-following add_rmsnorm sums into the residual stream; with one slice they are a plain
-linear with the residual in its epilogue followed by rmsnorm.
+their inner dimension is cut into slices (linear_split; 4 at 7B, one 8-wave workgroup
+per CU) whose fp32 products the following add_rmsnorm sums into the residual stream;
+with one slice they are a plain linear with the residual in its epilogue followed by
+rmsnorm.
 
 Every layer has its own prefix cache (one allocation [layers][B][capacity][H][Dh]);
 every layer's tree keys/values are kept until acceptance, then the accepted path is
