@@ -33,8 +33,8 @@ import torch
 
 from . import (ACT_SWIGLU, GREEDY, TYPICAL, KVCache, Tree, accept_path, add_rmsnorm, auto_split, embed,
                interleave_gate_up, kv_compact_layers, linear, linear_split, medusa_heads, medusa_heads_workspace,
-               new_workspace, rmsnorm, topk_tree_expand, topk_workspace, tree_attention, tree_attention_workspace,
-               verify_logits, verify_logits_workspace, MDT_BF16)
+               new_workspace, next_state, rmsnorm, topk_tree_expand, topk_workspace, tree_attention,
+               tree_attention_workspace, verify_logits, verify_logits_workspace, MDT_BF16)
 from .step import to_device
 
 LAYER_KEYS = ("g_attn", "Wqkv", "Wo", "g_mlp", "Wgu", "Wd")
@@ -120,16 +120,17 @@ class VerifyForward:
             linear(a, W, residual=self.x, out=self.x, stream=stream)
             rmsnorm(self.x, g, eps, out=out, stream=stream)
 
-    def layer(self, l: int, stream=None):
+    def layer(self, l: int, stream=None, prefix_len=None):
         """Enqueue decoder layer l: self.h holds rmsnorm(x) * g_attn of this layer on entry;
         on exit self.x is the new residual stream and self.h (or, after the last layer,
         self.xf) its norm for what follows."""
         w, lw = self.w, self.layers[l]
+        prefix_len = self.prefix_len if prefix_len is None else prefix_len
         B, T, H, Dh = w.B, self.tree.T, w.H, w.Dh
         qkv = self.qkv[l]
         linear(self.h, lw["Wqkv"], nseg=3, out=qkv, stream=stream)
         shp = (B, T, H, Dh)
-        tree_attention(qkv[0].view(shp), qkv[1].view(shp), qkv[2].view(shp), self.caches[l], self.prefix_len,
+        tree_attention(qkv[0].view(shp), qkv[1].view(shp), qkv[2].view(shp), self.caches[l], prefix_len,
                        self.tree, w.rope_theta, out=self.o.view(shp), k_rot=self.k_rot[l], ws=self.ws_attn,
                        stream=stream)
         self._close(self.o, lw["Wo"], self.split_o, lw["g_mlp"], self.h, stream)
@@ -138,25 +139,34 @@ class VerifyForward:
         self._close(self.a, lw["Wd"], self.split_d, self.g_final if last else self.layers[l + 1]["g_attn"],
                     self.xf if last else self.h, stream)
 
-    def run(self, stream=None):
+    def run(self, stream=None, h=None, prefix_len=None, new_prefix_len=None, tokens=None, path=None,
+            n_acc=None):
+        """Enqueue one step.  The keyword arguments replace the step's own input or output
+        tensors for this call (a chain of steps passes each step's own)."""
         w, t = self.w, self.base
-        medusa_heads(t["h"], t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
-        topk_tree_expand(self.logits, w.k_cfg, self.tree, self.prefix_len, self.topk_idx, self.topk_val,
-                         self.tokens, self.pos, ws=self.ws_topk, stream=stream)
-        embed(self.tokens.view(-1), self.E, out=self.x, stream=stream)
+        h = t["h"] if h is None else h
+        prefix_len = self.prefix_len if prefix_len is None else prefix_len
+        new_len = self.new_len if new_prefix_len is None else new_prefix_len
+        tokens = self.tokens if tokens is None else tokens
+        path = self.path if path is None else path
+        n_acc = self.n_acc if n_acc is None else n_acc
+        medusa_heads(h, t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
+        topk_tree_expand(self.logits, w.k_cfg, self.tree, prefix_len, self.topk_idx, self.topk_val,
+                         tokens, self.pos, ws=self.ws_topk, stream=stream)
+        embed(tokens.view(-1), self.E, out=self.x, stream=stream)
         g0 = self.layers[0]["g_attn"] if self.layers else self.g_final
         rmsnorm(self.x, g0, self.dw.norm_eps, out=self.h if self.layers else self.xf, stream=stream)
         for l in range(len(self.layers)):
-            self.layer(l, stream)
-        verify_logits(self.xf, t["Wlm"], self.tree, self.tokens, self.temperature, stats=self.stats,
+            self.layer(l, stream, prefix_len)
+        verify_logits(self.xf, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats,
                       edge=self.edge, ws=self.ws_verify, stream=stream)
-        accept_path(self.stats, self.edge, self.tokens, self.tree, self.mode, self.eps, self.delta,
-                    self.temperature, path=self.path, n_acc=self.n_acc, stream=stream)
+        accept_path(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta,
+                    self.temperature, path=path, n_acc=n_acc, stream=stream)
         if self.layers:
             B, T, H, Dh = w.B, self.tree.T, w.H, w.Dh
             v = self.qkv[:, 2].view(len(self.layers), B, T, H, Dh)
-            kv_compact_layers(self.path, self.n_acc, self.k_rot, v, self.caches[0], self.prefix_len,
-                              self.Kc.stride(0), new_prefix_len=self.new_len, stream=stream)
+            kv_compact_layers(path, n_acc, self.k_rot, v, self.caches[0], prefix_len,
+                              self.Kc.stride(0), new_prefix_len=new_len, stream=stream)
 
     def outputs(self) -> dict:
         torch.cuda.synchronize()
@@ -172,3 +182,39 @@ class VerifyForward:
         if self.layers:
             out.update(new_len=f(self.new_len), Kc=f(self.Kc), Vc=f(self.Vc))
         return out
+
+
+class ForwardLoop:
+    """Chained steps of the full forward (multi-step decoding through every layer).
+
+    Step s+1 starts from step s: its hidden state is the final normed row (what the LM
+    head reads) of each sequence's deepest accepted node (``next_state``), its prefix
+    length is step s's new length, and every layer's cache already holds step s's
+    accepted keys and values.  Every step has its own hidden-state, prefix-length, token,
+    path and n_acc tensors, so ``run()`` can be repeated (or replayed as a graph) from the
+    same start; the caches need room for one accepted path per step.
+    """
+
+    def __init__(self, fwd: VerifyForward, steps: int):
+        self.f = fwd
+        self.S = steps
+        B, T = fwd.w.B, fwd.tree.T
+        dev = fwd.dev
+        h0 = fwd.base["h"]
+        self.h = [h0] + [torch.empty_like(h0) for _ in range(steps)]
+        self.lens = [fwd.prefix_len] + [torch.empty_like(fwd.prefix_len) for _ in range(steps)]
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tokens = torch.empty((steps, B, T), **i32)
+        self.paths = torch.empty((steps, B, fwd.path.shape[1]), **i32)
+        self.n_acc = torch.empty((steps, B), **i32)
+
+    def run_step(self, s: int, stream=None):
+        f = self.f
+        f.run(stream, h=self.h[s], prefix_len=self.lens[s], new_prefix_len=self.lens[s + 1], tokens=self.tokens[s],
+              path=self.paths[s], n_acc=self.n_acc[s])
+        next_state(f.xf.view(f.w.B, f.tree.T, f.w.d), self.paths[s], self.n_acc[s], out=self.h[s + 1], stream=stream)
+
+    def run(self, stream=None):
+        for s in range(self.S):
+            self.run_step(s, stream)
+

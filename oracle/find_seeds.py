@@ -9,6 +9,7 @@ used.
     python -m oracle.find_seeds [name ...]
     python -m oracle.find_seeds --loop S [name ...]   # S chained steps ("name@loopS" entries)
     python -m oracle.find_seeds --forward name ...    # full-forward cases ("fwd:name" entries)
+    python -m oracle.find_seeds --forward-loop S name ...   # S chained forward steps ("fwd:name@loopS")
 
 Chained steps start from attention outputs, whose scale shrinks with the prefix
 length, so their logits are close together and only the small cases have loop
@@ -77,33 +78,35 @@ def loop_margin(w, seed: int, steps: int) -> float:
 FORWARD_REL = 0.05   # edge margins of the forward, relative to the largest |logit| (/ tau)
 
 
-def forward_margin(dw, seed: int) -> float:
-    """Normalised margin of a full-forward case (>= 1 passes): head margins against
-    MIN_MARGIN, verifier edge margins against FORWARD_REL of the largest logit (over tau),
-    which is well above the logits' difference after the bf16 layers."""
+def forward_margin(dw, seed: int, steps: int = 1) -> float:
+    """Normalised margin of a full-forward case (>= 1 passes), over every step of a chain
+    of ``steps``: head margins against MIN_MARGIN, verifier edge margins against
+    FORWARD_REL of the largest logit (over tau), which is well above the logits'
+    difference after the bf16 layers."""
     w = dw.base
-    inp = make_inputs(w, seed, parts=("h", "W1", "W2", "Wlm"))
+    inp = make_inputs(w, seed, parts=("h", "W1", "W2", "Wlm"), steps=steps)
     fin = forward_inputs(dw, seed)
-    layers = [layer_inputs(dw, seed, l) for l in range(dw.n_layers)]
+    layers = [layer_inputs(dw, seed, l, steps=steps) for l in range(dw.n_layers)]
     tree = otree.build_tree(w)
     m = float("inf")
     for run in w.accept:
-        r = oforward.forward(dw, inp, fin, layers, tree, run.mode, run.temperature, run.eps, run.delta)
-        m = min(m, margins.head_margin(r["logits"], w.k_cfg) / margins.MIN_MARGIN)
-        e = margins.edge_margins(r["z"], r["stats"], r["tokens"], tree, run.mode, run.eps, run.delta,
-                                 run.temperature)
-        m = min(m, float(e.min()) / (FORWARD_REL * float(np.abs(r["z"]).max()) / (run.temperature or 1.0)))
+        for r in oforward.forward_loop(dw, inp, fin, layers, tree, steps, run.mode, run.temperature, run.eps,
+                                       run.delta):
+            m = min(m, margins.head_margin(r["logits"], w.k_cfg) / margins.MIN_MARGIN)
+            e = margins.edge_margins(r["z"], r["stats"], r["tokens"], tree, run.mode, run.eps, run.delta,
+                                     run.temperature)
+            m = min(m, float(e.min()) / (FORWARD_REL * float(np.abs(r["z"]).max()) / (run.temperature or 1.0)))
     return m
 
 
-def main_forward(names):
+def main_forward(names, steps=1):
     seeds = json.load(open(OUT)) if os.path.exists(OUT) else {}
     for name in names:
         dw = FORWARD_CASES[name]
-        key = f"fwd:{name}"
+        key = f"fwd:{name}" if steps == 1 else f"fwd:{name}@loop{steps}"
         for attempt in range(100):
-            seed = 7000 + 100 * list(FORWARD_CASES).index(name) + attempt
-            m = forward_margin(dw, seed)
+            seed = 7000 + 100 * list(FORWARD_CASES).index(name) + attempt + (0 if steps == 1 else 50)
+            m = forward_margin(dw, seed, steps)
             print(f"{key} seed {seed}: normalised margin {m:.3f}", flush=True)
             if m >= 1.0:
                 seeds[key] = {"seed": seed, "margin": m}
@@ -136,6 +139,9 @@ if __name__ == "__main__":
     args = sys.argv[1:]
     if args[:1] == ["--forward"]:
         main_forward(args[1:])
+        raise SystemExit(0)
+    if args[:1] == ["--forward-loop"]:
+        main_forward(args[2:], int(args[1]))
         raise SystemExit(0)
     n_steps = 1
     if args[:1] == ["--loop"]:

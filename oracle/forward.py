@@ -98,3 +98,26 @@ def forward(dw, inp: dict, fin: dict, layers, tree: OracleTree, mode: str, tau: 
         caches.append((Kn, Vn))
     return dict(logits=logits, topk_idx=tk_idx, tokens=tokens, pos=pos, x_last=x, xf=xf, z=z, stats=stats,
                 edge=edge, paths=paths, n_acc=n_acc, k_rot=k_rots, v=vs, caches=caches, new_len=new_len)
+
+
+def forward_loop(dw, inp: dict, fin: dict, layers, tree: OracleTree, steps: int, mode: str, tau: float, eps=0.09,
+                 delta=0.3):
+    """Chain ``steps`` forward steps (summary page, section 3.2: the next iteration
+    continues from the last accepted token).  Step s+1's hidden state is the final normed
+    row (the LM head's input) of each sequence's deepest accepted node, its prefix length
+    the new length, and every layer's cache the compacted one.  Returns the step results."""
+    w = dw.base
+    cur = dict(inp)
+    lays = [dict(lw) for lw in layers]
+    out = []
+    for _ in range(steps):
+        r = forward(dw, cur, fin, lays, tree, mode, tau, eps, delta)
+        out.append(r)
+        T = tree.T
+        cur = dict(cur)
+        cur["h"] = np.stack([r["xf"][b * T + r["paths"][b][-1]] for b in range(w.B)])
+        cur["prefix_len"] = np.asarray(r["new_len"], dtype=np.int32)
+        for lw, (Kn, Vn) in zip(lays, r["caches"]):
+            lw["Kc"], lw["Vc"] = Kn, Vn
+    return out
+

@@ -91,3 +91,19 @@ def cache_row(C: np.ndarray, b: int, slot: int, page_table, page_size: int):
 
 def unique_rows(z: np.ndarray):
     return set(om.unique_argmax_rows(z))
+
+
+def exact_topk(row: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest values of a row, equal values by smaller index."""
+    order = np.lexsort((np.arange(row.shape[0]), -np.asarray(row, dtype=np.float64)))
+    return order[:k]
+
+
+def clear_topk_rows(ref: np.ndarray, diff: np.ndarray, k: int) -> np.ndarray:
+    """Per row of ``ref`` [..][V]: True where every gap between consecutive values of the
+    top k+1 exceeds twice ``diff`` (that row's largest GPU-vs-oracle difference), so the
+    top-k indices of two rows within ``diff`` of each other must agree."""
+    top = -np.sort(-ref, axis=-1)[..., :k + 1]
+    gaps = top[..., :-1] - top[..., 1:]
+    return gaps.min(axis=-1) > 2 * diff
+

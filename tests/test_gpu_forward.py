@@ -401,3 +401,88 @@ def test_compact_layers_paged():
                 assert torch.equal(Vp[l, pg, off].view(torch.int16), v[l, b, node].view(torch.int16))
     written = sum(int(n[b]) for b in range(B)) * nL
     assert int((Kp.view(torch.int16) != 0).any(dim=-1).any(dim=-1).sum()) == written
+
+
+@pytest.mark.parametrize("name", ["7b-mini-x2", "7b-mini-B2-x2"])
+def test_forward_loop(name):
+    """Three chained steps through both layers: each step starts from the final normed row
+    of the last accepted node, the new prefix length and the compacted caches.  The GPU
+    chain is compared with the oracle chain (both from the drawn inputs) while the two
+    agree: head logits and final rows within 2e-2, top-k rows exactly where the oracle's
+    gaps exceed twice the observed logit difference, accepted paths exactly where every
+    edge margin exceeds the bound that the final rows' difference puts on the logits.
+    Every step is also checked by properties of the GPU's own values (its top-k, tree
+    tokens, path structure, carried row, new lengths), and the prefix rows of every
+    layer's cache stay untouched."""
+    from medusa_tree_verification_heads_amd.forward import ForwardLoop, VerifyForward
+    from tests.parity_util import clear_topk_rows, exact_topk
+    S = 3
+    dw = FORWARD_CASES[name]
+    w = dw.base
+    seed = SEEDS[f"fwd:{name}@loop{S}"]["seed"]
+    inp = make_inputs(w, seed, parts=("h", "W1", "W2", "Wlm"), steps=S)
+    fin = forward_inputs(dw, seed)
+    layers = [layer_inputs(dw, seed, l, steps=S) for l in range(dw.n_layers)]
+    tree = otree.build_tree(w)
+    T, B = tree.T, w.B
+    Wlm = ostep.to_f64(inp["Wlm"])
+    for run in w.accept:
+        ref = ofw.forward_loop(dw, inp, fin, layers, tree, S, run.mode, run.temperature, run.eps, run.delta)
+        f = VerifyForward.from_numpy(dw, inp, fin, layers, mode=run.mode, temperature=run.temperature, eps=run.eps,
+                                     delta=run.delta)
+        loop = ForwardLoop(f, S)
+        together, steps_compared = True, 0
+        for s in range(S):
+            L = loop.lens[s].cpu().numpy()
+            loop.run_step(s)
+            torch.cuda.synchronize()
+            logits = f.logits.cpu().numpy()
+            topk = f.topk_idx.cpu().numpy()
+            tokens = loop.tokens[s].cpu().numpy()
+            n_acc = loop.n_acc[s].cpu().numpy()
+            paths = loop.paths[s].cpu().numpy()
+            xf_bits = _bits(f.xf)
+            for b in range(B):
+                for k in range(w.K + 1):
+                    assert topk[b, k].tolist() == exact_topk(logits[b, k], w.k_cfg).tolist(), (s, b, k)
+                for i in range(T):
+                    assert tokens[b, i] == topk[b, tree.depth[i], tree.rank[i]], (s, b, i)
+                path = paths[b, :n_acc[b]].tolist()
+                assert path[0] == 0 and all(tree.parent[path[j]] == path[j - 1] for j in range(1, len(path)))
+                assert np.array_equal(_bits(loop.h[s + 1])[b], xf_bits[b * T + path[-1]]), (s, b)
+            assert np.array_equal(loop.lens[s + 1].cpu().numpy(), L + n_acc), s
+            if not together:
+                continue
+            r = ref[s]
+            assert rel_err_rows(logits.astype(np.float64), r["logits"]) <= REL_TOL, s
+            diff = np.abs(logits.astype(np.float64) - r["logits"]).max(axis=-1)
+            clear = clear_topk_rows(r["logits"], diff, w.k_cfg)
+            for b in range(B):
+                for k in range(w.K + 1):
+                    if clear[b, k]:
+                        assert topk[b, k].tolist() == r["topk_idx"][b, k].tolist(), (s, b, k)
+            steps_compared += 1
+            if not np.array_equal(tokens, r["tokens"]):
+                # a near-tie in the heads (not clear above) gave other candidates: the chains part
+                note(f"forward loop {name} {run.mode} step {s}: candidates differ at a near-tie; chains part")
+                together = False
+                continue
+            xf = ostep.to_f64(xf_bits)
+            assert rel_err_rows(xf, r["xf"]) <= REL_TOL, s
+            em = om.edge_margins(r["z"], r["stats"], r["tokens"], tree, run.mode, run.eps, run.delta,
+                                 run.temperature)
+            dz = np.abs((xf - r["xf"]) @ Wlm.T).reshape(B, -1).max(axis=1)
+            for b in range(B):
+                need = max(om.MIN_MARGIN, 4 * dz[b] / (run.temperature or 0.5))
+                if np.array_equal(tokens[b], r["tokens"][b]) and em[b].min() >= need:
+                    assert paths[b, :n_acc[b]].tolist() == r["paths"][b], (s, b)
+            together = n_acc.tolist() == r["n_acc"] and all(
+                paths[b, :n_acc[b]].tolist() == r["paths"][b] for b in range(B))
+            note(f"forward loop {name} {run.mode} step {s}: {int(clear.sum())}/{clear.size} clear top-k rows, "
+                 f"chains agree: {together}")
+        assert steps_compared >= 1
+        for l in range(dw.n_layers):
+            for b in range(B):
+                L0 = int(inp["prefix_len"][b])
+                assert np.array_equal(_bits(f.Kc[l])[b, :L0], layers[l]["Kc"][b, :L0])
+                assert np.array_equal(_bits(f.Vc[l])[b, :L0], layers[l]["Vc"][b, :L0])

@@ -4,11 +4,14 @@
   margin >= 1e-3 (``tiny-fp32-T10@loop3`` in workloads/seeds.json): the GPU chain is
   compared with the oracle chain, integers bit-exactly.
 * Larger cases: after the first step the carried hidden states are attention outputs,
-  whose logits lie close together, so decisions are not margin-checked.  Each GPU
-  step is instead compared with the oracle run on that step's own GPU inputs
-  (hidden state, cache, prefix length): floating outputs within the tolerance, and
-  every integer output checked exactly against the GPU's own floating outputs
-  (top-k of its logits, tree tokens of its top-k, positions, the carried row).
+  whose logits lie close together, so a chain may legitimately leave the oracle's
+  chain at a near-tie.  The GPU chain is compared with the oracle chain (both started
+  from the drawn inputs; the oracle never sees a GPU value) step by step while the two
+  agree: head logits and node outputs within the tolerance, top-k rows exactly where
+  the oracle's gaps exceed twice the observed logit difference, accepted paths exactly
+  where every edge margin is >= 1e-3.  Once a step's candidates differ, later steps are
+  checked by properties of the GPU's own values only (top-k of its logits, tree tokens
+  of its top-k, positions, path structure, the carried row).
 * A chain equals independent single steps started from the chain's states.
 """
 
@@ -19,7 +22,7 @@ import torch
 from oracle import margins as om
 from oracle import step as ostep
 from oracle import tree as otree
-from tests.parity_util import REL_TOL, SEEDS, bf16_f64, note, rel_err_rows
+from tests.parity_util import REL_TOL, SEEDS, bf16_f64, clear_topk_rows, exact_topk, note, rel_err_rows
 from workloads import make_inputs, step_qkv
 from workloads.configs import get_case
 
@@ -68,59 +71,67 @@ def test_tiny_chain_matches_oracle_chain(run_idx):
     assert rel_err_rows(Kc.reshape(-1, w.H * w.Dh), ref[-1]["K_new"].reshape(-1, w.H * w.Dh)) <= REL_TOL
 
 
-def _exact_topk(row: np.ndarray, k: int) -> np.ndarray:
-    """Indices of the k largest float32 values, equal values by smaller index."""
-    order = np.lexsort((np.arange(row.shape[0]), -row.astype(np.float64)))
-    return order[:k]
-
-
 @pytest.mark.parametrize("run_idx", [0, 1])
 @pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged", "33b-mini"])
-def test_chain_steps_against_oracle_on_gpu_states(name, run_idx):
+def test_chain_against_oracle_chain(name, run_idx):
     seed = SEEDS[name]["seed"]
-    w, inp, qkv, run, loop = _make(name, seed, run_idx)
+    w, inp, qkv, run, loop = _make(name, seed, run_idx, want_logits=True)
     st = loop.step
     tree = otree.build_tree(w)
     T, B = tree.T, w.B
-    compared = 0
+    ref = ostep.decode_loop(w, inp, qkv, tree, run.mode, run.temperature, run.eps, run.delta)
+    together, compared = True, 0
     for s in range(STEPS):
-        # the step's own inputs, as the GPU holds them
-        state = dict(inp)
-        state.update(qkv[s])
-        state["h"] = _host(loop.h[s])
-        state["Kc"], state["Vc"] = _host(st.t["Kc"]), _host(st.t["Vc"])
         L = _host(loop.lens[s]).astype(np.int32)
-        state["prefix_len"] = L
         loop.run_step(s)
-        r = ostep.step(w, state, tree, run.mode, run.temperature, run.eps, run.delta)
         logits = _host(st.logits)
-        assert rel_err_rows(logits, r["logits"]) <= REL_TOL, s
-        o = bf16_f64(_host(st.o)) if w.dtype == "bf16" else _host(st.o).astype(np.float64)
-        assert rel_err_rows(o.reshape(-1, w.Dh), r["o"].reshape(-1, w.Dh)) <= REL_TOL, s
-        # integer outputs, exactly, against the GPU's own values
         topk = _host(st.topk_idx)
-        for b in range(B):
-            for k in range(w.K + 1):
-                assert topk[b, k].tolist() == _exact_topk(logits[b, k], w.k_cfg).tolist(), (s, b, k)
         tokens = _host(loop.tokens[s])
         pos = _host(st.pos)
+        n_acc = _host(loop.n_acc[s])
+        paths = _host(loop.paths[s])
+        hn = _host(loop.h[s + 1])
+        o_bits = _host(st.o).reshape(B, T, w.d)
+        # properties of the GPU's own values, at every step
+        for b in range(B):
+            for k in range(w.K + 1):
+                assert topk[b, k].tolist() == exact_topk(logits[b, k], w.k_cfg).tolist(), (s, b, k)
         for i in range(T):
             assert np.array_equal(tokens[:, i], topk[:, tree.depth[i], tree.rank[i]]), (s, i)
             assert np.array_equal(pos[:, i], L + tree.depth[i]), (s, i)
-        n_acc = _host(loop.n_acc[s])
-        paths = _host(loop.paths[s])
         assert np.array_equal(_host(loop.lens[s + 1]), L + n_acc), s
-        hn = _host(loop.h[s + 1])
-        o_bits = _host(st.o).reshape(B, T, w.d)
-        em = om.edge_margins(r["z"], r["stats"], r["tokens"], tree, run.mode, run.eps, run.delta, run.temperature)
         for b in range(B):
             path = paths[b, :n_acc[b]].tolist()
             assert path[0] == 0 and all(tree.parent[path[j]] == path[j - 1] for j in range(1, len(path))), (s, b)
             assert np.array_equal(hn[b], o_bits[b, path[-1]]), (s, b)
-            # same candidates and clear acceptance decisions: the same accepted path
-            if np.array_equal(tokens[b], r["tokens"][b]) and em[b].min() >= om.MIN_MARGIN:
-                assert path == r["paths"][b], (s, b)
+        if not together:
+            continue
+        # the oracle chain, while the two chains agree
+        r = ref[s]
+        assert rel_err_rows(logits, r["logits"]) <= REL_TOL, s
+        o = bf16_f64(_host(st.o)) if w.dtype == "bf16" else _host(st.o).astype(np.float64)
+        assert rel_err_rows(o.reshape(-1, w.Dh), r["o"].reshape(-1, w.Dh)) <= REL_TOL, s
+        diff = np.abs(logits.astype(np.float64) - r["logits"]).max(axis=-1)
+        clear = clear_topk_rows(r["logits"], diff, w.k_cfg)
+        for b in range(B):
+            for k in range(w.K + 1):
+                if clear[b, k]:
+                    assert topk[b, k].tolist() == r["topk_idx"][b, k].tolist(), (s, b, k)
+        if not np.array_equal(tokens, r["tokens"]):
+            note(f"{name} step {s}: candidates differ at a near-tie; the chains part")
+            together = False
+            continue
+        em = om.edge_margins(r["z"], r["stats"], r["tokens"], tree, run.mode, run.eps, run.delta, run.temperature)
+        dz = np.abs(_host(st.vlogits).astype(np.float64) - r["z"]).reshape(B, -1).max(axis=1)
+        for b in range(B):
+            # an edge test moves by at most 2|dz| (greedy) or 4|dz|/tau (typical, log-prob units)
+            need = max(om.MIN_MARGIN, 4 * dz[b] / (run.temperature or 0.5))
+            if np.array_equal(tokens[b], r["tokens"][b]) and em[b].min() >= need:
+                assert paths[b, :n_acc[b]].tolist() == r["paths"][b], (s, b)
                 compared += 1
+        together = n_acc.tolist() == r["n_acc"] and all(
+            paths[b, :n_acc[b]].tolist() == r["paths"][b] for b in range(B))
+        note(f"{name} step {s}: {int(clear.sum())} of {clear.size} top-k rows clear; chains agree: {together}")
     note(f"{name}: accepted paths compared on {compared} of {STEPS * B} sequence-steps")
     assert compared >= 1
 

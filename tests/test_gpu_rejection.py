@@ -25,19 +25,19 @@ TAU = 0.7
 CASES = ["tiny-fp32-T10", "7b-mini", "7b-B16-mini-paged", "33b-mini"]
 
 
-def _margin_ok(trace, B):
+def _margin_ok(trace, B, scale=1.0):
     m = np.full(B, np.inf)
     for kind, b, u, val in trace:
         if kind == "accept":
             if val < 1.0:
-                m[b] = min(m[b], abs(u - val) / 1e-4)
+                m[b] = min(m[b], abs(u - val) / (1e-4 * scale))
         else:
             c = val
             t = u * c[-1]
             i = int(np.searchsorted(c, t, side="right"))
             lo = c[i - 1] if i > 0 else 0.0
             hi = c[min(i, c.shape[0] - 1)]
-            m[b] = min(m[b], (min(t - lo, hi - t) / c[-1]) / 2e-5)
+            m[b] = min(m[b], (min(t - lo, hi - t) / c[-1]) / (2e-5 * scale))
     return bool((m >= 1.0).all())
 
 
@@ -126,28 +126,32 @@ def test_accept_rejection_all_accepted_and_all_rejected(name):
 
 
 def test_step_with_rejection_acceptance():
-    """The whole step with mode "rejection": the acceptance equals the oracle's walk on the
-    step's own GPU logits, and the compacted cache holds the accepted path."""
+    """The whole step with mode "rejection" against the oracle's walk on the oracle's own
+    step (its head and verifier logits from the drawn inputs): the GPU logits differ from
+    those by up to about 1e-4 of the probabilities involved here (the verifier rows come
+    through bf16 attention), so uniform draws are taken where the oracle's walk keeps ten
+    times the margins of the tests above; the compacted cache holds the accepted path."""
     from medusa_tree_verification_heads_amd.step import VerifyStep
     name = "7b-mini"
     w, inp = case_inputs(name)
-    tree = oracle_shared(name)["tree"]
-    for s in range(60):
+    sh = oracle_shared(name)
+    tree = sh["tree"]
+    for s in range(400):
         u = uniforms(w, 7100 + s)
-        st_inp = dict(inp)
-        st_inp.update(u)
-        st = VerifyStep(w, st_inp, "rejection", TAU)
-        st.run()
-        g = st.outputs()
-        z = g["vlogits"].astype(np.float64)
-        hl = g["logits"].astype(np.float64)
         trace = []
-        ref = ostep.accept_rejection(z, hl, g["tokens"], tree, TAU, u["u_accept"].astype(np.float64),
-                                     u["u_resample"].astype(np.float64), trace=trace)
-        if _margin_ok(trace, w.B):
+        ref = ostep.accept_rejection(sh["z"], sh["logits"], sh["tokens"], tree, TAU,
+                                     u["u_accept"].astype(np.float64), u["u_resample"].astype(np.float64),
+                                     trace=trace)
+        if _margin_ok(trace, w.B, scale=10.0):
             break
     else:
         pytest.fail("no uniform draw with margin")
+    st_inp = dict(inp)
+    st_inp.update(u)
+    st = VerifyStep(w, st_inp, "rejection", TAU)
+    st.run()
+    g = st.outputs()
+    assert np.array_equal(g["tokens"], sh["tokens"])
     for b in range(w.B):
         assert g["n_acc"][b] == ref[1][b]
         assert g["path"][b, :g["n_acc"][b]].tolist() == ref[0][b]
