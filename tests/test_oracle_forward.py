@@ -11,19 +11,30 @@
   of its root path run through the same layers as a plain chain (causal attention),
   the whole-model form of the single-layer per-path check.  A wrong mask, position
   or layer order breaks this at O(1).
+* Chained forward steps (summary page, section 3.2: the next iteration continues from
+  the last accepted token): a one-step chain is the forward step; each step's new
+  length is its length plus its accepted count and the next step's positions start
+  there; the next root token (LM head on the carried row) is the argmax of the
+  verifier row of the last accepted node, since both apply W_lm to the same vector;
+  every layer's cache keeps its earlier rows and gains exactly that layer's keys and
+  values of the accepted path.
 * The interleaved gate/up layout of the library's SwiGLU product is a row
   permutation of [Wg; Wu] with the stated pattern (host-side logic).
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
 
+from oracle import find_seeds
 from oracle import forward as ofw
 from oracle import step as ostep
 from oracle import tree as otree
 from workloads.configs import FORWARD_CASES, scaled
+from workloads import make_inputs
 from workloads.gen import forward_inputs, layer_inputs
 
 
@@ -119,6 +130,62 @@ def test_tree_forward_equals_path_chains(node):
     # one unit apart, far below what a wrong mask, position or layer order produces
     assert np.abs(a - b).max() <= 2e-2 * scale
     assert np.mean(a == b) > 0.9
+
+
+def _chain(name, seed, steps, run_idx):
+    dw = FORWARD_CASES[name]
+    w = dw.base
+    inp = make_inputs(w, seed, parts=("h", "W1", "W2", "Wlm"), steps=steps)
+    fin = forward_inputs(dw, seed)
+    layers = [layer_inputs(dw, seed, l, steps=steps) for l in range(dw.n_layers)]
+    tree = otree.build_tree(w)
+    run = w.accept[run_idx]
+    res = ofw.forward_loop(dw, inp, fin, layers, tree, steps, run.mode, run.temperature, run.eps, run.delta)
+    return dw, inp, fin, layers, tree, run, res
+
+
+@pytest.mark.parametrize("run_idx", [0, 1])
+def test_one_step_forward_chain_is_the_forward(run_idx):
+    dw, inp, fin, layers, tree, run, res = _chain("7b-mini-x2", 21, 1, run_idx)
+    ref = ofw.forward(dw, inp, fin, layers, tree, run.mode, run.temperature, run.eps, run.delta)
+    assert res[0]["paths"] == ref["paths"] and res[0]["n_acc"] == ref["n_acc"]
+    assert np.array_equal(res[0]["tokens"], ref["tokens"]) and np.array_equal(res[0]["xf"], ref["xf"])
+
+
+@pytest.mark.parametrize("run_idx", [0, 1])
+def test_forward_chain_invariants(run_idx):
+    steps = 3
+    dw, inp, fin, layers, tree, run, res = _chain("7b-mini-B2-x2", 23, steps, run_idx)
+    w, T = dw.base, tree.T
+    lens = np.asarray(inp["prefix_len"], dtype=np.int64)
+    prev = [(ostep.to_f64(lw["Kc"]), ostep.to_f64(lw["Vc"])) for lw in layers]
+    for s, r in enumerate(res):
+        assert np.array_equal(np.asarray(r["new_len"]), lens + np.asarray(r["n_acc"]))
+        assert np.array_equal(r["pos"][:, 0], lens)
+        for b in range(w.B):
+            last = r["paths"][b][-1]
+            if s + 1 < steps:
+                assert res[s + 1]["tokens"][b, 0] == int(np.argmax(r["z"][b * T + last]))
+            L = int(lens[b])
+            for l, (Kn, Vn) in enumerate(r["caches"]):
+                Kp, Vp = prev[l]
+                assert np.array_equal(Kn[b, :L], Kp[b, :L]) and np.array_equal(Vn[b, :L], Vp[b, :L])
+                for j, node in enumerate(r["paths"][b]):
+                    assert np.array_equal(Kn[b, L + j], r["k_rot"][l][b, node])
+                    assert np.array_equal(Vn[b, L + j], r["v"][l][b, node])
+                n = len(r["paths"][b])
+                assert np.array_equal(Kn[b, L + n:], Kp[b, L + n:])
+        lens = lens + np.asarray(r["n_acc"])
+        prev = r["caches"]
+
+
+@pytest.mark.parametrize("name", ["7b-mini-x2", "7b-mini-B2-x2"])
+def test_stored_forward_loop_seed_has_margin(name):
+    """The stored three-step forward-chain seeds pass their margin rule (re-checked)."""
+    seeds = json.load(open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "workloads", "seeds.json")))
+    rec = seeds[f"fwd:{name}@loop3"]
+    m = find_seeds.forward_margin(FORWARD_CASES[name], rec["seed"], 3)
+    assert m >= 1.0 and abs(m - rec["margin"]) < 1e-12
 
 
 def test_interleave_gate_up_layout():
