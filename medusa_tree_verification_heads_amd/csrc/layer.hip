@@ -27,10 +27,9 @@
 namespace {
 
 constexpr int kKC = 256;  // inner-dimension chunk staged in LDS
-constexpr int kNB = 64;   // weight rows per workgroup
+constexpr int kNB = 64;   // weight rows per workgroup of the 4-wave tile
 constexpr int kMBL = 64;  // x rows per workgroup
 constexpr int kThreads = 4 * kNB;
-constexpr int kZs = kNB + 1;  // row stride of the fp32 result tile in LDS
 
 enum Epi { kStore = 0, kResidual = 1, kSwiglu = 2, kPartial = 3 };
 
@@ -53,16 +52,20 @@ __device__ __forceinline__ float hi16(uint32_t u) { return bf16_to_f32(u >> 16);
 // x SiLU(x)-gated: silu(g) * u, silu(g) = g / (1 + e^-g).
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
-// grid (ceil(N/64), ceil(M/64), nsplit), block 256 (K2: 512, the tile on 8 waves that
-// split each chunk's k-steps, for grids of at most one workgroup per CU); blockIdx.z > 0
-// only for kPartial.
-template <int EPI, bool K2 = false>
-__global__ __launch_bounds__(K2 ? 2 * kThreads : kThreads) void linear_mfma(LinArgs a) {
-    constexpr int NTH = K2 ? 2 * kThreads : kThreads;
-    constexpr int kZOff = K2 ? 16384 : 0;  // K2: the halves' reduction buffer comes first
-    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, kNB>::kBytes];
-    static_assert(MfmaTile<kKC, kNB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
-    const int n0 = blockIdx.x * kNB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
+// grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.  NW = 0: the
+// 4-wave 64 x 64 tile (NB = 64, block 256).  NW > 0: the tile on 2 NW waves that split
+// each chunk's k-steps (NB = 16 NW, block 128 NW), for grids of at most one workgroup per
+// CU, NW chosen so that the grid covers the CUs.
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW ? 128 * NW : kThreads) void linear_mfma(LinArgs a) {
+    constexpr int NB = NW ? 16 * NW : kNB;
+    constexpr int NTH = NW ? 128 * NW : kThreads;
+    constexpr int kZs = NB + 1;                 // row stride of the fp32 result tile in LDS
+    constexpr int kZOff = NW ? 4096 * NW : 0;   // the k-halves' reduction buffer comes first
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, NB>::kBytes];
+    static_assert(MfmaTile<kKC, NB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
+    static_assert(EPI != kSwiglu || NB % 32 == 0, "SwiGLU tiles hold whole gate/up pairs");
+    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
     const int k0 = s * a.kslice;
     const int klen = min(a.kslice, a.K - k0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -72,19 +75,20 @@ __global__ __launch_bounds__(K2 ? 2 * kThreads : kThreads) void linear_mfma(LinA
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + (wave & 3) * 16 + c16] = acc[mt][e];
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
     };
-    if constexpr (K2)
-        mfma_tile_k2<kKC>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
+    if constexpr (NW > 0)
+        mfma_tile_k2<kKC, NW>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
     else
         mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
     __syncthreads();
 
     if constexpr (EPI == kPartial) {
         // four consecutive columns per item, 16-byte stores
+        constexpr int kItems = NB / 4;
         float* ps = a.part + (size_t)s * a.M * a.N;
-        for (int it = threadIdx.x; it < kMBL * (kNB / 4); it += NTH) {
-            const int row = it >> 4, c0 = 4 * (it & 15);
+        for (int it = threadIdx.x; it < kMBL * kItems; it += NTH) {
+            const int row = it / kItems, c0 = 4 * (it % kItems);
             const int m = m0 + row, n = n0 + c0;
             if (m >= a.M || n >= a.N) continue;
             const float* zr = zt + row * kZs + c0;
@@ -95,26 +99,29 @@ __global__ __launch_bounds__(K2 ? 2 * kThreads : kThreads) void linear_mfma(LinA
 
     if constexpr (EPI == kSwiglu) {
         // Weight rows 32j..32j+15 are gate rows 16j.., rows 32j+16..32j+31 the matching up
-        // rows: output column 16j + i = silu(gate_i) * up_i.  One thread, eight outputs.
-        const int row = threadIdx.x >> 2, og = threadIdx.x & 3;
-        const int jj = og >> 1, i0 = 8 * (og & 1);
-        const int m = m0 + row;
-        if (row < kMBL && m < a.M && n0 + 32 * jj < a.N) {
+        // rows: output column 16j + i = silu(gate_i) * up_i.  One item, eight outputs.
+        constexpr int kItems = NB / 16;
+        const int F = a.N >> 1;
+        for (int it = threadIdx.x; it < kMBL * kItems; it += NTH) {
+            const int row = it / kItems, og = it % kItems;
+            const int jj = og >> 1, i0 = 8 * (og & 1);
+            const int m = m0 + row;
+            if (m >= a.M || n0 + 32 * jj >= a.N) continue;
             const float* zr = zt + row * kZs + 32 * jj + i0;
             uint4 o;
             o.x = pack2(swiglu(zr[0], zr[16]), swiglu(zr[1], zr[17]));
             o.y = pack2(swiglu(zr[2], zr[18]), swiglu(zr[3], zr[19]));
             o.z = pack2(swiglu(zr[4], zr[20]), swiglu(zr[5], zr[21]));
             o.w = pack2(swiglu(zr[6], zr[22]), swiglu(zr[7], zr[23]));
-            const int F = a.N >> 1;
             *(uint4*)(a.y + (size_t)m * F + (n0 >> 1) + 16 * jj + i0) = o;
         }
     } else {
         // Eight consecutive columns per item; the columns are cut into nseg equal
         // segments, segment q going to y + q*M*(N/nseg) as its own [M][N/nseg] matrix.
+        constexpr int kItems = NB / 8;
         const int nsegc = a.N / a.nseg;
-        for (int it = threadIdx.x; it < kMBL * (kNB / 8); it += NTH) {
-            const int row = it >> 3, c0 = 8 * (it & 7);
+        for (int it = threadIdx.x; it < kMBL * kItems; it += NTH) {
+            const int row = it / kItems, c0 = 8 * (it % kItems);
             const int m = m0 + row, n = n0 + c0;
             if (m >= a.M || n >= a.N) continue;
             const float* zr = zt + row * kZs + c0;
@@ -205,6 +212,27 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
 }
 
+// Launches the product with the narrowest tile (3, 4, 6 or 8 groups of 16 weight rows, on
+// twice as many waves) whose grid fits one workgroup per CU, so that one round covers the
+// CUs; a wider grid takes the 4-wave 64 x 64 tile.
+template <int EPI>
+mdt_status launch_linear(const LinArgs& a, int nsplit, hipStream_t hs) {
+    const long rows = (long)((a.M + kMBL - 1) / kMBL) * nsplit;
+    const long cus = mdt_num_cus();
+    auto fits = [&](int nb) { return (a.N + nb - 1) / nb * rows <= cus; };
+    auto go = [&](auto kern, int nb, int threads) {
+        MDT_LAUNCH("linear_mfma", kern, dim3((a.N + nb - 1) / nb, (a.M + kMBL - 1) / kMBL, nsplit), dim3(threads), 0,
+                   hs, a);
+        return mdt_launched("linear_mfma");
+    };
+    if constexpr (EPI != kSwiglu)  // a SwiGLU tile holds whole 32-row gate/up pairs
+        if (fits(48)) return go(linear_mfma<EPI, 3>, 48, 384);
+    if (fits(64)) return go(linear_mfma<EPI, 4>, 64, 512);
+    if (fits(96)) return go(linear_mfma<EPI, 6>, 96, 768);
+    if (fits(128)) return go(linear_mfma<EPI, 8>, 128, 1024);
+    return go(linear_mfma<EPI, 0>, kNB, kThreads);
+}
+
 int kslice_for(int K, int nsplit) {
     int ks = (K + nsplit - 1) / nsplit;
     return (ks + 31) / 32 * 32;
@@ -250,21 +278,10 @@ extern "C" mdt_status mdt_linear(void* stream, int M, int N, int K, const void* 
         MDT_REQUIRE(!residual || nseg == 1, MDT_ERR_VALUE, "a residual needs nseg == 1");
     }
     LinArgs a{(const bf16_t*)x, (const bf16_t*)W, (const bf16_t*)residual, (bf16_t*)y, nullptr, M, N, K, K, nseg};
-    const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, 1);
-    // at most one workgroup per CU: the 8-wave tile hides more latency per SIMD
-    const bool k2 = (long)grid.x * grid.y <= mdt_num_cus();
     const hipStream_t hs = (hipStream_t)stream;
-    if (act == MDT_ACT_SWIGLU) {
-        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kSwiglu, true>), grid, dim3(2 * kThreads), 0, hs, a);
-        else MDT_LAUNCH("linear_mfma", linear_mfma<kSwiglu>, grid, dim3(kThreads), 0, hs, a);
-    } else if (residual) {
-        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kResidual, true>), grid, dim3(2 * kThreads), 0, hs, a);
-        else MDT_LAUNCH("linear_mfma", linear_mfma<kResidual>, grid, dim3(kThreads), 0, hs, a);
-    } else {
-        if (k2) MDT_LAUNCH("linear_mfma", (linear_mfma<kStore, true>), grid, dim3(2 * kThreads), 0, hs, a);
-        else MDT_LAUNCH("linear_mfma", linear_mfma<kStore>, grid, dim3(kThreads), 0, hs, a);
-    }
-    return mdt_launched("linear_mfma");
+    if (act == MDT_ACT_SWIGLU) return launch_linear<kSwiglu>(a, 1, hs);
+    if (residual) return launch_linear<kResidual>(a, 1, hs);
+    return launch_linear<kStore>(a, 1, hs);
 }
 
 extern "C" mdt_status mdt_linear_split(void* stream, int M, int N, int K, const void* x, const void* W, int nsplit,
@@ -277,12 +294,7 @@ extern "C" mdt_status mdt_linear_split(void* stream, int M, int N, int K, const 
     MDT_REQUIRE((K + ks - 1) / ks == nsplit, MDT_ERR_VALUE, "K=%d cannot be cut into %d slices of 32-multiples", K,
                 nsplit);
     LinArgs a{(const bf16_t*)x, (const bf16_t*)W, nullptr, nullptr, part, M, N, K, ks, 1};
-    const dim3 grid((N + kNB - 1) / kNB, (M + kMBL - 1) / kMBL, nsplit);
-    if ((long)grid.x * grid.y * grid.z <= mdt_num_cus())
-        MDT_LAUNCH("linear_mfma", (linear_mfma<kPartial, true>), grid, dim3(2 * kThreads), 0, (hipStream_t)stream, a);
-    else
-        MDT_LAUNCH("linear_mfma", linear_mfma<kPartial>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
-    return mdt_launched("linear_mfma");
+    return launch_linear<kPartial>(a, nsplit, (hipStream_t)stream);
 }
 
 extern "C" mdt_status mdt_rmsnorm(void* stream, int M, int d, const void* x, const void* g, float eps, void* y) {

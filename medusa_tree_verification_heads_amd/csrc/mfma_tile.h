@@ -237,27 +237,31 @@ __device__ __forceinline__ void mfma_tile128(const bf16_t* __restrict__ x, const
     epi(acc);
 }
 
-// The 64 x 64 tile on 8 waves: wave w multiplies weight rows 16 (w % 4) .. +16 against all
-// 64 x rows over the k-steps of half w / 4 of every chunk; at the end the second half's
-// accumulators are added to the first's through LDS (at offset 0, 16 KiB) and epi(acc)
-// runs on waves 0-3 only, with the layout of mfma_tile.  For grids of at most one
-// workgroup per CU, where the 4-wave tile leaves each SIMD a single wave to hide every
-// latency.  Block 512 threads; LDS MfmaTile<KC, NB>::kBytes (NB = 64).
-template <int KC, typename Epi>
+// A 64 x 16NW tile on 2NW waves: wave w multiplies weight rows 16 (w % NW) .. +16 against
+// all 64 x rows over the k-steps of half w / NW of every chunk; at the end the second
+// half's accumulators are added to the first's through LDS (at offset 0, NW * 4 KiB) and
+// epi(acc) runs on waves 0..NW-1 only, with the layout of mfma_tile.  For grids of at
+// most one workgroup per CU, where a 4-wave tile leaves each SIMD a single wave to hide
+// every latency; NW sets the tile width so that such a grid covers the CUs.  Block
+// 128 NW threads; LDS MfmaTile<KC, 16 NW>::kBytes.
+template <int KC, int NW = 4, typename Epi>
 __device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
                                              int d, int ld, int V, int m0, int n0, char* smem, Epi&& epi) {
-    constexpr int NT = 512;
-    constexpr int kStride = MfmaTile<KC, 64>::kStride;
+    constexpr int NB = 16 * NW;
+    constexpr int NT = 128 * NW;
+    constexpr int kStride = MfmaTile<KC, NB>::kStride;
     constexpr int kPR = KC / 8;
-    constexpr int kPPT = 64 * kPR / NT;
-    constexpr int kXPT = 64 * kPR / NT;
+    constexpr int kPPT = NB * kPR / NT;
+    constexpr int kXP = 64 * kPR;                  // x pieces per chunk
+    constexpr int kXPT = (kXP + NT - 1) / NT;      // the last round may be partial
+    constexpr bool kXRag = kXP % NT != 0;
     constexpr int kS = KC / 32;
-    static_assert(KC % 64 == 0 && 64 * kPR % NT == 0, "chunk shape");
+    static_assert(KC % 64 == 0 && NB * kPR % NT == 0, "chunk shape");
     bf16_t* xs = (bf16_t*)smem;
-    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, 64>::kXBytes);
+    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, NB>::kXBytes);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int wr = wave & 3, half = wave >> 2;
+    const int wr = wave % NW, half = wave / NW;
     const int nchunks = (d + KC - 1) / KC;
 
     u32x4 wA[kPPT], wB[kPPT], xr[kXPT];
@@ -269,13 +273,16 @@ __device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const
         const int p = threadIdx.x + NT * j;
         return (size_t)(rows0 + p / kPR) * ld + c * KC + 8 * (p % kPR);
     };
+    // x pieces past the tile's 64 rows (a partial last round) are neither read nor stored
+    auto x_piece = [&](int j) { return !kXRag || j < kXPT - 1 || (int)threadIdx.x + NT * j < kXP; };
     auto load_w = [&](int c, u32x4 (&wv)[kPPT]) {
 #pragma unroll
         for (int j = 0; j < kPPT; ++j) wv[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
     };
     auto load_x = [&](int c) {
 #pragma unroll
-        for (int j = 0; j < kXPT; ++j) xr[j] = *(const u32x4*)(x + (piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
+        for (int j = 0; j < kXPT; ++j)
+            xr[j] = *(const u32x4*)(x + (x_piece(j) && piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
     };
     auto store = [&](int c, const u32x4 (&wv)[kPPT]) {
         const u32x4 z{0, 0, 0, 0};
@@ -283,7 +290,11 @@ __device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const
         for (int j = 0; j < kPPT; ++j) {
             const int p = threadIdx.x + NT * j;
             *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wv[j] : z;
-            *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
+        }
+#pragma unroll
+        for (int j = 0; j < kXPT; ++j) {
+            const int p = threadIdx.x + NT * j;
+            if (x_piece(j)) *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
         }
     };
     f32x4 acc[4];
@@ -324,7 +335,7 @@ __device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const
         store(c + 2, wA);
         __syncthreads();
     }
-    float* red = (float*)smem;  // [4 waves][4 mt][4 e][64 lanes]
+    float* red = (float*)smem;  // [NW waves][4 mt][4 e][64 lanes]
     if (half == 1) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)

@@ -70,7 +70,11 @@ def _dot_err(x, W, K):
     return K * 2.0 ** -23 * (np.abs(x) @ np.abs(W).T)
 
 
-LIN_SHAPES = [(64, 192, 256), (37, 200, 320), (130, 96, 1376), (64, 512, 4096)]
+# On 256 CUs the tile width follows N and the row blocks: 48 columns (the small shapes),
+# 96 (22000; 6000 over three row blocks), 128 (31992) or the 4-wave 64 x 64 tile (40000),
+# each with a ragged last tile.
+LIN_SHAPES = [(64, 192, 256), (37, 200, 320), (130, 96, 1376), (64, 512, 4096), (64, 22000, 256),
+              (130, 6000, 288), (40, 31992, 256), (64, 40000, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", LIN_SHAPES)
@@ -136,7 +140,8 @@ def test_linear_segments(M, N, K):
         assert _bad(_bits(y[q]), ref[:, cols], bound[:, cols]) == 0
 
 
-@pytest.mark.parametrize("M,F,K", [(64, 1376, 512), (37, 48, 256), (64, 11008 // 4, 4096)])
+@pytest.mark.parametrize("M,F,K", [(64, 1376, 512), (37, 48, 256), (64, 11008 // 4, 4096), (64, 11008, 256),
+                                   (50, 16000, 256), (64, 20000, 256)])
 def test_linear_swiglu(M, F, K):
     import medusa_tree_verification_heads_amd as mdt
     note(f"swiglu M={M} F={F} K={K}")

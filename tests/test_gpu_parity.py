@@ -209,6 +209,46 @@ def test_stage_topk_ties_and_fallback(V, k):
             assert tok[b, i] == idx[b, t.depth[i], t.rank[i]]
 
 
+@pytest.mark.parametrize("V,tau", [(20000, 0.7), (32000, 0.0), (16500, 1.0)])
+def test_verify_wide_vocabulary(V, tau):
+    """One 64-row block over a vocabulary whose 64-column grid overfills the CUs (the
+    128-column tile on 16 waves): full logits, row statistics and edge logits against the
+    oracle's definitions, with a ragged last tile (20000, 16500)."""
+    import medusa_tree_verification_heads_amd as mdt
+    from oracle import step as ostep
+    from oracle import tree as otree
+    w = PARITY_CASES["7b-mini"]
+    tree = otree.build_tree(w)
+    dtree = mdt.Tree.for_workload(w).to_device("cuda")
+    d, T = 256, tree.T
+    rng = np.random.default_rng(V)
+    x = ostep.round_bf16(rng.standard_normal((T, d)))
+    W = ostep.round_bf16(rng.standard_normal((V, d)) * d ** -0.5)
+    tok = rng.integers(0, V, (1, T))
+    from workloads.gen import f32_to_bf16_bits
+    xd = torch.from_numpy(f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    Wd = torch.from_numpy(f32_to_bf16_bits(W.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    stats, edge, logits = mdt.verify_logits(xd, Wd, dtree, torch.from_numpy(tok.astype(np.int32)).cuda(), tau,
+                                            want_logits=True)
+    torch.cuda.synchronize()
+    z = x @ W.T
+    assert rel_err_rows(logits.cpu().numpy(), z) <= REL_TOL
+    st = _stats_np(stats.cpu().numpy())
+    scale = np.abs(z).max(axis=1)
+    for r in range(T):
+        ref = ostep.row_stats(z[r], tau)
+        assert abs(st["max"][r] - ref["max"]) <= REL_TOL * scale[r]
+        t2 = np.partition(z[r], -2)[-2:]
+        if t2[1] - t2[0] >= 1e-3:
+            assert st["argmax"][r] == ref["argmax"], r
+        if tau > 0:
+            assert abs(st["logZ"][r] - ref["logZ"]) <= REL_TOL * abs(ref["logZ"])
+            assert abs(st["entropy"][r] - ref["H"]) <= REL_TOL * max(abs(ref["H"]), 1e-3)
+    e = edge.cpu().numpy()
+    oe = ostep.edge_logits(z, tok, tree)
+    assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
+
+
 @pytest.mark.parametrize("name,run_idx", RUNS)
 def test_stage_verify_accept_from_oracle_x(name, run_idx):
     import medusa_tree_verification_heads_amd as mdt
