@@ -563,7 +563,8 @@ def linear_split(x, W, nsplit: int, out=None, stream=None):
 def auto_split(M: int, N: int, K: int, device=None) -> int:
     """Slices for a product whose 64 x 64 output tiles are too few to fill the GPU: grow
     while the workgroups stay within one per compute unit (where the library runs the
-    tile on 8 waves) and slices stay >= 512 long."""
+    tile on twice as many waves, splitting each chunk's k-steps) and slices stay >= 512
+    long."""
     cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
     tiles = -(-N // 64) * -(-M // 64)
     s = 1

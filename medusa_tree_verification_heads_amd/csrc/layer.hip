@@ -15,7 +15,8 @@
 //
 // The linear calls stream W once: with M <= 64 rows (a 64-node tree) every weight byte
 // is read once and used for 64 rows, so a product is bound by HBM, not by the matrix
-// cores.  Each workgroup multiplies a 64 x 64 tile (mfma_tile).  A weight with few
+// cores.  Each workgroup multiplies 64 x rows by 48 to 128 weight rows (mfma_tile.h; the
+// narrowest width whose grid still has one workgroup per CU).  A weight with few
 // 64-row blocks (the d x d output projection: 64 blocks for 256 CUs) has its inner
 // dimension cut into slices on more workgroups; their fp32 partial tiles are added
 // by the next call, which reads whole rows anyway (mdt_add_rmsnorm: the residual add
