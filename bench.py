@@ -11,7 +11,9 @@ events on its own stream (hipExtLaunchKernelGGL), giving each kernel's duration;
 the roofline object uses the dominant kernel's (the W2 head GEMV stream).  The
 timed region is K replays of a HIP graph that holds the whole step, between two
 torch.cuda.synchronize() calls (the events add dispatch gaps, so they stay out
-of it).  The CPU oracle is timed on the host on whole steps of the same
+of it); afterwards K more replays, each between two events, give the median, p10
+and p90 per step (``replay_us``), and a 1 GiB device copy gives the copy bandwidth
+that ``step_hbm.frac_of_copy`` divides by.  The CPU oracle is timed on the host on whole steps of the same
 workload for about 10 s.  A report of chained steps (``decode_loop``: each step
 starts from the previous step's last accepted node, replayed as one graph) gives
 the time per chained step and the synthetic acceptance; a report of the full
@@ -228,6 +230,27 @@ def full_depth_report(w, seed, step, mode, tau, eps, delta, replays):
     return rep
 
 
+def copy_bandwidth(mib: int = 1024, reps: int = 5) -> float:
+    """HBM bandwidth of a plain device-to-device copy of `mib` MiB (bytes read + written per
+    second, best of `reps` copies timed with events); the buffers are freed afterwards."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / best / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +327,7 @@ def main():
     per_kernel_us = {k: round(1e3 * float(np.mean(v)), 2) for k, v in per_kernel.items()}
     log(f"profiled eager pass: {eager_ms * 1e3:.1f} us/step; kernels {per_kernel_us}")
 
+    replay_us = None
     if args.no_graph:
         ms_per_step, timing = eager_ms, "eager launches with per-kernel events"
     else:
@@ -326,7 +350,19 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
         timing = "HIP-graph replay of the six calls"
+        # distribution (outside the timed region): every replay between two events
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        replay_us = {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+                     "p90": round(float(np.percentile(us, 90)), 2), "replays": args.steps}
+        log(f"per-replay us: {replay_us}")
     log(f"timed {args.steps} steps ({timing}): {ms_per_step * 1e3:.1f} us/step")
+    copy_gbps = copy_bandwidth()
 
     loop_rep = None
     if not args.no_graph and not args.no_loop:
@@ -370,8 +406,10 @@ def main():
                    "delta": delta, "seed": seed, "parallelism": "none (1 GPU)"},
         "tree_tokens_per_s": round(1e3 / ms_per_step * w.B * T, 1),
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved": round(step_gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(step_gbps / PEAK_HBM_GBPS, 4)},
+                     "unit": "GB/s", "frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(step_gbps / copy_gbps, 4)},
         "timing": timing,
+        "replay_us": replay_us,
         "per_kernel_us": per_kernel_us,
         "eager_ms_per_step": round(eager_ms, 5),
         "n_acc": step.n_acc.cpu().tolist()[:8],
