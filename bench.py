@@ -132,6 +132,7 @@ def decode_loop_report(w, inp, seed, step, mode, tau, eps, delta, replays):
     return {"steps": LOOP_STEPS, "us_per_step": round(us, 2), "mean_accepted_per_step": round(mean_acc, 3),
             "accepted_tokens_per_s": round(1e6 / us * mean_acc * w.B, 1),
             "n_acc_per_step": n_acc[:, 0].tolist(),
+            "lm_head": "steps after the first take the LM-head row from the verifier (next_logits)",
             "note": "synthetic random weights: the acceptance is not that of a trained model"}
 
 

@@ -11,6 +11,7 @@
  *   mdt_kv_compact        append the accepted path's keys/values to the cache
  *   mdt_accept_compact    the last two in one launch (same results)
  *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
+ *   mdt_next_logits       the next step's LM-head row, taken from the verifier
  *   mdt_accept_rejection  rejection-sampling acceptance on the tree (a third acceptance rule)
  *   mdt_kv_compact_layers mdt_kv_compact for every layer of a model in one launch
  *   mdt_embed, mdt_rmsnorm, mdt_add_rmsnorm, mdt_linear, mdt_linear_split
@@ -215,11 +216,12 @@ mdt_status mdt_tree_dev_init(const mdt_tree_host* tree, const void* dev_image, m
  * probabilities where needed.
  *
  *  dt      MDT_F32 or MDT_BF16: storage of h and all weights
- *  B,d,V,K sequences (1..64), hidden size (multiple of 8), vocabulary (>= 1), heads (1..MDT_MAX_HEADS)
+ *  B,d,V,K sequences (1..1024), hidden size (multiple of 8), vocabulary (>= 1), heads (1..MDT_MAX_HEADS)
  *  h       device [B][d]
  *  W1      device [K][d][d]   W1[k][out][in]
  *  W2      device [K][V][d]   row v of head k
- *  Wlm     device [V][d]
+ *  Wlm     device [V][d], or NULL: slot 0 is then not written (a chained step whose slot 0
+ *          already holds the LM-head row of its hidden state, see mdt_next_logits)
  *  logits  device f32 [B][K+1][V]  (output; slot 0 = LM head)
  *  ws      device workspace >= mdt_medusa_heads_workspace(B, d, K) bytes; holds the fp32
  *          head activations a[B][K][d] between the two kernels
@@ -459,6 +461,26 @@ mdt_status mdt_accept_rejection(void* stream, int B, int V, int K, const mdt_tre
  */
 mdt_status mdt_next_state(void* stream, mdt_dtype dt, int B, int T, int d, const void* x, const int32_t* path,
                           int path_stride, const int32_t* n_acc, void* h_next);
+
+/*
+ * LM-head slot of the next step: head_logits[b][0][:] = vlogits[b*T + path[b][n_acc[b] - 1]][:].
+ * The next step's hidden state is that node's output (mdt_next_state), and its LM-head
+ * row W_lm h_next is the verifier row mdt_verify_logits already computed for the node
+ * (summary page, section 3.2: the next root is the original model's prediction at the
+ * last accepted token).  A chained step can then call mdt_medusa_heads with Wlm = NULL
+ * and skip one stream of W_lm.
+ *  B, T, V, K   sequences, tree nodes (1..MDT_MAX_NODES), vocabulary, heads
+ *  vlogits      device f32 [B*T][V]: the full logits output of mdt_verify_logits
+ *  path, path_stride, n_acc
+ *               device, as written by mdt_accept_path / mdt_accept_compact
+ *  head_logits  device f32 [B][K+1][V]; only slot 0 of each sequence is written; must not
+ *               overlap vlogits
+ * A sequence whose n_acc is outside 1..path_stride or whose last path node is outside
+ * 0..T-1 gets a row of zeros.
+ * Errors: MDT_ERR_SHAPE, MDT_ERR_NULL, MDT_ERR_VALUE (overlap).
+ */
+mdt_status mdt_next_logits(void* stream, int B, int T, int V, int K, const float* vlogits, const int32_t* path,
+                           int path_stride, const int32_t* n_acc, float* head_logits);
 
 /*
  * mdt_kv_compact for a model of n_layers layers in one launch: layer l reads

@@ -96,6 +96,8 @@ _SIGS = [
                                    c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
     ("mdt_next_state", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                c_void_p]),
+    ("mdt_next_logits", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                                c_void_p]),
     ("mdt_accept_rejection", c_int, [c_void_p, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
                                      c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("mdt_kv_compact_layers", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
@@ -296,9 +298,10 @@ def medusa_heads_workspace(B, d, K) -> int:
 
 
 def medusa_heads(h, W1, W2, Wlm, logits=None, ws=None, stream=None):
-    """logits[b][0] = Wlm h_b; logits[b][k] = W2_k (SiLU(W1_k h_b) + h_b)."""
+    """logits[b][0] = Wlm h_b; logits[b][k] = W2_k (SiLU(W1_k h_b) + h_b).  Wlm None:
+    slot 0 is left as it is."""
     B, d = h.shape
-    K, V = W1.shape[0], Wlm.shape[0]
+    K, V = W1.shape[0], W2.shape[1]
     if logits is None:
         logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=h.device)
     ws, nb = _ws(medusa_heads_workspace(B, d, K), h.device, ws)
@@ -449,6 +452,16 @@ def next_state(x, path, n_acc, out=None, stream=None):
     _check(lib.mdt_next_state(_stream(stream), _dtype_code(x), B, T, d, _ptr(x), _ptr(path), path.shape[1],
                               _ptr(n_acc), _ptr(out)), "next_state")
     return out
+
+
+def next_logits(vlogits, path, n_acc, head_logits, stream=None):
+    """head_logits[b][0] = the verifier row (vlogits [B*T][V] or [B][T][V]) of sequence
+    b's deepest accepted node; returns head_logits."""
+    B, K1, V = head_logits.shape
+    T = vlogits.numel() // (B * V)
+    _check(lib.mdt_next_logits(_stream(stream), B, T, V, K1 - 1, _ptr(vlogits), _ptr(path), path.shape[1],
+                               _ptr(n_acc), _ptr(head_logits)), "next_logits")
+    return head_logits
 
 
 def accept_compact(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps, delta, temperature, k_rot, v,

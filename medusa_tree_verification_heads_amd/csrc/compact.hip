@@ -14,7 +14,9 @@
 // mdt_next_state: the node output of a sequence's deepest accepted node becomes the
 // hidden state the next step starts from (summary page, section 3.2: the next
 // iteration continues from the last accepted token).  One workgroup per sequence
-// copies that row with 16-byte moves.
+// copies that row with 16-byte moves.  mdt_next_logits copies the same node's verifier
+// logits row into the next step's LM-head slot (that row is the LM head applied to the
+// next hidden state), spread over many workgroups.
 #include "kv_slot.h"
 
 namespace {
@@ -61,6 +63,28 @@ __global__ __launch_bounds__(256) void next_state_kernel(const uint4* __restrict
     const long src = ((long)b * T + (ok ? node : 0)) * row_vec;
     uint4* dst = h_next + (long)b * row_vec;
     for (int e = threadIdx.x; e < row_vec; e += blockDim.x) dst[e] = ok ? x[src + e] : make_uint4(0, 0, 0, 0);
+}
+
+// grid (ceil(V / kNextLogitsPerWg), B): each thread moves four elements, all four loads
+// issued before the stores.
+constexpr int kNextLogitsPerWg = 4 * 256;
+
+__global__ __launch_bounds__(256) void next_logits_kernel(const float* __restrict__ z, const int32_t* __restrict__ path,
+                                                            int path_stride, const int32_t* __restrict__ n_acc, int T,
+                                                            int V, long out_stride, float* __restrict__ out) {
+    const int b = blockIdx.y;
+    const int n = n_acc[b];
+    const int node = path[(long)b * path_stride + min(max(n - 1, 0), path_stride - 1)];
+    const bool ok = n >= 1 && n <= path_stride && node >= 0 && node < T;
+    const float* src = z + ((long)b * T + (ok ? node : 0)) * V;
+    float* dst = out + (long)b * out_stride;
+    const int e0 = blockIdx.x * kNextLogitsPerWg + threadIdx.x;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = ok && e0 + 256 * j < V ? src[e0 + 256 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (e0 + 256 * j < V) dst[e0 + 256 * j] = v[j];
 }
 
 }  // namespace
@@ -154,4 +178,20 @@ extern "C" mdt_status mdt_next_state(void* stream, mdt_dtype dt, int B, int T, i
     MDT_LAUNCH("next_state_kernel", next_state_kernel, dim3(B), dim3(256), 0, (hipStream_t)stream, (const uint4*)x,
                path, path_stride, n_acc, T, (int)(row_bytes / 16), (uint4*)h_next);
     return mdt_launched("next_state_kernel");
+}
+
+extern "C" mdt_status mdt_next_logits(void* stream, int B, int T, int V, int K, const float* vlogits,
+                                      const int32_t* path, int path_stride, const int32_t* n_acc,
+                                      float* head_logits) {
+    MDT_REQUIRE(B >= 1 && B <= 65535 && T >= 1 && T <= MDT_MAX_NODES && V >= 1 && V <= (1 << 30) && K >= 1 &&
+                    K <= MDT_MAX_HEADS,
+                MDT_ERR_SHAPE, "bad shape B=%d T=%d V=%d K=%d", B, T, V, K);
+    MDT_REQUIRE(path_stride >= 1 && path_stride <= MDT_MAX_NODES, MDT_ERR_SHAPE, "path_stride out of range");
+    MDT_REQUIRE(vlogits && path && n_acc && head_logits, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(head_logits + (size_t)B * (K + 1) * V <= vlogits || vlogits + (size_t)B * T * V <= head_logits,
+                MDT_ERR_VALUE, "head_logits must not overlap vlogits");
+    MDT_LAUNCH("next_logits_kernel", next_logits_kernel, dim3((V + kNextLogitsPerWg - 1) / kNextLogitsPerWg, B),
+               dim3(256), 0, (hipStream_t)stream, vlogits, path, path_stride, n_acc, T, V, (long)(K + 1) * V,
+               head_logits);
+    return mdt_launched("next_logits_kernel");
 }

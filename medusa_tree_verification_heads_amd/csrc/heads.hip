@@ -291,7 +291,7 @@ mdt_status run(hipStream_t stream, int B, int d, int V, int K, const void* h, co
         S.nrows = d;
         S.silu = 1;
     }
-    {
+    if (Wlm) {  // NULL: the LM-head slot is left as it is
         GemvSeg& S = P1.seg[P1.nseg++];
         S.W = Wlm;
         S.x = h;
@@ -333,7 +333,7 @@ extern "C" mdt_status mdt_medusa_heads(void* stream, mdt_dtype dt, int B, int d,
     MDT_REQUIRE(d >= 8 && d % 8 == 0 && d <= 16384, MDT_ERR_SHAPE, "d=%d must be a multiple of 8 in 8..16384", d);
     MDT_REQUIRE(V >= 1, MDT_ERR_SHAPE, "V=%d must be >= 1", V);
     MDT_REQUIRE(K >= 1 && K <= MDT_MAX_HEADS, MDT_ERR_SHAPE, "K=%d out of range 1..%d", K, MDT_MAX_HEADS);
-    MDT_REQUIRE(h && W1 && W2 && Wlm && logits, MDT_ERR_NULL, "a tensor pointer is NULL");
+    MDT_REQUIRE(h && W1 && W2 && logits, MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_REQUIRE(mdt_aligned16(h) && mdt_aligned16(W1) && mdt_aligned16(W2) && mdt_aligned16(Wlm) &&
                     mdt_aligned16(logits),
                 MDT_ERR_ALIGN, "tensor pointers must be 16-byte aligned");

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(kThreads) void heads_mfma_w2(HeadsArgs a) {
 template <int MT1, int MT2>
 mdt_status launch_pair(const HeadsArgs& a, hipStream_t s) {
     const int lm_tiles = (a.V + kNB - 1) / kNB;
-    MDT_LAUNCH("heads_mfma_w1_lm", heads_mfma_w1_lm<MT1>, dim3(a.w1_tiles + lm_tiles), dim3(kThreads), 0, s, a);
+    // no W_lm: launch 1 streams W1 only and the LM-head slot is left as it is
+    MDT_LAUNCH("heads_mfma_w1_lm", heads_mfma_w1_lm<MT1>, dim3(a.w1_tiles + (a.Wlm ? lm_tiles : 0)), dim3(kThreads),
+               0, s, a);
     mdt_status st = mdt_launched("heads_mfma_w1_lm");
     if (st != MDT_OK) return st;
     MDT_LAUNCH("heads_mfma_w2", heads_mfma_w2<MT2>, dim3(lm_tiles, a.K), dim3(kThreads), 0, s, a);

@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path,
-               accept_rejection, kv_compact, medusa_heads, next_state,
+               accept_rejection, kv_compact, medusa_heads, next_logits, next_state,
                medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace)
 
@@ -80,9 +80,11 @@ class VerifyStep:
         self.ws_verify = new_workspace(verify_logits_workspace(dt, B, T, d, V), dev)
 
     def run(self, stream=None, h=None, qkv=None, prefix_len=None, new_prefix_len=None, tokens=None, path=None,
-            n_acc=None):
+            n_acc=None, vlogits=None, lm_head=True):
         """Enqueue one step.  The keyword arguments replace the step's own input or output
-        tensors for this call (a chain of steps passes each step's own)."""
+        tensors for this call (a chain of steps passes each step's own); ``vlogits`` is a
+        buffer for the verifier's full logits, and ``lm_head=False`` leaves the heads'
+        slot 0 as it is (already filled by ``next_logits``)."""
         t, w = self.t, self.w
         h = t["h"] if h is None else h
         q, k, v = (t["q"], t["k"], t["v"]) if qkv is None else qkv
@@ -91,16 +93,18 @@ class VerifyStep:
         tokens = self.tokens if tokens is None else tokens
         path = self.path if path is None else path
         n_acc = self.n_acc if n_acc is None else n_acc
-        medusa_heads(h, t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
+        vlogits = self.vlogits if vlogits is None else vlogits
+        medusa_heads(h, t["W1"], t["W2"], t["Wlm"] if lm_head else None, logits=self.logits, ws=self.ws_heads,
+                     stream=stream)
         topk_tree_expand(self.logits, w.k_cfg, self.tree, prefix_len, self.topk_idx, self.topk_val, tokens,
                          self.pos, ws=self.ws_topk, stream=stream)
         tree_attention(q, k, v, self.cache, prefix_len, self.tree, w.rope_theta, out=self.o,
                        k_rot=self.k_rot, ws=self.ws_attn, stream=stream)
         x = self.o.view(w.B * self.tree.T, w.d)
         verify_logits(x, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats, edge=self.edge,
-                      logits=self.vlogits, want_logits=self.vlogits is not None, ws=self.ws_verify, stream=stream)
+                      logits=vlogits, want_logits=vlogits is not None, ws=self.ws_verify, stream=stream)
         if self.rejection:
-            accept_rejection(self.vlogits, self.logits, tokens, self.tree, self.temperature, self.u_accept,
+            accept_rejection(vlogits, self.logits, tokens, self.tree, self.temperature, self.u_accept,
                              self.u_resample, path=path, n_acc=n_acc, next_token=self.next_token, stream=stream)
             kv_compact(path, n_acc, self.k_rot, v, self.cache, prefix_len, new_len, stream=stream)
             return
@@ -140,11 +144,17 @@ class DecodeLoop:
     tree's q/k/v inputs of every step are given (``qkv_steps``).  Every step reads
     and writes its own prefix-length, hidden-state, token, path and n_acc tensors,
     so ``run()`` can be repeated (or replayed as a graph) from the same start.
+
+    With ``reuse_lm_head`` (the default) the verifier also writes its full logits, and
+    step s+1's LM-head slot is step s's verifier row of the same node (``next_logits``,
+    enqueued at the start of step s+1, so that step s's own slot stays readable until
+    then): that row is W_lm applied to the next hidden state, so the heads skip their
+    W_lm stream on every step after the first.
     """
 
     def __init__(self, w, inp: dict, qkv_steps, mode: str = "greedy", temperature: float = 0.0, eps: float = 0.09,
                  delta: float = 0.3, device="cuda", fused_tail: bool = True, want_logits: bool = False,
-                 step: VerifyStep = None):
+                 step: VerifyStep = None, reuse_lm_head: bool = True):
         # an existing step (same inputs) can be reused: the chain only adds its own state tensors
         self.step = step or VerifyStep(w, inp, mode, temperature, eps, delta, device, want_logits=want_logits,
                                        fused_tail=fused_tail)
@@ -159,11 +169,19 @@ class DecodeLoop:
         self.tokens = torch.empty((S, B, T), **i32)
         self.paths = torch.empty((S, B, st.path.shape[1]), **i32)
         self.n_acc = torch.empty((S, B), **i32)
+        self.reuse = reuse_lm_head
+        self.vlogits = st.vlogits
+        if self.reuse and self.vlogits is None:
+            self.vlogits = torch.empty((B * T, w.V), dtype=torch.float32, device=dev)
 
     def run_step(self, s: int, stream=None):
         st, w = self.step, self.step.w
+        reuse = self.reuse and s > 0
+        if reuse:
+            next_logits(self.vlogits, self.paths[s - 1], self.n_acc[s - 1], st.logits, stream=stream)
         st.run(stream, h=self.h[s], qkv=self.qkv[s], prefix_len=self.lens[s], new_prefix_len=self.lens[s + 1],
-               tokens=self.tokens[s], path=self.paths[s], n_acc=self.n_acc[s])
+               tokens=self.tokens[s], path=self.paths[s], n_acc=self.n_acc[s], vlogits=self.vlogits,
+               lm_head=not reuse)
         next_state(st.o.view(w.B, st.tree.T, w.d), self.paths[s], self.n_acc[s], out=self.h[s + 1], stream=stream)
 
     def run(self, stream=None):

@@ -34,3 +34,20 @@ def test_heads_batch_matches_oracle(B):
     err = np.abs(g - ref).max(axis=2) / np.abs(ref).max(axis=2)
     note(f"heads B={B}: max rel err {err.max():.2e}")
     assert err.max() <= 1e-4
+
+
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_heads_without_lm_head(B):
+    """Wlm = NULL: slot 0 keeps what it held, slots 1..K are bit for bit those of the full call
+    (the vector-ALU path below four sequences, the matrix-core path from four on)."""
+    import medusa_tree_verification_heads_amd as mdt
+    from medusa_tree_verification_heads_amd.step import to_device
+    w = scaled(PARITY_CASES["7b-mini"], name=f"7b-mini-B{B}", B=B)
+    inp = make_inputs(w, 5151 + B, parts=("h", "W1", "W2", "Wlm"))
+    t = {k: to_device(inp[k], "cuda") for k in ("h", "W1", "W2", "Wlm")}
+    full = mdt.medusa_heads(t["h"], t["W1"], t["W2"], t["Wlm"])
+    part = torch.full_like(full, 7.5)
+    mdt.medusa_heads(t["h"], t["W1"], t["W2"], None, logits=part)
+    torch.cuda.synchronize()
+    assert torch.all(part[:, 0] == 7.5)
+    assert torch.equal(part[:, 1:], full[:, 1:])

@@ -38,21 +38,23 @@ def _host(x):
     return x.cpu().numpy()
 
 
-def _make(name, seed, run_idx, want_logits=False):
+def _make(name, seed, run_idx, want_logits=False, reuse=True):
     from medusa_tree_verification_heads_amd.step import DecodeLoop
     w = get_case(name)
     inp = make_inputs(w, seed, steps=STEPS)
     qkv = [step_qkv(w, seed, s) for s in range(STEPS)]
     run = w.accept[min(run_idx, len(w.accept) - 1)]
     note(f"loop {name} seed {seed} {run}")
-    loop = DecodeLoop(w, inp, qkv, run.mode, run.temperature, run.eps, run.delta, want_logits=want_logits)
+    loop = DecodeLoop(w, inp, qkv, run.mode, run.temperature, run.eps, run.delta, want_logits=want_logits,
+                      reuse_lm_head=reuse)
     return w, inp, qkv, run, loop
 
 
+@pytest.mark.parametrize("reuse", [True, False])
 @pytest.mark.parametrize("run_idx", [0, 1])
-def test_tiny_chain_matches_oracle_chain(run_idx):
+def test_tiny_chain_matches_oracle_chain(run_idx, reuse):
     seed = SEEDS["tiny-fp32-T10@loop3"]["seed"]
-    w, inp, qkv, run, loop = _make("tiny-fp32-T10", seed, run_idx)
+    w, inp, qkv, run, loop = _make("tiny-fp32-T10", seed, run_idx, reuse=reuse)
     loop.run()
     tree = otree.build_tree(w)
     ref = ostep.decode_loop(w, inp, qkv, tree, run.mode, run.temperature, run.eps, run.delta)
@@ -140,7 +142,9 @@ def test_chain_against_oracle_chain(name, run_idx):
 def test_chain_equals_independent_steps(name):
     from medusa_tree_verification_heads_amd.step import VerifyStep
     seed = SEEDS[name]["seed"]
-    w, inp, qkv, run, loop = _make(name, seed, 1)
+    # without the LM-head reuse: every step is then exactly the single step (with it, the
+    # LM-head slot comes from the verifier's fp32 sums instead of the head GEMV's)
+    w, inp, qkv, run, loop = _make(name, seed, 1, reuse=False)
     for s in range(STEPS):
         state = dict(inp)
         state.update(qkv[s])
@@ -179,3 +183,29 @@ def test_chain_repeats_and_replays_as_graph():
             assert np.array_equal(a, b)
         loop.run()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged"])
+def test_reused_lm_head_slot(name):
+    """With the LM-head reuse, step s >= 1's slot 0 is bit for bit step s-1's verifier row
+    of each sequence's deepest accepted node, the other slots are the heads of the carried
+    hidden state, and the root token is that row's top token."""
+    import medusa_tree_verification_heads_amd as mdt
+    w, inp, qkv, run, loop = _make(name, SEEDS[name]["seed"], 1)
+    st = loop.step
+    T = st.tree.T
+    prev = None
+    for s in range(STEPS):
+        loop.run_step(s)
+        logits = _host(st.logits)
+        if prev is not None:
+            z, paths, n_acc = prev
+            for b in range(w.B):
+                last = paths[b, n_acc[b] - 1]
+                assert np.array_equal(logits[b, 0], z[b * T + last]), (s, b)
+                assert _host(loop.tokens[s])[b, 0] == exact_topk(z[b * T + last], 1)[0]
+            # slots 1..K: the heads on the carried state, as a fresh heads call computes them
+            ref = mdt.medusa_heads(loop.h[s], st.t["W1"], st.t["W2"], st.t["Wlm"])
+            assert np.array_equal(logits[:, 1:], _host(ref)[:, 1:]), s
+        prev = (_host(loop.vlogits), _host(loop.paths[s]), _host(loop.n_acc[s]))
+

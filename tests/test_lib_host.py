@@ -177,6 +177,13 @@ def test_next_state_and_rejection_validation():
     assert n(None, 1, 1, 64, 4096, P, P, 0, P, P) == -2          # path_stride
     assert n(None, 1, 1, 64, 4096, None, P, 5, P, P) == -1
     assert n(None, 1, 1, 64, 4096, MIS, P, 5, P, P) == -4
+    nl = mdt.lib.mdt_next_logits
+    Z, O = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 30)    # non-overlapping stand-ins, never dereferenced
+    assert nl(None, 1, 0, 32000, 4, Z, P, 5, P, O) == -2           # T
+    assert nl(None, 1, 64, 32000, 0, Z, P, 5, P, O) == -2          # K
+    assert nl(None, 1, 64, 32000, 4, Z, P, 0, P, O) == -2          # path_stride
+    assert nl(None, 1, 64, 32000, 4, None, P, 5, P, O) == -1
+    assert nl(None, 1, 64, 32000, 4, Z, P, 5, P, ctypes.c_void_p((1 << 20) + 4096)) == -6   # overlap
     d = _tree_desc()
     r = mdt.lib.mdt_accept_rejection
     def rej(B=1, V=32000, K=4, tau=0.7, stride=5, vl=P):
