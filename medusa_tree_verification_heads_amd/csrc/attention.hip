@@ -389,9 +389,9 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;  // of query qi, replicated over g
 
-    // One staged tile: keys base..base+63, nvalid of them real.  Scores are kept in log2
-    // units (scale * log2 e folded into one multiply), so the softmax uses exp2.  Full
-    // prefix tiles skip the masking; the last prefix tile and tree tiles (bitmask) do not.
+    // One staged tile: keys base..base+63, nvalid of them real.  The softmax runs in log2
+    // units (scale * log2 e folded into the fma that forms each exponent), so it uses exp2.
+    // Full prefix tiles skip the masking; the last prefix tile and tree tiles (bitmask) do not.
     const float sl2 = scale * 1.4426950408889634f;
     auto attend_tile = [&](int base, int nvalid, bool masked) {
         f32x4 sacc[4];
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
                 for (int e = 0; e < 4; ++e) {
                     const int jj = kb * 16 + 4 * g + e;
                     const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
-                    const float sv = ok ? sacc[kb][e] * sl2 : -INFINITY;
+                    const float sv = ok ? sacc[kb][e] : -INFINITY;
                     sacc[kb][e] = sv;
                     tmax = fmaxf(tmax, sv);
                 }
@@ -423,22 +423,25 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sacc[kb][e] *= sl2;
-                    tmax = fmaxf(tmax, sacc[kb][e]);
-                }
+                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[kb][e]);
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // the raw scores' maximum scaled once: rounding is monotone, so this is the maximum
+        // of the scaled scores, and each score is scaled inside its exponent's fma
+        tmax *= sl2;
         const float m_new = fmaxf(m_run, tmax);
         const bool live = m_new != -INFINITY;
-        const float corr = live ? exp2f(m_run - m_new) : 1.f;
+        // v_exp_f32 itself: exp2f adds a rescaling around it for results below 2^-126, which
+        // cannot matter next to the row maximum's weight of 1 and cost five more VALU
+        // operations per score
+        const float corr = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         float tsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = live ? exp2f(sacc[kb][e] - m_new) : 0.f;
+                const float p = live ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, -m_new)) : 0.f;
                 sacc[kb][e] = p;
                 tsum += p;
             }
@@ -446,8 +449,11 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
         tsum += __shfl_xor(tsum, 32, 64);
         l_run = l_run * corr + tsum;
         m_run = m_new;
+        // corr is exactly 1 unless the running maximum grew, which over a long prefix is rare:
+        // the wave skips the 32 multiplies when no lane needs them
+        if (__any(corr != 1.f))
 #pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[db] *= corr;
+            for (int db = 0; db < 8; ++db) oacc[db] *= corr;
         // O^T += V^T P^T; within a 32-key step the key order is 4g+t (t<4), then 16+4g+(t-4)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
