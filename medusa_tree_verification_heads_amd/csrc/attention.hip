@@ -230,7 +230,9 @@ struct AttnArgs {
     double inv_freq[kDh / 2];  // theta^(-2m/Dh), computed once on the host
 };
 
-// One (sequence, head, key split) per workgroup; NWB waves, wave w owns queries 16w..16w+15.
+// One (sequence, head, key split) per workgroup; NWB waves, wave w owns the QT query tiles
+// 16 (QT w + t) .. +15, t < QT.  With QT = 2 every K and V fragment a wave reads from LDS
+// feeds both of its tiles, and 8 waves cover a 256-node tree with registers to spare.
 // Workgroups 0..nsplit-1 attend to prefix key ranges; workgroup nsplit rotates the tree
 // keys (writing k_rot) and attends to them, masked by the ancestor-or-self bitmask.
 // Grid (nsplit + 1, H, B); all partials are merged by attn_combine.
@@ -240,7 +242,7 @@ struct AttnArgs {
 // a wave wait for every load in flight.  Prefix pieces outside the split or on an
 // unmapped page read the first 16 bytes of q instead (always present) and are zeroed
 // when stored (a validity bit per piece); the pages of a paged cache are looked up in LDS.
-template <int NWB, bool PAGED>
+template <int NWB, bool PAGED, int QT = 1>
 __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     constexpr int NT = 64 * NWB;
     constexpr int PPT = kTile * (kDh / 8) / NT;  // 16-byte K pieces per thread per tile
@@ -265,21 +267,25 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     const int psz = PAGED ? A.cache.page_size : 1;
     const int pg0 = j_begin / psz;
 
-    // this wave's 16 queries (loaded first, so that waiting for them waits for nothing else):
-    // lane holds query qi, dims 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
-    const int qi = wave * 16 + c16;
-    const bool q_ok = qi < T;
-    const int qc = q_ok ? qi : 0;
-    u32x4 bq[4];
-    uint64_t qa[MDT_MAX_NODES / 64];
-    {
+    // this wave's queries (loaded first, so that waiting for them waits for nothing else):
+    // in tile t the lane holds query qi[t], dims 32s + 8g .. +8; s = 0,1 hold x_m and
+    // s = 2,3 hold x_{m+64}
+    int qi[QT], dq_raw[QT];
+    bool q_ok[QT];
+    u32x4 bq[QT][4];
+    uint64_t qa[QT][MDT_MAX_NODES / 64];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        qi[t] = (wave * QT + t) * 16 + c16;
+        q_ok[t] = qi[t] < T;
+        const int qc = q_ok[t] ? qi[t] : 0;
         const long node = (((long)b * T + qc) * H + h) * kDh;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
+        for (int s = 0; s < 4; ++s) bq[t][s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
 #pragma unroll
-        for (int w = 0; w < MDT_MAX_NODES / 64; ++w) qa[w] = A.anc[(long)qc * A.W + min(w, A.W - 1)];
+        for (int w = 0; w < MDT_MAX_NODES / 64; ++w) qa[t][w] = A.anc[(long)qc * A.W + min(w, A.W - 1)];
+        dq_raw[t] = A.depth[qc];
     }
-    const int dq_raw = A.depth[qc];
 
     if (PAGED) {
         const int np = j_end > j_begin ? (j_end - 1) / psz - pg0 + 1 : 0;  // <= kMaxSplitPages (host plan)
@@ -371,104 +377,129 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
         cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
     __syncthreads();  // cos/sin table ready
-    {
-        if (!q_ok)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bq[s] = u32x4{0, 0, 0, 0};
-        const int dq = q_ok ? min(max(dq_raw, 0), A.max_depth) : 0;
+    for (int t = 0; t < QT; ++t) {
+        if (!q_ok[t])
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bq[t][s] = u32x4{0, 0, 0, 0};
+        const int dq = q_ok[t] ? min(max(dq_raw[t], 0), A.max_depth) : 0;
         const float2* row = cs + dq * (kDh / 2);
-        rotate8(bq[0], bq[2], row, 8 * g);
-        rotate8(bq[1], bq[3], row, 32 + 8 * g);
+        rotate8(bq[t][0], bq[t][2], row, 8 * g);
+        rotate8(bq[t][1], bq[t][3], row, 32 + 8 * g);
 #pragma unroll
         for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
-            if (!(tree_split && q_ok && w < A.W)) qa[w] = 0;
+            if (!(tree_split && q_ok[t] && w < A.W)) qa[t][w] = 0;
     }
 
-    f32x4 oacc[8];
+    f32x4 oacc[QT][8];
+    float m_run[QT], l_run[QT];  // of query qi[t], replicated over g
 #pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;  // of query qi, replicated over g
+    for (int t = 0; t < QT; ++t) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+    }
 
     // One staged tile: keys base..base+63, nvalid of them real.  The softmax runs in log2
     // units (scale * log2 e folded into the fma that forms each exponent), so it uses exp2.
     // Full prefix tiles skip the masking; the last prefix tile and tree tiles (bitmask) do not.
     const float sl2 = scale * 1.4426950408889634f;
     auto attend_tile = [&](int base, int nvalid, bool masked) {
-        f32x4 sacc[4];
+        f32x4 sacc[QT][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[QT];
+#pragma unroll
+            for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             const bf16_t* krow = Ks + (kb * 16 + c16) * kKStride + 8 * g;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16(*(const u32x4*)(krow + 32 * s), bq[s], acc);
-            sacc[kb] = acc;
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 kf = *(const u32x4*)(krow + 32 * s);
+#pragma unroll
+                for (int t = 0; t < QT; ++t) acc[t] = mfma16(kf, bq[t][s], acc[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < QT; ++t) sacc[t][kb] = acc[t];
         }
-        float tmax = -INFINITY;
-        if (masked) {
-            // tiles start at multiples of 64, so a tree tile reads one word of the query's mask
-            // row; a prefix tile is only cut at nvalid
-            const int wi = base >> 6;
-            const uint64_t qw = !tree_split ? ~0ull : wi == 0 ? qa[0] : wi == 1 ? qa[1] : wi == 2 ? qa[2] : qa[3];
+        u32x4 bp[QT][2];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            float tmax = -INFINITY;
+            if (masked) {
+                // tiles start at multiples of 64, so a tree tile reads one word of the query's
+                // mask row; a prefix tile is only cut at nvalid
+                const int wi = base >> 6;
+                const uint64_t qw = !tree_split ? ~0ull
+                                  : wi == 0     ? qa[t][0]
+                                  : wi == 1     ? qa[t][1]
+                                  : wi == 2     ? qa[t][2]
+                                                : qa[t][3];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = kb * 16 + 4 * g + e;
+                        const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
+                        const float sv = ok ? sacc[t][kb][e] : -INFINITY;
+                        sacc[t][kb][e] = sv;
+                        tmax = fmaxf(tmax, sv);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[t][kb][e]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            // the raw scores' maximum scaled once: rounding is monotone, so this is the maximum
+            // of the scaled scores, and each score is scaled inside its exponent's fma
+            tmax *= sl2;
+            const float m_new = fmaxf(m_run[t], tmax);
+            const bool live = m_new != -INFINITY;
+            // v_exp_f32 itself: exp2f adds a rescaling around it for results below 2^-126,
+            // which cannot matter next to the row maximum's weight of 1 and cost five more
+            // VALU operations per score
+            const float corr = live ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;
+            float tsum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int jj = kb * 16 + 4 * g + e;
-                    const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
-                    const float sv = ok ? sacc[kb][e] : -INFINITY;
-                    sacc[kb][e] = sv;
-                    tmax = fmaxf(tmax, sv);
+                    const float p = live ? __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][e], sl2, -m_new)) : 0.f;
+                    sacc[t][kb][e] = p;
+                    tsum += p;
                 }
-        } else {
+            tsum += __shfl_xor(tsum, 16, 64);
+            tsum += __shfl_xor(tsum, 32, 64);
+            l_run[t] = l_run[t] * corr + tsum;
+            m_run[t] = m_new;
+            // corr is exactly 1 unless the running maximum grew, which over a long prefix is
+            // rare: the wave skips the 32 multiplies when no lane needs them
+            if (__any(corr != 1.f))
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                for (int db = 0; db < 8; ++db) oacc[t][db] *= corr;
+            // within a 32-key step the key order is 4g+e (e<4), then 16+4g+(e-4)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[kb][e]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // the raw scores' maximum scaled once: rounding is monotone, so this is the maximum
-        // of the scaled scores, and each score is scaled inside its exponent's fma
-        tmax *= sl2;
-        const float m_new = fmaxf(m_run, tmax);
-        const bool live = m_new != -INFINITY;
-        // v_exp_f32 itself: exp2f adds a rescaling around it for results below 2^-126, which
-        // cannot matter next to the row maximum's weight of 1 and cost five more VALU
-        // operations per score
-        const float corr = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        float tsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p = live ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, -m_new)) : 0.f;
-                sacc[kb][e] = p;
-                tsum += p;
+            for (int ks = 0; ks < 2; ++ks) {
+                bp[t][ks][0] = pack_bf16(sacc[t][2 * ks][0], sacc[t][2 * ks][1]);
+                bp[t][ks][1] = pack_bf16(sacc[t][2 * ks][2], sacc[t][2 * ks][3]);
+                bp[t][ks][2] = pack_bf16(sacc[t][2 * ks + 1][0], sacc[t][2 * ks + 1][1]);
+                bp[t][ks][3] = pack_bf16(sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]);
             }
-        tsum += __shfl_xor(tsum, 16, 64);
-        tsum += __shfl_xor(tsum, 32, 64);
-        l_run = l_run * corr + tsum;
-        m_run = m_new;
-        // corr is exactly 1 unless the running maximum grew, which over a long prefix is rare:
-        // the wave skips the 32 multiplies when no lane needs them
-        if (__any(corr != 1.f))
-#pragma unroll
-            for (int db = 0; db < 8; ++db) oacc[db] *= corr;
-        // O^T += V^T P^T; within a 32-key step the key order is 4g+t (t<4), then 16+4g+(t-4)
+        }
+        // O^T += V^T P^T, every V fragment feeding each of the wave's query tiles
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            u32x4 bp;
-            bp[0] = pack_bf16(sacc[2 * ks][0], sacc[2 * ks][1]);
-            bp[1] = pack_bf16(sacc[2 * ks][2], sacc[2 * ks][3]);
-            bp[2] = pack_bf16(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]);
-            bp[3] = pack_bf16(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 const bf16_t* vrow = Vt + (db * 16 + c16) * kVStride + 32 * ks + 4 * g;
                 const u32x2 lo = *(const u32x2*)vrow;
                 const u32x2 hi = *(const u32x2*)(vrow + 16);
                 const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = mfma16(av, bp, oacc[db]);
+#pragma unroll
+                for (int t = 0; t < QT; ++t) oacc[t][db] = mfma16(av, bp[t][ks], oacc[t][db]);
             }
         }
     };
@@ -517,16 +548,19 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
         }
     }
 
-    if (qi < A.Tpad) {
-        const long base = (((long)b * H + h) * (A.nsplit + 1) + split) * A.Tpad + qi;
-        float* po = A.part_o + base * kDh;
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+    for (int t = 0; t < QT; ++t) {
+        if (qi[t] < A.Tpad) {
+            const long base = (((long)b * H + h) * (A.nsplit + 1) + split) * A.Tpad + qi[t];
+            float* po = A.part_o + base * kDh;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[db][e];
-        if (g == 0) {
-            A.part_ml[base * 2 + 0] = m_run;
-            A.part_ml[base * 2 + 1] = l_run;
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[t][db][e];
+            if (g == 0) {
+                A.part_ml[base * 2 + 0] = m_run[t];
+                A.part_ml[base * 2 + 1] = l_run[t];
+            }
         }
     }
 }
@@ -675,10 +709,11 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
     const dim3 grid(p.nsplit + 1, H, B);
     const bool paged = cache->layout == MDT_KV_PAGED;
+    // up to 8 query tiles: one per wave; up to 16: two per wave on 8 waves
     auto kern = p.nwb == 4 ? (paged ? attn_tree_mfma<4, true> : attn_tree_mfma<4, false>)
               : p.nwb == 8 ? (paged ? attn_tree_mfma<8, true> : attn_tree_mfma<8, false>)
-                           : (paged ? attn_tree_mfma<16, true> : attn_tree_mfma<16, false>);
-    MDT_LAUNCH("attn_tree_mfma", kern, grid, dim3(64 * p.nwb), 0, s, A);
+                           : (paged ? attn_tree_mfma<8, true, 2> : attn_tree_mfma<8, false, 2>);
+    MDT_LAUNCH("attn_tree_mfma", kern, grid, dim3(64 * (p.nwb == 16 ? 8 : p.nwb)), 0, s, A);
     st = mdt_launched("attn_tree_mfma");
     if (st != MDT_OK) return st;
     MDT_LAUNCH("attn_combine", attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,
