@@ -93,10 +93,19 @@ def cpu_baseline(w, inp, mode, tau, eps, delta):
             break
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
+    # the same oracle on one core: one step
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        ostep.step(w, inp, tree, mode, tau, eps, delta)
+        dt1 = time.perf_counter() - t1
+    model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                 platform.processor() or "cpu") if os.path.exists("/proc/cpuinfo") else platform.processor()
     return {"value": round(n / dt, 6), "unit": "verify-steps/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n} full oracle steps of {w.name} (all six stages, float64 NumPy, bf16 weights upcast "
-                      f"inside each step), inputs in host memory; {dt:.1f} s; host {platform.processor() or 'cpu'}, "
-                      f"{len(os.sched_getaffinity(0))} affinity cores"}
+                      f"inside each step), inputs in host memory; {dt:.1f} s; host {model}, "
+                      f"{len(os.sched_getaffinity(0))} affinity cores of {os.cpu_count()}",
+            "single_core": {"value": round(1.0 / dt1, 6), "cores": 1, "sample": f"1 oracle step, {dt1:.1f} s"}}
 
 
 def decode_loop_report(w, inp, seed, step, mode, tau, eps, delta, replays):
