@@ -2,7 +2,7 @@
 
 At the 7B-shaped step every weight is read once per use: W1 (K d^2), W2 (K d V) and W_lm
 twice (the LM head on h, the verifier on the tree rows), plus the prefix keys and values
-once; activations and outputs add under 0.2 %.  The dominant kernel's per-launch figure is
+once; the tree tensors, logits and other small reads and writes add under 0.3 %.  The dominant kernel's per-launch figure is
 W2 plus its own small reads and writes.  The full forward adds every decoder layer's
 weights (q, k, v, output: 4 d^2; gate, up, down: 3 d F; two norm gains) and prefix cache.
 """
@@ -20,7 +20,7 @@ def test_step_bytes_at_the_headline():
     kv = e * 2 * 1024 * w.H * w.Dh
     assert weights == 134_217_728 + 1_048_576_000 + 2 * 262_144_000   # W1 + W2 + 2 W_lm
     assert ab["total"] > weights + kv
-    assert (ab["total"] - weights - kv) / ab["total"] < 2e-3
+    assert (ab["total"] - weights - kv) / ab["total"] < 3e-3
     assert ab["total"] == 1_728_587_776
     # the dominant launch: W2 once, plus a (fp32 in) and its logits (fp32 out)
     assert ab["heads_gemv_w2"] == e * K * V * d + 4 * K * d + 4 * K * V
