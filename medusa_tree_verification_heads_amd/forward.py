@@ -33,7 +33,7 @@ import torch
 
 from . import (ACT_SWIGLU, GREEDY, TYPICAL, KVCache, Tree, accept_path, add_rmsnorm, auto_split, embed,
                interleave_gate_up, kv_compact_layers, linear, linear_split, medusa_heads, medusa_heads_workspace,
-               new_workspace, next_state, rmsnorm, topk_tree_expand, topk_workspace, tree_attention,
+               new_workspace, next_logits, next_state, rmsnorm, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace, MDT_BF16)
 from .step import to_device
 
@@ -140,9 +140,11 @@ class VerifyForward:
                     self.xf if last else self.h, stream)
 
     def run(self, stream=None, h=None, prefix_len=None, new_prefix_len=None, tokens=None, path=None,
-            n_acc=None):
+            n_acc=None, vlogits=None, lm_head=True):
         """Enqueue one step.  The keyword arguments replace the step's own input or output
-        tensors for this call (a chain of steps passes each step's own)."""
+        tensors for this call (a chain of steps passes each step's own); ``vlogits`` receives
+        the verifier's full logits, and ``lm_head=False`` leaves the heads' slot 0 as it is
+        (already filled by ``next_logits``)."""
         w, t = self.w, self.base
         h = t["h"] if h is None else h
         prefix_len = self.prefix_len if prefix_len is None else prefix_len
@@ -150,7 +152,8 @@ class VerifyForward:
         tokens = self.tokens if tokens is None else tokens
         path = self.path if path is None else path
         n_acc = self.n_acc if n_acc is None else n_acc
-        medusa_heads(h, t["W1"], t["W2"], t["Wlm"], logits=self.logits, ws=self.ws_heads, stream=stream)
+        medusa_heads(h, t["W1"], t["W2"], t["Wlm"] if lm_head else None, logits=self.logits, ws=self.ws_heads,
+                     stream=stream)
         topk_tree_expand(self.logits, w.k_cfg, self.tree, prefix_len, self.topk_idx, self.topk_val,
                          tokens, self.pos, ws=self.ws_topk, stream=stream)
         embed(tokens.view(-1), self.E, out=self.x, stream=stream)
@@ -159,7 +162,8 @@ class VerifyForward:
         for l in range(len(self.layers)):
             self.layer(l, stream, prefix_len)
         verify_logits(self.xf, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats,
-                      edge=self.edge, ws=self.ws_verify, stream=stream)
+                      edge=self.edge, logits=vlogits, want_logits=vlogits is not None, ws=self.ws_verify,
+                      stream=stream)
         accept_path(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta,
                     self.temperature, path=path, n_acc=n_acc, stream=stream)
         if self.layers:
@@ -192,12 +196,17 @@ class ForwardLoop:
     length is step s's new length, and every layer's cache already holds step s's
     accepted keys and values.  Every step has its own hidden-state, prefix-length, token,
     path and n_acc tensors, so ``run()`` can be repeated (or replayed as a graph) from the
-    same start; the caches need room for one accepted path per step.
+    same start; the caches need room for one accepted path per step.  As in the single-layer
+    chain, step s+1's LM-head slot is step s's verifier row of the same node
+    (``next_logits``, unless ``reuse_lm_head=False``), so the heads skip W_lm after step 0.
     """
 
-    def __init__(self, fwd: VerifyForward, steps: int):
+    def __init__(self, fwd: VerifyForward, steps: int, reuse_lm_head: bool = True):
         self.f = fwd
         self.S = steps
+        self.reuse = reuse_lm_head
+        self.vlogits = (torch.empty((fwd.w.B * fwd.tree.T, fwd.w.V), dtype=torch.float32, device=fwd.dev)
+                        if reuse_lm_head else None)
         B, T = fwd.w.B, fwd.tree.T
         dev = fwd.dev
         h0 = fwd.base["h"]
@@ -210,8 +219,11 @@ class ForwardLoop:
 
     def run_step(self, s: int, stream=None):
         f = self.f
+        reuse = self.reuse and s > 0
+        if reuse:
+            next_logits(self.vlogits, self.paths[s - 1], self.n_acc[s - 1], f.logits, stream=stream)
         f.run(stream, h=self.h[s], prefix_len=self.lens[s], new_prefix_len=self.lens[s + 1], tokens=self.tokens[s],
-              path=self.paths[s], n_acc=self.n_acc[s])
+              path=self.paths[s], n_acc=self.n_acc[s], vlogits=self.vlogits, lm_head=not reuse)
         next_state(f.xf.view(f.w.B, f.tree.T, f.w.d), self.paths[s], self.n_acc[s], out=self.h[s + 1], stream=stream)
 
     def run(self, stream=None):

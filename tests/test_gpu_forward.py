@@ -408,8 +408,9 @@ def test_compact_layers_paged():
     assert int((Kp.view(torch.int16) != 0).any(dim=-1).any(dim=-1).sum()) == written
 
 
+@pytest.mark.parametrize("reuse", [True, False])
 @pytest.mark.parametrize("name", ["7b-mini-x2", "7b-mini-B2-x2"])
-def test_forward_loop(name):
+def test_forward_loop(name, reuse):
     """Three chained steps through both layers: each step starts from the final normed row
     of the last accepted node, the new prefix length and the compacted caches.  The GPU
     chain is compared with the oracle chain (both from the drawn inputs) while the two
@@ -435,7 +436,7 @@ def test_forward_loop(name):
         ref = ofw.forward_loop(dw, inp, fin, layers, tree, S, run.mode, run.temperature, run.eps, run.delta)
         f = VerifyForward.from_numpy(dw, inp, fin, layers, mode=run.mode, temperature=run.temperature, eps=run.eps,
                                      delta=run.delta)
-        loop = ForwardLoop(f, S)
+        loop = ForwardLoop(f, S, reuse_lm_head=reuse)
         together, steps_compared = True, 0
         for s in range(S):
             L = loop.lens[s].cpu().numpy()
