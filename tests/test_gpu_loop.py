@@ -209,3 +209,22 @@ def test_reused_lm_head_slot(name):
             assert np.array_equal(logits[:, 1:], _host(ref)[:, 1:]), s
         prev = (_host(loop.vlogits), _host(loop.paths[s]), _host(loop.n_acc[s]))
 
+
+
+def test_next_logits_rows_and_invalid_sequences():
+    """mdt_next_logits copies each sequence's last accepted node's verifier row into slot 0
+    exactly, leaves slots 1..K alone, and writes zeros for a sequence whose n_acc or last
+    path node is out of range."""
+    import medusa_tree_verification_heads_amd as mdt
+    B, T, V, K, stride = 4, 10, 3001, 3, 4
+    g = torch.Generator(device="cuda").manual_seed(5)
+    z = torch.randn((B * T, V), device="cuda", generator=g)
+    head = torch.full((B, K + 1, V), 9.0, device="cuda")
+    path = torch.tensor([[0, 2, 5, -1], [0, 1, -1, -1], [0, 3, 7, 9], [0, 12, -1, -1]], dtype=torch.int32,
+                        device="cuda")
+    n_acc = torch.tensor([3, 0, 4, 2], dtype=torch.int32, device="cuda")   # b=1: n_acc 0; b=3: node 12 >= T
+    mdt.next_logits(z, path, n_acc, head)
+    zh, hh = _host(z), _host(head)
+    assert np.array_equal(hh[0, 0], zh[0 * T + 5]) and np.array_equal(hh[2, 0], zh[2 * T + 9])
+    assert np.all(hh[1, 0] == 0) and np.all(hh[3, 0] == 0)
+    assert np.all(hh[:, 1:] == 9.0)
