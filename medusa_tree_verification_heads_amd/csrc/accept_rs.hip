@@ -204,7 +204,11 @@ __global__ __launch_bounds__(kRsThreads) void accept_rs_kernel(RsArgs A) {
     }
     if (!none) {
         // inverse CDF: the entry where the running sum first exceeds u * total, running sums
-        // in vocabulary order (thread sums, then a scan over threads)
+        // in vocabulary order (thread sums, then a scan over threads).  Thread t covers
+        // [lo_t, hi_t) with hi_t = base + its inclusive sum and lo_t taken from thread t-1's
+        // hi (the wave's base for lane 0, which equals the previous wave's last hi bit for
+        // bit), so adjacent ranges share their bound exactly; the smallest claiming thread
+        // wins (an LDS atomic minimum), so the pick is the same on every run.
         float own = 0.f;
 #pragma unroll
         for (int j = 0; j < kRsPer; ++j) own += r[j];
@@ -216,6 +220,7 @@ __global__ __launch_bounds__(kRsThreads) void accept_rs_kernel(RsArgs A) {
             if (lane >= off) incl += t;
         }
         if (lane == 63) red[wave] = incl;
+        if (tid == 0) pick = 0x7fffffff;
         __syncthreads();
         float base = 0.f, total = 0.f;
 #pragma unroll
@@ -224,9 +229,11 @@ __global__ __launch_bounds__(kRsThreads) void accept_rs_kernel(RsArgs A) {
             total += red[w];
         }
         const float target = A.u_res[b] * total;
-        const float excl = base + incl - own;
-        if (own > 0.f && excl <= target && target < excl + own) {
-            float run = excl;
+        const float prev = __shfl_up(incl, 1, 64);
+        const float hi = base + incl;
+        const float lo = lane == 0 ? base : base + prev;
+        if (own > 0.f && lo <= target && target < hi) {
+            float run = lo;
             int y = -1, last = -1;
 #pragma unroll
             for (int j = 0; j < kRsPer; ++j) {
@@ -234,15 +241,11 @@ __global__ __launch_bounds__(kRsThreads) void accept_rs_kernel(RsArgs A) {
                 last = r[j] > 0.f ? j : last;
                 y = (y < 0 && run > target) ? j : y;
             }
-            pick = v0 + (y >= 0 ? y : last);  // a rounding shortfall keeps the range's last entry
+            atomicMin(&pick, v0 + (y >= 0 ? y : last));  // a rounding shortfall keeps the range's last entry
         }
         __syncthreads();
-        if (tid == 0 && pick < 0) {
+        if (pick == 0x7fffffff) {
             // target at or past the total by rounding: the last entry with mass
-            pick = -2;
-        }
-        __syncthreads();
-        if (pick == -2) {
             int last = -1;
 #pragma unroll
             for (int j = 0; j < kRsPer; ++j) last = r[j] > 0.f ? j : last;

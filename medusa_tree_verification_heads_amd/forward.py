@@ -58,6 +58,8 @@ class VerifyForward:
         w = dw.base
         assert w.dtype == "bf16" and not w.paged, "the full forward runs on bf16 contiguous caches"
         self.dw, self.w = dw, w
+        if mode not in ("greedy", "typical"):
+            raise ValueError(f"unknown acceptance mode {mode!r} (greedy or typical)")
         self.mode = GREEDY if mode == "greedy" else TYPICAL
         self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
         self.base, self.E, self.g_final, self.layers = base, E, g_final, layers

@@ -36,6 +36,8 @@ class VerifyStep:
                  delta: float = 0.3, device="cuda", want_logits: bool = False, tree: Tree = None,
                  fused_tail: bool = True):
         self.w = w
+        if mode not in ("greedy", "typical", "rejection"):
+            raise ValueError(f"unknown acceptance mode {mode!r} (greedy, typical or rejection)")
         # rejection sampling (mode "rejection") reads full verifier rows and the step's
         # uniforms (inp["u_accept"], inp["u_resample"]); its acceptance and compaction are
         # two calls
@@ -155,6 +157,10 @@ class DecodeLoop:
     def __init__(self, w, inp: dict, qkv_steps, mode: str = "greedy", temperature: float = 0.0, eps: float = 0.09,
                  delta: float = 0.3, device="cuda", fused_tail: bool = True, want_logits: bool = False,
                  step: VerifyStep = None, reuse_lm_head: bool = True):
+        # the chain takes each next root from the LM-head row, so a sampled next token (the
+        # rejection sampler's) has nowhere to go: chaining it is not supported
+        if (step.rejection if step is not None else mode == "rejection"):
+            raise ValueError("DecodeLoop does not chain rejection sampling")
         # an existing step (same inputs) can be reused: the chain only adds its own state tensors
         self.step = step or VerifyStep(w, inp, mode, temperature, eps, delta, device, want_logits=want_logits,
                                        fused_tail=fused_tail)

@@ -160,3 +160,44 @@ def test_step_with_rejection_acceptance():
         for j, node in enumerate(ref[0][b]):
             assert np.array_equal(g["Kc"][b, L + j], g["k_rot"][b, node])
     assert np.array_equal(g["new_len"], inp["prefix_len"] + g["n_acc"])
+
+
+@pytest.mark.parametrize("V", [4096, 32000])
+def test_final_draw_on_range_boundaries(V):
+    """The final draw when u * total falls exactly on a bound between two threads' ranges of
+    the running sum (or between two entries, or at 0).  A root-only tree makes the draw come
+    straight from the root's verifier row; that row puts 2^-6 of the mass on each of 64
+    entries (logit 0, the rest -1e6, temperature log2(e) so every exponential is exactly 1
+    or 0), so every running sum is exact in float32 and float64 alike and the oracle's
+    inverse CDF is the unique answer: the first entry whose running sum exceeds u."""
+    import medusa_tree_verification_heads_amd as mdt
+    from oracle import tree as otree
+    tau = float(np.float32(1.4426950408889634))
+    rng = np.random.default_rng(V)
+    chosen = np.sort(rng.choice(V, 64, replace=False))
+    # u at: 0, every boundary between two 32-entry thread ranges that splits the chosen set,
+    # a few boundaries between entries of one thread, and just below 1
+    thread_of = chosen // 32
+    cuts = [0] + [int(np.searchsorted(thread_of, t)) for t in np.unique(thread_of)[1:]]
+    cuts += [5, 17, 63]
+    us = sorted(set(c / 64 for c in cuts)) + [float(np.float32(1) - np.float32(2 ** -24))]
+    B = len(us)
+    z = np.full((B, V), -1e6, dtype=np.float32)
+    z[:, chosen] = 0.0
+    heads = np.zeros((B, 2, V), dtype=np.float32)
+    tokens = np.zeros((B, 1), dtype=np.int32)
+    ua = np.zeros((B, 1), dtype=np.float32)
+    ur = np.array(us, dtype=np.float32)
+    assert all(float(x) == u for x, u in zip(ur, us))
+    note(f"final draw on bounds V={V} B={B}")
+    tree = mdt.Tree.cartesian(())
+    path, n_acc, nxt = mdt.accept_rejection(torch.from_numpy(z).cuda(), torch.from_numpy(heads).cuda(),
+                                            torch.from_numpy(tokens).cuda(), tree.to_device("cuda"), tau,
+                                            torch.from_numpy(ua).cuda(), torch.from_numpy(ur).cuda())
+    torch.cuda.synchronize()
+    ref = ostep.accept_rejection(z.astype(np.float64), heads.astype(np.float64), tokens, otree.cartesian_tree(()),
+                                 tau, ua.astype(np.float64), ur.astype(np.float64))
+    assert n_acc.cpu().numpy().tolist() == [1] * B
+    assert nxt.cpu().numpy().tolist() == ref[2]
+    # the expected entries: the first chosen entry past u's count of chosen entries
+    assert ref[2] == [int(chosen[min(int(round(u * 64)), 63)]) for u in us]

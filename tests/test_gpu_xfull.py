@@ -10,6 +10,7 @@ passes under the returned row statistics, and the cache rows are exact copies of
 path's rotated keys and values with every other row untouched.
 """
 
+import functools
 import math
 
 import numpy as np
@@ -45,24 +46,37 @@ def _passes(mode, tau, eps, delta, tok, st, edge):
     return lp > thr, abs(lp - thr)
 
 
-@pytest.mark.timeout(400)
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_step(name):
-    from medusa_tree_verification_heads_amd.step import VerifyStep
+@functools.lru_cache(maxsize=1)
+def _workload_state(name):
+    """Inputs and the oracle's head logits of one full-size workload (the runs of a workload
+    share them; one workload is held at a time)."""
     w = WORKLOADS[name]
     seed = _seed(name)
-    run = w.accept[-1]
-    note(f"full size {name} seed {seed} run {run}")
     inp = make_inputs(w, seed)
+    logits, _ = ostep.medusa_heads(inp["h"], inp["W1"], inp["W2"], inp["Wlm"])
+    return w, seed, inp, logits
+
+
+RUNS = [(n, i) for n in FULL for i in range(len(WORKLOADS[n].accept))]
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name,run_idx", RUNS)
+def test_full_size_step(name, run_idx):
+    """Every acceptance run each workload names, at full size."""
+    from medusa_tree_verification_heads_amd.step import VerifyStep
+    w, seed, inp, logits = _workload_state(name)
+    run = w.accept[run_idx]
+    note(f"full size {name} seed {seed} run {run}")
     s = VerifyStep(w, inp, run.mode, run.temperature, run.eps, run.delta)
     s.run()
     g = s.outputs()
+    del s
     tree = otree.build_tree(w)
     T, B, K1, k = tree.T, w.B, w.K + 1, w.k_cfg
     rng = np.random.default_rng(seed)
 
     # heads: all logits
-    logits, _ = ostep.medusa_heads(inp["h"], inp["W1"], inp["W2"], inp["Wlm"])
     err = rel_err_rows(g["logits"], logits)
     note(f"{name}: heads rel err {err:.2e}")
     assert err <= REL_TOL

@@ -237,3 +237,15 @@ def test_compact_layers_validation():
     assert f(ks=64 * 4096 - 8) == -2              # stride smaller than one layer
     assert f(cs=1029 * 4096 - 8) == -2
     assert f(vs=-8) == -4 and f(ks=3) == -4       # negative or not a 16-byte multiple
+
+
+def test_unknown_mode_strings_are_rejected():
+    """A typo in the acceptance mode must not silently run typical acceptance, and the chain
+    refuses rejection sampling (its sampled next token has no place in the chain)."""
+    from medusa_tree_verification_heads_amd.step import DecodeLoop, VerifyStep
+    w = PARITY_CASES["7b-mini"]
+    for bad in ("greedly", "Typical", "rejection_sampling", ""):
+        with pytest.raises(ValueError):
+            VerifyStep(w, {}, mode=bad)
+    with pytest.raises(ValueError):
+        DecodeLoop(w, {}, [], mode="rejection")
