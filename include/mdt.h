@@ -231,6 +231,26 @@ mdt_status mdt_medusa_heads(void* stream, mdt_dtype dt, int B, int d, int V, int
                             const void* h, const void* W1, const void* W2, const void* Wlm,
                             float* logits, void* ws, size_t ws_bytes);
 
+/*
+ * mdt_medusa_heads without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It allocates nothing; the head activations live in a fixed array
+ * of MDT_HEADS_NOALLOC_MAX_BYTES in device memory that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up once per device, on the
+ * first call made with that device current).  Every call on one GPU shares that array
+ * and leaves its last contents there: calls that overlap on one GPU (two streams, two
+ * threads) race and must be ordered by the caller.  Nothing in it needs clearing (the
+ * first kernel writes every activation the second reads).  Arguments, layouts and
+ * results as mdt_medusa_heads.
+ * Errors: as mdt_medusa_heads; MDT_ERR_WORKSPACE when B*K*d*4 bytes exceed
+ * MDT_HEADS_NOALLOC_MAX_BYTES (checked first, before any HIP call); MDT_ERR_HIP when the
+ * array's device address cannot be obtained.
+ */
+#define MDT_HEADS_NOALLOC_MAX_BYTES (4u << 20)
+mdt_status mdt_medusa_heads_noalloc(void* stream, mdt_dtype dt, int B, int d, int V, int K,
+                                    const void* h, const void* W1, const void* W2, const void* Wlm,
+                                    float* logits);
+
 /* ------------------------------------------------------------------------- */
 /* 2. Top-k and tree expansion                                                */
 /* ------------------------------------------------------------------------- */

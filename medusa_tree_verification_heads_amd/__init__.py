@@ -76,6 +76,8 @@ _SIGS = [
     ("mdt_medusa_heads_workspace", c_size, [c_int, c_int, c_int]),
     ("mdt_medusa_heads", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_size]),
+    ("mdt_medusa_heads_noalloc", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p]),
     ("mdt_topk_workspace", c_size, [c_int, c_int, c_int, c_int]),
     ("mdt_topk_tree_expand", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(TreeDev),
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size]),
@@ -307,6 +309,19 @@ def medusa_heads(h, W1, W2, Wlm, logits=None, ws=None, stream=None):
     ws, nb = _ws(medusa_heads_workspace(B, d, K), h.device, ws)
     _check(lib.mdt_medusa_heads(_stream(stream), _dtype_code(h), B, d, V, K, _ptr(h), _ptr(W1), _ptr(W2), _ptr(Wlm),
                                 _ptr(logits), _ptr(ws), nb), "medusa_heads")
+    return logits
+
+
+HEADS_NOALLOC_MAX_BYTES = 4 << 20
+
+
+def medusa_heads_noalloc(h, W1, W2, Wlm, logits, stream=None):
+    """medusa_heads with the activations in the library's fixed device array (no workspace,
+    nothing allocated; ``logits`` must be given).  Calls overlapping on one GPU race."""
+    B, d = h.shape
+    K, V = W1.shape[0], W2.shape[1]
+    _check(lib.mdt_medusa_heads_noalloc(_stream(stream), _dtype_code(h), B, d, V, K, _ptr(h), _ptr(W1), _ptr(W2),
+                                        _ptr(Wlm), _ptr(logits)), "medusa_heads_noalloc")
     return logits
 
 

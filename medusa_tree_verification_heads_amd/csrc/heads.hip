@@ -17,6 +17,8 @@
 // (heads_mfma.hip), where each weight byte serves every sequence.
 // Rows of all heads of a launch form one grid; a workgroup owns a contiguous row
 // block of one head.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -345,4 +347,53 @@ extern "C" mdt_status mdt_medusa_heads(void* stream, mdt_dtype dt, int B, int d,
     if (dt == MDT_BF16 && mdt_heads_mfma_applies(B, d)) return mdt_heads_mfma(s, B, d, V, K, h, W1, W2, Wlm, logits, ws);
     if (dt == MDT_BF16) return run<bf16_t>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
     return run<float>(s, B, d, V, K, h, W1, W2, Wlm, logits, (float*)ws);
+}
+
+// ---------------------------------------------------------------------------
+// mdt_medusa_heads_noalloc: the same two kernels with their activations in a fixed
+// device array of this library instead of a caller workspace.
+// ---------------------------------------------------------------------------
+
+// One copy per device, alive until the process ends.  Host code never passes this name
+// to a kernel (on the host it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MDT_HEADS_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+mdt_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    MDT_REQUIRE(e == hipSuccess, MDT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    MDT_REQUIRE(dev >= 0 && dev < kMaxDevices, MDT_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            MDT_REQUIRE(e == hipSuccess && p, MDT_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MDT_OK;
+}
+}  // namespace
+
+extern "C" mdt_status mdt_medusa_heads_noalloc(void* stream, mdt_dtype dt, int B, int d, int V, int K, const void* h,
+                                               const void* W1, const void* W2, const void* Wlm, float* logits) {
+    MDT_REQUIRE(B >= 1 && d >= 1 && K >= 1, MDT_ERR_SHAPE, "B=%d d=%d K=%d must be >= 1", B, d, K);
+    const size_t need = mdt_medusa_heads_workspace(B, d, K);
+    MDT_REQUIRE(need <= (size_t)MDT_HEADS_NOALLOC_MAX_BYTES, MDT_ERR_WORKSPACE,
+                "B*K*d*4 = %zu bytes exceeds the fixed scratch of %u bytes (use mdt_medusa_heads with a workspace)",
+                need, (unsigned)MDT_HEADS_NOALLOC_MAX_BYTES);
+    void* ws = nullptr;
+    const mdt_status st = scratch_address(&ws);
+    if (st != MDT_OK) return st;
+    return mdt_medusa_heads(stream, dt, B, d, V, K, h, W1, W2, Wlm, logits, ws, MDT_HEADS_NOALLOC_MAX_BYTES);
 }

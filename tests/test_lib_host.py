@@ -249,3 +249,11 @@ def test_unknown_mode_strings_are_rejected():
             VerifyStep(w, {}, mode=bad)
     with pytest.raises(ValueError):
         DecodeLoop(w, {}, [], mode="rejection")
+
+
+def test_noalloc_heads_rejects_oversize():
+    """The allocation-free heads call refuses activations beyond its fixed device array
+    before any HIP call."""
+    assert mdt.lib.mdt_medusa_heads_noalloc(None, mdt.MDT_BF16, 9, 16384, 32000, 8, 16, 16, 16, 16, 16) == -7
+    assert b"exceeds the fixed scratch" in mdt.lib.mdt_last_error()
+    assert mdt.lib.mdt_medusa_heads_noalloc(None, mdt.MDT_BF16, 0, 4096, 32000, 4, 16, 16, 16, 16, 16) == -2
