@@ -1,0 +1,172 @@
+// A 64 x NB tile of x W^T for at most 64 x rows, with both operands staged in LDS by
+// direct global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land in LDS
+// without passing through registers).
+//
+// The inner dimension is walked in chunks of KC dims held in an S-stage ring: while the
+// waves multiply chunk c out of LDS, the loads of chunks c+1 .. c+S-1 are in flight, and
+// one barrier per chunk both publishes chunk c and frees the buffer that chunk c+S-1 is
+// then loaded into.  A load instruction fills 1 KiB of LDS contiguously (lane l at
+// +16 l), so the layout is chosen through the global addresses: row r of a chunk takes
+// KC/8 consecutive 16-byte slots, and slot j of the row holds the row's piece
+// j ^ (r mod 16).  Every instruction still reads whole rows of the chunk (runs of 2 KC
+// bytes), and the 16 rows of an MFMA fragment read fall into 16 distinct bank groups.
+//
+// Waves: CG column groups x KS inner-dimension groups.  Wave (cg, kh) multiplies x rows
+// 0..63 against weight rows cg NB/CG .. +NB/CG over the k-steps kh, kh + KS, ... of each
+// chunk; the KS partial products are then summed through LDS in kh order, and epi(acc)
+// runs on the kh = 0 waves with acc[nt][mt] holding weight rows cg NB/CG + 16 nt + l%16 and
+// x rows 16 mt + 4 (l/16) + e (the 16x16 MFMA output layout).
+//
+// Rows of x past M and of W past V read the last valid row (their products are never
+// stored by a caller that honours M and V); pieces past d read the row's first piece and
+// the k-steps past d are skipped.  d must be a multiple of 32.
+#pragma once
+
+#include "mfma_tile.h"
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most N vector-memory operations of this wave are outstanding and every LDS
+// operation is done (s_waitcnt vmcnt(N) lgkmcnt(0)), then meet the workgroup at a barrier.
+// __syncthreads() would also wait for every load still in flight (its fence covers the
+// direct-to-LDS loads), which is exactly the overlap the ring exists for.  The empty asm
+// statements keep the compiler from moving memory accesses across the barrier; the
+// lgkmcnt(0) makes every LDS read of the previous chunk complete before any wave can
+// refill that buffer.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int KC, int NB, int CG, int KS, int S>
+struct DmaTile {
+    static constexpr int NW = CG * KS;
+    static constexpr int NT = 64 * NW;
+    static constexpr int kPR = KC / 8;                 // 16-byte pieces per row per chunk
+    static constexpr int kWBytes = NB * KC * 2;
+    static constexpr int kXBytes = 64 * KC * 2;
+    static constexpr int kStage = kWBytes + kXBytes;
+    static constexpr int kIW = NB * kPR / 64 / NW;     // weight load instructions per wave per chunk
+    static constexpr int kIX = 64 * kPR / 64 / NW;     // x load instructions per wave per chunk
+    static constexpr int kLoads = kIW + kIX;
+    static constexpr int kRedBytes = (KS - 1) * (NB / 16) * 4 * 64 * 16;  // k-group partials
+    static constexpr int kRingBytes = S * kStage;
+    static_assert(KC % 128 == 0, "a chunk row spans at least 16 pieces (the swizzle's period)");
+    static_assert((KC / 32) % KS == 0, "k-steps divide among the k-groups");
+    static_assert(NB % (16 * CG) == 0, "columns divide among the column groups");
+    static_assert(NB * kPR % (64 * NW) == 0 && 64 * kPR % (64 * NW) == 0, "loads divide among the waves");
+    static_assert(S >= 2 && S <= 4, "2 to 4 stages");
+    static_assert(kLoads * (S - 2) < 64, "vmcnt range");
+};
+
+template <int KC, int NB, int CG, int KS, int S, int AUX = 0, typename Epi>
+__device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M, int d,
+                                         int V, int n0, char* smem, Epi&& epi) {
+    using P = DmaTile<KC, NB, CG, KS, S>;
+    constexpr int kPR = P::kPR;
+    constexpr int NTW = NB / CG / 16;   // weight fragments per wave
+    constexpr int KSS = KC / 32 / KS;   // k-steps per wave per chunk
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int cg = wave % CG, kh = wave / CG;
+    const int nch = (d + KC - 1) / KC;
+
+    // chunk c into ring slot c % S: instruction i of the chunk covers linear slots
+    // 64 i .. 64 i + 63, slot q holding piece (q % kPR) ^ (row % 16) of row q / kPR
+    auto issue = [&](int c) {
+        char* st = smem + (c % S) * P::kStage;
+#pragma unroll
+        for (int j = 0; j < P::kIW; ++j) {
+            const int i = wave * P::kIW + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = (q % kPR) ^ (r & 15);
+            const int k = c * KC + 8 * p;
+            const bf16_t* src = W + (size_t)min(n0 + r, V - 1) * d + (k < d ? k : 0);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, AUX);
+        }
+#pragma unroll
+        for (int j = 0; j < P::kIX; ++j) {
+            const int i = wave * P::kIX + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = (q % kPR) ^ (r & 15);
+            const int k = c * KC + 8 * p;
+            const bf16_t* src = x + (size_t)min(r, M - 1) * d + (k < d ? k : 0);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P::kWBytes + 1024 * i), 16, 0, 0);
+        }
+    };
+
+    f32x4 acc[NTW][4];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c) {
+        const char* st = smem + (c % S) * P::kStage;
+        const bf16_t* ws = (const bf16_t*)st;
+        const bf16_t* xs = (const bf16_t*)(st + P::kWBytes);
+        const int nsteps = min(KC, d - c * KC) / 32;
+#pragma unroll
+        for (int s2 = 0; s2 < KSS; ++s2) {
+            const int s = kh + KS * s2;
+            if (s < nsteps) {
+                const int pp = (4 * s + g) ^ c16;  // rows of a fragment start at multiples of 16
+                u32x4 a[4], b[NTW];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) a[mt] = *(const u32x4*)(xs + ((16 * mt + c16) * kPR + pp) * 8);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    b[nt] = *(const u32x4*)(ws + ((cg * (NB / CG) + 16 * nt + c16) * kPR + pp) * 8);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mfma16(a[mt], b[nt], acc[nt][mt]);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int c = 0; c < S - 1; ++c)
+        if (c < nch) issue(c);
+    for (int c = 0; c < nch; ++c) {
+        // chunk c has landed once at most min(S - 2, nch - 1 - c) later chunks are outstanding
+        const int later = min(S - 2, nch - 1 - c);
+        if (later >= 2)
+            ring_barrier<2 * P::kLoads>();
+        else if (later == 1)
+            ring_barrier<P::kLoads>();
+        else
+            ring_barrier<0>();
+        if (c + S - 1 < nch) issue(c + S - 1);
+        compute(c);
+    }
+    __syncthreads();  // every wave is done with the ring: it becomes the reduction buffer
+    if (KS > 1) {
+        float* red = (float*)smem;  // [KS-1][CG][NTW][4 mt][4 e][64 lanes]
+        if (kh > 0) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        red[(((((kh - 1) * CG + cg) * NTW + nt) * 4 + mt) * 4 + e) * 64 + lane] = acc[nt][mt][e];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[nt][mt][e] += red[(((((k2 - 1) * CG + cg) * NTW + nt) * 4 + mt) * 4 + e) * 64 + lane];
+        }
+    }
+    if (kh == 0) epi(acc);
+}

@@ -20,6 +20,7 @@
 #include <climits>
 #include <math.h>
 
+#include "dma_tile.h"
 #include "mfma_tile.h"
 
 namespace {
@@ -196,6 +197,57 @@ __global__ __launch_bounds__(128 * NW) void verify_mfma_k2(const bf16_t* __restr
     tile_epilogue<kMB, NB, NT>(zt, 0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
+// At most 64 node rows (one tree of a single sequence, the batch-1 shapes): dma_tile, the
+// 64 x NB tile fed by direct global-to-LDS loads through an S-stage ring, then the
+// statistics epilogue over NB columns on all threads.  grid ceil(V / NB), block 64 CG KS.
+#ifndef MDT_VDMA_KC
+#define MDT_VDMA_KC 128
+#endif
+#ifndef MDT_VDMA_CG
+#define MDT_VDMA_CG 4
+#endif
+#ifndef MDT_VDMA_KS
+#define MDT_VDMA_KS 2
+#endif
+#ifndef MDT_VDMA_S
+#define MDT_VDMA_S 3
+#endif
+#ifndef MDT_VDMA_AUX
+#define MDT_VDMA_AUX 2  // cache policy of the weight loads: streamed (read once)
+#endif
+constexpr int kDmaNB = 128;
+using VDma = DmaTile<MDT_VDMA_KC, kDmaNB, MDT_VDMA_CG, MDT_VDMA_KS, MDT_VDMA_S>;
+
+__global__ __launch_bounds__(VDma::NT) void verify_dma(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+                                                       int M, int d, int V, float tau, int nblk_n,
+                                                       Part* __restrict__ part, float* __restrict__ logits_opt,
+                                                       const int32_t* __restrict__ parent,
+                                                       const int32_t* __restrict__ tokens, int T,
+                                                       float* __restrict__ edge) {
+    constexpr int NB = kDmaNB, CG = MDT_VDMA_CG;
+    constexpr int kZOff = VDma::kRedBytes;  // the logits tile after the k-groups' partials
+    constexpr int kEpi = kZOff + kMB * (NB + 1) * 4;
+    constexpr int kLds = VDma::kRingBytes > kEpi ? VDma::kRingBytes : kEpi;
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    const int n0 = blockIdx.x * NB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15, cg = wave % CG;
+    const EdgePre pre = edge_preload<kMB>(0, M, parent, tokens, T);
+    float* zt = (float*)(smem + kZOff);  // [64][NB + 1]
+    dma_tile<MDT_VDMA_KC, NB, CG, MDT_VDMA_KS, MDT_VDMA_S, MDT_VDMA_AUX>(
+        x, W, M, d, V, n0, smem, [&](const f32x4 (&acc)[NB / CG / 16][4]) {
+#pragma unroll
+            for (int nt = 0; nt < NB / CG / 16; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        zt[(mt * 16 + 4 * g + e) * (NB + 1) + cg * (NB / CG) + 16 * nt + c16] = acc[nt][mt][e];
+        });
+    __syncthreads();
+    tile_epilogue<kMB, NB, VDma::NT>(zt, 0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
+}
+
 // Many node rows (batches, 256-node trees): 128 x 128 tiles (mfma_tile128), grid
 // (ceil(M/128), ceil(V/128)) row-block-major, partials per 128 vocabulary columns.
 template <int KC>
@@ -338,8 +390,13 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     const bool big = dt == MDT_BF16 && M >= kBigRows;
     // one row block whose 64-column grid overfills the CUs: the 16-wave tile, 128 columns
     const long cus = mdt_num_cus();
-    const bool wide = dt == MDT_BF16 && M <= kMB && (V + 63) / 64 > cus && (V + 127) / 128 <= cus;
-    const int nb_cols = big || wide ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
+#ifndef MDT_VERIFY_NO_DMA
+    const bool dma = dt == MDT_BF16 && M <= kMB;
+#else
+    const bool dma = false;
+#endif
+    const bool wide = !dma && dt == MDT_BF16 && M <= kMB && (V + 63) / 64 > cus && (V + 127) / 128 <= cus;
+    const int nb_cols = big || wide || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
     if (big) {
@@ -347,6 +404,9 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
         MDT_LAUNCH("verify_mfma", kern, dim3((M + 127) / 128, nblk_n), dim3(256), 0, s, (const bf16_t*)x,
                    (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
                    edge_logit);
+    } else if (dma) {
+        MDT_LAUNCH("verify_mfma", verify_dma, dim3(nblk_n), dim3(VDma::NT), 0, s, (const bf16_t*)x, (const bf16_t*)Wlm,
+                   M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T, edge_logit);
     } else if (wide) {
         auto kern = verify_mfma_k2<MDT_VERIFY_KC, 8>;
         MDT_LAUNCH("verify_mfma", kern, dim3(nblk_n), dim3(1024), 0, s, (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V,

@@ -306,3 +306,43 @@ def test_stage_compact_from_oracle_path(name):
         for j, node in enumerate(p):
             assert np.array_equal(cache_row(Kn, b, L + j, pt, w.page_size), kr[b, node])
     assert new_len.cpu().numpy().tolist() == [int(inp["prefix_len"][b]) + n for b, n in enumerate(orr["n_acc"])]
+
+
+@pytest.mark.parametrize("T,d,V", [(1, 96, 1000), (17, 160, 5003), (64, 4128, 2048), (40, 128, 129), (64, 256, 32000)])
+def test_verify_small_rows_ragged(T, d, V):
+    """At most 64 node rows (one sequence's tree): inner dimensions that leave a partial
+    last chunk (96, 160, 4128), a single row, vocabularies with ragged last tiles.  Full
+    logits, row statistics and edge logits against the oracle's definitions."""
+    import medusa_tree_verification_heads_amd as mdt
+    from oracle import step as ostep
+    from oracle import tree as otree
+    from workloads.gen import f32_to_bf16_bits
+    note(f"verify small rows T={T} d={d} V={V}")
+    tree = otree.cartesian_tree(()) if T == 1 else otree.scored_tree_greedy(4, 10, T)
+    dtree = (mdt.Tree.cartesian(()) if T == 1 else mdt.Tree.scored(4, 10, T)).to_device("cuda")
+    rng = np.random.default_rng(T * 1000 + d)
+    x = ostep.round_bf16(rng.standard_normal((T, d)))
+    W = ostep.round_bf16(rng.standard_normal((V, d)) * d ** -0.5)
+    tok = rng.integers(0, V, (1, T))
+    xd = torch.from_numpy(f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    Wd = torch.from_numpy(f32_to_bf16_bits(W.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    for tau in (0.0, 0.7):
+        stats, edge, logits = mdt.verify_logits(xd, Wd, dtree, torch.from_numpy(tok.astype(np.int32)).cuda(), tau,
+                                                want_logits=True)
+        torch.cuda.synchronize()
+        z = x @ W.T
+        assert rel_err_rows(logits.cpu().numpy(), z) <= REL_TOL
+        st = _stats_np(stats.cpu().numpy())
+        scale = np.abs(z).max(axis=1)
+        for r in range(T):
+            ref = ostep.row_stats(z[r], tau)
+            assert abs(st["max"][r] - ref["max"]) <= REL_TOL * scale[r]
+            t2 = np.partition(z[r], -2)[-2:]
+            if t2[1] - t2[0] >= 1e-3:
+                assert st["argmax"][r] == ref["argmax"], r
+            if tau > 0:
+                assert abs(st["logZ"][r] - ref["logZ"]) <= REL_TOL * abs(ref["logZ"])
+                assert abs(st["entropy"][r] - ref["H"]) <= REL_TOL * max(abs(ref["H"]), 1e-3)
+        e = edge.cpu().numpy()
+        oe = ostep.edge_logits(z, tok, tree)
+        assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
