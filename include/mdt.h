@@ -10,6 +10,7 @@
  *   mdt_accept_path       greedy or typical acceptance -> longest accepted path
  *   mdt_kv_compact        append the accepted path's keys/values to the cache
  *   mdt_accept_compact    the last two in one launch (same results)
+ *   mdt_verify_accept_compact  the last three in two launches (same results)
  *   mdt_next_state        hidden state the next step starts from (multi-step decoding)
  *   mdt_next_logits       the next step's LM-head row, taken from the verifier
  *   mdt_accept_rejection  rejection-sampling acceptance on the tree (a third acceptance rule)
@@ -424,6 +425,25 @@ mdt_status mdt_accept_compact(void* stream, mdt_dtype dt, int B, int H, int Dh, 
                               int mode, float eps, float delta, float temperature, int32_t* path, int path_stride,
                               int32_t* n_acc, const void* k_rot, const void* v, const mdt_kv_cache* cache,
                               const int32_t* prefix_len, int32_t* new_prefix_len);
+
+/*
+ * mdt_verify_logits, mdt_accept_path and mdt_kv_compact in two launches: the verifier's
+ * tile kernel, then one workgroup per sequence that merges its rows' statistics, selects
+ * the accepted path and appends its keys and values to the cache (the end of one
+ * iteration: summary page, section 3.2, and "Tree Attention" steps 5-6).  Every output --
+ * stats, edge_logit, logits_opt, path, n_acc, the cache rows, new_prefix_len -- is exactly
+ * what the three calls write in sequence with the same arguments (one temperature serves
+ * the verifier and the acceptance).  Arguments as in those calls, with x [B*T][d] the node
+ * outputs and k_rot, v [B][T][H][Dh]; ws >= mdt_verify_logits_workspace(dt, B, T, d, V).
+ * Every check of the three calls runs before the first launch, with the same error codes.
+ */
+mdt_status mdt_verify_accept_compact(void* stream, mdt_dtype dt, int B, int T, int d, int V, int H, int Dh,
+                                     const void* x, const void* Wlm, const mdt_tree_dev* tree,
+                                     const int32_t* tree_tokens, float temperature, int mode, float eps, float delta,
+                                     mdt_row_stats* stats, float* edge_logit, float* logits_opt, int32_t* path,
+                                     int path_stride, int32_t* n_acc, const void* k_rot, const void* v,
+                                     const mdt_kv_cache* cache, const int32_t* prefix_len, int32_t* new_prefix_len,
+                                     void* ws, size_t ws_bytes);
 
 /*
  * Rejection-sampling acceptance on the tree.  "Accelerating LLM Inference with

@@ -96,6 +96,11 @@ _SIGS = [
     ("mdt_accept_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, ctypes.POINTER(TreeDev), c_void_p, c_void_p,
                                    c_void_p, c_int, c_float, c_float, c_float, c_void_p, c_int, c_void_p, c_void_p,
                                    c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p]),
+    ("mdt_verify_accept_compact", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                          c_void_p, ctypes.POINTER(TreeDev), c_void_p, c_float, c_int, c_float,
+                                          c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                          c_void_p, ctypes.POINTER(KVCacheDesc), c_void_p, c_void_p, c_void_p,
+                                          c_size]),
     ("mdt_next_state", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                c_void_p]),
     ("mdt_next_logits", c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
@@ -495,6 +500,35 @@ def accept_compact(stats, edge, tree_tokens, tree: DeviceTree, mode: int, eps, d
                                   ctypes.byref(cache.desc), _ptr(prefix_len), _ptr(new_prefix_len)),
            "accept_compact")
     return path, n_acc, new_prefix_len
+
+
+def verify_accept_compact(x, Wlm, tree: DeviceTree, tree_tokens, temperature: float, mode: int, eps, delta, k_rot,
+                          v, cache: KVCache, prefix_len, stats=None, edge=None, logits=None, want_logits=False,
+                          path=None, n_acc=None, new_prefix_len=None, path_stride=None, ws=None, stream=None):
+    """verify_logits, accept_path and kv_compact in two launches; returns
+    (stats, edge, logits or None, path, n_acc, new_prefix_len)."""
+    M, d = x.shape
+    V = Wlm.shape[0]
+    B, T = tree_tokens.shape
+    _, _, H, Dh = k_rot.shape
+    dev = x.device
+    stats = torch.empty((M, 4), dtype=torch.int32, device=dev) if stats is None else stats
+    edge = torch.empty((B, T), dtype=torch.float32, device=dev) if edge is None else edge
+    if want_logits and logits is None:
+        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    path_stride = tree.tree.max_depth + 1 if path_stride is None else path_stride
+    path = torch.empty((B, path_stride), dtype=torch.int32, device=dev) if path is None else path
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    new_prefix_len = torch.empty_like(prefix_len) if new_prefix_len is None else new_prefix_len
+    dt = _dtype_code(x)
+    ws, nb = _ws(verify_logits_workspace(dt, B, T, d, V), dev, ws)
+    _check(lib.mdt_verify_accept_compact(_stream(stream), dt, B, T, d, V, H, Dh, _ptr(x), _ptr(Wlm),
+                                         ctypes.byref(tree.desc), _ptr(tree_tokens), float(temperature), int(mode),
+                                         float(eps), float(delta), _ptr(stats), _ptr(edge),
+                                         _ptr(logits) if want_logits else None, _ptr(path), path_stride, _ptr(n_acc),
+                                         _ptr(k_rot), _ptr(v), ctypes.byref(cache.desc), _ptr(prefix_len),
+                                         _ptr(new_prefix_len), _ptr(ws), nb), "verify_accept_compact")
+    return stats, edge, logits if want_logits else None, path, n_acc, new_prefix_len
 
 
 def kv_compact_layers(path, n_acc, k_rot, v, cache: KVCache, prefix_len, cache_layer_stride: int,

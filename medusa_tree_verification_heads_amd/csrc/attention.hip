@@ -641,6 +641,9 @@ Plan plan(int B, int T, int H, int capacity) {
             best_tps = tps;
         }
     }
+#ifdef MDT_ATTN_TPS
+    best_tps = MDT_ATTN_TPS < tiles ? MDT_ATTN_TPS : tiles;
+#endif
     p.tiles_per_split = best_tps;
     p.nsplit = (tiles + best_tps - 1) / best_tps;
     // prefix splits plus one tree split

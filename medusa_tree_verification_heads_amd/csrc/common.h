@@ -94,6 +94,28 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
+// XCD-aware tile order for a grid of Mb x Nb workgroups that share weight blocks across the
+// Mb row blocks.  The dispatcher deals workgroups round-robin over the 8 XCDs (linear id g
+// goes to XCD g % 8), and each XCD has its own L2.  The linear ids are remapped so that
+// all Mb workgroups of one weight block land on the same XCD, one after another: XCD x
+// takes weight blocks x, x + 8, ... (of the first Nb - Nb % 8), each with its Mb row
+// blocks; the remaining blocks keep the plain order.
+#ifndef MDT_NUM_XCD
+#define MDT_NUM_XCD 8
+#endif
+__device__ __forceinline__ void xcd_tile(int g, int Mb, int Nb, int& m, int& n) {
+    const int nfull = Nb - Nb % MDT_NUM_XCD;
+    if (g < Mb * nfull) {
+        const int xcd = g % MDT_NUM_XCD, slot = g / MDT_NUM_XCD;
+        m = slot % Mb;
+        n = (slot / Mb) * MDT_NUM_XCD + xcd;
+    } else {
+        const int r = g - Mb * nfull;
+        m = r % Mb;
+        n = nfull + r / Mb;
+    }
+}
+
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {

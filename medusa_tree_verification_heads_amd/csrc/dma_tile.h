@@ -42,6 +42,12 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0) alone.  At the end of a pipelined iteration the next iteration's
+// first fragments are complete by then (the MFMAs issued in between take longer); with
+// nothing pending across the loop's back edge, the compiler's own wait before the next
+// MFMAs covers only the reads issued in the same iteration.
+__device__ __forceinline__ void lds_done() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8)); }
+
 template <int KC, int NB, int CG, int KS, int S>
 struct DmaTile {
     static constexpr int NW = CG * KS;
@@ -169,4 +175,145 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
         }
     }
     if (kh == 0) epi(acc);
+}
+
+// The 16-byte piece of a chunk row that sits in slot j of the row's LDS slots: rows of
+// 16 or more pieces XOR with the row's low four bits; rows of 8 pieces (128 bytes, half a
+// bank window) with bits 1..3, the row's parity already splitting the window.  Either way
+// the 16 rows of an MFMA fragment read land in 16 distinct bank groups.
+template <int kPR>
+__device__ __forceinline__ int dma_swz(int j, int r) {
+    static_assert(kPR == 8 || kPR % 16 == 0, "8 or a multiple of 16 pieces per row");
+    return kPR >= 16 ? (j ^ (r & 15)) : (j ^ ((r >> 1) & 7));
+}
+
+// An MB x NB tile of x W^T (x rows m0.., weight rows n0..) for products with many x rows,
+// staged like dma_tile (direct global-to-LDS loads into an S-stage ring of KC-dim chunks)
+// without splitting the inner dimension: WM x WN waves, wave (wm, wn) = (w / WN, w % WN)
+// owns x rows wm MB/WM .. and weight rows wn NB/WN .., i.e. MTW x NTW MFMA fragments.
+//
+// Software pipeline: the fragments of k-step s+1 are read from LDS while the MFMAs of step
+// s run (two register sets), and the one barrier per chunk sits before the chunk's last
+// k-step -- its fragments are already in registers, so the barrier both publishes chunk
+// c+1 and frees chunk c's buffer, which is refilled with chunk c+S right away, and the
+// first fragments of chunk c+1 are read while the last MFMAs of chunk c run.
+// epi(acc) runs on every wave: acc[nt][mt] holds weight rows wn NB/WN + 16 nt + l%16 and x
+// rows wm MB/WM + 16 mt + 4 (l/16) + e.  Rows past M / V read the last valid row; d must be
+// a multiple of KC.
+template <int MB, int NB, int WM, int WN, int KC, int S>
+struct DmaGemm {
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = 64 * NW;
+    static constexpr int kPR = KC / 8;
+    static constexpr int kXBytes = MB * KC * 2;
+    static constexpr int kWBytes = NB * KC * 2;
+    static constexpr int kStage = kXBytes + kWBytes;
+    static constexpr int kIX = MB * kPR / 64 / NW;
+    static constexpr int kIW = NB * kPR / 64 / NW;
+    static constexpr int kLoads = kIX + kIW;
+    static constexpr int kRingBytes = S * kStage;
+    static constexpr int MTW = MB / WM / 16;
+    static constexpr int NTW = NB / WN / 16;
+    static constexpr int KSTEPS = KC / 32;
+    static_assert(KC % 64 == 0 && (kPR == 8 || kPR % 16 == 0), "chunk shape");
+    static_assert(MB * kPR % (64 * NW) == 0 && NB * kPR % (64 * NW) == 0, "loads divide among the waves");
+    static_assert(MB % (16 * WM) == 0 && NB % (16 * WN) == 0, "fragments divide among the waves");
+    static_assert(S >= 2 && S <= 4 && kLoads * (S - 1) < 64, "stages / vmcnt range");
+};
+
+template <int MB, int NB, int WM, int WN, int KC, int S, int AUX = 0, typename Epi>
+__device__ __forceinline__ void dma_gemm_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
+                                              int d, int V, int m0, int n0, char* smem, Epi&& epi) {
+    using P = DmaGemm<MB, NB, WM, WN, KC, S>;
+    constexpr int kPR = P::kPR, MTW = P::MTW, NTW = P::NTW, KSTEPS = P::KSTEPS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nch = d / KC;
+
+    auto issue = [&](int c) {
+        char* st = smem + (c % S) * P::kStage;
+#pragma unroll
+        for (int j = 0; j < P::kIX; ++j) {
+            const int i = wave * P::kIX + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
+            const bf16_t* src = x + (size_t)min(m0 + r, M - 1) * d + c * KC + 8 * p;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < P::kIW; ++j) {
+            const int i = wave * P::kIW + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
+            const bf16_t* src = W + (size_t)min(n0 + r, V - 1) * d + c * KC + 8 * p;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P::kXBytes + 1024 * i), 16, 0,
+                                             AUX);
+        }
+    };
+    // wait until chunk c has landed (at most `later` chunks issued after it outstanding),
+    // then meet at the barrier
+    auto landed = [&](int later) {
+        if (later >= 3)
+            ring_barrier<3 * P::kLoads>();
+        else if (later == 2)
+            ring_barrier<2 * P::kLoads>();
+        else if (later == 1)
+            ring_barrier<P::kLoads>();
+        else
+            ring_barrier<0>();
+    };
+
+    f32x4 acc[NTW][MTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 fa[2][MTW], fb[2][NTW];
+    // fragments of k-step s of the chunk in ring slot `slot` into register set `set`
+    auto read = [&](int slot, int s, int set) {
+        const bf16_t* xs = (const bf16_t*)(smem + slot * P::kStage);
+        const bf16_t* ws = (const bf16_t*)(smem + slot * P::kStage + P::kXBytes);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) {
+            const int row = wm * (MB / WM) + 16 * mt + c16;
+            fa[set][mt] = *(const u32x4*)(xs + (row * kPR + dma_swz<kPR>(4 * s + g, row)) * 8);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int row = wn * (NB / WN) + 16 * nt + c16;
+            fb[set][nt] = *(const u32x4*)(ws + (row * kPR + dma_swz<kPR>(4 * s + g, row)) * 8);
+        }
+    };
+    auto mma = [&](int set) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) acc[nt][mt] = mfma16(fa[set][mt], fb[set][nt], acc[nt][mt]);
+    };
+
+#pragma unroll
+    for (int c = 0; c < S; ++c)
+        if (c < nch) issue(c);
+    landed(min(S - 1, nch - 1));
+    read(0, 0, 0);
+    lds_done();
+    for (int c = 0; c < nch; ++c) {
+        const int slot = c % S;
+#pragma unroll
+        for (int s = 0; s + 1 < KSTEPS; ++s) {
+            read(slot, s + 1, (s + 1) & 1);
+            mma(s & 1);
+        }
+        // chunk c's last fragments are in registers: publish chunk c+1, free chunk c's buffer
+        if (c + 1 < nch) {
+            landed(min(S - 2, nch - 2 - c));
+            if (c + S < nch) issue(c + S);
+            read((c + 1) % S, 0, KSTEPS & 1);
+        }
+        mma((KSTEPS - 1) & 1);
+        lds_done();
+    }
+    __syncthreads();  // the ring is free for the caller's epilogue
+    epi(acc);
 }

@@ -22,12 +22,13 @@
 
 #include "dma_tile.h"
 #include "mfma_tile.h"
+#include "verify_core.h"
 
 namespace {
 
 constexpr int kNB = 64;          // vocabulary columns per workgroup
 constexpr int kMB = 64;          // node rows per workgroup (bf16 path)
-constexpr int kBigRows = 256;    // from this many node rows on: 128 x 128 tiles
+constexpr int kBigRows = 256;    // from this many node rows on: the compute-bound tiles
 constexpr int kZStride = kNB + 1;
 #ifndef MDT_VERIFY_KC
 #define MDT_VERIFY_KC 256        // dims per staged chunk (LDS holds one 64-row tile of x and of W)
@@ -35,39 +36,6 @@ constexpr int kZStride = kNB + 1;
 #ifndef MDT_VERIFY_NB
 #define MDT_VERIFY_NB 64         // vocabulary columns per MFMA workgroup (4 waves of 16 per 64)
 #endif
-
-struct Part {
-    float m;
-    int a;
-    float s;
-    float u;
-};
-
-__device__ __forceinline__ Part part_merge(Part p, Part q, float tau) {
-    if (q.m == -INFINITY) return p;
-    if (p.m == -INFINITY) return q;
-    Part r;
-    r.m = fmaxf(p.m, q.m);
-    r.a = better(p.m, p.a, q.m, q.a) ? p.a : q.a;
-    if (tau > 0.f) {
-        const float dp = (p.m - r.m) / tau, dq = (q.m - r.m) / tau;
-        const float fp = expf(dp), fq = expf(dq);
-        r.s = fp * p.s + fq * q.s;
-        r.u = fp * (p.u + p.s * dp) + fq * (q.u + q.s * dq);
-    } else {
-        r.s = r.u = 0.f;
-    }
-    return r;
-}
-
-__device__ __forceinline__ Part shfl_xor_part(Part p, int off) {
-    Part q;
-    q.m = __shfl_xor(p.m, off, 64);
-    q.a = __shfl_xor(p.a, off, 64);
-    q.s = __shfl_xor(p.s, off, 64);
-    q.u = __shfl_xor(p.u, off, 64);
-    return q;
-}
 
 // Reduce a logits tile zt[MT][NB + 1] (rows m0.., cols n0..) to per-row partials,
 // write optional full logits and the edge logits that fall inside the tile.
@@ -115,7 +83,7 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
         }
     }
 #pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
+    for (int off = 1; off < TPR; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau > 0.f ? 1.f / tau : 0.f);
     if (q == 0 && row < M) part[(long)row * nblk_n + n0 / NB] = p;
     if (logits_opt && row < M)
         for (int c = q * CPT; c < q * CPT + CPT && c < ncol; ++c) logits_opt[(long)row * V + n0 + c] = z[c];
@@ -149,9 +117,11 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
     constexpr int MB = 16 * MT;
     static_assert(MfmaTile<KC, NB, MT>::kBytes >= MB * (NB + 1) * 4, "the logits tile must fit");
     __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB, MT>::kBytes];
-    // MMAJOR: blockIdx.x walks the node-row blocks, so the workgroups that read one block
-    // of weight rows are dispatched together and share it through the caches
-    const int n0 = (MMAJOR ? blockIdx.y : blockIdx.x) * NB, m0 = (MMAJOR ? blockIdx.x : blockIdx.y) * MB;
+    // MMAJOR: the workgroups that read one block of weight rows run on one XCD, one after
+    // another, and share it through its L2
+    int mb = blockIdx.y, nb = blockIdx.x;
+    if (MMAJOR) xcd_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, mb, nb);
+    const int n0 = nb * NB, m0 = mb * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
@@ -248,6 +218,66 @@ __global__ __launch_bounds__(VDma::NT) void verify_dma(const bf16_t* __restrict_
     tile_epilogue<kMB, NB, VDma::NT>(zt, 0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
+// Many node rows (batches, 256-node trees) with the DMA-staged tile: 256 x 128 tiles on 8
+// waves (4 x 2, each 64 x 64: two waves per SIMD hide each other's LDS and barrier waits;
+// four waves of 128 x 64 were 12 % slower, 128-row tiles slower still), 64-dim chunks in a
+// 3-stage ring, the row blocks of one weight block together on one XCD, partials per 128
+// columns.  grid (ceil(M/256), ceil(V/128)).
+#ifndef MDT_VBIG_MB
+#define MDT_VBIG_MB 256
+#endif
+#ifndef MDT_VBIG_S
+#define MDT_VBIG_S 3
+#endif
+#ifndef MDT_VBIG_AUX
+#define MDT_VBIG_AUX 0
+#endif
+#ifndef MDT_VBIG_WM
+#define MDT_VBIG_WM 4
+#endif
+#ifndef MDT_VBIG_WN
+#define MDT_VBIG_WN 2
+#endif
+#ifndef MDT_VBIG_KC
+#define MDT_VBIG_KC 64
+#endif
+constexpr int kBigMB = MDT_VBIG_MB;
+using VBig = DmaGemm<kBigMB, 128, MDT_VBIG_WM, MDT_VBIG_WN, MDT_VBIG_KC, MDT_VBIG_S>;
+
+__global__ __launch_bounds__(VBig::NT) void verify_dma_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+                                                           int M, int d, int V, float tau, int nblk_n,
+                                                           Part* __restrict__ part, float* __restrict__ logits_opt,
+                                                           const int32_t* __restrict__ parent,
+                                                           const int32_t* __restrict__ tokens, int T,
+                                                           float* __restrict__ edge) {
+    constexpr int MB = kBigMB, NB = 128, kZ = NB + 1;
+    constexpr int kEpi = MB * kZ * 4;
+    constexpr int kLds = VBig::kRingBytes > kEpi ? VBig::kRingBytes : kEpi;
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    int mb, nb;  // the row blocks of one weight block together, on one XCD
+    xcd_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, mb, nb);
+    const int m0 = mb * MB, n0 = nb * NB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    constexpr int WM = MDT_VBIG_WM, WN = MDT_VBIG_WN;
+    const int wm = wave / WN, wn = wave % WN;
+    const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
+    float* zt = (float*)smem;  // [MB][NB + 1], reuses the ring
+    dma_gemm_tile<MB, NB, WM, WN, MDT_VBIG_KC, MDT_VBIG_S, MDT_VBIG_AUX>(
+        x, W, M, d, V, m0, n0, smem, [&](const f32x4 (&acc)[VBig::NTW][VBig::MTW]) {
+#pragma unroll
+            for (int nt = 0; nt < VBig::NTW; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < VBig::MTW; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        zt[((MB / WM) * wm + 16 * mt + 4 * g + e) * kZ + (NB / WN) * wn + 16 * nt + c16] =
+                            acc[nt][mt][e];
+        });
+    __syncthreads();
+    tile_epilogue<MB, NB, VBig::NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
+}
+
 // Many node rows (batches, 256-node trees): 128 x 128 tiles (mfma_tile128), grid
 // (ceil(M/128), ceil(V/128)) row-block-major, partials per 128 vocabulary columns.
 template <int KC>
@@ -260,7 +290,9 @@ __global__ __launch_bounds__(256) void verify_mfma128(const bf16_t* __restrict__
     constexpr int kZ = 128 + 1;
     constexpr int kLds = MfmaTile128<KC>::kBytes > 128 * kZ * 4 ? MfmaTile128<KC>::kBytes : 128 * kZ * 4;
     __shared__ __attribute__((aligned(16))) char smem[kLds];
-    const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 128;
+    int mb, nb;  // the row blocks of one weight block together, on one XCD
+    xcd_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, mb, nb);
+    const int m0 = mb * 128, n0 = nb * 128;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
@@ -312,46 +344,20 @@ __global__ __launch_bounds__(256) void verify_f32(const float* __restrict__ x, c
                       edge_preload<16>(m0, M, parent, tokens, T));
 }
 
-// Merge row partials in block order; grid (M), block 64.  Also writes the edge
-// entries that no tile owns (root, out-of-range tokens).
-__global__ __launch_bounds__(64) void verify_merge(const Part* __restrict__ part, int nblk_n, int V, float tau,
-                                                   mdt_row_stats* __restrict__ stats, const int32_t* __restrict__ tokens,
-                                                   const int32_t* __restrict__ parent, int T, float* __restrict__ edge) {
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x;
-    // all loads of a batch are issued before the merges (one round trip per 512 partials)
-    const Part* pr = part + (long)row * nblk_n;
-    Part p{-INFINITY, INT_MAX, 0.f, 0.f};
-    for (int j0 = 0; j0 < nblk_n; j0 += 64 * 8) {
-        Part q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = pr[min(j0 + lane + 64 * u, nblk_n - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (j0 + lane + 64 * u < nblk_n) p = part_merge(p, q[u], tau);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau);
-    if (lane == 0) {
-        mdt_row_stats st;
-        st.max = p.m;
-        st.argmax = p.a;
-        if (tau > 0.f) {
-            const float lnS = logf(p.s);
-            st.logZ = p.m / tau + lnS;
-            st.entropy = lnS - p.u / p.s;
-        } else {
-            st.logZ = 0.f;
-            st.entropy = 0.f;
-        }
-        stats[row] = st;
-        const int c = row % T;
-        const int tok = tokens[row];
-        const int pr = parent[c];
-        if (c == 0)
-            edge[row] = 0.f;
-        else if (tok < 0 || tok >= V || pr < 0 || pr >= T)
-            edge[row] = -INFINITY;
+// Merge row partials; grid ceil(M / 4), block 64: each 16-lane group of the wave merges one
+// row (merge_row).  Also writes the edge entries that no tile owns (root, out-of-range
+// tokens).
+__global__ __launch_bounds__(64) void verify_merge(const Part* __restrict__ part, int M, int nblk_n, int V,
+                                                   float tau, mdt_row_stats* __restrict__ stats,
+                                                   const int32_t* __restrict__ tokens,
+                                                   const int32_t* __restrict__ parent, int T,
+                                                   float* __restrict__ edge) {
+    const int row = blockIdx.x * (64 / kMergeLanes) + (int)threadIdx.x / kMergeLanes;
+    const int sub = threadIdx.x % kMergeLanes;
+    const Part p = merge_row(part + (long)min(row, M - 1) * nblk_n, nblk_n, tau > 0.f ? 1.f / tau : 0.f, sub);
+    if (sub == 0 && row < M) {
+        stats[row] = row_stats_of(p, tau);
+        edge_defaults(row, T, V, tokens, parent, edge);
     }
 }
 
@@ -364,10 +370,10 @@ extern "C" size_t mdt_verify_logits_workspace(mdt_dtype dt, int B, int T, int d,
     return (size_t)B * T * ((V + kNB - 1) / kNB) * sizeof(Part);
 }
 
-extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T, int d, int V, const void* x,
-                                        const void* Wlm, const mdt_tree_dev* tree, const int32_t* tree_tokens,
-                                        float temperature, mdt_row_stats* stats, float* edge_logit,
-                                        float* logits_opt, void* ws, size_t ws_bytes) {
+mdt_status mdt_verify_tiles(hipStream_t s, mdt_dtype dt, int B, int T, int d, int V, const void* x, const void* Wlm,
+                            const mdt_tree_dev* tree, const int32_t* tree_tokens, float temperature,
+                            mdt_row_stats* stats, float* edge_logit, float* logits_opt, void* ws, size_t ws_bytes,
+                            int* nblk_n_out) {
     MDT_REQUIRE(dt == MDT_F32 || dt == MDT_BF16, MDT_ERR_DTYPE, "dtype %d not supported", (int)dt);
     mdt_status st = mdt_check_tree(tree);
     if (st != MDT_OK) return st;
@@ -385,7 +391,6 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
     MDT_REQUIRE(ws_bytes >= mdt_verify_logits_workspace(dt, B, T, d, V), MDT_ERR_WORKSPACE, "workspace too small");
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
-    hipStream_t s = (hipStream_t)stream;
     const int M = B * T;
     const bool big = dt == MDT_BF16 && M >= kBigRows;
     // one row block whose 64-column grid overfills the CUs: the 16-wave tile, 128 columns
@@ -399,7 +404,11 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
     const int nb_cols = big || wide || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
-    if (big) {
+    if (big && d % MDT_VBIG_KC == 0) {
+        MDT_LAUNCH("verify_mfma", verify_dma_big, dim3((M + kBigMB - 1) / kBigMB, nblk_n), dim3(VBig::NT), 0, s,
+                   (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
+                   tree_tokens, T, edge_logit);
+    } else if (big) {  // inner dimension not a multiple of the chunk
         auto kern = verify_mfma128<64>;
         MDT_LAUNCH("verify_mfma", kern, dim3((M + 127) / 128, nblk_n), dim3(256), 0, s, (const bf16_t*)x,
                    (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
@@ -429,9 +438,21 @@ extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T
                            (const float*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
                            tree_tokens, T, edge_logit);
     }
-    st = mdt_launched(dt == MDT_BF16 ? "verify_mfma" : "verify_f32");
+    *nblk_n_out = nblk_n;
+    return mdt_launched(dt == MDT_BF16 ? "verify_mfma" : "verify_f32");
+}
+
+extern "C" mdt_status mdt_verify_logits(void* stream, mdt_dtype dt, int B, int T, int d, int V, const void* x,
+                                        const void* Wlm, const mdt_tree_dev* tree, const int32_t* tree_tokens,
+                                        float temperature, mdt_row_stats* stats, float* edge_logit,
+                                        float* logits_opt, void* ws, size_t ws_bytes) {
+    hipStream_t s = (hipStream_t)stream;
+    int nblk_n = 0;
+    const mdt_status st = mdt_verify_tiles(s, dt, B, T, d, V, x, Wlm, tree, tree_tokens, temperature, stats,
+                                           edge_logit, logits_opt, ws, ws_bytes, &nblk_n);
     if (st != MDT_OK) return st;
-    MDT_LAUNCH("verify_merge", verify_merge, dim3(M), dim3(64), 0, s, part, nblk_n, V, temperature, stats, tree_tokens,
-                       tree->parent, T, edge_logit);
+    constexpr int kRowsPerWave = 64 / kMergeLanes;
+    MDT_LAUNCH("verify_merge", verify_merge, dim3((B * T + kRowsPerWave - 1) / kRowsPerWave), dim3(64), 0, s, (const Part*)ws, B * T, nblk_n, V,
+               temperature, stats, tree_tokens, tree->parent, T, edge_logit);
     return mdt_launched("verify_merge");
 }

@@ -6,7 +6,9 @@ workspace once, and ``run()`` enqueues
     medusa_heads -> topk_tree_expand -> tree_attention -> verify_logits
     -> accept_path -> kv_compact
 
-(the last two as the single launch accept_compact unless ``fused_tail=False``)
+(by default the last two as the single launch accept_compact; ``tail`` can select
+verify_accept_compact -- the verifier's tiles, then one launch per sequence that merges
+the row statistics, accepts and compacts -- and ``fused_tail=False`` the separate calls)
 with no host synchronisation, so a step can also be captured in a HIP graph.
 The order is the information flow of the summary page ("Medusa: Simple LLM
 Inference Acceleration Framework with Multiple Decoding Heads", section 3.2).
@@ -18,7 +20,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path,
+from . import (GREEDY, TYPICAL, MDT_BF16, MDT_F32, KVCache, Tree, accept_compact, accept_path, verify_accept_compact,
                accept_rejection, kv_compact, medusa_heads, next_logits, next_state,
                medusa_heads_workspace, new_workspace, topk_tree_expand, topk_workspace, tree_attention,
                tree_attention_workspace, verify_logits, verify_logits_workspace)
@@ -34,7 +36,7 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
 class VerifyStep:
     def __init__(self, w, inp: dict, mode: str = "greedy", temperature: float = 0.0, eps: float = 0.09,
                  delta: float = 0.3, device="cuda", want_logits: bool = False, tree: Tree = None,
-                 fused_tail: bool = True):
+                 fused_tail: bool = True, tail: str = "accept_compact"):
         self.w = w
         if mode not in ("greedy", "typical", "rejection"):
             raise ValueError(f"unknown acceptance mode {mode!r} (greedy, typical or rejection)")
@@ -43,7 +45,13 @@ class VerifyStep:
         # two calls
         self.rejection = mode == "rejection"
         want_logits = want_logits or self.rejection
-        self.fused_tail = fused_tail and not self.rejection
+        # how the step ends: "verify_accept_compact" (verifier tiles, then merge, acceptance and
+        # compaction in one launch), "accept_compact" (verify_logits, then acceptance and
+        # compaction in one launch) or "separate" (the three calls); all write the same bits
+        if tail not in ("verify_accept_compact", "accept_compact", "separate"):
+            raise ValueError(f"unknown tail {tail!r}")
+        self.tail = "separate" if (not fused_tail or self.rejection) else tail
+        self.fused_tail = self.tail != "separate"
         self.mode = GREEDY if mode == "greedy" else TYPICAL
         self.temperature, self.eps, self.delta = float(temperature), float(eps), float(delta)
         dev = torch.device(device)
@@ -103,6 +111,12 @@ class VerifyStep:
         tree_attention(q, k, v, self.cache, prefix_len, self.tree, w.rope_theta, out=self.o,
                        k_rot=self.k_rot, ws=self.ws_attn, stream=stream)
         x = self.o.view(w.B * self.tree.T, w.d)
+        if self.tail == "verify_accept_compact":
+            verify_accept_compact(x, t["Wlm"], self.tree, tokens, self.temperature, self.mode, self.eps, self.delta,
+                                  self.k_rot, v, self.cache, prefix_len, stats=self.stats, edge=self.edge,
+                                  logits=vlogits, want_logits=vlogits is not None, path=path, n_acc=n_acc,
+                                  new_prefix_len=new_len, ws=self.ws_verify, stream=stream)
+            return
         verify_logits(x, t["Wlm"], self.tree, tokens, self.temperature, stats=self.stats, edge=self.edge,
                       logits=vlogits, want_logits=vlogits is not None, ws=self.ws_verify, stream=stream)
         if self.rejection:
@@ -110,7 +124,7 @@ class VerifyStep:
                              self.u_resample, path=path, n_acc=n_acc, next_token=self.next_token, stream=stream)
             kv_compact(path, n_acc, self.k_rot, v, self.cache, prefix_len, new_len, stream=stream)
             return
-        if self.fused_tail:
+        if self.tail == "accept_compact":
             accept_compact(self.stats, self.edge, tokens, self.tree, self.mode, self.eps, self.delta,
                            self.temperature, self.k_rot, v, self.cache, prefix_len, path=path,
                            n_acc=n_acc, new_prefix_len=new_len, stream=stream)

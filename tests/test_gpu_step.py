@@ -13,12 +13,13 @@ pytestmark = pytest.mark.gpu
 KEYS = ("logits", "topk_idx", "tokens", "pos", "o", "k_rot", "stats", "edge", "path", "n_acc", "new_len", "Kc", "Vc")
 
 
-def _make(name, run_idx=1, fused_tail=True):
+def _make(name, run_idx=1, fused_tail=True, tail="verify_accept_compact", want_logits=False):
     from medusa_tree_verification_heads_amd.step import VerifyStep
     w, inp = case_inputs(name)
     run = w.accept[min(run_idx, len(w.accept) - 1)]
-    note(f"step {name} {run} fused_tail={fused_tail}")
-    return VerifyStep(w, inp, run.mode, run.temperature, run.eps, run.delta, fused_tail=fused_tail)
+    note(f"step {name} {run} fused_tail={fused_tail} tail={tail}")
+    return VerifyStep(w, inp, run.mode, run.temperature, run.eps, run.delta, fused_tail=fused_tail, tail=tail,
+                      want_logits=want_logits)
 
 
 def _same(a, b):
@@ -39,12 +40,17 @@ def test_repeated_steps_are_bit_identical(name):
 @pytest.mark.parametrize("run_idx", [0, 1])
 @pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged", "33b-mini", "tiny-fp32-T10"])
 def test_fused_tail_matches_separate_calls(name, run_idx):
-    """accept_compact writes exactly what accept_path then kv_compact write."""
-    sep = _make(name, run_idx, fused_tail=False)
+    """verify_accept_compact writes exactly what verify_logits, accept_path and kv_compact
+    write, and so does verify_logits then accept_compact (full logits included)."""
+    sep = _make(name, run_idx, fused_tail=False, want_logits=True)
     sep.run()
-    fused = _make(name, run_idx, fused_tail=True)
-    fused.run()
-    _same(sep.outputs(), fused.outputs())
+    ref = sep.outputs()
+    for tail in ("accept_compact", "verify_accept_compact"):
+        fused = _make(name, run_idx, tail=tail, want_logits=True)
+        fused.run()
+        out = fused.outputs()
+        _same(ref, out)
+        assert np.array_equal(ref["vlogits"], out["vlogits"])
 
 
 @pytest.mark.parametrize("name", ["7b-mini", "7b-B16-mini-paged"])

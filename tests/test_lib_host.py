@@ -168,6 +168,15 @@ def test_verify_accept_compact_validation():
     assert fused(dt=1, H=1, Dh=3) == -2                       # the kv_compact checks
     assert fused(dt=2) == -3
     assert fused(kr=None) == -1 and fused(kr=MIS) == -4
+    vac = mdt.lib.mdt_verify_accept_compact
+    def tail(T=64, d=4096, tau=0.7, mode=1, eps=0.09, stride=5, H=32, Dh=128, dt=1, kr=P, nb=1 << 30):
+        return vac(None, dt, 1, T, d, 32000, H, Dh, P, P, ctypes.byref(d_), P, tau, mode, eps, 0.3, P, P, None, P,
+                   stride, P, kr, P, ctypes.byref(c), P, P, P, nb)
+    d_ = d
+    assert tail(mode=3) == -6 and tail(eps=0.0) == -6 and tail(stride=4) == -2   # the accept_path checks
+    assert tail(H=1, Dh=3) == -2 and tail(kr=None) == -1                          # the kv_compact checks
+    assert tail(T=63) == -2 and tail(d=4008) == -2 and tail(tau=-1.0) == -6       # the verify_logits checks
+    assert tail(nb=16) == -7
 
 
 def test_next_state_and_rejection_validation():
