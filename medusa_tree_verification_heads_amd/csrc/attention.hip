@@ -19,6 +19,8 @@
 //     positions (writing k_rot, which is what gets cached) and attends to them
 //     under the ancestor-or-self bitmask.  Rotation angles come from a per-depth
 //     cos/sin table built in LDS.  Partial (m, l, O) go to the workspace.
+//     Trees of up to 128 nodes use attn_stream, the same pass with the prefix tiles
+//     streamed by direct global-to-LDS loads through a ring (see there).
 //  2. attn_combine: per (sequence, head, node) merge the partials, write o (bf16).
 // fp32 path: one wave per (sequence, head, node) walks all allowed keys on VALU.
 #include <math.h>
@@ -26,6 +28,7 @@
 #include <cmath>
 
 #include "common.h"
+#include "dma_tile.h"
 
 namespace {
 
@@ -39,7 +42,8 @@ constexpr int kDh = 128;           // head dim of the MFMA path
 constexpr int kKStride = kDh + 8;  // LDS row stride of K tile (elements)
 constexpr int kVStride = kTile + 4;  // LDS row stride of transposed V tile (elements)
 constexpr int kMaxSplitPages = 4096;  // page-table entries a workgroup stages in LDS
-constexpr int kMaxTilesPerSplit = (kMaxSplitPages - 2) * 1 / kTile;  // holds for page_size >= 1
+constexpr int kMaxTilesPerSplit = (2048 - 2) * 1 / kTile;  // page-table entries of a split fit both kernels' LDS
+                                                            // (page_size >= 1)
 
 struct KV {
     const void* k;
@@ -565,6 +569,307 @@ __global__ __launch_bounds__(64 * NWB) void attn_tree_mfma(AttnArgs A) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant: K and V tiles by direct global-to-LDS loads
+// ---------------------------------------------------------------------------
+//
+// The same split-KV flash pass (one (sequence, head, key split) per workgroup, waves owning
+// query tiles, S^T = K Q^T then O^T = V^T P^T on MFMA, online softmax in log2 units, the
+// last workgroup of each (sequence, head) attending to the rotated tree keys under the
+// ancestor bitmask), with the prefix tiles streamed through a kRing-stage LDS ring filled
+// by global_load_lds_dwordx4: while a tile is multiplied, the next kRing - 1 tiles are in
+// flight and no register holds them.  Both tiles stay row-major (one 256-byte row per key)
+// with their 16-byte pieces swizzled per row: K row r keeps piece p in slot p ^ (r mod 16)
+// (its MFMA fragments read 16 rows at once), V row r in slot p ^ (2 r mod 16); V^T
+// fragments come from the LDS transpose read ds_read_b64_tr_b16 -- in each 16-lane group,
+// lane i receives element i mod 4 of the 8 bytes read by lane 4 e + i / 4 as its element
+// e -- so 4 key rows x 16 dims land as 16 lanes x 4 keys.  The swizzles keep the fragment
+// and transpose reads free of bank conflicts.
+#ifndef MDT_ATTN_RING
+#define MDT_ATTN_RING 2
+#endif
+constexpr int kRing = MDT_ATTN_RING;
+constexpr int kStreamPages = 2048;              // page-table entries a streaming workgroup stages
+constexpr int kTileBytes = kTile * kDh * 2;     // one K (or V) tile: 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;     // K then V
+
+__device__ __forceinline__ int kslot(int p, int r) { return p ^ (r & 15); }
+__device__ __forceinline__ int vslot(int p, int r) { return p ^ ((2 * r) & 14); }
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+template <int NWB, bool PAGED, int QT = 1>
+__global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
+    constexpr int NT = 64 * NWB;
+    constexpr int kInstr = kTile * (kDh / 8) / 64;  // load instructions per tile (K or V): 16
+    constexpr int kIPW = 2 * kInstr / NWB;          // per wave per tile, K and V together
+    static_assert(2 * kInstr % NWB == 0 && kIPW * (kRing - 2) < 64, "loads divide among the waves");
+    __shared__ __attribute__((aligned(1024))) char ring[kRing * kStageBytes];
+    __shared__ float2 cs[(MDT_MAX_HEADS + 1) * (kDh / 2)];  // cos/sin per (depth, pair)
+    __shared__ int pages[PAGED ? kStreamPages : 1];          // physical page of each page of the split
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const bool tree_split = split == A.nsplit;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int H = A.H, T = A.T;
+    const int L = clamp_len(A.prefix_len, b, A.cache.capacity);
+    const int j_begin = tree_split ? 0 : split * A.tiles_per_split * kTile;
+    const int j_end = tree_split ? 0 : min(L, j_begin + A.tiles_per_split * kTile);
+    const int ntiles = j_end > j_begin ? (j_end - j_begin + kTile - 1) / kTile : 0;
+    const float scale = 1.f / sqrtf((float)kDh);
+    const bf16_t* Kg = (const bf16_t*)A.cache.k;
+    const bf16_t* Vg = (const bf16_t*)A.cache.v;
+    const int psz = PAGED ? A.cache.page_size : 1;
+    const int pg0 = j_begin / psz;
+
+    // this wave's queries, loaded first: in tile t the lane holds query qi[t], dims
+    // 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
+    int qi[QT], dq_raw[QT];
+    bool q_ok[QT];
+    u32x4 bq[QT][4];
+    uint64_t qa[QT][MDT_MAX_NODES / 64];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        qi[t] = (wave * QT + t) * 16 + c16;
+        q_ok[t] = qi[t] < T;
+        const int qc = q_ok[t] ? qi[t] : 0;
+        const long node = (((long)b * T + qc) * H + h) * kDh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[t][s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
+#pragma unroll
+        for (int w = 0; w < MDT_MAX_NODES / 64; ++w) qa[t][w] = A.anc[(long)qc * A.W + min(w, A.W - 1)];
+        dq_raw[t] = A.depth[qc];
+    }
+    if (PAGED) {
+        const int np = j_end > j_begin ? (j_end - 1) / psz - pg0 + 1 : 0;  // <= kStreamPages (host plan)
+        for (int e = tid; e < np; e += NT) {
+            const int pg = pg0 + e;
+            const int page = pg < A.cache.max_pages ? A.cache.table[(long)b * A.cache.max_pages + pg] : -1;
+            pages[e] = (page >= 0 && page < A.cache.num_pages) ? page : -1;
+        }
+        __syncthreads();
+    }
+    // element offset of prefix key j (j_begin <= j < j_end); an unmapped page reads the
+    // pool's first row (a caller error: the value is meaningless but the access stays inside)
+    auto key_off = [&](int j) -> long {
+        if (!PAGED) return (((long)b * A.cache.capacity + j) * H + h) * kDh;
+        const int page = pages[j / psz - pg0];
+        return page < 0 ? 0 : (((long)page * psz + j % psz) * H + h) * kDh;
+    };
+    // the tile of keys t0 .. t0 + 63 into ring slot `slot`; keys past the split's end repeat
+    // its last key (they are masked)
+    auto issue = [&](int t0, int slot) {
+        char* kst = ring + slot * kStageBytes;
+#pragma unroll
+        for (int j = 0; j < kIPW; ++j) {
+            const int i = wave * kIPW + j;
+            const bool isv = i >= kInstr;
+            const int ii = isv ? i - kInstr : i;
+            const int q = 64 * ii + lane;
+            const int r = q >> 4, sl = q & 15;
+            const int p = isv ? vslot(sl, r) : kslot(sl, r);  // the swizzles are involutions
+            const long off = key_off(min(t0 + r, j_end - 1));
+            const bf16_t* src = (isv ? Vg : Kg) + off + 8 * p;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(kst + (isv ? kTileBytes : 0) + 1024 * ii),
+                                             16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kRing - 1; ++s)
+        if (s < ntiles) issue(j_begin + s * kTile, s);
+
+    for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
+        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
+    __syncthreads();  // cos/sin table ready
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        if (!q_ok[t])
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bq[t][s] = u32x4{0, 0, 0, 0};
+        const int dq = q_ok[t] ? min(max(dq_raw[t], 0), A.max_depth) : 0;
+        const float2* row = cs + dq * (kDh / 2);
+        rotate8(bq[t][0], bq[t][2], row, 8 * g);
+        rotate8(bq[t][1], bq[t][3], row, 32 + 8 * g);
+#pragma unroll
+        for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
+            if (!(tree_split && q_ok[t] && w < A.W)) qa[t][w] = 0;
+    }
+
+    f32x4 oacc[QT][8];
+    float m_run[QT], l_run[QT];  // of query qi[t], replicated over g
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+    }
+
+    const float sl2 = scale * 1.4426950408889634f;
+    // One tile in ring slot `slot`: keys base..base+63, nvalid of them real.
+    auto attend_tile = [&](int slot, int base, int nvalid, bool masked) {
+        const bf16_t* Ks = (const bf16_t*)(ring + slot * kStageBytes);
+        const bf16_t* Vs = (const bf16_t*)(ring + slot * kStageBytes + kTileBytes);
+        f32x4 sacc[QT][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            f32x4 acc[QT];
+#pragma unroll
+            for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = kb * 16 + c16;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 kf = *(const u32x4*)(Ks + (r * 16 + kslot(4 * s + g, r)) * 8);
+#pragma unroll
+                for (int t = 0; t < QT; ++t) acc[t] = mfma16(kf, bq[t][s], acc[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < QT; ++t) sacc[t][kb] = acc[t];
+        }
+        u32x4 bp[QT][2];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            float tmax = -INFINITY;
+            if (masked) {
+                const int wi = base >> 6;
+                const uint64_t qw = !tree_split ? ~0ull
+                                  : wi == 0     ? qa[t][0]
+                                  : wi == 1     ? qa[t][1]
+                                  : wi == 2     ? qa[t][2]
+                                                : qa[t][3];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = kb * 16 + 4 * g + e;
+                        const bool ok = jj < nvalid && ((qw >> jj) & 1ull);
+                        const float sv = ok ? sacc[t][kb][e] : -INFINITY;
+                        sacc[t][kb][e] = sv;
+                        tmax = fmaxf(tmax, sv);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[t][kb][e]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax *= sl2;
+            const float m_new = fmaxf(m_run[t], tmax);
+            const bool live = m_new != -INFINITY;
+            const float corr = live ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;
+            float tsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = live ? __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][e], sl2, -m_new)) : 0.f;
+                    sacc[t][kb][e] = p;
+                    tsum += p;
+                }
+            tsum += __shfl_xor(tsum, 16, 64);
+            tsum += __shfl_xor(tsum, 32, 64);
+            l_run[t] = l_run[t] * corr + tsum;
+            m_run[t] = m_new;
+            if (__any(corr != 1.f))
+#pragma unroll
+                for (int db = 0; db < 8; ++db) oacc[t][db] *= corr;
+            // within a 32-key step the key order is 4g+e (e<4), then 16+4g+(e-4)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bp[t][ks][0] = pack_bf16(sacc[t][2 * ks][0], sacc[t][2 * ks][1]);
+                bp[t][ks][1] = pack_bf16(sacc[t][2 * ks][2], sacc[t][2 * ks][3]);
+                bp[t][ks][2] = pack_bf16(sacc[t][2 * ks + 1][0], sacc[t][2 * ks + 1][1]);
+                bp[t][ks][3] = pack_bf16(sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]);
+            }
+        }
+        // O^T += V^T P^T: lane (dim 16 db + c16, group g) takes keys 32 ks + 4 g + e and
+        // 32 ks + 16 + 4 g + e (e < 4) by two transpose reads; as a source lane it reads the 8
+        // bytes of key row 32 ks + 16 hf + 4 g + c16 / 4, dims 16 db + 4 (c16 mod 4) ..
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                u32x2 half[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int r = 32 * ks + 16 * hf + 4 * g + (c16 >> 2);
+                    const int p = 2 * db + ((c16 & 3) >> 1);
+                    const bf16_t* src = Vs + (r * 16 + vslot(p, r)) * 8 + 4 * (c16 & 1);
+                    const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s_t*)(src));
+                    half[hf] = __builtin_bit_cast(u32x2, v);
+                }
+                const u32x4 av = {half[0][0], half[0][1], half[1][0], half[1][1]};
+#pragma unroll
+                for (int t = 0; t < QT; ++t) oacc[t][db] = mfma16(av, bp[t][ks], oacc[t][db]);
+            }
+        }
+    };
+
+    // prefix tiles of this split: the tile kRing - 1 ahead is requested once a slot frees up
+    for (int t = 0; t < ntiles; ++t) {
+        const int later = min(kRing - 2, ntiles - 1 - t);
+        if (later >= 2)
+            ring_barrier<2 * kIPW>();
+        else if (later == 1)
+            ring_barrier<kIPW>();
+        else
+            ring_barrier<0>();
+        if (t + kRing - 1 < ntiles) issue(j_begin + (t + kRing - 1) * kTile, (t + kRing - 1) % kRing);
+        const int base = j_begin + t * kTile;
+        attend_tile(t % kRing, base, min(kTile, j_end - base), j_end - base < kTile);
+    }
+
+    // tree keys: rotate k at L + depth, store k_rot, stage into slot 0, attend under the bitmask
+    if (tree_split) {
+        bf16_t* Ks = (bf16_t*)ring;
+        bf16_t* Vs = (bf16_t*)(ring + kTileBytes);
+        for (int tb = 0; tb < T; tb += kTile) {
+            __syncthreads();
+            for (int c = tid; c < kTile * 8; c += NT) {
+                const int key = c >> 3, dc = c & 7, j = tb + key;
+                u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
+                if (j < T) {
+                    const long node = (((long)b * T + j) * H + h) * kDh;
+                    klo = *(const u32x4*)(A.k + node + 8 * dc);
+                    khi = *(const u32x4*)(A.k + node + 64 + 8 * dc);
+                    rotate8(klo, khi, cs + min(max(A.depth[j], 0), A.max_depth) * (kDh / 2), 8 * dc);
+                    *(u32x4*)(A.k_rot + node + 8 * dc) = klo;
+                    *(u32x4*)(A.k_rot + node + 64 + 8 * dc) = khi;
+                }
+                *(u32x4*)(Ks + (key * 16 + kslot(dc, key)) * 8) = klo;
+                *(u32x4*)(Ks + (key * 16 + kslot(dc + 8, key)) * 8) = khi;
+            }
+            for (int c = tid; c < kTile * 16; c += NT) {
+                const int key = c >> 4, p = c & 15, j = tb + key;
+                u32x4 vv = {0, 0, 0, 0};
+                if (j < T) vv = *(const u32x4*)(A.v + (((long)b * T + j) * H + h) * kDh + 8 * p);
+                *(u32x4*)(Vs + (key * 16 + vslot(p, key)) * 8) = vv;
+            }
+            __syncthreads();
+            attend_tile(0, tb, min(kTile, T - tb), true);
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        if (qi[t] < A.Tpad) {
+            const long base = (((long)b * H + h) * (A.nsplit + 1) + split) * A.Tpad + qi[t];
+            float* po = A.part_o + base * kDh;
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[t][db][e];
+            if (g == 0) {
+                A.part_ml[base * 2 + 0] = m_run[t];
+                A.part_ml[base * 2 + 1] = l_run[t];
+            }
+        }
+    }
+}
+
 // Merge the split partials of every (sequence, head, node). grid (T, H, B), block 64.
 __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                    int T, int Tpad, int H, int nsplit, bf16_t* __restrict__ out) {
@@ -713,8 +1018,12 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     const dim3 grid(p.nsplit + 1, H, B);
     const bool paged = cache->layout == MDT_KV_PAGED;
     // up to 8 query tiles: one per wave; up to 16: two per wave on 8 waves
-    auto kern = p.nwb == 4 ? (paged ? attn_tree_mfma<4, true> : attn_tree_mfma<4, false>)
-              : p.nwb == 8 ? (paged ? attn_tree_mfma<8, true> : attn_tree_mfma<8, false>)
+    // trees of up to 128 nodes (one query tile per wave) stream their tiles through the LDS
+    // ring; 256-node trees (two query tiles per wave, the softmax between the products
+    // dominating) keep the register-staged kernel, which measured faster there (767 against
+    // 855 us at the 33B shape) while the stream is faster or equal on the smaller trees
+    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true> : attn_stream<4, false>)
+              : p.nwb == 8 ? (paged ? attn_stream<8, true> : attn_stream<8, false>)
                            : (paged ? attn_tree_mfma<8, true, 2> : attn_tree_mfma<8, false, 2>);
     MDT_LAUNCH("attn_tree_mfma", kern, grid, dim3(64 * (p.nwb == 16 ? 8 : p.nwb)), 0, s, A);
     st = mdt_launched("attn_tree_mfma");
