@@ -14,7 +14,8 @@ torch.cuda.synchronize() calls (the events add dispatch gaps, so they stay out
 of it); afterwards K more replays, each between two events, give the median, p10
 and p90 per step (``replay_us``), and a 1 GiB device copy gives the copy bandwidth
 that ``step_hbm.frac_of_copy`` divides by.  The CPU oracle is timed on the host on whole steps of the same
-workload for about 10 s.  A report of chained steps (``decode_loop``: each step
+workload (its one-time bf16 -> float64 upcast reported apart, then the median of 3 steps with all
+BLAS threads and of 3 with one).  A report of chained steps (``decode_loop``: each step
 starts from the previous step's last accepted node, replayed as one graph) gives
 the time per chained step and the synthetic acceptance; a report of the full
 verify forward (``full_depth``: the tree through all 32 decoder layers of the
@@ -77,35 +78,43 @@ def measured_traffic(kernel: str, workload: str, digest: str):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(w, inp, mode, tau, eps, delta):
-    """The oracle as it stands, one full step on the host cores."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(w, inp, mode, tau, eps, delta, nsteps=3):
+    """The oracle as it stands, timed on whole steps on the host cores: the one-time upcast of
+    the bf16 inputs to float64 is timed and reported on its own, then the median of nsteps
+    steps on the float64 inputs with every BLAS thread, then the median of nsteps on one."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import step as ostep
     from oracle import tree as otree
     tree = otree.build_tree(w)
-    # whole oracle steps until about 10 s of host time (at most 30 s, at least one step)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        ostep.step(w, inp, tree, mode, tau, eps, delta)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or dt + dt / n > 30.0:
-            break
+    t0 = time.perf_counter()
+    inp64 = {k: (ostep.to_f64(v) if isinstance(v, np.ndarray) and v.dtype == np.uint16 else v)
+             for k, v in inp.items()}
+    upcast_s = time.perf_counter() - t0
+
+    def median_step():
+        ts = []
+        for _ in range(nsteps):
+            t = time.perf_counter()
+            ostep.step(w, inp64, tree, mode, tau, eps, delta)
+            ts.append(time.perf_counter() - t)
+        return float(np.median(ts)), ts
+
+    med, ts = median_step()
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
-    # the same oracle on one core: one step
-    from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
-        t1 = time.perf_counter()
-        ostep.step(w, inp, tree, mode, tau, eps, delta)
-        dt1 = time.perf_counter() - t1
+        med1, ts1 = median_step()
     model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
                  platform.processor() or "cpu") if os.path.exists("/proc/cpuinfo") else platform.processor()
-    return {"value": round(n / dt, 6), "unit": "verify-steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} full oracle steps of {w.name} (all six stages, float64 NumPy, bf16 weights upcast "
-                      f"inside each step), inputs in host memory; {dt:.1f} s; host {model}, "
-                      f"{len(os.sched_getaffinity(0))} affinity cores of {os.cpu_count()}",
-            "single_core": {"value": round(1.0 / dt1, 6), "cores": 1, "sample": f"1 oracle step, {dt1:.1f} s"}}
+    return {"value": round(1.0 / med, 6), "unit": "verify-steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"median of {nsteps} full oracle steps of {w.name} (all six stages, float64 NumPy) on "
+                      f"inputs already upcast to float64 in host memory (steps {', '.join(f'{t:.2f}' for t in ts)} s); "
+                      f"host {model}, {len(os.sched_getaffinity(0))} affinity cores of {os.cpu_count()}",
+            "upcast_s": round(upcast_s, 3),
+            "single_core": {"value": round(1.0 / med1, 6), "cores": 1,
+                            "sample": f"median of {nsteps} steps with one BLAS thread "
+                                      f"({', '.join(f'{t:.2f}' for t in ts1)} s)"}}
 
 
 def decode_loop_report(w, inp, seed, step, mode, tau, eps, delta, replays):

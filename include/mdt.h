@@ -66,7 +66,16 @@ extern "C" {
 #define MDT_MAX_HEADS 8     /* Medusa heads K */
 #define MDT_MAX_TOPK 32     /* per-head top-k */
 
-typedef enum mdt_status {
+/* Every enum below is a 32-bit int on both sides of the ABI.  C++ sees each with a fixed
+ * underlying type, so that any int32 a C caller passes (an unknown dtype, say) is a valid
+ * value of the type, which the argument checks then reject with an error code. */
+#ifdef __cplusplus
+#define MDT_ENUM(name) enum name : int32_t
+#else
+#define MDT_ENUM(name) enum name
+#endif
+
+typedef MDT_ENUM(mdt_status) {
     MDT_OK = 0,
     MDT_ERR_NULL = -1,        /* a required pointer is NULL */
     MDT_ERR_SHAPE = -2,       /* a size is out of range or sizes are inconsistent */
@@ -80,22 +89,22 @@ typedef enum mdt_status {
     MDT_ERR_ALLOC = -10       /* host allocation failed */
 } mdt_status;
 
-typedef enum mdt_dtype {
+typedef MDT_ENUM(mdt_dtype) {
     MDT_F32 = 0,   /* float32 storage */
     MDT_BF16 = 1   /* bfloat16 storage */
 } mdt_dtype;
 
-typedef enum mdt_accept_mode {
+typedef MDT_ENUM(mdt_accept_mode) {
     MDT_ACCEPT_GREEDY = 0,
     MDT_ACCEPT_TYPICAL = 1
 } mdt_accept_mode;
 
-typedef enum mdt_act {
+typedef MDT_ENUM(mdt_act) {
     MDT_ACT_NONE = 0,   /* mdt_linear: plain product */
     MDT_ACT_SWIGLU = 1  /* mdt_linear: SwiGLU of an interleaved gate/up product */
 } mdt_act;
 
-typedef enum mdt_kv_layout {
+typedef MDT_ENUM(mdt_kv_layout) {
     MDT_KV_CONTIG = 0,  /* k,v: [B][capacity][H][Dh] */
     MDT_KV_PAGED = 1    /* k,v: [num_pages][page_size][H][Dh] + page_table [B][max_pages] */
 } mdt_kv_layout;

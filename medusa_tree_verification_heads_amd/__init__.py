@@ -24,7 +24,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmdt.so")
+# MDT_LIB_PATH selects another build of the library (the host-sanitizer test loads the
+# host-only ASan/UBSan build this way)
+LIB_PATH = os.environ.get("MDT_LIB_PATH") or os.path.join(_PKG, "libmdt.so")
 
 MDT_F32, MDT_BF16 = 0, 1
 GREEDY, TYPICAL = 0, 1
