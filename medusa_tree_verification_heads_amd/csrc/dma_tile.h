@@ -19,7 +19,8 @@
 //
 // Rows of x past M and of W past V read the last valid row (their products are never
 // stored by a caller that honours M and V); pieces past d read the row's first piece and
-// the k-steps past d are skipped.  d must be a multiple of 32.
+// the k-steps past d are skipped.  The product runs over the first d columns of rows that
+// are ld elements apart (a slice of a longer inner dimension); d must be a multiple of 32.
 #pragma once
 
 #include "mfma_tile.h"
@@ -71,7 +72,7 @@ struct DmaTile {
 
 template <int KC, int NB, int CG, int KS, int S, int AUX = 0, typename Epi>
 __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M, int d,
-                                         int V, int n0, char* smem, Epi&& epi) {
+                                         int ld, int V, int n0, char* smem, Epi&& epi) {
     using P = DmaTile<KC, NB, CG, KS, S>;
     constexpr int kPR = P::kPR;
     constexpr int NTW = NB / CG / 16;   // weight fragments per wave
@@ -91,7 +92,7 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
             const int q = 64 * i + lane;
             const int r = q / kPR, p = (q % kPR) ^ (r & 15);
             const int k = c * KC + 8 * p;
-            const bf16_t* src = W + (size_t)min(n0 + r, V - 1) * d + (k < d ? k : 0);
+            const bf16_t* src = W + (size_t)min(n0 + r, V - 1) * ld + (k < d ? k : 0);
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, AUX);
         }
 #pragma unroll
@@ -100,7 +101,7 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
             const int q = 64 * i + lane;
             const int r = q / kPR, p = (q % kPR) ^ (r & 15);
             const int k = c * KC + 8 * p;
-            const bf16_t* src = x + (size_t)min(r, M - 1) * d + (k < d ? k : 0);
+            const bf16_t* src = x + (size_t)min(r, M - 1) * ld + (k < d ? k : 0);
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P::kWBytes + 1024 * i), 16, 0, 0);
         }
     };

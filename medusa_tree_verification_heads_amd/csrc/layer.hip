@@ -23,6 +23,7 @@
 // and the following RMSNorm), so no workgroup waits for another.
 #include <math.h>
 
+#include "dma_tile.h"
 #include "mfma_tile.h"
 
 namespace {
@@ -53,37 +54,12 @@ __device__ __forceinline__ float hi16(uint32_t u) { return bf16_to_f32(u >> 16);
 // x SiLU(x)-gated: silu(g) * u, silu(g) = g / (1 + e^-g).
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
-// grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.  NW = 0: the
-// 4-wave 64 x 64 tile (NB = 64, block 256).  NW > 0: the tile on 2 NW waves that split
-// each chunk's k-steps (NB = 16 NW, block 128 NW), for grids of at most one workgroup per
-// CU, NW chosen so that the grid covers the CUs.
-template <int EPI, int NW>
-__global__ __launch_bounds__(NW ? 128 * NW : kThreads) void linear_mfma(LinArgs a) {
-    constexpr int NB = NW ? 16 * NW : kNB;
-    constexpr int NTH = NW ? 128 * NW : kThreads;
-    constexpr int kZs = NB + 1;                 // row stride of the fp32 result tile in LDS
-    constexpr int kZOff = NW ? 4096 * NW : 0;   // the k-halves' reduction buffer comes first
-    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, NB>::kBytes];
-    static_assert(MfmaTile<kKC, NB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
-    static_assert(EPI != kSwiglu || NB % 32 == 0, "SwiGLU tiles hold whole gate/up pairs");
-    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
-    const int k0 = s * a.kslice;
-    const int klen = min(a.kslice, a.K - k0);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    float* zt = (float*)(smem + kZOff);  // [64][kZs], reuses the operand tiles
-    auto to_lds = [&](const f32x4 (&acc)[4]) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
-    };
-    if constexpr (NW > 0)
-        mfma_tile_k2<kKC, NW>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
-    else
-        mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
-    __syncthreads();
-
+// The stores of a product's 64 x NB result tile zt (row stride NB + 1, in LDS) by NTH
+// threads: fp32 slices (kPartial), the SwiGLU of gate/up column pairs, or bf16 columns in
+// nseg segments (optionally plus the residual).
+template <int EPI, int NB, int NTH>
+__device__ __forceinline__ void linear_epilogue(const LinArgs& a, const float* zt, int m0, int n0, int s) {
+    constexpr int kZs = NB + 1;
     if constexpr (EPI == kPartial) {
         // four consecutive columns per item, 16-byte stores
         constexpr int kItems = NB / 4;
@@ -143,6 +119,73 @@ __global__ __launch_bounds__(NW ? 128 * NW : kThreads) void linear_mfma(LinArgs 
             *(uint4*)(a.y + (size_t)q * a.M * nsegc + (size_t)m * nsegc + (n - q * nsegc)) = o;
         }
     }
+}
+
+// grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.  NW = 0: the
+// 4-wave 64 x 64 tile (NB = 64, block 256).  NW > 0: the tile on 2 NW waves that split
+// each chunk's k-steps (NB = 16 NW, block 128 NW), for grids of at most one workgroup per
+// CU, NW chosen so that the grid covers the CUs.
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW ? 128 * NW : kThreads) void linear_mfma(LinArgs a) {
+    constexpr int NB = NW ? 16 * NW : kNB;
+    constexpr int NTH = NW ? 128 * NW : kThreads;
+    constexpr int kZs = NB + 1;                 // row stride of the fp32 result tile in LDS
+    constexpr int kZOff = NW ? 4096 * NW : 0;   // the k-halves' reduction buffer comes first
+    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, NB>::kBytes];
+    static_assert(MfmaTile<kKC, NB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
+    static_assert(EPI != kSwiglu || NB % 32 == 0, "SwiGLU tiles hold whole gate/up pairs");
+    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
+    const int k0 = s * a.kslice;
+    const int klen = min(a.kslice, a.K - k0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    float* zt = (float*)(smem + kZOff);  // [64][kZs], reuses the operand tiles
+    auto to_lds = [&](const f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
+    };
+    if constexpr (NW > 0)
+        mfma_tile_k2<kKC, NW>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
+    else
+        mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
+    __syncthreads();
+    linear_epilogue<EPI, NB, NTH>(a, zt, m0, n0, s);
+}
+
+// The same product on dma_tile: both operands staged by direct global-to-LDS loads through
+// an S-stage ring of 128-dim chunks, CG column groups x KS k-groups of waves (chosen per
+// tile width so that the loads divide evenly among the waves).  grid as linear_mfma.
+template <int EPI, int NB, int CG, int KS, int S>
+__global__ __launch_bounds__(64 * CG * KS) void linear_dma(LinArgs a) {
+    using P = DmaTile<128, NB, CG, KS, S>;
+    constexpr int NTH = P::NT;
+    constexpr int kZs = NB + 1;
+    constexpr int kZOff = P::kRedBytes;  // the result tile after the k-groups' partials
+    constexpr int kEpi = kZOff + kMBL * kZs * 4;
+    constexpr int kLds = P::kRingBytes > kEpi ? P::kRingBytes : kEpi;
+    static_assert(EPI != kSwiglu || NB % 32 == 0, "SwiGLU tiles hold whole gate/up pairs");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
+    const int k0 = s * a.kslice;
+    const int klen = min(a.kslice, a.K - k0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15, cg = wave % CG;
+    float* zt = (float*)(smem + kZOff);
+    dma_tile<128, NB, CG, KS, S, 2>(a.x + (size_t)m0 * a.K + k0, a.W + k0, a.M - m0, klen, a.K, a.N, n0, smem,
+                                    [&](const f32x4 (&acc)[NB / CG / 16][4]) {
+#pragma unroll
+                                        for (int nt = 0; nt < NB / CG / 16; ++nt)
+#pragma unroll
+                                            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                                                for (int e = 0; e < 4; ++e)
+                                                    zt[(mt * 16 + 4 * g + e) * kZs + cg * (NB / CG) + 16 * nt +
+                                                       c16] = acc[nt][mt][e];
+                                    });
+    __syncthreads();
+    linear_epilogue<EPI, NB, NTH>(a, zt, m0, n0, s);
 }
 
 // One workgroup of kNormThreads per row (a row of d = 4096 is 512 16-byte pieces: one
@@ -226,6 +269,15 @@ mdt_status launch_linear(const LinArgs& a, int nsplit, hipStream_t hs) {
                    hs, a);
         return mdt_launched("linear_mfma");
     };
+#ifndef MDT_LINEAR_REGISTER_STAGED
+    if (a.K % 32 == 0 && (nsplit == 1 || a.kslice % 32 == 0)) {
+        if constexpr (EPI != kSwiglu)  // a SwiGLU tile holds whole 32-row gate/up pairs
+            if (fits(48)) return go(linear_dma<EPI, 48, 1, 4, 4>, 48, 256);
+        if (fits(64)) return go(linear_dma<EPI, 64, 4, 2, 4>, 64, 512);
+        if (fits(96)) return go(linear_dma<EPI, 96, 2, 4, 3>, 96, 512);
+        return go(linear_dma<EPI, 128, 4, 2, 3>, 128, 512);
+    }
+#endif
     if constexpr (EPI != kSwiglu)  // a SwiGLU tile holds whole 32-row gate/up pairs
         if (fits(48)) return go(linear_mfma<EPI, 3>, 48, 384);
     if (fits(64)) return go(linear_mfma<EPI, 4>, 64, 512);

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(VDma::NT) void verify_dma(const bf16_t* __restrict_
     const EdgePre pre = edge_preload<kMB>(0, M, parent, tokens, T);
     float* zt = (float*)(smem + kZOff);  // [64][NB + 1]
     dma_tile<MDT_VDMA_KC, NB, CG, MDT_VDMA_KS, MDT_VDMA_S, MDT_VDMA_AUX>(
-        x, W, M, d, V, n0, smem, [&](const f32x4 (&acc)[NB / CG / 16][4]) {
+        x, W, M, d, d, V, n0, smem, [&](const f32x4 (&acc)[NB / CG / 16][4]) {
 #pragma unroll
             for (int nt = 0; nt < NB / CG / 16; ++nt)
 #pragma unroll
