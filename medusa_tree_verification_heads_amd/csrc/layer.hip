@@ -15,7 +15,7 @@
 //
 // The linear calls stream W once: with M <= 64 rows (a 64-node tree) every weight byte
 // is read once and used for 64 rows, so a product is bound by HBM, not by the matrix
-// cores.  Each workgroup multiplies 64 x rows by 48 to 128 weight rows (mfma_tile.h; the
+// cores.  Each workgroup multiplies 64 x rows by 48 to 128 weight rows (dma_tile.h; the
 // narrowest width whose grid still has one workgroup per CU).  A weight with few
 // 64-row blocks (the d x d output projection: 64 blocks for 256 CUs) has its inner
 // dimension cut into slices on more workgroups; their fp32 partial tiles are added
@@ -24,14 +24,10 @@
 #include <math.h>
 
 #include "dma_tile.h"
-#include "mfma_tile.h"
 
 namespace {
 
-constexpr int kKC = 256;  // inner-dimension chunk staged in LDS
-constexpr int kNB = 64;   // weight rows per workgroup of the 4-wave tile
 constexpr int kMBL = 64;  // x rows per workgroup
-constexpr int kThreads = 4 * kNB;
 
 enum Epi { kStore = 0, kResidual = 1, kSwiglu = 2, kPartial = 3 };
 
@@ -121,42 +117,10 @@ __device__ __forceinline__ void linear_epilogue(const LinArgs& a, const float* z
     }
 }
 
-// grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.  NW = 0: the
-// 4-wave 64 x 64 tile (NB = 64, block 256).  NW > 0: the tile on 2 NW waves that split
-// each chunk's k-steps (NB = 16 NW, block 128 NW), for grids of at most one workgroup per
-// CU, NW chosen so that the grid covers the CUs.
-template <int EPI, int NW>
-__global__ __launch_bounds__(NW ? 128 * NW : kThreads) void linear_mfma(LinArgs a) {
-    constexpr int NB = NW ? 16 * NW : kNB;
-    constexpr int NTH = NW ? 128 * NW : kThreads;
-    constexpr int kZs = NB + 1;                 // row stride of the fp32 result tile in LDS
-    constexpr int kZOff = NW ? 4096 * NW : 0;   // the k-halves' reduction buffer comes first
-    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<kKC, NB>::kBytes];
-    static_assert(MfmaTile<kKC, NB>::kBytes >= kZOff + kMBL * kZs * 4, "the result tile must fit");
-    static_assert(EPI != kSwiglu || NB % 32 == 0, "SwiGLU tiles hold whole gate/up pairs");
-    const int n0 = blockIdx.x * NB, m0 = blockIdx.y * kMBL, s = blockIdx.z;
-    const int k0 = s * a.kslice;
-    const int klen = min(a.kslice, a.K - k0);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    float* zt = (float*)(smem + kZOff);  // [64][kZs], reuses the operand tiles
-    auto to_lds = [&](const f32x4 (&acc)[4]) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * kZs + wave * 16 + c16] = acc[mt][e];
-    };
-    if constexpr (NW > 0)
-        mfma_tile_k2<kKC, NW>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
-    else
-        mfma_tile<kKC, kNB>(a.x + k0, a.W + k0, a.M, klen, a.K, a.N, m0, n0, smem, to_lds);
-    __syncthreads();
-    linear_epilogue<EPI, NB, NTH>(a, zt, m0, n0, s);
-}
-
-// The same product on dma_tile: both operands staged by direct global-to-LDS loads through
-// an S-stage ring of 128-dim chunks, CG column groups x KS k-groups of waves (chosen per
-// tile width so that the loads divide evenly among the waves).  grid as linear_mfma.
+// One 64 x NB tile of a product on dma_tile: both operands staged by direct global-to-LDS
+// loads through an S-stage ring of 128-dim chunks, CG column groups x KS k-groups of waves
+// (chosen per tile width so that the loads divide evenly among the waves).
+// grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.
 template <int EPI, int NB, int CG, int KS, int S>
 __global__ __launch_bounds__(64 * CG * KS) void linear_dma(LinArgs a) {
     using P = DmaTile<128, NB, CG, KS, S>;
@@ -269,21 +233,12 @@ mdt_status launch_linear(const LinArgs& a, int nsplit, hipStream_t hs) {
                    hs, a);
         return mdt_launched("linear_mfma");
     };
-#ifndef MDT_LINEAR_REGISTER_STAGED
-    if (a.K % 32 == 0 && (nsplit == 1 || a.kslice % 32 == 0)) {
-        if constexpr (EPI != kSwiglu)  // a SwiGLU tile holds whole 32-row gate/up pairs
-            if (fits(48)) return go(linear_dma<EPI, 48, 1, 4, 4>, 48, 256);
-        if (fits(64)) return go(linear_dma<EPI, 64, 4, 2, 4>, 64, 512);
-        if (fits(96)) return go(linear_dma<EPI, 96, 2, 4, 3>, 96, 512);
-        return go(linear_dma<EPI, 128, 4, 2, 3>, 128, 512);
-    }
-#endif
+    // check_linear and kslice_for keep K and every slice a multiple of 32
     if constexpr (EPI != kSwiglu)  // a SwiGLU tile holds whole 32-row gate/up pairs
-        if (fits(48)) return go(linear_mfma<EPI, 3>, 48, 384);
-    if (fits(64)) return go(linear_mfma<EPI, 4>, 64, 512);
-    if (fits(96)) return go(linear_mfma<EPI, 6>, 96, 768);
-    if (fits(128)) return go(linear_mfma<EPI, 8>, 128, 1024);
-    return go(linear_mfma<EPI, 0>, kNB, kThreads);
+        if (fits(48)) return go(linear_dma<EPI, 48, 1, 4, 4>, 48, 256);
+    if (fits(64)) return go(linear_dma<EPI, 64, 4, 2, 4>, 64, 512);
+    if (fits(96)) return go(linear_dma<EPI, 96, 2, 4, 3>, 96, 512);
+    return go(linear_dma<EPI, 128, 4, 2, 3>, 128, 512);
 }
 
 int kslice_for(int K, int nsplit) {

@@ -1,5 +1,5 @@
 // A 64 x NB tile of x W^T (bf16 inputs, fp32 MFMA accumulation) over the full inner
-// dimension, shared by the verifier and the linear layers.
+// dimension: the verifier for 65 to 255 node rows and the heads of a batch.
 //
 // grid.x walks NB-row blocks of W, grid.y 64-row blocks of x; NB/16 waves.  Per chunk of
 // KC dims, the workgroup moves its NB weight rows and 64 x rows into LDS with
@@ -235,119 +235,4 @@ __device__ __forceinline__ void mfma_tile128(const bf16_t* __restrict__ x, const
         __syncthreads();
     }
     epi(acc);
-}
-
-// A 64 x 16NW tile on 2NW waves: wave w multiplies weight rows 16 (w % NW) .. +16 against
-// all 64 x rows over the k-steps of half w / NW of every chunk; at the end the second
-// half's accumulators are added to the first's through LDS (at offset 0, NW * 4 KiB) and
-// epi(acc) runs on waves 0..NW-1 only, with the layout of mfma_tile.  For grids of at
-// most one workgroup per CU, where a 4-wave tile leaves each SIMD a single wave to hide
-// every latency; NW sets the tile width so that such a grid covers the CUs.  Block
-// 128 NW threads; LDS MfmaTile<KC, 16 NW>::kBytes.
-template <int KC, int NW = 4, typename Epi>
-__device__ __forceinline__ void mfma_tile_k2(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
-                                             int d, int ld, int V, int m0, int n0, char* smem, Epi&& epi) {
-    constexpr int NB = 16 * NW;
-    constexpr int NT = 128 * NW;
-    constexpr int kStride = MfmaTile<KC, NB>::kStride;
-    constexpr int kPR = KC / 8;
-    constexpr int kPPT = NB * kPR / NT;
-    constexpr int kXP = 64 * kPR;                  // x pieces per chunk
-    constexpr int kXPT = (kXP + NT - 1) / NT;      // the last round may be partial
-    constexpr bool kXRag = kXP % NT != 0;
-    constexpr int kS = KC / 32;
-    static_assert(KC % 64 == 0 && NB * kPR % NT == 0, "chunk shape");
-    bf16_t* xs = (bf16_t*)smem;
-    bf16_t* ws = (bf16_t*)(smem + MfmaTile<KC, NB>::kXBytes);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int wr = wave % NW, half = wave / NW;
-    const int nchunks = (d + KC - 1) / KC;
-
-    u32x4 wA[kPPT], wB[kPPT], xr[kXPT];
-    auto piece_in = [&](int c, int j, int rows0, int nrows) {
-        const int p = threadIdx.x + NT * j;
-        return c < nchunks && 8 * (p % kPR) < d - c * KC && rows0 + p / kPR < nrows;
-    };
-    auto piece_at = [&](int c, int j, int rows0) {
-        const int p = threadIdx.x + NT * j;
-        return (size_t)(rows0 + p / kPR) * ld + c * KC + 8 * (p % kPR);
-    };
-    // x pieces past the tile's 64 rows (a partial last round) are neither read nor stored
-    auto x_piece = [&](int j) { return !kXRag || j < kXPT - 1 || (int)threadIdx.x + NT * j < kXP; };
-    auto load_w = [&](int c, u32x4 (&wv)[kPPT]) {
-#pragma unroll
-        for (int j = 0; j < kPPT; ++j) wv[j] = ld_stream(W + (piece_in(c, j, n0, V) ? piece_at(c, j, n0) : 0));
-    };
-    auto load_x = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < kXPT; ++j)
-            xr[j] = *(const u32x4*)(x + (x_piece(j) && piece_in(c, j, m0, M) ? piece_at(c, j, m0) : 0));
-    };
-    auto store = [&](int c, const u32x4 (&wv)[kPPT]) {
-        const u32x4 z{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kPPT; ++j) {
-            const int p = threadIdx.x + NT * j;
-            *(u32x4*)(ws + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, n0, V) ? wv[j] : z;
-        }
-#pragma unroll
-        for (int j = 0; j < kXPT; ++j) {
-            const int p = threadIdx.x + NT * j;
-            if (x_piece(j)) *(u32x4*)(xs + (p / kPR) * kStride + 8 * (p % kPR)) = piece_in(c, j, m0, M) ? xr[j] : z;
-        }
-    };
-    f32x4 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c) {
-        const int nsteps = min(KC, d - c * KC) / 32;  // <= 0 past the end
-        const bf16_t* wrow = ws + (wr * 16 + c16) * kStride + 8 * g;
-#pragma unroll
-        for (int s2 = 0; s2 < kS / 2; ++s2) {
-            const int s = half * (kS / 2) + s2;
-            if (s < nsteps) {
-                const u32x4 b = *(const u32x4*)(wrow + 32 * s);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const u32x4 a = *(const u32x4*)(xs + (mt * 16 + c16) * kStride + 32 * s + 8 * g);
-                    acc[mt] = mfma16(a, b, acc[mt]);
-                }
-            }
-        }
-    };
-    load_w(0, wA);
-    load_x(0);
-    load_w(1, wB);
-    store(0, wA);
-    __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-        load_x(c + 1);
-        load_w(c + 2, wA);
-        compute(c);
-        __syncthreads();
-        store(c + 1, wB);
-        __syncthreads();
-        load_x(c + 2);
-        load_w(c + 3, wB);
-        compute(c + 1);
-        __syncthreads();
-        store(c + 2, wA);
-        __syncthreads();
-    }
-    float* red = (float*)smem;  // [NW waves][4 mt][4 e][64 lanes]
-    if (half == 1) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) red[((wr * 4 + mt) * 4 + e) * 64 + lane] = acc[mt][e];
-    }
-    __syncthreads();
-    if (half == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[mt][e] += red[((wr * 4 + mt) * 4 + e) * 64 + lane];
-        epi(acc);
-    }
 }

@@ -136,37 +136,6 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
     tile_epilogue<MB, NB, NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
-// At most 64 node rows and a vocabulary whose 64-column grid overfills the CUs while
-// its 16 NW-column grid fits one workgroup per CU (V = 32000: 250 workgroups): the tile on
-// 2 NW waves (mfma_tile_k2), then the statistics epilogue over 16 NW columns on all
-// threads.  grid ceil(V / (16 NW)), block 128 NW.
-template <int KC, int NW>
-__global__ __launch_bounds__(128 * NW) void verify_mfma_k2(const bf16_t* __restrict__ x,
-                                                           const bf16_t* __restrict__ W, int M, int d, int V,
-                                                           float tau, int nblk_n, Part* __restrict__ part,
-                                                           float* __restrict__ logits_opt,
-                                                           const int32_t* __restrict__ parent,
-                                                           const int32_t* __restrict__ tokens, int T,
-                                                           float* __restrict__ edge) {
-    constexpr int NB = 16 * NW, NT = 128 * NW;
-    constexpr int kZOff = 4096 * NW;  // after the k-halves' reduction buffer
-    static_assert(MfmaTile<KC, NB>::kBytes >= kZOff + kMB * (NB + 1) * 4, "the logits tile must fit");
-    __shared__ __attribute__((aligned(16))) char smem[MfmaTile<KC, NB>::kBytes];
-    const int n0 = blockIdx.x * NB;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    const EdgePre pre = edge_preload<kMB>(0, M, parent, tokens, T);
-    float* zt = (float*)(smem + kZOff);  // [64][NB + 1]
-    mfma_tile_k2<KC, NW>(x, W, M, d, d, V, 0, n0, smem, [&](const f32x4 (&acc)[4]) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zt[(mt * 16 + 4 * g + e) * (NB + 1) + wave * 16 + c16] = acc[mt][e];
-    });
-    __syncthreads();
-    tile_epilogue<kMB, NB, NT>(zt, 0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
-}
-
 // At most 64 node rows (one tree of a single sequence, the batch-1 shapes): dma_tile, the
 // 64 x NB tile fed by direct global-to-LDS loads through an S-stage ring, then the
 // statistics epilogue over NB columns on all threads.  grid ceil(V / NB), block 64 CG KS.
@@ -393,15 +362,12 @@ mdt_status mdt_verify_tiles(hipStream_t s, mdt_dtype dt, int B, int T, int d, in
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     const int M = B * T;
     const bool big = dt == MDT_BF16 && M >= kBigRows;
-    // one row block whose 64-column grid overfills the CUs: the 16-wave tile, 128 columns
-    const long cus = mdt_num_cus();
 #ifndef MDT_VERIFY_NO_DMA
     const bool dma = dt == MDT_BF16 && M <= kMB;
 #else
     const bool dma = false;
 #endif
-    const bool wide = !dma && dt == MDT_BF16 && M <= kMB && (V + 63) / 64 > cus && (V + 127) / 128 <= cus;
-    const int nb_cols = big || wide || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
+    const int nb_cols = big || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
     if (big && d % MDT_VBIG_KC == 0) {
@@ -416,10 +382,6 @@ mdt_status mdt_verify_tiles(hipStream_t s, mdt_dtype dt, int B, int T, int d, in
     } else if (dma) {
         MDT_LAUNCH("verify_mfma", verify_dma, dim3(nblk_n), dim3(VDma::NT), 0, s, (const bf16_t*)x, (const bf16_t*)Wlm,
                    M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T, edge_logit);
-    } else if (wide) {
-        auto kern = verify_mfma_k2<MDT_VERIFY_KC, 8>;
-        MDT_LAUNCH("verify_mfma", kern, dim3(nblk_n), dim3(1024), 0, s, (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V,
-                   temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T, edge_logit);
     } else if (dt == MDT_BF16 && M > kMB) {
         // several node-row blocks: row-block-major grid (each weight block streamed once)
         auto kern = verify_mfma<MDT_VERIFY_KC, MDT_VERIFY_NB, 4, true>;
