@@ -89,6 +89,45 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// Cross-lane steps without LDS.  v_permlane32_swap(x, x) gives every lane the pair
+// (x[l mod 32], x[32 + l mod 32]), v_permlane16_swap(x, x) the pair (x[row 2k], x[row 2k+1])
+// of its 16-lane rows; combining the pair in that order leaves the same value in both
+// partner lanes.
+__device__ __forceinline__ float2 swap32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float xor_max_16_32(float x) {
+    float2 p = swap32(x);
+    p = swap16(fmaxf(p.x, p.y));
+    return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float xor_sum_16_32(float x) {
+    float2 p = swap32(x);
+    p = swap16(p.x + p.y);
+    return p.x + p.y;
+}
+// Sum over the wave, every lane getting the same value: DPP within each row of 16 (lane
+// pairs, quad pairs, mirrored halves, mirrored rows), then the two swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x = dpp_plus<0xb1>(x);   // quad_perm [1,0,3,2]
+    x = dpp_plus<0x4e>(x);   // quad_perm [2,3,0,1]
+    x = dpp_plus<0x141>(x);  // row_half_mirror
+    x = dpp_plus<0x140>(x);  // row_mirror
+    return xor_sum_16_32(x);
+}
+
 // (value desc, index asc) total order used by every top-k / argmax decision.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
