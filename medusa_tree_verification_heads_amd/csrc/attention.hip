@@ -226,9 +226,7 @@ struct AttnArgs {
     double theta;
     int T, Tpad, H, W, nsplit, tiles_per_split, max_depth;
     int page_shift;            // log2 of a paged cache's page size, -1 if not a power of two
-    int tree_last;             // 1: a sequence's last key range also does the tree; 0: a
-                               // workgroup of its own (key range index nsplit)
-    int nparts;                // partial states per (sequence, head)
+    int nparts;                // partial states per (sequence, head): nsplit ranges, then the tree
     double inv_freq[kDh / 2];  // theta^(-2m/Dh), computed once on the host
 };
 
@@ -240,12 +238,10 @@ struct AttnArgs {
 // tiles 16 (QT w + t) .. +15 (with QT = 2 every K and V fragment a wave reads from LDS feeds
 // both of its tiles, and 8 waves cover a 256-node tree).  Per 64-key tile: S^T = K Q^T,
 // then O^T = V^T P^T on MFMA 16x16x32 bf16, so the probabilities stay in registers; online
-// softmax in log2 units.  The tree keys are rotated at their depth positions (writing
-// k_rot), staged in the ring and attended to under the ancestor-or-self bitmask by one
-// workgroup per (sequence, head): an extra one (key range index nsplit) when the whole grid
-// fits one round of the CUs, so that it runs beside the prefix ranges, otherwise the one of
-// the sequence's last (partial, so shortest) key range after its prefix tiles.  Grid
-// (H, B, nparts), key ranges outermost; ranges past a sequence's prefix exit at once.
+// softmax in log2 units.  One more workgroup per (sequence, head) rotates the tree keys at
+// their depth positions (writing k_rot), stages them in the ring and attends to them under
+// the ancestor-or-self bitmask.  Grid (H, B, nsplit + 1), the z index outermost: the key
+// ranges in order (the ranges that end past a short prefix exit at once), then the tree.
 //
 // The prefix tiles stream through a RING-stage LDS ring filled by global_load_lds_dwordx4:
 // while a tile is multiplied, the next RING - 1 tiles are in flight and no register holds
@@ -287,7 +283,7 @@ __device__ __forceinline__ void lds_wait16(u32x2 (&v)[8][2]) {
 }
 
 template <int NWB, bool PAGED, int QT, int KT, int RING>
-__global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
+__global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  // two waves per SIMD
     static_assert(KT == 32 || KT == 64, "32- or 64-key tiles");
     constexpr int NT = 64 * NWB;
     constexpr int kTileB = KT * kDh * 2;             // one K (or V) tile
@@ -300,15 +296,16 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
     char* const ring = lds;
     float2* const cs = (float2*)(lds + RING * kStageB);            // cos/sin per (depth, pair)
     int* const pages = (int*)(lds + RING * kStageB + kCsBytes);  // physical page of each page of the split
-    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+    // z < nsplit: prefix key range z; z = nsplit: the tree keys
+    const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
+    const bool tree_split = z == A.nsplit;
+    const int split = z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int H = A.H, T = A.T;
     const int L = clamp_len(A.prefix_len, b, A.cache.capacity);
-    const int span = A.tiles_per_split * kTile;
-    const bool tree_split = A.tree_last ? split == (L > 0 ? (L - 1) / span : 0) : split == A.nsplit;
-    const int j_begin = split < A.nsplit ? split * span : 0;
-    const int j_end = split < A.nsplit ? min(L, j_begin + span) : 0;
+    const int j_begin = tree_split ? 0 : split * A.tiles_per_split * kTile;
+    const int j_end = tree_split ? 0 : min(L, j_begin + A.tiles_per_split * kTile);
     const int ntiles = j_end > j_begin ? (j_end - j_begin + KT - 1) / KT : 0;
     if (!tree_split && ntiles == 0) {
         // a key range past this sequence's prefix: an empty partial (attn_combine skips it)
@@ -317,7 +314,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
             for (int t = 0; t < QT; ++t) {
                 const int qi = (wave * QT + t) * 16 + c16;
                 if (qi < A.Tpad) {
-                    const long base = (((long)b * H + h) * A.nparts + split) * A.Tpad + qi;
+                    const long base = (((long)b * H + h) * A.nparts + z) * A.Tpad + qi;
                     A.part_ml[base * 2 + 0] = -INFINITY;
                     A.part_ml[base * 2 + 1] = 0.f;
                 }
@@ -336,7 +333,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
     int qi[QT], dq_raw[QT];
     bool q_ok[QT];
     u32x4 bq[QT][4];
-    uint64_t qa[QT][MDT_MAX_NODES / 64];
+    uint64_t qa[QT][MDT_MAX_NODES / 64];  // ancestor rows, loaded for the tree keys only
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         qi[t] = (wave * QT + t) * 16 + c16;
@@ -345,8 +342,6 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
         const long node = (((long)b * T + qc) * H + h) * kDh;
 #pragma unroll
         for (int s = 0; s < 4; ++s) bq[t][s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
-#pragma unroll
-        for (int w = 0; w < MDT_MAX_NODES / 64; ++w) qa[t][w] = A.anc[(long)qc * A.W + min(w, A.W - 1)];
         dq_raw[t] = A.depth[qc];
     }
     if (PAGED) {
@@ -434,9 +429,6 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
         const float2* row = cs + dq * (kDh / 2);
         rotate8(bq[t][0], bq[t][2], row, 8 * g);
         rotate8(bq[t][1], bq[t][3], row, 32 + 8 * g);
-#pragma unroll
-        for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
-            if (!(tree_split && q_ok[t] && w < A.W)) qa[t][w] = 0;
     }
 
     f32x4 oacc[QT][8];
@@ -554,7 +546,12 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
         };
         read_v(0);
         lds_wait16(vh[0]);
-        if constexpr (KS == 2) {
+        if constexpr (KS == 2 && QT > 1) {  // registers: one step of V fragments at a time
+            pv(0);
+            read_v(1);
+            lds_wait16(vh[1]);
+            pv(1);
+        } else if constexpr (KS == 2) {
             read_v(1);
             __builtin_amdgcn_sched_barrier(0);
             pv(0);
@@ -602,6 +599,11 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
     // tree keys (one workgroup per sequence and head): rotate k at L + depth, store k_rot,
     // stage into slot 0, attend under the bitmask
     if (tree_split) {
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+            for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
+                qa[t][w] = q_ok[t] && w < A.W ? A.anc[(long)qi[t] * A.W + w] : 0ull;
         bf16_t* Ks = (bf16_t*)ring;
         bf16_t* Vs = (bf16_t*)(ring + kTileB);
         for (int tb = 0; tb < T; tb += KT) {
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_stream(AttnArgs A) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         if (qi[t] < A.Tpad) {
-            const long base = (((long)b * H + h) * A.nparts + split) * A.Tpad + qi[t];
+            const long base = (((long)b * H + h) * A.nparts + z) * A.Tpad + qi[t];
             float* po = A.part_o + base * kDh;
 #pragma unroll
             for (int db = 0; db < 8; ++db)
@@ -692,7 +694,7 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
 }
 
 struct Plan {
-    int Tpad, nsplit, tiles_per_split, nwb, tree_last, nparts;
+    int Tpad, nsplit, tiles_per_split, nwb, nparts;
     size_t po_bytes, pml_bytes;
 };
 
@@ -728,12 +730,7 @@ Plan plan(int B, int T, int H, int capacity) {
 #endif
     p.tiles_per_split = best_tps;
     p.nsplit = (tiles + best_tps - 1) / best_tps;
-    // a separate tree workgroup when all of them fit one round (two per CU)
-    p.tree_last = bh * (p.nsplit + 1) > 2 * kPlanCUs ? 1 : 0;
-#ifdef MDT_ATTN_TREE_LAST
-    p.tree_last = MDT_ATTN_TREE_LAST;
-#endif
-    p.nparts = p.nsplit + (p.tree_last ? 0 : 1);
+    p.nparts = p.nsplit + 1;
     p.po_bytes = ((size_t)B * H * p.nparts * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
     p.pml_bytes = (size_t)B * H * p.nparts * p.Tpad * 2 * sizeof(float);
     return p;
@@ -799,7 +796,7 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
         }
     AttnArgs A{kv, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix_len, tree->depth, tree->anc,
                (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
-               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.tree_last, p.nparts, {}};
+               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.nparts, {}};
     for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
     const dim3 grid(H, B, p.nparts);
     const bool paged = cache->layout == MDT_KV_PAGED;
