@@ -231,36 +231,43 @@ struct AttnArgs {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: prefix key ranges streamed by direct global-to-LDS loads
+// bf16 kernels: prefix keys streamed by direct global-to-LDS loads
 // ---------------------------------------------------------------------------
 //
-// One (sequence, head, prefix key range) per workgroup; NWB waves, wave w owns the QT query
+// A workgroup of NWB waves works on one (sequence, head) at a time; wave w owns the QT query
 // tiles 16 (QT w + t) .. +15 (with QT = 2 every K and V fragment a wave reads from LDS feeds
-// both of its tiles, and 8 waves cover a 256-node tree).  Per 64-key tile: S^T = K Q^T,
-// then O^T = V^T P^T on MFMA 16x16x32 bf16, so the probabilities stay in registers; online
-// softmax in log2 units.  One more workgroup per (sequence, head) rotates the tree keys at
-// their depth positions (writing k_rot), stages them in the ring and attends to them under
-// the ancestor-or-self bitmask.  Grid (H, B, nsplit + 1), the z index outermost: the key
-// ranges in order (the ranges that end past a short prefix exit at once), then the tree.
-//
-// The prefix tiles stream through a RING-stage LDS ring filled by global_load_lds_dwordx4:
-// while a tile is multiplied, the next RING - 1 tiles are in flight and no register holds
-// them; the loads of the next tile go out in parts between the blocks of S.  Both tiles stay
+// both of its tiles, and 8 waves cover a 256-node tree).  Per 64-key tile: S^T = K Q^T, then
+// O^T = V^T P^T on MFMA 16x16x32 bf16, so the probabilities stay in registers; online
+// softmax in log2 units.  Prefix tiles stream through a two-stage LDS ring filled by
+// global_load_lds_dwordx4: while a tile is multiplied the next one is in flight and no
+// register holds it; its loads go out in parts between the blocks of S.  Both tiles stay
 // row-major (one 256-byte row per key) with their 16-byte pieces swizzled per row: K row r
 // keeps piece p in slot p ^ (r mod 16) (its MFMA fragments read 16 rows at once), V row r in
 // slot p ^ (2 r mod 16); V^T fragments come from the LDS transpose read ds_read_b64_tr_b16 --
 // in each 16-lane group, lane i receives element i mod 4 of the 8 bytes read by lane
 // 4 e + i / 4 as its element e -- so 4 key rows x 16 dims land as 16 lanes x 4 keys.  The
-// swizzles keep the fragment and transpose reads free of bank conflicts.
+// swizzles keep the fragment and transpose reads free of bank conflicts.  The tree keys
+// are rotated at their depth positions (writing k_rot), staged in the ring by ordinary
+// stores and attended to under the ancestor-or-self bitmask.
 //
-// Waiting: the loop's only waits for the ring are its barriers (ring_barrier).  All LDS of
-// the kernel is one array: with separate arrays the compiler tags each access with its
-// array and then makes every read of the ring wait for all direct-to-LDS loads in flight
-// (vmcnt(0) before each tile's first fragment read), which serialises the ring.  The
-// transpose reads are issued as inline assembly for the same reason (the compiler's own
-// form of that read always waits), with an explicit lgkmcnt wait that the MFMAs depend on.
-constexpr int kStreamPages = 2048;              // page-table entries a streaming workgroup stages
+// One workgroup per (sequence, head, key range) plus one per (sequence, head) for the tree.
+// (A persistent schedule -- a fixed grid walking equal shares of all prefix tiles with the
+// ring running across (sequence, head) boundaries -- was no faster: at 7b-B16 its tiles
+// took longer, at 33B the gain came from fewer partial states, which the split choice
+// below now gives directly.)
+//
+// Waiting: the loops' only waits for the ring are their barriers (ring_barrier).  All LDS of
+// a kernel is one array: with separate arrays the compiler tags each access with its array
+// and then makes every read of the ring wait for all direct-to-LDS loads in flight (vmcnt(0)
+// before each tile's first fragment read), which serialises the ring.  The transpose reads
+// are issued as inline assembly for the same reason (the compiler's own form of that read
+// always waits), with an explicit lgkmcnt wait that the MFMAs depend on.
+constexpr int kStreamPages = 2048;               // page-table entries a workgroup stages
+constexpr int kTileBytes = kTile * kDh * 2;      // one K (or V) tile: 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;      // K then V
+constexpr int kRingBytes = 2 * kStageBytes;      // two stages
 constexpr int kCsBytes = (MDT_MAX_HEADS + 1) * (kDh / 2) * (int)sizeof(float2);
+constexpr int kInstr = kTile * (kDh / 8) / 64;   // load instructions per tile (K or V): 16
 
 __device__ __forceinline__ int kslot(int p, int r) { return p ^ (r & 15); }
 __device__ __forceinline__ int vslot(int p, int r) { return p ^ ((2 * r) & 14); }
@@ -282,102 +289,337 @@ __device__ __forceinline__ void lds_wait16(u32x2 (&v)[8][2]) {
                    "+v"(v[6][0]), "+v"(v[6][1]), "+v"(v[7][0]), "+v"(v[7][1]));
 }
 
-template <int NWB, bool PAGED, int QT, int KT, int RING>
+// Per-wave query state: in tile t the lane holds query qi(t) = 16 (QT wave + t) + lane % 16,
+// dims 32 s + 8 g .. +8 of the rotated query (s = 0, 1: x_m; s = 2, 3: x_{m+64}), its
+// running (m, l) (replicated over g) and O^T accumulators (lane: dims 16 db + 4 g + e).
+template <int QT>
+struct QueryState {
+    u32x4 bq[QT][4];
+    f32x4 oacc[QT][8];
+    float m_run[QT], l_run[QT];
+};
+
+__device__ __forceinline__ int query_of(int QT_, int t) {
+    return (((int)threadIdx.x >> 6) * QT_ + t) * 16 + ((int)threadIdx.x & 15);
+}
+
+// Request the raw queries of (b, h) (rows past T read node 0 and are zeroed when rotated).
+template <int QT>
+__device__ __forceinline__ void load_queries(const AttnArgs& A, int b, int h, u32x4 (&bq)[QT][4]) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const int qi = query_of(QT, t);
+        const long node = (((long)b * A.T + (qi < A.T ? qi : 0)) * A.H + h) * kDh;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[t][s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
+    }
+}
+
+// cos/sin of every (depth, pair) at positions L .. L + max_depth, by the workgroup's threads
+// (published by the caller's barrier).
+__device__ __forceinline__ void fill_rope_table(const AttnArgs& A, int L, float2* cs, int nthreads) {
+    for (int e = threadIdx.x; e < (A.max_depth + 1) * (kDh / 2); e += nthreads)
+        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
+}
+
+// Rotate raw queries into st.bq and reset the running state.
+template <int QT>
+__device__ __forceinline__ void start_queries(const AttnArgs& A, const u32x4 (&raw)[QT][4], const int (&dq)[QT],
+                                              const float2* cs, QueryState<QT>& st) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const bool ok = query_of(QT, t) < A.T;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) st.bq[t][s] = ok ? raw[t][s] : u32x4{0, 0, 0, 0};
+        const float2* row = cs + dq[t] * (kDh / 2);
+        rotate8(st.bq[t][0], st.bq[t][2], row, 8 * g);
+        rotate8(st.bq[t][1], st.bq[t][3], row, 32 + 8 * g);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) st.oacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m_run[t] = -INFINITY;
+        st.l_run[t] = 0.f;
+    }
+}
+
+// Partial state of the wave's queries into partial slot `slot` (rows of Tpad per slot).
+template <int QT>
+__device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, const QueryState<QT>& st) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const int qi = query_of(QT, t);
+        if (qi < A.Tpad) {
+            const long base = slot * A.Tpad + qi;
+            float* po = A.part_o + base * kDh;
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = st.oacc[t][db][e];
+            if (g == 0) {
+                A.part_ml[base * 2 + 0] = st.m_run[t];
+                A.part_ml[base * 2 + 1] = st.l_run[t];
+            }
+        }
+    }
+}
+
+// One 64-key tile of the LDS stage `stage`, nvalid of its keys real; masked tiles also keep
+// only the keys whose bit is set in qw[t] (bit j: key j of the tile; all ones for prefix
+// keys, the ancestor-or-self bits for tree keys).  hook(kb) runs after each 16-key block of
+// S.  (The mask words come in as values: selecting one of a query's four words here would
+// index a register array with a run-time index, which puts the whole state in scratch.)
+template <int QT, typename Hook>
+__device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool masked, const uint64_t (&qw)[QT],
+                                            float sl2, QueryState<QT>& st, Hook&& hook) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const bf16_t* Ks = (const bf16_t*)stage;
+    const bf16_t* Vs = (const bf16_t*)(stage + kTileBytes);
+    constexpr int KB = kTile / 16, KS = kTile / 32;
+    f32x4 sacc[QT][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        f32x4 acc[QT];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = kb * 16 + c16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 kf = *(const u32x4*)(Ks + (r * 16 + kslot(4 * s + g, r)) * 8);
+#pragma unroll
+            for (int t = 0; t < QT; ++t) acc[t] = mfma16(kf, st.bq[t][s], acc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < QT; ++t) sacc[t][kb] = acc[t];
+        hook(kb);
+    }
+    u32x4 bp[QT][KS];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        float tmax = -INFINITY;
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jj = kb * 16 + 4 * g + e;
+                    if (!(jj < nvalid && ((qw[t] >> jj) & 1ull))) sacc[t][kb][e] = -INFINITY;
+                    tmax = fmaxf(tmax, sacc[t][kb][e]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[t][kb][e]);
+        }
+        tmax = xor_max_16_32(tmax) * sl2;
+        // The reference maximum moves only when a score exceeds it by more than 2^8, so that
+        // the accumulators are rarely rescaled; weights stay below 256 (fine for the bf16
+        // probabilities and the fp32 sums).  A row with no key yet keeps -inf and a
+        // reference of 0 (its weights are exp2(-inf) = 0).
+        const float m_new = tmax > st.m_run[t] + 8.f ? tmax : st.m_run[t];
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(st.m_run[t] - m_ref);
+        float tsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][e], sl2, -m_ref));
+                sacc[t][kb][e] = p;
+                tsum += p;
+            }
+        st.l_run[t] = st.l_run[t] * corr + xor_sum_16_32(tsum);
+        st.m_run[t] = m_new;
+        if (__any(corr != 1.f))
+#pragma unroll
+            for (int db = 0; db < 8; ++db) st.oacc[t][db] *= corr;
+        // within a 32-key step the key order is 4g+e (e<4), then 16+4g+(e-4)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bp[t][ks][0] = pack_bf16(sacc[t][2 * ks][0], sacc[t][2 * ks][1]);
+            bp[t][ks][1] = pack_bf16(sacc[t][2 * ks][2], sacc[t][2 * ks][3]);
+            bp[t][ks][2] = pack_bf16(sacc[t][2 * ks + 1][0], sacc[t][2 * ks + 1][1]);
+            bp[t][ks][3] = pack_bf16(sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]);
+        }
+    }
+    // O^T += V^T P^T: lane (dim 16 db + c16, group g) takes keys 32 ks + 4 g + e and
+    // 32 ks + 16 + 4 g + e (e < 4) by two transpose reads; as a source lane it reads the 8
+    // bytes of key row 32 ks + 16 hf + 4 g + c16 / 4, dims 16 db + 4 (c16 mod 4) ..
+    u32x2 vh[KS][8][2];
+    auto read_v = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int r = 32 * ks + 16 * hf + 4 * g + (c16 >> 2);
+                const int p = 2 * db + ((c16 & 3) >> 1);
+                vh[ks][db][hf] = ds_read_tr16(Vs + (r * 16 + vslot(p, r)) * 8 + 4 * (c16 & 1));
+            }
+    };
+    auto pv = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const u32x4 av = {vh[ks][db][0][0], vh[ks][db][0][1], vh[ks][db][1][0], vh[ks][db][1][1]};
+#pragma unroll
+            for (int t = 0; t < QT; ++t) st.oacc[t][db] = mfma16(av, bp[t][ks], st.oacc[t][db]);
+        }
+    };
+    read_v(0);
+    lds_wait16(vh[0]);
+    if constexpr (QT > 1) {  // registers: one step of V fragments at a time
+        pv(0);
+        read_v(1);
+        lds_wait16(vh[1]);
+        pv(1);
+    } else {  // the reads of step 1 go out while the MFMAs of step 0 run
+        read_v(1);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait16(vh[1]);
+        pv(1);
+    }
+}
+
+// The tree keys of (b, h): rotate k at L + depth, store k_rot, stage 64 keys at a time into
+// the ring's first stage (ordinary stores) and attend under the ancestor-or-self bitmask.
+// The ring must be idle; cs holds the table of sequence b.
+template <int QT, int NT>
+__device__ __forceinline__ void tree_pass(const AttnArgs& A, int b, int h, char* ring, const float2* cs, float sl2,
+                                          bool busy, QueryState<QT>& st) {
+    const int T = A.T, H = A.H, tid = threadIdx.x;
+    bf16_t* Ks = (bf16_t*)ring;
+    bf16_t* Vs = (bf16_t*)(ring + kTileBytes);
+    for (int tb = 0; tb < T; tb += kTile) {
+        __syncthreads();
+        for (int c = tid; c < kTile * 8; c += NT) {
+            const int key = c >> 3, dc = c & 7, j = tb + key;
+            u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
+            if (j < T) {
+                const long node = (((long)b * T + j) * H + h) * kDh;
+                klo = *(const u32x4*)(A.k + node + 8 * dc);
+                khi = *(const u32x4*)(A.k + node + 64 + 8 * dc);
+                rotate8(klo, khi, cs + min(max(A.depth[j], 0), A.max_depth) * (kDh / 2), 8 * dc);
+                *(u32x4*)(A.k_rot + node + 8 * dc) = klo;
+                *(u32x4*)(A.k_rot + node + 64 + 8 * dc) = khi;
+            }
+            *(u32x4*)(Ks + (key * 16 + kslot(dc, key)) * 8) = klo;
+            *(u32x4*)(Ks + (key * 16 + kslot(dc + 8, key)) * 8) = khi;
+        }
+        for (int c = tid; c < kTile * 16; c += NT) {
+            const int key = c >> 4, p = c & 15, j = tb + key;
+            u32x4 vv = {0, 0, 0, 0};
+            if (j < T) vv = *(const u32x4*)(A.v + (((long)b * T + j) * H + h) * kDh + 8 * p);
+            *(u32x4*)(Vs + (key * 16 + vslot(p, key)) * 8) = vv;
+        }
+        uint64_t qw[QT];  // the ancestor-or-self bits of the tile's keys tb .. tb + 63
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            const int qi = query_of(QT, t);
+            qw[t] = qi < T && (tb >> 6) < A.W ? A.anc[(long)qi * A.W + (tb >> 6)] : 0ull;
+        }
+        __syncthreads();
+        if (busy) attend_tile<QT>(ring, min(kTile, T - tb), true, qw, sl2, st, [](int) {});
+    }
+}
+
+// Load instruction j of a wave (of 2 kInstr per tile): which cache (k or v), its row of the
+// tile, its piece and its 1-KiB block of the stage.
+template <int NWB>
+struct LoadSlot {
+    static constexpr int kIPW = 2 * kInstr / NWB;
+    __device__ __forceinline__ static bool isv(int j) { return ((int)threadIdx.x >> 6) * kIPW + j >= kInstr; }
+    __device__ __forceinline__ static int block(int j) {
+        const int i = ((int)threadIdx.x >> 6) * kIPW + j;
+        return i >= kInstr ? i - kInstr : i;
+    }
+    __device__ __forceinline__ static int row(int j) { return (64 * block(j) + ((int)threadIdx.x & 63)) >> 4; }
+    __device__ __forceinline__ static int piece(int j) {
+        const int q = 64 * block(j) + ((int)threadIdx.x & 63), r = q >> 4, sl = q & 15;
+        return isv(j) ? vslot(sl, r) : kslot(sl, r);  // the swizzles are involutions
+    }
+    __device__ __forceinline__ static int lds_offset(int j) { return (isv(j) ? kTileBytes : 0) + 1024 * block(j); }
+};
+
+// One (sequence, head, key range) per workgroup, or the tree of one (sequence, head).
+// Grid (H, B, nsplit + 1), the z index outermost: the key ranges in order (the ranges that
+// end past a short prefix exit at once), then the tree.
+template <int NWB, bool PAGED, int QT>
 __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  // two waves per SIMD
-    static_assert(KT == 32 || KT == 64, "32- or 64-key tiles");
     constexpr int NT = 64 * NWB;
-    constexpr int kTileB = KT * kDh * 2;             // one K (or V) tile
-    constexpr int kStageB = 2 * kTileB;              // K then V
-    constexpr int kInstr = KT * (kDh / 8) / 64;      // load instructions per tile (K or V)
-    constexpr int kIPW = 2 * kInstr / NWB;          // per wave per tile, K and V together
-    static_assert(2 * kInstr % NWB == 0 && kIPW * (RING - 2) < 64, "loads divide among the waves");
+    using LS = LoadSlot<NWB>;
+    constexpr int kIPW = LS::kIPW;
+    static_assert(2 * kInstr % NWB == 0, "loads divide among the waves");
     constexpr int kPageBytes = PAGED ? kStreamPages * 4 : 0;
-    __shared__ __attribute__((aligned(1024))) char lds[RING * kStageB + kCsBytes + kPageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[kRingBytes + kCsBytes + kPageBytes];
     char* const ring = lds;
-    float2* const cs = (float2*)(lds + RING * kStageB);            // cos/sin per (depth, pair)
-    int* const pages = (int*)(lds + RING * kStageB + kCsBytes);  // physical page of each page of the split
+    float2* const cs = (float2*)(lds + kRingBytes);                  // cos/sin per (depth, pair)
+    int* const pages = (int*)(lds + kRingBytes + kCsBytes);          // physical page of each page of the range
     // z < nsplit: prefix key range z; z = nsplit: the tree keys
     const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
     const bool tree_split = z == A.nsplit;
-    const int split = z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int H = A.H, T = A.T;
+    const int wave = threadIdx.x >> 6;
+    const int H = A.H;
     const int L = clamp_len(A.prefix_len, b, A.cache.capacity);
-    const int j_begin = tree_split ? 0 : split * A.tiles_per_split * kTile;
+    const int j_begin = tree_split ? 0 : z * A.tiles_per_split * kTile;
     const int j_end = tree_split ? 0 : min(L, j_begin + A.tiles_per_split * kTile);
-    const int ntiles = j_end > j_begin ? (j_end - j_begin + KT - 1) / KT : 0;
+    const int ntiles = j_end > j_begin ? (j_end - j_begin + kTile - 1) / kTile : 0;
+    const long slot = ((long)b * H + h) * A.nparts + z;
+    QueryState<QT> st;
     if (!tree_split && ntiles == 0) {
         // a key range past this sequence's prefix: an empty partial (attn_combine skips it)
-        if (g == 0)
 #pragma unroll
-            for (int t = 0; t < QT; ++t) {
-                const int qi = (wave * QT + t) * 16 + c16;
-                if (qi < A.Tpad) {
-                    const long base = (((long)b * H + h) * A.nparts + z) * A.Tpad + qi;
-                    A.part_ml[base * 2 + 0] = -INFINITY;
-                    A.part_ml[base * 2 + 1] = 0.f;
-                }
+        for (int t = 0; t < QT; ++t) {
+            st.m_run[t] = -INFINITY;
+            st.l_run[t] = 0.f;
+            const int qi = query_of(QT, t);
+            if (qi < A.Tpad && (threadIdx.x & 63) < 16) {
+                A.part_ml[(slot * A.Tpad + qi) * 2 + 0] = -INFINITY;
+                A.part_ml[(slot * A.Tpad + qi) * 2 + 1] = 0.f;
             }
+        }
         return;
     }
-    const float scale = 1.f / sqrtf((float)kDh);
     const bf16_t* Kg = (const bf16_t*)A.cache.k;
     const bf16_t* Vg = (const bf16_t*)A.cache.v;
     const int psz = PAGED ? A.cache.page_size : 1;
     const int psh = PAGED ? A.page_shift : 0;  // log2 of the page size, or -1
     const int pg0 = j_begin / psz;
 
-    // this wave's queries, loaded first: in tile t the lane holds query qi[t], dims
-    // 32s + 8g .. +8; s = 0,1 hold x_m and s = 2,3 hold x_{m+64}
-    int qi[QT], dq_raw[QT];
-    bool q_ok[QT];
-    u32x4 bq[QT][4];
-    uint64_t qa[QT][MDT_MAX_NODES / 64];  // ancestor rows, loaded for the tree keys only
+    u32x4 raw[QT][4];
+    load_queries<QT>(A, b, h, raw);
+    int dq[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-        qi[t] = (wave * QT + t) * 16 + c16;
-        q_ok[t] = qi[t] < T;
-        const int qc = q_ok[t] ? qi[t] : 0;
-        const long node = (((long)b * T + qc) * H + h) * kDh;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bq[t][s] = *(const u32x4*)(A.q + node + 32 * s + 8 * g);
-        dq_raw[t] = A.depth[qc];
+        const int qi = query_of(QT, t);
+        dq[t] = qi < A.T ? min(max(A.depth[qi], 0), A.max_depth) : 0;
     }
     if (PAGED) {
         const int np = j_end > j_begin ? (j_end - 1) / psz - pg0 + 1 : 0;  // <= kStreamPages (host plan)
-        for (int e = tid; e < np; e += NT) {
+        for (int e = threadIdx.x; e < np; e += NT) {
             const int pg = pg0 + e;
             const int page = pg < A.cache.max_pages ? A.cache.table[(long)b * A.cache.max_pages + pg] : -1;
             pages[e] = (page >= 0 && page < A.cache.num_pages) ? page : -1;
         }
         __syncthreads();
     }
-    // The tile of keys t0 .. t0 + 63 into ring slot `slot`; keys past the split's end repeat
-    // its last key (they are masked).  Per load instruction j the lane's row, piece and
-    // cache (k or v) are fixed, so its source is src0[j] + (cache row of key t0 + row) *
-    // H * Dh; every offset is formed before the first load goes out (the page lookups are
-    // LDS reads).  An unmapped page reads the pool's first row (a caller error: the value
-    // is meaningless but the access stays inside).
+    // Per load instruction j the lane's row, piece and cache (k or v) are fixed, so its
+    // source is src0[j] + (cache row of key t0 + row) * H * Dh; keys past the range's end
+    // repeat its last key (they are masked).  An unmapped page reads the pool's first row (a
+    // caller error: the value is meaningless but the access stays inside).
     const bf16_t* src0[kIPW];
-    int rowj[kIPW];
 #pragma unroll
-    for (int j = 0; j < kIPW; ++j) {
-        const int i = wave * kIPW + j;
-        const bool isv = i >= kInstr;
-        const int ii = isv ? i - kInstr : i;
-        const int q = 64 * ii + lane;
-        const int r = q >> 4, sl = q & 15;
-        const int p = isv ? vslot(sl, r) : kslot(sl, r);  // the swizzles are involutions
-        rowj[j] = r;
-        src0[j] = (isv ? Vg : Kg) + (PAGED ? 0 : (size_t)b * A.cache.capacity * H * kDh) + h * kDh + 8 * p;
-    }
+    for (int j = 0; j < kIPW; ++j)
+        src0[j] = (LS::isv(j) ? Vg : Kg) + (PAGED ? 0 : (size_t)b * A.cache.capacity * H * kDh) + h * kDh +
+                  8 * LS::piece(j);
     const unsigned HK = (unsigned)(H * kDh);
     // sources of the tile of keys t0 .. (formed together: the page lookups are LDS reads)
     auto sources_with = [&](int t0, const bf16_t* (&src)[kIPW], bool pow2) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kIPW; ++j) {
-            const int key = min(t0 + rowj[j], j_end - 1);
+            const int key = min(t0 + LS::row(j), j_end - 1);
             unsigned row = (unsigned)key;
             if (PAGED) {
                 const int pq = pow2 ? key >> psh : key / psz;
@@ -393,277 +635,74 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
         else
             sources_with(t0, src, false);
     };
-    // load instructions j0 .. j1 - 1 of a tile into ring slot `slot`
-    auto issue_part = [&](const bf16_t* const (&src)[kIPW], int slot, int j0, int j1) __attribute__((always_inline)) {
-        char* kst = ring + slot * kStageB;
+    // load instructions j0 .. j1 - 1 of a tile into ring stage `stage`
+    auto issue_part = [&](const bf16_t* const (&src)[kIPW], int stage, int j0, int j1) __attribute__((always_inline)) {
+        char* kst = ring + stage * kStageBytes;
 #pragma unroll
         for (int j = 0; j < kIPW; ++j) {
             if (j < j0 || j >= j1) continue;
-            const int i = wave * kIPW + j;
-            const bool isv = i >= kInstr;
-            const int ii = isv ? i - kInstr : i;
-            __builtin_amdgcn_global_load_lds((const void*)src[j],
-                                             (lds_void_t*)(kst + (isv ? kTileB : 0) + 1024 * ii), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)src[j], (lds_void_t*)(kst + LS::lds_offset(j)), 16, 0, 0);
         }
     };
-    auto issue = [&](int t0, int slot) __attribute__((always_inline)) {
+    if (ntiles > 0) {
         const bf16_t* src[kIPW];
-        sources(t0, src);
-        issue_part(src, slot, 0, kIPW);
-    };
-#pragma unroll
-    for (int s = 0; s < RING - 1; ++s)
-        if (s < ntiles) issue(j_begin + s * KT, s);
-
-    for (int e = tid; e < (A.max_depth + 1) * (kDh / 2); e += NT)
-        cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
-    // cos/sin table ready; the tiles already requested stay in flight (a plain
-    // __syncthreads would wait for them)
+        sources(j_begin, src);
+        issue_part(src, 0, 0, kIPW);
+    }
+    fill_rope_table(A, L, cs, NT);
+    // cos/sin table ready; the tile already requested stays in flight (a plain
+    // __syncthreads would wait for it)
     ring_barrier<63>();
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        if (!q_ok[t])
-#pragma unroll
-            for (int s = 0; s < 4; ++s) bq[t][s] = u32x4{0, 0, 0, 0};
-        const int dq = q_ok[t] ? min(max(dq_raw[t], 0), A.max_depth) : 0;
-        const float2* row = cs + dq * (kDh / 2);
-        rotate8(bq[t][0], bq[t][2], row, 8 * g);
-        rotate8(bq[t][1], bq[t][3], row, 32 + 8 * g);
-    }
+    start_queries<QT>(A, raw, dq, cs, st);
 
-    f32x4 oacc[QT][8];
-    float m_run[QT], l_run[QT];  // of query qi[t], replicated over g
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-    }
-
-    const float sl2 = scale * 1.4426950408889634f;
-    // One tile in ring slot `slot`, nvalid of its KT keys real; tb >= 0: the keys are tree
-    // nodes tb .., also under the ancestor-or-self bitmask (tb < 0: prefix keys).
-    auto attend_tile = [&](int slot, int nvalid, bool masked, int tb, auto&& hook) __attribute__((always_inline)) {
-        const bf16_t* Ks = (const bf16_t*)(ring + slot * kStageB);
-        const bf16_t* Vs = (const bf16_t*)(ring + slot * kStageB + kTileB);
-        constexpr int KB = KT / 16, KS = KT / 32;
-        f32x4 sacc[QT][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            f32x4 acc[QT];
-#pragma unroll
-            for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int r = kb * 16 + c16;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4 kf = *(const u32x4*)(Ks + (r * 16 + kslot(4 * s + g, r)) * 8);
-#pragma unroll
-                for (int t = 0; t < QT; ++t) acc[t] = mfma16(kf, bq[t][s], acc[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < QT; ++t) sacc[t][kb] = acc[t];
-            hook(kb);
-        }
-        u32x4 bp[QT][KS];
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-            float tmax = -INFINITY;
-            if (masked) {
-                const int wi = tb >> 6;
-                const uint64_t qw = tb < 0 ? ~0ull
-                                           : (wi == 0 ? qa[t][0]
-                                              : wi == 1 ? qa[t][1]
-                                              : wi == 2 ? qa[t][2]
-                                                        : qa[t][3]) >> (tb & 63);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int jj = kb * 16 + 4 * g + e;
-                        if (!(jj < nvalid && ((qw >> jj) & 1ull))) sacc[t][kb][e] = -INFINITY;
-                        tmax = fmaxf(tmax, sacc[t][kb][e]);
-                    }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[t][kb][e]);
-            }
-            tmax = xor_max_16_32(tmax) * sl2;
-            // The reference maximum moves only when a score exceeds it by more than 2^8, so
-            // that the accumulators are rarely rescaled; weights stay below 256 (fine for the
-            // bf16 probabilities and the fp32 sums).  A row with no key yet keeps -inf and a
-            // reference of 0 (its weights are exp2(-inf) = 0).
-            const float m_new = tmax > m_run[t] + 8.f ? tmax : m_run[t];
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-            const float corr = __builtin_amdgcn_exp2f(m_run[t] - m_ref);
-            float tsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][e], sl2, -m_ref));
-                    sacc[t][kb][e] = p;
-                    tsum += p;
-                }
-            l_run[t] = l_run[t] * corr + xor_sum_16_32(tsum);
-            m_run[t] = m_new;
-            if (__any(corr != 1.f))
-#pragma unroll
-                for (int db = 0; db < 8; ++db) oacc[t][db] *= corr;
-            // within a 32-key step the key order is 4g+e (e<4), then 16+4g+(e-4)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bp[t][ks][0] = pack_bf16(sacc[t][2 * ks][0], sacc[t][2 * ks][1]);
-                bp[t][ks][1] = pack_bf16(sacc[t][2 * ks][2], sacc[t][2 * ks][3]);
-                bp[t][ks][2] = pack_bf16(sacc[t][2 * ks + 1][0], sacc[t][2 * ks + 1][1]);
-                bp[t][ks][3] = pack_bf16(sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]);
-            }
-        }
-        // O^T += V^T P^T: lane (dim 16 db + c16, group g) takes keys 32 ks + 4 g + e and
-        // 32 ks + 16 + 4 g + e (e < 4) by two transpose reads; as a source lane it reads the 8
-        // bytes of key row 32 ks + 16 hf + 4 g + c16 / 4, dims 16 db + 4 (c16 mod 4) ..
-        // The reads of step 1 go out while the MFMAs of step 0 run.
-        u32x2 vh[KS][8][2];
-        auto read_v = [&](int ks) {
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int r = 32 * ks + 16 * hf + 4 * g + (c16 >> 2);
-                    const int p = 2 * db + ((c16 & 3) >> 1);
-                    vh[ks][db][hf] = ds_read_tr16(Vs + (r * 16 + vslot(p, r)) * 8 + 4 * (c16 & 1));
-                }
-        };
-        auto pv = [&](int ks) {
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const u32x4 av = {vh[ks][db][0][0], vh[ks][db][0][1], vh[ks][db][1][0], vh[ks][db][1][1]};
-#pragma unroll
-                for (int t = 0; t < QT; ++t) oacc[t][db] = mfma16(av, bp[t][ks], oacc[t][db]);
-            }
-        };
-        read_v(0);
-        lds_wait16(vh[0]);
-        if constexpr (KS == 2 && QT > 1) {  // registers: one step of V fragments at a time
-            pv(0);
-            read_v(1);
-            lds_wait16(vh[1]);
-            pv(1);
-        } else if constexpr (KS == 2) {
-            read_v(1);
-            __builtin_amdgcn_sched_barrier(0);
-            pv(0);
-            __builtin_amdgcn_sched_barrier(0);
-            lds_wait16(vh[1]);
-            pv(1);
-        } else {
-            pv(0);
-        }
-    };
-
+    const float sl2 = (1.f / sqrtf((float)kDh)) * 1.4426950408889634f;
     // a wave whose query tiles are all padding only loads and meets the barriers
     const bool busy = wave * 16 * QT < A.Tpad;
-    // prefix tiles of this split: the tile RING - 1 ahead is requested once a slot frees up
+    uint64_t all_keys[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) all_keys[t] = ~0ull;
     for (int t = 0; t < ntiles; ++t) {
-        const int later = min(RING - 2, ntiles - 1 - t);
-        if (later >= 2)
-            ring_barrier<2 * kIPW>();
-        else if (later == 1)
-            ring_barrier<kIPW>();
-        else
-            ring_barrier<0>();
-        // the tile RING - 1 ahead goes out in parts between the blocks of S, so that the
-        // waves' load instructions do not all queue at once after the barrier
-        const bool ahead = t + RING - 1 < ntiles;
+        ring_barrier<0>();  // tile t has landed, every wave is done with tile t - 1
+        const bool ahead = t + 1 < ntiles;
         const bf16_t* src[kIPW];
-        if (ahead) sources(j_begin + (t + RING - 1) * KT, src);
-        const int nslot = (t + RING - 1) % RING;
-        constexpr int KB = KT / 16;
+        if (ahead) sources(j_begin + (t + 1) * kTile, src);
+        const int nstage = (t + 1) & 1;
         auto hook = [&](int kb) __attribute__((always_inline)) {
             if (ahead) {
                 __builtin_amdgcn_sched_barrier(0);
-                issue_part(src, nslot, kb * kIPW / KB, (kb + 1) * kIPW / KB);
+                issue_part(src, nstage, kb * kIPW / 4, (kb + 1) * kIPW / 4);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        const int base = j_begin + t * KT;
-        if (busy) {
-            attend_tile(t % RING, min(KT, j_end - base), j_end - base < KT, -1, hook);
-        } else if (ahead) {
-            issue_part(src, nslot, 0, kIPW);
-        }
+        const int base = j_begin + t * kTile;
+        if (busy)
+            attend_tile<QT>(ring + (t & 1) * kStageBytes, min(kTile, j_end - base), j_end - base < kTile, all_keys,
+                            sl2, st, hook);
+        else if (ahead)
+            issue_part(src, nstage, 0, kIPW);
     }
-
-    // tree keys (one workgroup per sequence and head): rotate k at L + depth, store k_rot,
-    // stage into slot 0, attend under the bitmask
-    if (tree_split) {
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-#pragma unroll
-            for (int w = 0; w < MDT_MAX_NODES / 64; ++w)
-                qa[t][w] = q_ok[t] && w < A.W ? A.anc[(long)qi[t] * A.W + w] : 0ull;
-        bf16_t* Ks = (bf16_t*)ring;
-        bf16_t* Vs = (bf16_t*)(ring + kTileB);
-        for (int tb = 0; tb < T; tb += KT) {
-            __syncthreads();
-            for (int c = tid; c < KT * 8; c += NT) {
-                const int key = c >> 3, dc = c & 7, j = tb + key;
-                u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
-                if (j < T) {
-                    const long node = (((long)b * T + j) * H + h) * kDh;
-                    klo = *(const u32x4*)(A.k + node + 8 * dc);
-                    khi = *(const u32x4*)(A.k + node + 64 + 8 * dc);
-                    rotate8(klo, khi, cs + min(max(A.depth[j], 0), A.max_depth) * (kDh / 2), 8 * dc);
-                    *(u32x4*)(A.k_rot + node + 8 * dc) = klo;
-                    *(u32x4*)(A.k_rot + node + 64 + 8 * dc) = khi;
-                }
-                *(u32x4*)(Ks + (key * 16 + kslot(dc, key)) * 8) = klo;
-                *(u32x4*)(Ks + (key * 16 + kslot(dc + 8, key)) * 8) = khi;
-            }
-            for (int c = tid; c < KT * 16; c += NT) {
-                const int key = c >> 4, p = c & 15, j = tb + key;
-                u32x4 vv = {0, 0, 0, 0};
-                if (j < T) vv = *(const u32x4*)(A.v + (((long)b * T + j) * H + h) * kDh + 8 * p);
-                *(u32x4*)(Vs + (key * 16 + vslot(p, key)) * 8) = vv;
-            }
-            __syncthreads();
-            if (busy) attend_tile(0, min(KT, T - tb), true, tb, [](int) {});
-        }
-    }
-
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        if (qi[t] < A.Tpad) {
-            const long base = (((long)b * H + h) * A.nparts + z) * A.Tpad + qi[t];
-            float* po = A.part_o + base * kDh;
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = oacc[t][db][e];
-            if (g == 0) {
-                A.part_ml[base * 2 + 0] = m_run[t];
-                A.part_ml[base * 2 + 1] = l_run[t];
-            }
-        }
-    }
+    if (tree_split) tree_pass<QT, NT>(A, b, h, ring, cs, sl2, busy, st);
+    write_partial<QT>(A, slot, st);
 }
 
-// Merge the split partials of every (sequence, head, node). grid (T, H, B), block 64.
-__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                   int T, int Tpad, int H, int nsplit, bf16_t* __restrict__ out) {
-    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Merge the partial states of every (sequence, head, node): nparts consecutive slots per
+// (sequence, head).  grid (T, H, B), block 64.
+__device__ __forceinline__ void merge_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                               int Tpad, int i, long s0, int n, long tree_slot, float& M,
+                                               float& den, float& na, float& nb) {
     const int lane = threadIdx.x;
-    const long pbase = ((long)b * H + h) * nsplit * Tpad + i;
-    // splits in batches of 8, all loads of a batch first; running max and sums rescale
-    // between batches (maxima are in log2 units)
-    float M = -INFINITY, den = 0.f, na = 0.f, nb = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    // partial slots s0 .. s0 + n - 1 and tree_slot (if >= 0), in batches of 8, all loads of a
+    // batch first; running max and sums rescale between batches (maxima in log2 units)
+    const int total = n + (tree_slot >= 0 ? 1 : 0);
+    M = -INFINITY;
+    den = na = nb = 0.f;
+    for (int u0 = 0; u0 < total; u0 += 8) {
         float ms[8], ls[8], oa[8], ob[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const long pidx = pbase + (long)min(s0 + u, nsplit - 1) * Tpad;
+            const int k = min(u0 + u, total - 1);
+            const long slot = k < n ? s0 + k : tree_slot;
+            const long pidx = slot * Tpad + i;
             ms[u] = part_ml[pidx * 2];
             ls[u] = part_ml[pidx * 2 + 1];
             oa[u] = part_o[pidx * kDh + lane];
@@ -672,7 +711,7 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
         float bm = M;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            if (s0 + u < nsplit) bm = fmaxf(bm, ms[u]);
+            if (u0 + u < total) bm = fmaxf(bm, ms[u]);
         if (bm == -INFINITY) continue;
         const float r = exp2f(M - bm);  // 0 while M is -inf
         den *= r;
@@ -680,7 +719,7 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
         nb *= r;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            if (s0 + u >= nsplit || ms[u] == -INFINITY) continue;
+            if (u0 + u >= total || ms[u] == -INFINITY) continue;
             const float wgt = exp2f(ms[u] - bm);
             den += ls[u] * wgt;
             na += oa[u] * wgt;
@@ -688,6 +727,14 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ par
         }
         M = bm;
     }
+}
+
+__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                   int T, int Tpad, int H, int nparts, bf16_t* __restrict__ out) {
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    float M, den, na, nb;
+    merge_partials(part_o, part_ml, Tpad, i, ((long)b * H + h) * nparts, nparts, -1, M, den, na, nb);
     bf16_t* o = out + (((long)b * T + i) * H + h) * kDh;
     o[lane] = f32_to_bf16(na / den);
     o[lane + 64] = f32_to_bf16(nb / den);
@@ -698,41 +745,34 @@ struct Plan {
     size_t po_bytes, pml_bytes;
 };
 
-// Split choice by a cost model in units of one 64-key tile: a workgroup costs a fixed
-// setup plus its tiles (the tree's about three), and the workgroups run one per CU in rounds
-// of kPlanCUs.  More splits shorten every workgroup but add rounds and partial-state traffic
-// for the combine.  A fixed CU count (MI355X) keeps the plan, and so the workspace size,
-// device-independent.
+// Key ranges per (sequence, head): five or six (measured best at every workload shape: more
+// ranges add per-workgroup set-up and partial states for the combine, about 2 us per range
+// at 7b-B16 and 6 us at 33B; fewer leave a long tail), six when all workgroups fit one round
+// of the CUs, and at least enough for 128 workgroups.  A paged cache's range stages its page
+// numbers in LDS, at most kMaxTilesPerSplit tiles' worth.  The plan depends only on the
+// shape, so the workspace size does too.
 constexpr int kPlanCUs = 256;
-constexpr double kSetupTiles = 1.2, kTreeTiles = 3.0, kCombineTilesPerSplit = 0.1;
 
-Plan plan(int B, int T, int H, int capacity) {
+Plan plan(int B, int T, int H, int capacity, bool paged) {
     Plan p;
     p.Tpad = (T + 15) / 16 * 16;
     const int waves = p.Tpad / 16;
     p.nwb = waves <= 4 ? 4 : (waves <= 8 ? 8 : 16);
     const int tiles = capacity > 0 ? (capacity + kTile - 1) / kTile : 1;
     const long bh = (long)B * H;
-    double best = 1e300;
-    int best_tps = tiles < kMaxTilesPerSplit ? tiles : kMaxTilesPerSplit;
-    for (int tps = 1; tps <= tiles && tps <= kMaxTilesPerSplit; ++tps) {
-        const int ns = (tiles + tps - 1) / tps;
-        const long rounds = (bh * (ns + 1) + kPlanCUs - 1) / kPlanCUs;
-        const double per_wg = kSetupTiles + (tps > kTreeTiles ? tps : kTreeTiles);
-        const double cost = rounds * per_wg + kCombineTilesPerSplit * ns * ((bh + kPlanCUs - 1) / kPlanCUs);
-        if (cost < best - 1e-9) {
-            best = cost;
-            best_tps = tps;
-        }
-    }
+    int ns = bh <= kPlanCUs ? 6 : 5;
+    ns = max(ns, (int)((128 + bh - 1) / bh));
+    int tps = (tiles + ns - 1) / ns;
+    if (paged) tps = min(tps, kMaxTilesPerSplit);
 #ifdef MDT_ATTN_TPS
-    best_tps = MDT_ATTN_TPS < tiles ? MDT_ATTN_TPS : tiles;
+    tps = MDT_ATTN_TPS;
 #endif
-    p.tiles_per_split = best_tps;
-    p.nsplit = (tiles + best_tps - 1) / best_tps;
-    p.nparts = p.nsplit + 1;
-    p.po_bytes = ((size_t)B * H * p.nparts * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
-    p.pml_bytes = (size_t)B * H * p.nparts * p.Tpad * 2 * sizeof(float);
+    p.tiles_per_split = max(1, min(tps, tiles));
+    p.nsplit = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.nparts = p.nsplit + 1;  // the key ranges, then the tree
+    const size_t slots = (size_t)B * H * p.nparts;
+    p.po_bytes = (slots * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
+    p.pml_bytes = slots * p.Tpad * 2 * sizeof(float);
     return p;
 }
 
@@ -741,8 +781,9 @@ Plan plan(int B, int T, int H, int capacity) {
 extern "C" size_t mdt_tree_attention_workspace(mdt_dtype dt, int B, int T, int H, int Dh, int capacity) {
     if (dt != MDT_BF16 || B < 1 || T < 1 || H < 1) return 0;
     (void)Dh;
-    const Plan p = plan(B, T, H, capacity);
-    return p.po_bytes + p.pml_bytes;
+    // either cache layout (a paged cache may need more, shorter key ranges)
+    const Plan pc = plan(B, T, H, capacity, false), pp = plan(B, T, H, capacity, true);
+    return max(pc.po_bytes + pc.pml_bytes, pp.po_bytes + pp.pml_bytes);
 }
 
 extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int H, int Dh, const mdt_tree_dev* tree,
@@ -786,7 +827,7 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
                    theta, (float*)out, (float*)k_rot);
         return mdt_launched("attn_valu");
     }
-    const Plan p = plan(B, T, H, cache->capacity);
+    const Plan p = plan(B, T, H, cache->capacity, cache->layout == MDT_KV_PAGED);
     MDT_REQUIRE(ws, MDT_ERR_WORKSPACE, "workspace is NULL");
     MDT_REQUIRE(mdt_aligned16(ws), MDT_ERR_ALIGN, "workspace must be 16-byte aligned");
     MDT_REQUIRE(ws_bytes >= p.po_bytes + p.pml_bytes, MDT_ERR_WORKSPACE, "workspace too small");
@@ -798,20 +839,13 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
                (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
                tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.nparts, {}};
     for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
-    const dim3 grid(H, B, p.nparts);
     const bool paged = cache->layout == MDT_KV_PAGED;
-#ifndef MDT_ATTN_KT
-#define MDT_ATTN_KT 64
-#endif
-#ifndef MDT_ATTN_RING
-#define MDT_ATTN_RING 2
-#endif
-    constexpr int KT = MDT_ATTN_KT, RG = MDT_ATTN_RING;
     // up to 8 query tiles: one per wave (4 or 8 waves); up to 16: two per wave on 8 waves
-    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true, 1, KT, RG> : attn_stream<4, false, 1, KT, RG>)
-              : p.nwb == 8 ? (paged ? attn_stream<8, true, 1, KT, RG> : attn_stream<8, false, 1, KT, RG>)
-                           : (paged ? attn_stream<8, true, 2, KT, RG> : attn_stream<8, false, 2, KT, RG>);
-    MDT_LAUNCH("attn_stream", kern, grid, dim3(64 * (p.nwb == 16 ? 8 : p.nwb)), 0, s, A);
+    const int threads = 64 * (p.nwb == 16 ? 8 : p.nwb);
+    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true, 1> : attn_stream<4, false, 1>)
+              : p.nwb == 8 ? (paged ? attn_stream<8, true, 1> : attn_stream<8, false, 1>)
+                           : (paged ? attn_stream<8, true, 2> : attn_stream<8, false, 2>);
+    MDT_LAUNCH("attn_stream", kern, dim3(H, B, p.nparts), dim3(threads), 0, s, A);
     st = mdt_launched("attn_stream");
     if (st != MDT_OK) return st;
     MDT_LAUNCH("attn_combine", attn_combine, dim3(T, H, B), dim3(64), 0, s, A.part_o, A.part_ml, T, p.Tpad, H,
