@@ -113,3 +113,54 @@ def test_chain_equals_causal_attention():
             p = np.exp(sc - sc.max())
             ref = (p / p.sum()) @ vf[:i + 1, h]
             assert np.max(np.abs(go[i, h] - ref)) <= REL_TOL * np.max(np.abs(ref)), (i, h)
+
+
+# (cartesian ranks, paged, page size): 106 nodes on 8 waves, 213 nodes on 8 waves of two query
+# tiles; page sizes that are not powers of two take the division path of the page lookup
+SCHEDULES = {
+    "T106-paged24": ((5, 4, 4), True, 24),
+    "T213-paged16": ((4, 4, 3, 3), True, 16),
+    "T213-contig": ((4, 4, 3, 3), False, 0),
+    "T41-paged48": ((4, 3, 2), True, 48),
+}
+
+
+@pytest.mark.parametrize("name", list(SCHEDULES))
+def test_attention_key_ranges(name):
+    """Few (sequence, head) pairs and long prefixes of mixed length: many key ranges per
+    pair, ranges past a short prefix (empty partial states), a partial last tile, the tree
+    workgroup, and the paged lookups -- against the oracle, row by row."""
+    import medusa_tree_verification_heads_amd as mdt
+    s, paged, page = SCHEDULES[name]
+    H, Dh = 2, 128
+    ot = otree.cartesian_tree(s)
+    T = ot.T
+    L = np.array([0, 700, 1301], dtype=np.int32)
+    B = len(L)
+    note(f"attention key ranges {name}: T={T} B={B} prefixes={L.tolist()} paged={paged} page={page}")
+    rng = np.random.default_rng(T + 17 * page)
+    q, k, v = (_draw(rng, (B, T, H, Dh), 0.3, True) for _ in range(3))
+    if paged:
+        npg = [max(1, -(-int(L[b]) // page)) for b in range(B)]
+        pool = sum(npg) + 3
+        perm = rng.permutation(pool)
+        pt = np.full((B, max(npg) + 2), -1, dtype=np.int32)
+        o = 0
+        for b in range(B):
+            pt[b, :npg[b]] = perm[o:o + npg[b]]
+            o += npg[b]
+        Kc, Vc = _draw(rng, (pool, page, H, Dh), 0.3, True), _draw(rng, (pool, page, H, Dh), 0.3, True)
+    else:
+        pt = None
+        Kc, Vc = _draw(rng, (B, int(L.max()) + 5, H, Dh), 0.3, True), _draw(rng, (B, int(L.max()) + 5, H, Dh), 0.3, True)
+    tree = mdt.Tree.cartesian(s)
+    cache = mdt.KVCache(_dev(Kc), _dev(Vc), None if pt is None else torch.from_numpy(pt).cuda(), page or 16)
+    out, k_rot = mdt.tree_attention(_dev(q), _dev(k), _dev(v), cache, torch.from_numpy(L).cuda(),
+                                    tree.to_device("cuda"))
+    torch.cuda.synchronize()
+    ro, rk = ostep.tree_attention(q, k, v, Kc, Vc, L, ot, 10000.0, bf16_store=True, page_table=pt,
+                                  page_size=page or 16)
+    go, gk = ostep.to_f64(_host(out)), ostep.to_f64(_host(k_rot))
+    eo, ek = rel_err_rows(go, ro), rel_err_rows(gk, rk)
+    note(f"  o rel err {eo:.2e}, k_rot rel err {ek:.2e}")
+    assert eo <= REL_TOL and ek <= REL_TOL
