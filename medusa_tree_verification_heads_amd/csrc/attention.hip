@@ -198,15 +198,16 @@ __device__ __forceinline__ float2 rope_cs_table_entry(int pos, double inv_freq) 
     return make_float2(c, s);
 }
 
-// Rotate the 8 pairs (lo[t], hi[t]) = (x_m, x_{m+64}), m = m0 + t, with cos/sin row cs.
-__device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const float2* cs, int m0) {
+// Rotate the 8 pairs (lo[t], hi[t]) = (x_m, x_{m+64}), m = m0 + t, with cos/sin row cs, and
+// multiply the rotated values by sc before they are rounded to bf16.
+__device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const float2* cs, int m0, float sc = 1.f) {
     u32x4 a, b;
 #pragma unroll
     for (int t = 0; t < 8; t += 2) {
         const float2 r0 = cs[m0 + t], r1 = cs[m0 + t + 1];
         const float x0 = elt(lo, t), y0 = elt(hi, t), x1 = elt(lo, t + 1), y1 = elt(hi, t + 1);
-        a[t >> 1] = pack_bf16(x0 * r0.x - y0 * r0.y, x1 * r1.x - y1 * r1.y);
-        b[t >> 1] = pack_bf16(y0 * r0.x + x0 * r0.y, y1 * r1.x + x1 * r1.y);
+        a[t >> 1] = pack_bf16((x0 * r0.x - y0 * r0.y) * sc, (x1 * r1.x - y1 * r1.y) * sc);
+        b[t >> 1] = pack_bf16((y0 * r0.x + x0 * r0.y) * sc, (y1 * r1.x + x1 * r1.y) * sc);
     }
     lo = a;
     hi = b;
@@ -262,22 +263,36 @@ struct AttnArgs {
 // before each tile's first fragment read), which serialises the ring.  The transpose reads
 // are issued as inline assembly for the same reason (the compiler's own form of that read
 // always waits), with an explicit lgkmcnt wait that the MFMAs depend on.
+#ifndef MDT_ATTN_AUX
+#define MDT_ATTN_AUX 2  // cache policy of the K and V loads: non-temporal (read once)
+#endif
+#ifndef MDT_ATTN_S4
+#define MDT_ATTN_S4 2
+#endif
+#ifndef MDT_ATTN_S8
+#define MDT_ATTN_S8 2
+#endif
 constexpr int kStreamPages = 2048;               // page-table entries a workgroup stages
 constexpr int kTileBytes = kTile * kDh * 2;      // one K (or V) tile: 16 KiB
 constexpr int kStageBytes = 2 * kTileBytes;      // K then V
-constexpr int kRingBytes = 2 * kStageBytes;      // two stages
 constexpr int kCsBytes = (MDT_MAX_HEADS + 1) * (kDh / 2) * (int)sizeof(float2);
 constexpr int kInstr = kTile * (kDh / 8) / 64;   // load instructions per tile (K or V): 16
 
 __device__ __forceinline__ int kslot(int p, int r) { return p ^ (r & 15); }
 __device__ __forceinline__ int vslot(int p, int r) { return p ^ ((2 * r) & 14); }
 
-// ds_read_b64_tr_b16 of the 8 bytes at LDS address p (see above on why it is assembly).
-__device__ __forceinline__ u32x2 ds_read_tr16(const void* p) {
+// ds_read_b64_tr_b16 of the 8 bytes at LDS byte address a + OFF (see above on why it is
+// assembly; the offset rides in the instruction's immediate field).
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t a) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
     u32x2 r;
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
     return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 // Wait for this wave's LDS reads; the 16 values count as written by the wait, so nothing
@@ -323,10 +338,12 @@ __device__ __forceinline__ void fill_rope_table(const AttnArgs& A, int L, float2
         cs[e] = rope_cs_table_entry(L + e / (kDh / 2), A.inv_freq[e % (kDh / 2)]);
 }
 
-// Rotate raw queries into st.bq and reset the running state.
+// Rotate raw queries into st.bq, scaled by log2(e) / sqrt(Dh) so that their products with the
+// keys are the scores in log2 units of the softmax, and reset the running state.
 template <int QT>
 __device__ __forceinline__ void start_queries(const AttnArgs& A, const u32x4 (&raw)[QT][4], const int (&dq)[QT],
                                               const float2* cs, QueryState<QT>& st) {
+    const float sl2 = (1.f / sqrtf((float)kDh)) * 1.4426950408889634f;
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -334,8 +351,8 @@ __device__ __forceinline__ void start_queries(const AttnArgs& A, const u32x4 (&r
 #pragma unroll
         for (int s = 0; s < 4; ++s) st.bq[t][s] = ok ? raw[t][s] : u32x4{0, 0, 0, 0};
         const float2* row = cs + dq[t] * (kDh / 2);
-        rotate8(st.bq[t][0], st.bq[t][2], row, 8 * g);
-        rotate8(st.bq[t][1], st.bq[t][3], row, 32 + 8 * g);
+        rotate8(st.bq[t][0], st.bq[t][2], row, 8 * g, sl2);
+        rotate8(st.bq[t][1], st.bq[t][3], row, 32 + 8 * g, sl2);
 #pragma unroll
         for (int db = 0; db < 8; ++db) st.oacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m_run[t] = -INFINITY;
@@ -365,24 +382,33 @@ __device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, cons
     }
 }
 
-// One 64-key tile of the LDS stage `stage`, nvalid of its keys real; masked tiles also keep
-// only the keys whose bit is set in qw[t] (bit j: key j of the tile; all ones for prefix
-// keys, the ancestor-or-self bits for tree keys).  hook(kb) runs after each 16-key block of
-// S.  (The mask words come in as values: selecting one of a query's four words here would
-// index a register array with a run-time index, which puts the whole state in scratch.)
+// The scores S^T of one tile, as the 16x16 MFMA output blocks of its 16-key blocks, each less
+// the reference its query's running maximum had when the tile was multiplied (0 before the
+// first key): the accumulators start from minus that reference.
+template <int QT>
+struct QkAcc {
+    f32x4 s[QT][kTile / 16];
+};
+
+template <int QT>
+__device__ __forceinline__ float score_base(const QueryState<QT>& st, int t) {
+    return st.m_run[t] == -INFINITY ? 0.f : st.m_run[t];
+}
+
+// S^T = K Q^T for one 64-key tile (K tile at `kst`); hook(kb) runs after each 16-key block.
 template <int QT, typename Hook>
-__device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool masked, const uint64_t (&qw)[QT],
-                                            float sl2, QueryState<QT>& st, Hook&& hook) {
+__device__ __forceinline__ void qk_tile(const char* kst, const QueryState<QT>& st, QkAcc<QT>& sa, Hook&& hook) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-    const bf16_t* Ks = (const bf16_t*)stage;
-    const bf16_t* Vs = (const bf16_t*)(stage + kTileBytes);
-    constexpr int KB = kTile / 16, KS = kTile / 32;
-    f32x4 sacc[QT][KB];
+    const bf16_t* Ks = (const bf16_t*)kst;
+    constexpr int KB = kTile / 16;
+    float a0[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) a0[t] = -score_base(st, t);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         f32x4 acc[QT];
 #pragma unroll
-        for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < QT; ++t) acc[t] = f32x4{a0[t], a0[t], a0[t], a0[t]};
         const int r = kb * 16 + c16;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -391,10 +417,23 @@ __device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool 
             for (int t = 0; t < QT; ++t) acc[t] = mfma16(kf, st.bq[t][s], acc[t]);
         }
 #pragma unroll
-        for (int t = 0; t < QT; ++t) sacc[t][kb] = acc[t];
+        for (int t = 0; t < QT; ++t) sa.s[t][kb] = acc[t];
         hook(kb);
     }
-    u32x4 bp[QT][KS];
+}
+
+// The online-softmax step of one tile of scores (nvalid of its keys real): update (m, l),
+// rescale the O^T accumulators and leave the probabilities as bf16 MFMA operands in bp.
+// Masked tiles also keep only the keys whose bit is set in qw[t] (bit j: key j of the tile;
+// all ones for prefix keys, the ancestor-or-self bits for tree keys).  (The mask words come
+// in as values: selecting one of a query's four words here would index a register array
+// with a run-time index, which puts the whole state in scratch.)
+template <int QT>
+__device__ __forceinline__ void softmax_tile(QkAcc<QT>& sa, int nvalid, bool masked, const uint64_t (&qw)[QT],
+                                             QueryState<QT>& st, u32x4 (&bp)[QT][kTile / 32]) {
+    const int g = (threadIdx.x & 63) >> 4;
+    constexpr int KB = kTile / 16, KS = kTile / 32;
+    auto& sacc = sa.s;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         float tmax = -INFINITY;
@@ -413,23 +452,37 @@ __device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[t][kb][e]);
         }
-        tmax = xor_max_16_32(tmax) * sl2;
+        const float m_base = score_base(st, t);
+        tmax = xor_max_16_32(tmax) + m_base;  // the tile's largest score
         // The reference maximum moves only when a score exceeds it by more than 2^8, so that
         // the accumulators are rarely rescaled; weights stay below 256 (fine for the bf16
         // probabilities and the fp32 sums).  A row with no key yet keeps -inf and a
-        // reference of 0 (its weights are exp2(-inf) = 0).
+        // reference of 0 (its weights are exp2(-inf) = 0).  While the reference stays, the
+        // accumulated scores are already relative to it.
         const float m_new = tmax > st.m_run[t] + 8.f ? tmax : st.m_run[t];
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float corr = __builtin_amdgcn_exp2f(st.m_run[t] - m_ref);
+        const float delta = m_ref - m_base;
         float tsum = 0.f;
+        if (__all(delta == 0.f)) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][e], sl2, -m_ref));
-                sacc[t][kb][e] = p;
-                tsum += p;
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(sacc[t][kb][e]);
+                    sacc[t][kb][e] = p;
+                    tsum += p;
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(sacc[t][kb][e] - delta);
+                    sacc[t][kb][e] = p;
+                    tsum += p;
+                }
+        }
         st.l_run[t] = st.l_run[t] * corr + xor_sum_16_32(tsum);
         st.m_run[t] = m_new;
         if (__any(corr != 1.f))
@@ -444,20 +497,52 @@ __device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool 
             bp[t][ks][3] = pack_bf16(sacc[t][2 * ks + 1][2], sacc[t][2 * ks + 1][3]);
         }
     }
-    // O^T += V^T P^T: lane (dim 16 db + c16, group g) takes keys 32 ks + 4 g + e and
-    // 32 ks + 16 + 4 g + e (e < 4) by two transpose reads; as a source lane it reads the 8
-    // bytes of key row 32 ks + 16 hf + 4 g + c16 / 4, dims 16 db + 4 (c16 mod 4) ..
-    u32x2 vh[KS][8][2];
-    auto read_v = [&](int ks) __attribute__((always_inline)) {
+}
+
+// Scores and softmax of one 64-key tile (see qk_tile and softmax_tile).
+template <int QT, typename Hook>
+__device__ __forceinline__ void scores_tile(const char* kst, int nvalid, bool masked, const uint64_t (&qw)[QT],
+                                            QueryState<QT>& st, u32x4 (&bp)[QT][kTile / 32], Hook&& hook) {
+    QkAcc<QT> sa;
+    qk_tile<QT>(kst, st, sa, hook);
+    softmax_tile<QT>(sa, nvalid, masked, qw, st, bp);
+}
+
+// Per-lane byte offsets of the V^T fragment reads within a V tile: lane (dim 16 db + c16,
+// group g) takes keys 32 ks + 4 g + e and 32 ks + 16 + 4 g + e (e < 4) by two transpose
+// reads; as a source lane it reads the 8 bytes of key row 32 ks + 16 hf + 4 g + c16 / 4,
+// dims 16 db + 4 (c16 mod 4) ..  The rows 32 ks + 16 hf add a multiple of 16 to the row, which
+// leaves its swizzle alone: that part is the reads' immediate offset.
+struct VOffsets {
+    uint32_t o[8];
+};
+__device__ __forceinline__ VOffsets v_offsets() {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int r0 = 4 * g + (c16 >> 2);
+    VOffsets v;
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < 8; ++db) {
+        const int p = 2 * db + ((c16 & 3) >> 1);
+        v.o[db] = (uint32_t)((r0 * 16 + vslot(p, r0)) * 16 + 8 * (c16 & 1));
+    }
+    return v;
+}
+
+template <int KS>
+__device__ __forceinline__ void read_v_step(uint32_t vbase, const VOffsets& vo, u32x2 (&vh)[8][2]) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int r = 32 * ks + 16 * hf + 4 * g + (c16 >> 2);
-                const int p = 2 * db + ((c16 & 3) >> 1);
-                vh[ks][db][hf] = ds_read_tr16(Vs + (r * 16 + vslot(p, r)) * 8 + 4 * (c16 & 1));
-            }
-    };
+    for (int db = 0; db < 8; ++db) {
+        vh[db][0] = ds_read_tr16<KS * 32 * kDh * 2>(vbase + vo.o[db]);
+        vh[db][1] = ds_read_tr16<(KS * 32 + 16) * kDh * 2>(vbase + vo.o[db]);
+    }
+}
+
+// O^T += V^T P^T for one 64-key tile (V tile at `vst`, probabilities from scores_tile).
+template <int QT>
+__device__ __forceinline__ void values_tile(const char* vst, const VOffsets& vo, const u32x4 (&bp)[QT][kTile / 32],
+                                            QueryState<QT>& st) {
+    const uint32_t vbase = lds_addr(vst);
+    u32x2 vh[2][8][2];
     auto pv = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
@@ -466,15 +551,15 @@ __device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool 
             for (int t = 0; t < QT; ++t) st.oacc[t][db] = mfma16(av, bp[t][ks], st.oacc[t][db]);
         }
     };
-    read_v(0);
+    read_v_step<0>(vbase, vo, vh[0]);
     lds_wait16(vh[0]);
     if constexpr (QT > 1) {  // registers: one step of V fragments at a time
         pv(0);
-        read_v(1);
+        read_v_step<1>(vbase, vo, vh[1]);
         lds_wait16(vh[1]);
         pv(1);
     } else {  // the reads of step 1 go out while the MFMAs of step 0 run
-        read_v(1);
+        read_v_step<1>(vbase, vo, vh[1]);
         __builtin_amdgcn_sched_barrier(0);
         pv(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -483,12 +568,21 @@ __device__ __forceinline__ void attend_tile(const char* stage, int nvalid, bool 
     }
 }
 
+// One whole 64-key tile of the LDS stage `stage` (K, then V).
+template <int QT, typename Hook>
+__device__ __forceinline__ void attend_tile(const char* stage, const VOffsets& vo, int nvalid, bool masked,
+                                            const uint64_t (&qw)[QT], QueryState<QT>& st, Hook&& hook) {
+    u32x4 bp[QT][kTile / 32];
+    scores_tile<QT>(stage, nvalid, masked, qw, st, bp, hook);
+    values_tile<QT>(stage + kTileBytes, vo, bp, st);
+}
+
 // The tree keys of (b, h): rotate k at L + depth, store k_rot, stage 64 keys at a time into
 // the ring's first stage (ordinary stores) and attend under the ancestor-or-self bitmask.
 // The ring must be idle; cs holds the table of sequence b.
 template <int QT, int NT>
-__device__ __forceinline__ void tree_pass(const AttnArgs& A, int b, int h, char* ring, const float2* cs, float sl2,
-                                          bool busy, QueryState<QT>& st) {
+__device__ __forceinline__ void tree_pass(const AttnArgs& A, int b, int h, char* ring, const float2* cs,
+                                          const VOffsets& vo, bool busy, QueryState<QT>& st) {
     const int T = A.T, H = A.H, tid = threadIdx.x;
     bf16_t* Ks = (bf16_t*)ring;
     bf16_t* Vs = (bf16_t*)(ring + kTileBytes);
@@ -521,7 +615,7 @@ __device__ __forceinline__ void tree_pass(const AttnArgs& A, int b, int h, char*
             qw[t] = qi < T && (tb >> 6) < A.W ? A.anc[(long)qi * A.W + (tb >> 6)] : 0ull;
         }
         __syncthreads();
-        if (busy) attend_tile<QT>(ring, min(kTile, T - tb), true, qw, sl2, st, [](int) {});
+        if (busy) attend_tile<QT>(ring, vo, min(kTile, T - tb), true, qw, st, [](int) {});
     }
 }
 
@@ -546,12 +640,14 @@ struct LoadSlot {
 // One (sequence, head, key range) per workgroup, or the tree of one (sequence, head).
 // Grid (H, B, nsplit + 1), the z index outermost: the key ranges in order (the ranges that
 // end past a short prefix exit at once), then the tree.
-template <int NWB, bool PAGED, int QT>
+template <int NWB, bool PAGED, int QT, int S>
 __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  // two waves per SIMD
     constexpr int NT = 64 * NWB;
     using LS = LoadSlot<NWB>;
     constexpr int kIPW = LS::kIPW;
     static_assert(2 * kInstr % NWB == 0, "loads divide among the waves");
+    static_assert(S >= 2 && S <= 4 && (S - 2) * kIPW < 64, "ring stages / vmcnt range");
+    constexpr int kRingBytes = S * kStageBytes;
     constexpr int kPageBytes = PAGED ? kStreamPages * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char lds[kRingBytes + kCsBytes + kPageBytes];
     char* const ring = lds;
@@ -641,32 +737,45 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
 #pragma unroll
         for (int j = 0; j < kIPW; ++j) {
             if (j < j0 || j >= j1) continue;
-            __builtin_amdgcn_global_load_lds((const void*)src[j], (lds_void_t*)(kst + LS::lds_offset(j)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)src[j], (lds_void_t*)(kst + LS::lds_offset(j)), 16, 0,
+                                             MDT_ATTN_AUX);
         }
     };
-    if (ntiles > 0) {
-        const bf16_t* src[kIPW];
-        sources(j_begin, src);
-        issue_part(src, 0, 0, kIPW);
-    }
+    // tiles 0 .. S - 2 into stages 0 .. S - 2
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < ntiles) {
+            const bf16_t* src[kIPW];
+            sources(j_begin + t * kTile, src);
+            issue_part(src, t, 0, kIPW);
+        }
     fill_rope_table(A, L, cs, NT);
-    // cos/sin table ready; the tile already requested stays in flight (a plain
-    // __syncthreads would wait for it)
+    // cos/sin table ready; the tiles already requested stay in flight (a plain
+    // __syncthreads would wait for them)
     ring_barrier<63>();
     start_queries<QT>(A, raw, dq, cs, st);
 
-    const float sl2 = (1.f / sqrtf((float)kDh)) * 1.4426950408889634f;
+    const VOffsets vo = v_offsets();
     // a wave whose query tiles are all padding only loads and meets the barriers
     const bool busy = wave * 16 * QT < A.Tpad;
     uint64_t all_keys[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) all_keys[t] = ~0ull;
     for (int t = 0; t < ntiles; ++t) {
-        ring_barrier<0>();  // tile t has landed, every wave is done with tile t - 1
-        const bool ahead = t + 1 < ntiles;
+        // tile t has landed once at most the loads of the later tiles already requested
+        // (t + 1 .. t + S - 2) are outstanding; every wave is done with tile t - 1, whose
+        // stage now takes tile t + S - 1
+        const int later = min(S - 2, ntiles - 1 - t);
+        if (S > 3 && later >= 2)
+            ring_barrier<(S > 3 ? 2 : 0) * kIPW>();
+        else if (S > 2 && later == 1)
+            ring_barrier<(S > 2 ? 1 : 0) * kIPW>();
+        else
+            ring_barrier<0>();
+        const bool ahead = t + S - 1 < ntiles;
         const bf16_t* src[kIPW];
-        if (ahead) sources(j_begin + (t + 1) * kTile, src);
-        const int nstage = (t + 1) & 1;
+        if (ahead) sources(j_begin + (t + S - 1) * kTile, src);
+        const int nstage = (t + S - 1) % S;
         auto hook = [&](int kb) __attribute__((always_inline)) {
             if (ahead) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -676,12 +785,12 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
         };
         const int base = j_begin + t * kTile;
         if (busy)
-            attend_tile<QT>(ring + (t & 1) * kStageBytes, min(kTile, j_end - base), j_end - base < kTile, all_keys,
-                            sl2, st, hook);
+            attend_tile<QT>(ring + (t % S) * kStageBytes, vo, min(kTile, j_end - base), j_end - base < kTile,
+                            all_keys, st, hook);
         else if (ahead)
             issue_part(src, nstage, 0, kIPW);
     }
-    if (tree_split) tree_pass<QT, NT>(A, b, h, ring, cs, sl2, busy, st);
+    if (tree_split) tree_pass<QT, NT>(A, b, h, ring, cs, vo, busy, st);
     write_partial<QT>(A, slot, st);
 }
 
@@ -842,9 +951,10 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     const bool paged = cache->layout == MDT_KV_PAGED;
     // up to 8 query tiles: one per wave (4 or 8 waves); up to 16: two per wave on 8 waves
     const int threads = 64 * (p.nwb == 16 ? 8 : p.nwb);
-    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true, 1> : attn_stream<4, false, 1>)
-              : p.nwb == 8 ? (paged ? attn_stream<8, true, 1> : attn_stream<8, false, 1>)
-                           : (paged ? attn_stream<8, true, 2> : attn_stream<8, false, 2>);
+    constexpr int S4 = MDT_ATTN_S4, S8 = MDT_ATTN_S8;
+    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true, 1, S4> : attn_stream<4, false, 1, S4>)
+              : p.nwb == 8 ? (paged ? attn_stream<8, true, 1, S8> : attn_stream<8, false, 1, S8>)
+                           : (paged ? attn_stream<8, true, 2, S8> : attn_stream<8, false, 2, S8>);
     MDT_LAUNCH("attn_stream", kern, dim3(H, B, p.nparts), dim3(threads), 0, s, A);
     st = mdt_launched("attn_stream");
     if (st != MDT_OK) return st;
