@@ -310,8 +310,12 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16_t* __restrict__ x, cons
         if (c + 1 < nch) {
             landed(min(S - 2, nch - 2 - c));
             if (c + S < nch) issue(c + S);
-            read((c + 1) % S, 0, KSTEPS & 1);
         }
+        // The first fragments of chunk c+1 go out before the last MFMAs of chunk c.  The read
+        // is unconditional (after the last chunk it reads a ring slot whose values are never
+        // used) so that every path into the MFMAs below has the same LDS reads in flight:
+        // otherwise the compiler's wait before them also covers these reads.
+        read((c + 1) % S, 0, KSTEPS & 1);
         mma((KSTEPS - 1) & 1);
         lds_done();
     }
