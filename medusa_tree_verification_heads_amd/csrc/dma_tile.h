@@ -322,3 +322,111 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16_t* __restrict__ x, cons
     __syncthreads();  // the ring is free for the caller's epilogue
     epi(acc);
 }
+
+// dma_gemm_tile's staging with a wider tile: each chunk brings MB + NB rows, so a 256 x 256
+// tile moves a third fewer bytes through the L2 -> LDS path per MFMA than 256 x 128 (the x rows,
+// re-read by every weight block, are the larger share).  Per k-step a wave reads its MTW x
+// fragments into one of two register sets and refills each weight fragment register with
+// the next step's fragment right after that fragment's MFMAs ("rolling"), which keeps
+// MTW x NTW = 4 x 8 accumulator fragments and the operands of two steps within two waves
+// per SIMD.  The barrier sits before a chunk's last k-step, whose fragments are already in
+// registers; the next chunk's first fragments are read during that step.  KC / 32 must be
+// even (register sets alternate with the k-step's parity).  epi(acc) as for dma_gemm_tile.
+template <int MB, int NB, int WM, int WN, int KC, int S, int AUX = 0, typename Epi>
+__device__ __forceinline__ void dma_gemm_wide(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
+                                              int d, int V, int m0, int n0, char* smem, Epi&& epi) {
+    using P = DmaGemm<MB, NB, WM, WN, KC, S>;
+    constexpr int kPR = P::kPR, MTW = P::MTW, NTW = P::NTW, KSTEPS = P::KSTEPS;
+    static_assert(KSTEPS % 2 == 0, "k-steps per chunk must be even");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nch = d / KC;
+
+    auto issue = [&](int c) {
+        char* st = smem + (c % S) * P::kStage;
+#pragma unroll
+        for (int j = 0; j < P::kIX; ++j) {
+            const int i = wave * P::kIX + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
+            const bf16_t* src = x + (size_t)min(m0 + r, M - 1) * d + c * KC + 8 * p;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < P::kIW; ++j) {
+            const int i = wave * P::kIW + j;
+            const int q = 64 * i + lane;
+            const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
+            const bf16_t* src = W + (size_t)min(n0 + r, V - 1) * d + c * KC + 8 * p;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P::kXBytes + 1024 * i), 16, 0,
+                                             AUX);
+        }
+    };
+    auto landed = [&](int later) {
+        if (later >= 3)
+            ring_barrier<3 * P::kLoads>();
+        else if (later == 2)
+            ring_barrier<2 * P::kLoads>();
+        else if (later == 1)
+            ring_barrier<P::kLoads>();
+        else
+            ring_barrier<0>();
+    };
+
+    f32x4 acc[NTW][MTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 fa[2][MTW], fb[NTW];
+    auto read_a = [&](int slot, int s, int set) {
+        const bf16_t* xs = (const bf16_t*)(smem + slot * P::kStage);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) {
+            const int row = wm * (MB / WM) + 16 * mt + c16;
+            fa[set][mt] = *(const u32x4*)(xs + (row * kPR + dma_swz<kPR>(4 * s + g, row)) * 8);
+        }
+    };
+    auto read_b = [&](int slot, int s, int nt) {
+        const bf16_t* ws = (const bf16_t*)(smem + slot * P::kStage + P::kXBytes);
+        const int row = wn * (NB / WN) + 16 * nt + c16;
+        return *(const u32x4*)(ws + (row * kPR + dma_swz<kPR>(4 * s + g, row)) * 8);
+    };
+    // the MFMAs of one k-step (register set `set`, weight fragments fb), each weight
+    // fragment refilled from (nslot, ns) once its MFMAs are issued
+    auto step = [&](int set, int nslot, int ns) {
+        read_a(nslot, ns, set ^ 1);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) acc[nt][mt] = mfma16(fa[set][mt], fb[nt], acc[nt][mt]);
+            fb[nt] = read_b(nslot, ns, nt);
+        }
+    };
+
+#pragma unroll
+    for (int c = 0; c < S; ++c)
+        if (c < nch) issue(c);
+    landed(min(S - 1, nch - 1));
+    read_a(0, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) fb[nt] = read_b(0, 0, nt);
+    lds_done();
+    for (int c = 0; c < nch; ++c) {
+        const int slot = c % S;
+#pragma unroll
+        for (int s = 0; s + 1 < KSTEPS; ++s) step(s & 1, slot, s + 1);
+        // chunk c's last fragments are in registers: publish chunk c+1, free chunk c's buffer;
+        // the last step reads chunk c+1's first fragments (after the last chunk: a ring slot
+        // whose values are never used, so that every path has the same reads in flight)
+        if (c + 1 < nch) {
+            landed(min(S - 2, nch - 2 - c));
+            if (c + S < nch) issue(c + S);
+        }
+        step((KSTEPS - 1) & 1, (c + 1) % S, 0);
+        lds_done();
+    }
+    __syncthreads();  // the ring is free for the caller's epilogue
+    epi(acc);
+}

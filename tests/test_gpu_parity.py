@@ -346,3 +346,47 @@ def test_verify_small_rows_ragged(T, d, V):
         e = edge.cpu().numpy()
         oe = ostep.edge_logits(z, tok, tree)
         assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
+
+
+@pytest.mark.parametrize("B,T,d,V", [(16, 42, 256, 5003), (4, 256, 128, 2000), (4, 256, 192, 1900),
+                                     (5, 220, 128, 777), (8, 160, 64, 32000)])
+def test_verify_many_rows_ragged(B, T, d, V):
+    """256 and more node rows (batches, large trees): the 256 x 128 tile (672 rows) and the
+    256 x 256 tile (1024 and more rows), with vocabularies whose last tile is partial or whose
+    last tile's second half lies past the vocabulary (1900), a row count that leaves a partial
+    last row block (1100), and a single 64-dim chunk.  Row statistics and edge logits against
+    the oracle's definitions, per row."""
+    import medusa_tree_verification_heads_amd as mdt
+    from oracle import step as ostep
+    from oracle import tree as otree
+    from workloads.gen import f32_to_bf16_bits
+    note(f"verify many rows B={B} T={T} d={d} V={V}")
+    tree = otree.scored_tree_greedy(4, 10, T)
+    dtree = mdt.Tree.scored(4, 10, T).to_device("cuda")
+    M = B * T
+    rng = np.random.default_rng(M + d + V)
+    x = ostep.round_bf16(rng.standard_normal((M, d)))
+    W = ostep.round_bf16(rng.standard_normal((V, d)) * d ** -0.5)
+    tok = rng.integers(0, V, (B, T))
+    xd = torch.from_numpy(f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    Wd = torch.from_numpy(f32_to_bf16_bits(W.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    z = x @ W.T
+    scale = np.abs(z).max(axis=1)
+    for tau in (0.0, 0.7):
+        stats, edge, logits = mdt.verify_logits(xd, Wd, dtree, torch.from_numpy(tok.astype(np.int32)).cuda(), tau,
+                                                want_logits=True)
+        torch.cuda.synchronize()
+        assert rel_err_rows(logits.cpu().numpy(), z) <= REL_TOL
+        st = _stats_np(stats.cpu().numpy())
+        for r in range(M):
+            ref = ostep.row_stats(z[r], tau)
+            assert abs(st["max"][r] - ref["max"]) <= REL_TOL * scale[r], r
+            t2 = np.partition(z[r], -2)[-2:]
+            if t2[1] - t2[0] >= 1e-3:
+                assert st["argmax"][r] == ref["argmax"], r
+            if tau > 0:
+                assert abs(st["logZ"][r] - ref["logZ"]) <= REL_TOL * abs(ref["logZ"]), r
+                assert abs(st["entropy"][r] - ref["H"]) <= REL_TOL * max(abs(ref["H"]), 1e-3), r
+        e = edge.cpu().numpy()
+        oe = ostep.edge_logits(z, tok, tree)
+        assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
