@@ -247,26 +247,33 @@ __global__ __launch_bounds__(VBig::NT) void verify_dma_big(const bf16_t* __restr
     tile_epilogue<MB, NB, VBig::NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
-// The most node rows (from kWideRows on): 256 x 256 tiles of dma_gemm_wide on 8 waves (4 x 2,
-// each 64 x 128), 64-dim chunks in a 2-stage ring; the epilogue runs twice, once per half of
-// 128 columns (the result tile of one half fills the LDS), partials per 128 columns.
-// grid (ceil(M/256), ceil(V/256)).
+// The most node rows: 256-row tiles of dma_gemm_wide on 8 waves (4 x 2), 64-dim chunks in a
+// 2-stage ring, NB = 256 weight rows (each wave 64 x 128; from kWideRows node rows on) or
+// NB = 192 (each wave 64 x 96; from kWide192Rows on: three 256-row blocks make 501
+// workgroups, two rounds of the CUs, where 256 x 256 tiles would make 1.5).  The
+// epilogue runs once per PW columns (the result tile of all NB columns does not fit the
+// LDS), partials per PW columns.  grid (ceil(M/256), ceil(V/NB)).
 #ifndef MDT_VWIDE_MIN_ROWS
 #define MDT_VWIDE_MIN_ROWS 1024
 #endif
+#ifndef MDT_VWIDE192_MIN_ROWS
+#define MDT_VWIDE192_MIN_ROWS 512
+#endif
 constexpr int kWideRows = MDT_VWIDE_MIN_ROWS;
-using VWide = DmaGemm<256, 256, 4, 2, 64, 2>;
+constexpr int kWide192Rows = MDT_VWIDE192_MIN_ROWS;
 
-__global__ __launch_bounds__(VWide::NT) void verify_dma_wide(const bf16_t* __restrict__ x,
-                                                             const bf16_t* __restrict__ W, int M, int d, int V,
-                                                             float tau, int nblk_n, Part* __restrict__ part,
-                                                             float* __restrict__ logits_opt,
-                                                             const int32_t* __restrict__ parent,
-                                                             const int32_t* __restrict__ tokens, int T,
-                                                             float* __restrict__ edge) {
-    constexpr int MB = 256, NB = 256, NH = 128, kZ = NH + 1;
+template <int NB, int PW>
+__global__ __launch_bounds__(512) void verify_dma_wide(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+                                                       int M, int d, int V, float tau, int nblk_n,
+                                                       Part* __restrict__ part, float* __restrict__ logits_opt,
+                                                       const int32_t* __restrict__ parent,
+                                                       const int32_t* __restrict__ tokens, int T,
+                                                       float* __restrict__ edge) {
+    using G = DmaGemm<256, NB, 4, 2, 64, 2>;
+    static_assert(G::NT == 512 && NB % PW == 0 && PW % 16 == 0, "tile shape");
+    constexpr int MB = 256, kZ = PW + 1, NW = NB / 2;  // NW: weight rows per wave column
     constexpr int kEpi = MB * kZ * 4;
-    constexpr int kLds = VWide::kRingBytes > kEpi ? VWide::kRingBytes : kEpi;
+    constexpr int kLds = G::kRingBytes > kEpi ? G::kRingBytes : kEpi;
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
     int mb, nb;  // the row blocks of one weight block together, on one XCD
     xcd_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, mb, nb);
@@ -275,22 +282,24 @@ __global__ __launch_bounds__(VWide::NT) void verify_dma_wide(const bf16_t* __res
     const int g = lane >> 4, c16 = lane & 15;
     const int wm = wave / 2, wn = wave % 2;
     const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
-    float* zt = (float*)smem;  // [MB][NH + 1], reuses the ring
+    float* zt = (float*)smem;  // [MB][PW + 1], reuses the ring
     dma_gemm_wide<MB, NB, 4, 2, 64, 2, MDT_VBIG_AUX>(
-        x, W, M, d, V, m0, n0, smem, [&](const f32x4 (&acc)[VWide::NTW][VWide::MTW]) {
-            for (int half = 0; half < 2; ++half) {
-                if (n0 + NH * half >= V) break;  // uniform: a half past the vocabulary has no partial
-                if (wn == half)
+        x, W, M, d, V, m0, n0, smem, [&](const f32x4 (&acc)[G::NTW][G::MTW]) {
+            for (int pass = 0; pass < NB / PW; ++pass) {
+                if (n0 + PW * pass >= V) break;  // uniform: columns past the vocabulary have no partial
 #pragma unroll
-                    for (int nt = 0; nt < VWide::NTW; ++nt)
+                for (int nt = 0; nt < G::NTW; ++nt) {
+                    const int col = NW * wn + 16 * nt - PW * pass;  // this fragment's first column in the pass
+                    if (col >= 0 && col < PW)
 #pragma unroll
-                        for (int mt = 0; mt < VWide::MTW; ++mt)
+                        for (int mt = 0; mt < G::MTW; ++mt)
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                zt[(64 * wm + 16 * mt + 4 * g + e) * kZ + 16 * nt + c16] = acc[nt][mt][e];
+                                zt[(64 * wm + 16 * mt + 4 * g + e) * kZ + col + c16] = acc[nt][mt][e];
+                }
                 __syncthreads();
-                tile_epilogue<MB, NH, VWide::NT>(zt, m0, n0 + NH * half, M, V, tau, nblk_n, part, logits_opt,
-                                                 parent, tokens, T, edge, pre);
+                tile_epilogue<MB, PW, G::NT>(zt, m0, n0 + PW * pass, M, V, tau, nblk_n, part, logits_opt, parent,
+                                             tokens, T, edge, pre);
                 __syncthreads();
             }
         });
@@ -416,13 +425,22 @@ mdt_status mdt_verify_tiles(hipStream_t s, mdt_dtype dt, int B, int T, int d, in
 #else
     const bool dma = false;
 #endif
-    const int nb_cols = big || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;  // columns per partial
+    const bool wide = big && d % 64 == 0 && M >= kWideRows;
+    const bool wide192 = big && d % 64 == 0 && !wide && M >= kWide192Rows;
+    // columns per partial
+    const int nb_cols = wide192 ? 64 : big || dma ? 128 : dt == MDT_BF16 ? MDT_VERIFY_NB : kNB;
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
-    if (big && M >= kWideRows && d % 64 == 0) {
-        MDT_LAUNCH("verify_mfma", verify_dma_wide, dim3((M + 255) / 256, (V + 255) / 256), dim3(VWide::NT), 0, s,
-                   (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,
-                   tree_tokens, T, edge_logit);
+    if (wide) {
+        auto kern = verify_dma_wide<256, 128>;
+        MDT_LAUNCH("verify_mfma", kern, dim3((M + 255) / 256, (V + 255) / 256), dim3(512), 0, s, (const bf16_t*)x,
+                   (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
+                   edge_logit);
+    } else if (wide192) {
+        auto kern = verify_dma_wide<192, 64>;
+        MDT_LAUNCH("verify_mfma", kern, dim3((M + 255) / 256, (V + 191) / 192), dim3(512), 0, s, (const bf16_t*)x,
+                   (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
+                   edge_logit);
     } else if (big && d % MDT_VBIG_KC == 0) {
         MDT_LAUNCH("verify_mfma", verify_dma_big, dim3((M + kBigMB - 1) / kBigMB, nblk_n), dim3(VBig::NT), 0, s,
                    (const bf16_t*)x, (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent,

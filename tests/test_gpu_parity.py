@@ -348,14 +348,14 @@ def test_verify_small_rows_ragged(T, d, V):
         assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
 
 
-@pytest.mark.parametrize("B,T,d,V", [(16, 42, 256, 5003), (4, 256, 128, 2000), (4, 256, 192, 1900),
+@pytest.mark.parametrize("B,T,d,V", [(16, 42, 256, 5003), (4, 160, 128, 1000), (4, 256, 128, 2000), (4, 256, 192, 1900),
                                      (5, 220, 128, 777), (8, 160, 64, 32000)])
 def test_verify_many_rows_ragged(B, T, d, V):
-    """256 and more node rows (batches, large trees): the 256 x 128 tile (672 rows) and the
-    256 x 256 tile (1024 and more rows), with vocabularies whose last tile is partial or whose
-    last tile's second half lies past the vocabulary (1900), a row count that leaves a partial
-    last row block (1100), and a single 64-dim chunk.  Row statistics and edge logits against
-    the oracle's definitions, per row."""
+    """512 and more node rows (batches, large trees): the 256 x 192 tile (640 and 672 rows,
+    partials per 64 columns) and the 256 x 256 tile (1024 and more rows), with vocabularies
+    whose last tile is partial or ends within its first pass (1900, 5003), a row count that
+    leaves a partial last row block (1100), and a single 64-dim chunk.  Row statistics and
+    edge logits against the oracle's definitions, per row."""
     import medusa_tree_verification_heads_amd as mdt
     from oracle import step as ostep
     from oracle import tree as otree
