@@ -263,9 +263,11 @@ struct AttnArgs {
 // before each tile's first fragment read), which serialises the ring.  The transpose reads
 // are issued as inline assembly for the same reason (the compiler's own form of that read
 // always waits), with an explicit lgkmcnt wait that the MFMAs depend on.
-#ifndef MDT_ATTN_AUX
-#define MDT_ATTN_AUX 2  // cache policy of the K and V loads: non-temporal (read once)
-#endif
+// Cache policy of the K and V loads: non-temporal (streamed, read once) when the caches of
+// the call hold more than the last-level cache (256 MiB), the default policy otherwise (a
+// smaller cache stays resident from one decoding step to the next).
+constexpr long kStreamedKvBytes = 256l << 20;
+constexpr int kAuxStreamed = 2, kAuxDefault = 0;
 #ifndef MDT_ATTN_S4
 #define MDT_ATTN_S4 2
 #endif
@@ -640,7 +642,7 @@ struct LoadSlot {
 // One (sequence, head, key range) per workgroup, or the tree of one (sequence, head).
 // Grid (H, B, nsplit + 1), the z index outermost: the key ranges in order (the ranges that
 // end past a short prefix exit at once), then the tree.
-template <int NWB, bool PAGED, int QT, int S>
+template <int NWB, bool PAGED, int QT, int S, int AUX>
 __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  // two waves per SIMD
     constexpr int NT = 64 * NWB;
     using LS = LoadSlot<NWB>;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
         for (int j = 0; j < kIPW; ++j) {
             if (j < j0 || j >= j1) continue;
             __builtin_amdgcn_global_load_lds((const void*)src[j], (lds_void_t*)(kst + LS::lds_offset(j)), 16, 0,
-                                             MDT_ATTN_AUX);
+                                             AUX);
         }
     };
     // tiles 0 .. S - 2 into stages 0 .. S - 2
@@ -952,9 +954,16 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
     // up to 8 query tiles: one per wave (4 or 8 waves); up to 16: two per wave on 8 waves
     const int threads = 64 * (p.nwb == 16 ? 8 : p.nwb);
     constexpr int S4 = MDT_ATTN_S4, S8 = MDT_ATTN_S8;
-    auto kern = p.nwb == 4 ? (paged ? attn_stream<4, true, 1, S4> : attn_stream<4, false, 1, S4>)
-              : p.nwb == 8 ? (paged ? attn_stream<8, true, 1, S8> : attn_stream<8, false, 1, S8>)
-                           : (paged ? attn_stream<8, true, 2, S8> : attn_stream<8, false, 2, S8>);
+    const bool streamed = (long)B * cache->capacity * H * kDh * 2 * (long)sizeof(bf16_t) > kStreamedKvBytes;
+    auto pick = [&](auto k_def, auto k_nt) { return streamed ? k_nt : k_def; };
+    auto kern = p.nwb == 4
+                    ? (paged ? pick(attn_stream<4, true, 1, S4, kAuxDefault>, attn_stream<4, true, 1, S4, kAuxStreamed>)
+                             : pick(attn_stream<4, false, 1, S4, kAuxDefault>, attn_stream<4, false, 1, S4, kAuxStreamed>))
+              : p.nwb == 8
+                    ? (paged ? pick(attn_stream<8, true, 1, S8, kAuxDefault>, attn_stream<8, true, 1, S8, kAuxStreamed>)
+                             : pick(attn_stream<8, false, 1, S8, kAuxDefault>, attn_stream<8, false, 1, S8, kAuxStreamed>))
+                    : (paged ? pick(attn_stream<8, true, 2, S8, kAuxDefault>, attn_stream<8, true, 2, S8, kAuxStreamed>)
+                             : pick(attn_stream<8, false, 2, S8, kAuxDefault>, attn_stream<8, false, 2, S8, kAuxStreamed>));
     MDT_LAUNCH("attn_stream", kern, dim3(H, B, p.nparts), dim3(threads), 0, s, A);
     st = mdt_launched("attn_stream");
     if (st != MDT_OK) return st;
