@@ -222,7 +222,7 @@ struct AttnArgs {
     const int32_t* depth;
     const uint64_t* anc;
     bf16_t* k_rot;
-    float* part_o;
+    bf16_t* part_o;            // per partial state: O / l, bf16 (normalised: its scale is l's)
     float* part_ml;
     double theta;
     int T, Tpad, H, W, nsplit, tiles_per_split, max_depth;
@@ -362,7 +362,9 @@ __device__ __forceinline__ void start_queries(const AttnArgs& A, const u32x4 (&r
     }
 }
 
-// Partial state of the wave's queries into partial slot `slot` (rows of Tpad per slot).
+// Partial state of the wave's queries into partial slot `slot` (rows of Tpad per slot): (m, l)
+// in fp32 and the normalised output O / l in bf16 (a convex combination of value rows, so
+// bf16 keeps its relative error at 2^-9 whatever the scale; it halves the partials' traffic).
 template <int QT>
 __device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, const QueryState<QT>& st) {
     const int g = (threadIdx.x & 63) >> 4;
@@ -371,11 +373,15 @@ __device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, cons
         const int qi = query_of(QT, t);
         if (qi < A.Tpad) {
             const long base = slot * A.Tpad + qi;
-            float* po = A.part_o + base * kDh;
+            bf16_t* po = A.part_o + base * kDh;
+            const float inv_l = st.l_run[t] > 0.f ? 1.f / st.l_run[t] : 0.f;
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) po[db * 16 + 4 * g + e] = st.oacc[t][db][e];
+            for (int db = 0; db < 8; ++db) {
+                u32x2 w;
+                w[0] = pack_bf16(st.oacc[t][db][0] * inv_l, st.oacc[t][db][1] * inv_l);
+                w[1] = pack_bf16(st.oacc[t][db][2] * inv_l, st.oacc[t][db][3] * inv_l);
+                *(u32x2*)(po + db * 16 + 4 * g) = w;
+            }
             if (g == 0) {
                 A.part_ml[base * 2 + 0] = st.m_run[t];
                 A.part_ml[base * 2 + 1] = st.l_run[t];
@@ -798,7 +804,7 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
 
 // Merge the partial states of every (sequence, head, node): nparts consecutive slots per
 // (sequence, head).  grid (T, H, B), block 64.
-__device__ __forceinline__ void merge_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+__device__ __forceinline__ void merge_partials(const bf16_t* __restrict__ part_o, const float* __restrict__ part_ml,
                                                int Tpad, int i, long s0, int n, long tree_slot, float& M,
                                                float& den, float& na, float& nb) {
     const int lane = threadIdx.x;
@@ -816,8 +822,8 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
             const long pidx = slot * Tpad + i;
             ms[u] = part_ml[pidx * 2];
             ls[u] = part_ml[pidx * 2 + 1];
-            oa[u] = part_o[pidx * kDh + lane];
-            ob[u] = part_o[pidx * kDh + lane + 64];
+            oa[u] = bf16_to_f32(part_o[pidx * kDh + lane]);
+            ob[u] = bf16_to_f32(part_o[pidx * kDh + lane + 64]);
         }
         float bm = M;
 #pragma unroll
@@ -831,8 +837,8 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (u0 + u >= total || ms[u] == -INFINITY) continue;
-            const float wgt = exp2f(ms[u] - bm);
-            den += ls[u] * wgt;
+            const float wgt = exp2f(ms[u] - bm) * ls[u];  // the partial's O is o * l
+            den += wgt;
             na += oa[u] * wgt;
             nb += ob[u] * wgt;
         }
@@ -840,7 +846,7 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
     }
 }
 
-__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+__global__ __launch_bounds__(64) void attn_combine(const bf16_t* __restrict__ part_o, const float* __restrict__ part_ml,
                                                    int T, int Tpad, int H, int nparts, bf16_t* __restrict__ out) {
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
@@ -882,7 +888,7 @@ Plan plan(int B, int T, int H, int capacity, bool paged) {
     p.nsplit = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
     p.nparts = p.nsplit + 1;  // the key ranges, then the tree
     const size_t slots = (size_t)B * H * p.nparts;
-    p.po_bytes = (slots * p.Tpad * kDh * sizeof(float) + 255) & ~(size_t)255;
+    p.po_bytes = (slots * p.Tpad * kDh * sizeof(bf16_t) + 255) & ~(size_t)255;
     p.pml_bytes = slots * p.Tpad * 2 * sizeof(float);
     return p;
 }
@@ -947,7 +953,7 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
         for (page_shift = 0; (1 << page_shift) < cache->page_size; ++page_shift) {
         }
     AttnArgs A{kv, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix_len, tree->depth, tree->anc,
-               (bf16_t*)k_rot, (float*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
+               (bf16_t*)k_rot, (bf16_t*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
                tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.nparts, {}};
     for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
     const bool paged = cache->layout == MDT_KV_PAGED;
