@@ -228,6 +228,7 @@ struct AttnArgs {
     int T, Tpad, H, W, nsplit, tiles_per_split, max_depth;
     int page_shift;            // log2 of a paged cache's page size, -1 if not a power of two
     int nparts;                // partial states per (sequence, head): nsplit ranges, then the tree
+    int tree_first;            // the tree workgroups take grid z = 0 (else z = nsplit)
     double inv_freq[kDh / 2];  // theta^(-2m/Dh), computed once on the host
 };
 
@@ -647,7 +648,10 @@ struct LoadSlot {
 
 // One (sequence, head, key range) per workgroup, or the tree of one (sequence, head).
 // Grid (H, B, nsplit + 1), the z index outermost: the key ranges in order (the ranges that
-// end past a short prefix exit at once), then the tree.
+// start past a short prefix exit at once) and the trees.  Small trees come last, where their
+// short workgroups fill the CUs that the last key ranges leave idle; trees of more than 128
+// nodes come first (a tree workgroup then does several masked tiles and would lengthen the
+// tail).
 template <int NWB, bool PAGED, int QT, int S, int AUX>
 __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  // two waves per SIMD
     constexpr int NT = 64 * NWB;
@@ -662,7 +666,9 @@ __global__ __launch_bounds__(64 * NWB, 8 / NWB) void attn_stream(AttnArgs A) {  
     float2* const cs = (float2*)(lds + kRingBytes);                  // cos/sin per (depth, pair)
     int* const pages = (int*)(lds + kRingBytes + kCsBytes);          // physical page of each page of the range
     // z < nsplit: prefix key range z; z = nsplit: the tree keys
-    const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
+    // grid z: the key ranges in order and the tree (first or last); z = nsplit below means the tree
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int z = A.tree_first ? ((int)blockIdx.z == 0 ? A.nsplit : (int)blockIdx.z - 1) : (int)blockIdx.z;
     const bool tree_split = z == A.nsplit;
     const int wave = threadIdx.x >> 6;
     const int H = A.H;
@@ -954,7 +960,8 @@ extern "C" mdt_status mdt_tree_attention(void* stream, mdt_dtype dt, int B, int 
         }
     AttnArgs A{kv, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, prefix_len, tree->depth, tree->anc,
                (bf16_t*)k_rot, (bf16_t*)ws, (float*)((char*)ws + p.po_bytes), theta, T, p.Tpad, H,
-               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.nparts, {}};
+               tree->anc_words, p.nsplit, p.tiles_per_split, tree->max_depth, page_shift, p.nparts,
+               p.Tpad > 128 ? 1 : 0, {}};
     for (int m = 0; m < kDh / 2; ++m) A.inv_freq[m] = std::pow(theta, -2.0 * (double)m / (double)kDh);
     const bool paged = cache->layout == MDT_KV_PAGED;
     // up to 8 query tiles: one per wave (4 or 8 waves); up to 16: two per wave on 8 waves
