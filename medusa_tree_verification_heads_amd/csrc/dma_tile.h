@@ -49,6 +49,20 @@ __device__ __forceinline__ void ring_barrier() {
 // MFMAs covers only the reads issued in the same iteration.
 __device__ __forceinline__ void lds_done() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8)); }
 
+// Wait until at most `later` chunks of I load instructions each, issued after the awaited
+// one, are outstanding (0 <= later <= L), then meet the workgroup at the barrier.
+template <int I, int L>
+__device__ __forceinline__ void chunk_landed(int later) {
+    if constexpr (L == 0) {
+        ring_barrier<0>();
+    } else {
+        if (later >= L)
+            ring_barrier<L * I>();
+        else
+            chunk_landed<I, L - 1>(later);
+    }
+}
+
 template <int KC, int NB, int CG, int KS, int S>
 struct DmaTile {
     static constexpr int NW = CG * KS;
@@ -327,31 +341,59 @@ __device__ __forceinline__ void dma_gemm_tile(const bf16_t* __restrict__ x, cons
 // tile moves a third fewer bytes through the L2 -> LDS path per MFMA than 256 x 128 (the x rows,
 // re-read by every weight block, are the larger share).  Per k-step a wave reads its MTW x
 // fragments into one of two register sets and refills each weight fragment register with
-// the next step's fragment right after that fragment's MFMAs ("rolling"), which keeps
-// MTW x NTW = 4 x 8 accumulator fragments and the operands of two steps within two waves
-// per SIMD.  The barrier sits before a chunk's last k-step, whose fragments are already in
-// registers; the next chunk's first fragments are read during that step.  KC / 32 must be
-// even (register sets alternate with the k-step's parity).  epi(acc) as for dma_gemm_tile.
+// the next step's fragment right after that fragment's MFMAs ("rolling"), which keeps the
+// accumulators and the operands of two steps within two waves per SIMD.  The barrier sits
+// before a chunk's last k-step, whose fragments are already in registers; the next chunk's
+// first fragments are read during that step.  KC / 32 must be even (register sets alternate
+// with the k-step's parity).  The x rows' load instructions need not divide among the waves
+// (224-row tiles: 28 instructions on 8 waves): instruction i goes to wave i mod NW.
+// epi(acc) as for dma_gemm_tile.
+template <int MB, int NB, int WM, int WN, int KC, int S>
+struct DmaGemmWide {
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = 64 * NW;
+    static constexpr int kPR = KC / 8;
+    static constexpr int kXBytes = MB * KC * 2;
+    static constexpr int kWBytes = NB * KC * 2;
+    static constexpr int kStage = kXBytes + kWBytes;
+    static constexpr int kRingBytes = S * kStage;
+    static constexpr int kNIX = MB * kPR / 64;               // x load instructions per chunk
+    static constexpr int kIXmax = (kNIX + NW - 1) / NW;      // per wave, at most
+    static constexpr int kIXlow = kNIX % NW;                 // waves below this index issue kIXmax
+    static constexpr int kIW = NB * kPR / 64 / NW;           // weight load instructions per wave
+    static constexpr int MTW = MB / WM / 16;
+    static constexpr int NTW = NB / WN / 16;
+    static constexpr int KSTEPS = KC / 32;
+    static_assert(KC % 64 == 0 && (kPR == 8 || kPR % 16 == 0), "chunk shape");
+    static_assert(MB * kPR % 64 == 0 && NB * kPR % (64 * NW) == 0, "whole load instructions");
+    static_assert(MB % (16 * WM) == 0 && NB % (16 * WN) == 0, "fragments divide among the waves");
+    static_assert(S >= 2 && (kIXmax + kIW) * (S - 1) < 64, "stages / vmcnt range");
+};
+
 template <int MB, int NB, int WM, int WN, int KC, int S, int AUX = 0, typename Epi>
 __device__ __forceinline__ void dma_gemm_wide(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M,
                                               int d, int V, int m0, int n0, char* smem, Epi&& epi) {
-    using P = DmaGemm<MB, NB, WM, WN, KC, S>;
+    using P = DmaGemmWide<MB, NB, WM, WN, KC, S>;
     constexpr int kPR = P::kPR, MTW = P::MTW, NTW = P::NTW, KSTEPS = P::KSTEPS;
     static_assert(KSTEPS % 2 == 0, "k-steps per chunk must be even");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int wm = wave / WN, wn = wave % WN;
     const int nch = d / KC;
+    // this wave's load instructions per chunk (the first kIXlow waves issue one x load more)
+    const bool xmore = P::kIXlow == 0 || wave < P::kIXlow;
 
     auto issue = [&](int c) {
         char* st = smem + (c % S) * P::kStage;
 #pragma unroll
-        for (int j = 0; j < P::kIX; ++j) {
-            const int i = wave * P::kIX + j;
-            const int q = 64 * i + lane;
-            const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
-            const bf16_t* src = x + (size_t)min(m0 + r, M - 1) * d + c * KC + 8 * p;
-            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, 0);
+        for (int j = 0; j < P::kIXmax; ++j) {
+            const int i = j * P::NW + wave;
+            if (i < P::kNIX) {
+                const int q = 64 * i + lane;
+                const int r = q / kPR, p = dma_swz<kPR>(q % kPR, r);
+                const bf16_t* src = x + (size_t)min(m0 + r, M - 1) * d + c * KC + 8 * p;
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + 1024 * i), 16, 0, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < P::kIW; ++j) {
@@ -363,15 +405,13 @@ __device__ __forceinline__ void dma_gemm_wide(const bf16_t* __restrict__ x, cons
                                              AUX);
         }
     };
+    // wait until at most `later` chunks issued after the awaited one are outstanding
     auto landed = [&](int later) {
-        if (later >= 3)
-            ring_barrier<3 * P::kLoads>();
-        else if (later == 2)
-            ring_barrier<2 * P::kLoads>();
-        else if (later == 1)
-            ring_barrier<P::kLoads>();
+        constexpr int kHi = P::kIXmax + P::kIW, kLo = (P::kIXlow ? P::kIXmax - 1 : P::kIXmax) + P::kIW;
+        if (xmore)
+            chunk_landed<kHi, S - 1>(min(later, S - 1));
         else
-            ring_barrier<0>();
+            chunk_landed<kLo, S - 1>(min(later, S - 1));
     };
 
     f32x4 acc[NTW][MTW];
@@ -408,7 +448,7 @@ __device__ __forceinline__ void dma_gemm_wide(const bf16_t* __restrict__ x, cons
 #pragma unroll
     for (int c = 0; c < S; ++c)
         if (c < nch) issue(c);
-    landed(min(S - 1, nch - 1));
+    landed(nch - 1);
     read_a(0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) fb[nt] = read_b(0, 0, nt);

@@ -58,14 +58,18 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
                               const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens, int T,
                               float* __restrict__ edge, EdgePre pre) {
     constexpr int kZS = NB + 1;         // row stride of zt
-    constexpr int TPR = NT / MT;        // threads per row
+    // threads per row: the largest power of two with TPR * MT <= NT (with 224 rows on 512
+    // threads the last 64 threads only take part in the edge pass)
+    constexpr int TPR = NT / MT >= 16 ? 16 : NT / MT >= 8 ? 8 : NT / MT >= 4 ? 4 : NT / MT >= 2 ? 2 : 1;
     constexpr int CPT = NB / TPR;       // columns per thread
+    static_assert(NB % TPR == 0, "columns divide among a row's threads");
     const int t = threadIdx.x;
     const int r = t / TPR, q = t % TPR;
+    const bool has_row = r < MT;
     const int row = m0 + r;
-    const int ncol = min(NB, V - n0);
+    const int ncol = has_row ? min(NB, V - n0) : 0;
     Part p{-INFINITY, INT_MAX, 0.f, 0.f};
-    const float* z = zt + r * kZS;
+    const float* z = zt + min(r, MT - 1) * kZS;
     for (int c = q * CPT; c < q * CPT + CPT; ++c) {
         if (c >= ncol) break;
         if (better(z[c], n0 + c, p.m, p.a)) {
@@ -84,8 +88,8 @@ __device__ void tile_epilogue(const float* zt, int m0, int n0, int M, int V, flo
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) p = part_merge(p, shfl_xor_part(p, off), tau > 0.f ? 1.f / tau : 0.f);
-    if (q == 0 && row < M) part[(long)row * nblk_n + n0 / NB] = p;
-    if (logits_opt && row < M)
+    if (has_row && q == 0 && row < M) part[(long)row * nblk_n + n0 / NB] = p;
+    if (logits_opt && has_row && row < M)
         for (int c = q * CPT; c < q * CPT + CPT && c < ncol; ++c) logits_opt[(long)row * V + n0 + c] = z[c];
     // edges: node c of sequence b reads row b*T + parent(c) at column token(b, c)
     const int first_b = m0 / T, last_b = min(M - 1, m0 + MT - 1) / T;
@@ -247,12 +251,13 @@ __global__ __launch_bounds__(VBig::NT) void verify_dma_big(const bf16_t* __restr
     tile_epilogue<MB, NB, VBig::NT>(zt, m0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
 
-// The most node rows: 256-row tiles of dma_gemm_wide on 8 waves (4 x 2), 64-dim chunks in a
-// 2-stage ring, NB = 256 weight rows (each wave 64 x 128; from kWideRows node rows on) or
-// NB = 192 (each wave 64 x 96; from kWide192Rows on: three 256-row blocks make 501
-// workgroups, two rounds of the CUs, where 256 x 256 tiles would make 1.5).  The
-// epilogue runs once per PW columns (the result tile of all NB columns does not fit the
-// LDS), partials per PW columns.  grid (ceil(M/256), ceil(V/NB)).
+// The most node rows: tiles of dma_gemm_wide on 8 waves, 64-dim chunks in a 2-stage ring:
+// 256 x 256 (4 x 2 waves of 64 x 128) from kWideRows node rows on; from kWide192Rows on,
+// NB = 192 weight rows (501 workgroups for three row blocks, two rounds of the CUs, where
+// 256-column tiles would make 1.5) with 256 x rows (4 x 2 waves of 64 x 96) or, when that
+// takes as many row blocks and pads fewer rows, 224 (2 x 4 waves of 112 x 48; 672 rows are
+// three blocks exactly).  The epilogue runs once per PW columns (the result tile of all NB
+// columns does not fit the LDS), partials per PW columns.  grid (ceil(M/MB), ceil(V/NB)).
 #ifndef MDT_VWIDE_MIN_ROWS
 #define MDT_VWIDE_MIN_ROWS 1024
 #endif
@@ -262,16 +267,16 @@ __global__ __launch_bounds__(VBig::NT) void verify_dma_big(const bf16_t* __restr
 constexpr int kWideRows = MDT_VWIDE_MIN_ROWS;
 constexpr int kWide192Rows = MDT_VWIDE192_MIN_ROWS;
 
-template <int NB, int PW>
+template <int MB, int NB, int WM, int WN, int PW>
 __global__ __launch_bounds__(512) void verify_dma_wide(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
                                                        int M, int d, int V, float tau, int nblk_n,
                                                        Part* __restrict__ part, float* __restrict__ logits_opt,
                                                        const int32_t* __restrict__ parent,
                                                        const int32_t* __restrict__ tokens, int T,
                                                        float* __restrict__ edge) {
-    using G = DmaGemm<256, NB, 4, 2, 64, 2>;
+    using G = DmaGemmWide<MB, NB, WM, WN, 64, 2>;
     static_assert(G::NT == 512 && NB % PW == 0 && PW % 16 == 0, "tile shape");
-    constexpr int MB = 256, kZ = PW + 1, NW = NB / 2;  // NW: weight rows per wave column
+    constexpr int kZ = PW + 1, RW = MB / WM, CW = NB / WN;  // rows / columns per wave
     constexpr int kEpi = MB * kZ * 4;
     constexpr int kLds = G::kRingBytes > kEpi ? G::kRingBytes : kEpi;
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
@@ -280,22 +285,22 @@ __global__ __launch_bounds__(512) void verify_dma_wide(const bf16_t* __restrict_
     const int m0 = mb * MB, n0 = nb * NB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN, wn = wave % WN;
     const EdgePre pre = edge_preload<MB>(m0, M, parent, tokens, T);
     float* zt = (float*)smem;  // [MB][PW + 1], reuses the ring
-    dma_gemm_wide<MB, NB, 4, 2, 64, 2, MDT_VBIG_AUX>(
+    dma_gemm_wide<MB, NB, WM, WN, 64, 2, MDT_VBIG_AUX>(
         x, W, M, d, V, m0, n0, smem, [&](const f32x4 (&acc)[G::NTW][G::MTW]) {
             for (int pass = 0; pass < NB / PW; ++pass) {
                 if (n0 + PW * pass >= V) break;  // uniform: columns past the vocabulary have no partial
 #pragma unroll
                 for (int nt = 0; nt < G::NTW; ++nt) {
-                    const int col = NW * wn + 16 * nt - PW * pass;  // this fragment's first column in the pass
+                    const int col = CW * wn + 16 * nt - PW * pass;  // this fragment's first column in the pass
                     if (col >= 0 && col < PW)
 #pragma unroll
                         for (int mt = 0; mt < G::MTW; ++mt)
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                zt[(64 * wm + 16 * mt + 4 * g + e) * kZ + col + c16] = acc[nt][mt][e];
+                                zt[(RW * wm + 16 * mt + 4 * g + e) * kZ + col + c16] = acc[nt][mt][e];
                 }
                 __syncthreads();
                 tile_epilogue<MB, PW, G::NT>(zt, m0, n0 + PW * pass, M, V, tau, nblk_n, part, logits_opt, parent,
@@ -432,12 +437,17 @@ mdt_status mdt_verify_tiles(hipStream_t s, mdt_dtype dt, int B, int T, int d, in
     const int nblk_n = (V + nb_cols - 1) / nb_cols;
     Part* part = (Part*)ws;
     if (wide) {
-        auto kern = verify_dma_wide<256, 128>;
+        auto kern = verify_dma_wide<256, 256, 4, 2, 128>;
         MDT_LAUNCH("verify_mfma", kern, dim3((M + 255) / 256, (V + 255) / 256), dim3(512), 0, s, (const bf16_t*)x,
                    (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
                    edge_logit);
+    } else if (wide192 && (M + 223) / 224 == (M + 255) / 256) {
+        auto kern = verify_dma_wide<224, 192, 2, 4, 64>;
+        MDT_LAUNCH("verify_mfma", kern, dim3((M + 223) / 224, (V + 191) / 192), dim3(512), 0, s, (const bf16_t*)x,
+                   (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
+                   edge_logit);
     } else if (wide192) {
-        auto kern = verify_dma_wide<192, 64>;
+        auto kern = verify_dma_wide<256, 192, 4, 2, 64>;
         MDT_LAUNCH("verify_mfma", kern, dim3((M + 255) / 256, (V + 191) / 192), dim3(512), 0, s, (const bf16_t*)x,
                    (const bf16_t*)Wlm, M, d, V, temperature, nblk_n, part, logits_opt, tree->parent, tree_tokens, T,
                    edge_logit);

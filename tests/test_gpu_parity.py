@@ -348,11 +348,12 @@ def test_verify_small_rows_ragged(T, d, V):
         assert np.all(e[:, 0] == 0) and np.all(np.abs(e - oe) <= REL_TOL * scale.max())
 
 
-@pytest.mark.parametrize("B,T,d,V", [(16, 42, 256, 5003), (4, 160, 128, 1000), (4, 256, 128, 2000), (4, 256, 192, 1900),
+@pytest.mark.parametrize("B,T,d,V", [(16, 42, 256, 5003), (4, 160, 128, 1000), (6, 120, 128, 3000), (4, 256, 128, 2000), (4, 256, 192, 1900),
                                      (5, 220, 128, 777), (8, 160, 64, 32000)])
 def test_verify_many_rows_ragged(B, T, d, V):
-    """512 and more node rows (batches, large trees): the 256 x 192 tile (640 and 672 rows,
-    partials per 64 columns) and the 256 x 256 tile (1024 and more rows), with vocabularies
+    """512 and more node rows (batches, large trees): 224 x 192 tiles (640 and 672 rows: three
+    row blocks, the same as 256-row blocks, fewer padded rows), the 256 x 192 tile (720 rows),
+    both with partials per 64 columns, and the 256 x 256 tile (1024 and more rows), with vocabularies
     whose last tile is partial or ends within its first pass (1900, 5003), a row count that
     leaves a partial last row block (1100), and a single 64-dim chunk.  Row statistics and
     edge logits against the oracle's definitions, per row."""
