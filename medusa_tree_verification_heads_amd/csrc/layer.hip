@@ -119,7 +119,9 @@ __device__ __forceinline__ void linear_epilogue(const LinArgs& a, const float* z
 
 // One 64 x NB tile of a product on dma_tile: both operands staged by direct global-to-LDS
 // loads through an S-stage ring of 128-dim chunks, CG column groups x KS k-groups of waves
-// (chosen per tile width so that the loads divide evenly among the waves).
+// (chosen per tile width so that the loads divide evenly among the waves).  Column block b
+// walks its chunks from chunk b on, so that neighbouring workgroups read different parts of
+// their weight rows at any one time.
 // grid (ceil(N/NB), ceil(M/64), nsplit); blockIdx.z > 0 only for kPartial.
 template <int EPI, int NB, int CG, int KS, int S>
 __global__ __launch_bounds__(64 * CG * KS) void linear_dma(LinArgs a) {
@@ -147,7 +149,8 @@ __global__ __launch_bounds__(64 * CG * KS) void linear_dma(LinArgs a) {
                                                 for (int e = 0; e < 4; ++e)
                                                     zt[(mt * 16 + 4 * g + e) * kZs + cg * (NB / CG) + 16 * nt +
                                                        c16] = acc[nt][mt][e];
-                                    });
+                                    },
+                                    blockIdx.x);
     __syncthreads();
     linear_epilogue<EPI, NB, NTH>(a, zt, m0, n0, s);
 }
