@@ -142,7 +142,9 @@ __global__ __launch_bounds__(4 * NB) void verify_mfma(const bf16_t* __restrict__
 
 // At most 64 node rows (one tree of a single sequence, the batch-1 shapes): dma_tile, the
 // 64 x NB tile fed by direct global-to-LDS loads through an S-stage ring, then the
-// statistics epilogue over NB columns on all threads.  grid ceil(V / NB), block 64 CG KS.
+// statistics epilogue over NB columns on all threads.  Column block b walks the chunks from
+// chunk b on (spreading the weight reads over the memory channels).  grid ceil(V / NB),
+// block 64 CG KS.
 #ifndef MDT_VDMA_KC
 #define MDT_VDMA_KC 128
 #endif
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(VDma::NT) void verify_dma(const bf16_t* __restrict_
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         zt[(mt * 16 + 4 * g + e) * (NB + 1) + cg * (NB / CG) + 16 * nt + c16] = acc[nt][mt][e];
-        });
+        }, blockIdx.x);
     __syncthreads();
     tile_epilogue<kMB, NB, VDma::NT>(zt, 0, n0, M, V, tau, nblk_n, part, logits_opt, parent, tokens, T, edge, pre);
 }
