@@ -155,61 +155,122 @@ __global__ __launch_bounds__(64 * CG * KS) void linear_dma(LinArgs a) {
     linear_epilogue<EPI, NB, NTH>(a, zt, m0, n0, s);
 }
 
-// One workgroup of kNormThreads per row (a row of d = 4096 is 512 16-byte pieces: one
-// per thread, so every slice load of the row is in flight at once).  With nparts > 0
-// the row first becomes x + part[0] + ... + part[nparts-1] (fp32, in that order),
-// rounded once to bf16 and written back; the norm is taken of the stored row.
+// One workgroup of kNormThreads per row.  With nparts > 0 the row first becomes
+// x + part[0] + ... + part[nparts-1] (fp32, in that order), rounded once to bf16 and
+// written back; the norm is taken of the stored row.
+//
+// A row of at most NP * kNormThreads 16-byte pieces (d = 4096: 512 pieces, one per thread)
+// is held in registers: every load of the row (x, the first kPartsHeld partial slices and
+// g) is issued before the first is used, so the call costs about one memory latency, and
+// the stored row is not read back.  NP = 0 walks longer rows piece by piece.
 constexpr int kNormThreads = 512;
+constexpr int kPartsHeld = 8;
 
+template <int NP>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(uint4* __restrict__ x, const float4* __restrict__ part,
                                                                int nparts, long part_stride,
                                                                const uint4* __restrict__ g, int nvec, float inv_d,
                                                                float eps, uint4* __restrict__ y) {
     __shared__ float red[kNormThreads / 64];
     uint4* xr = x + (size_t)blockIdx.x * nvec;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < nvec; i += kNormThreads) {
-        uint4 q = xr[i];
-        if (nparts > 0) {
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[2 * j] = lo16(w[j]), v[2 * j + 1] = hi16(w[j]);
-            const float4* pr = part + ((size_t)blockIdx.x * nvec + i) * 2;
-            float4 sa = pr[0], sb = pr[1];
-            for (int p = 1; p < nparts; ++p) {
-                const float4 ta = pr[p * part_stride], tb = pr[p * part_stride + 1];
-                sa.x += ta.x, sa.y += ta.y, sa.z += ta.z, sa.w += ta.w;
-                sb.x += tb.x, sb.y += tb.y, sb.z += tb.z, sb.w += tb.w;
-            }
-            q.x = pack2(v[0] + sa.x, v[1] + sa.y);
-            q.y = pack2(v[2] + sa.z, v[3] + sa.w);
-            q.z = pack2(v[4] + sb.x, v[5] + sb.y);
-            q.w = pack2(v[6] + sb.z, v[7] + sb.w);
-            xr[i] = q;
-        }
+    uint4* yr = y + (size_t)blockIdx.x * nvec;
+    const float4* prow = part + (size_t)blockIdx.x * nvec * 2;
+    // x (+ the partial slices) of one piece, rounded to bf16
+    auto add_parts = [&](uint4 q, float4 sa, float4 sb) {
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[2 * j] = lo16(w[j]), v[2 * j + 1] = hi16(w[j]);
+        q.x = pack2(v[0] + sa.x, v[1] + sa.y);
+        q.y = pack2(v[2] + sa.z, v[3] + sa.w);
+        q.z = pack2(v[4] + sb.x, v[5] + sb.y);
+        q.w = pack2(v[6] + sb.z, v[7] + sb.w);
+        return q;
+    };
+    auto add4 = [](float4& s, const float4& t) { s.x += t.x, s.y += t.y, s.z += t.z, s.w += t.w; };
+    auto sumsq = [](const uint4& q) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float a = lo16(w[j]), b = hi16(w[j]);
             ss += a * a + b * b;
         }
-    }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
-    const float r = rsqrtf(tot * inv_d + eps);
-    uint4* yr = y + (size_t)blockIdx.x * nvec;
-    for (int i = threadIdx.x; i < nvec; i += kNormThreads) {
-        const uint4 q = xr[i], gg = g[i];
+        return ss;
+    };
+    auto normed = [](const uint4& q, const uint4& gg, float r) {
         const uint32_t w[4] = {q.x, q.y, q.z, q.w}, gw[4] = {gg.x, gg.y, gg.z, gg.w};
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = pack2(lo16(w[j]) * r * lo16(gw[j]), hi16(w[j]) * r * hi16(gw[j]));
-        yr[i] = make_uint4(o[0], o[1], o[2], o[3]);
+        return make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    auto finish = [&](float ss) {
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+        return rsqrtf(tot * inv_d + eps);
+    };
+
+    if constexpr (NP > 0) {
+        uint4 q[NP], gg[NP];
+        float4 pa[kPartsHeld][NP], pb[kPartsHeld][NP];
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int i = min((int)threadIdx.x + j * kNormThreads, nvec - 1);
+            q[j] = xr[i];
+            gg[j] = g[i];
+        }
+#pragma unroll
+        for (int p = 0; p < kPartsHeld; ++p)
+            if (p < nparts)
+#pragma unroll
+                for (int j = 0; j < NP; ++j) {
+                    const float4* pr = prow + (size_t)min((int)threadIdx.x + j * kNormThreads, nvec - 1) * 2;
+                    pa[p][j] = pr[p * part_stride];
+                    pb[p][j] = pr[p * part_stride + 1];
+                }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int i = threadIdx.x + j * kNormThreads;
+            if (i >= nvec) continue;
+            if (nparts > 0) {
+                float4 sa = pa[0][j], sb = pb[0][j];
+#pragma unroll
+                for (int p = 1; p < kPartsHeld; ++p)
+                    if (p < nparts) add4(sa, pa[p][j]), add4(sb, pb[p][j]);
+                for (int p = kPartsHeld; p < nparts; ++p)
+                    add4(sa, prow[(size_t)i * 2 + p * part_stride]), add4(sb, prow[(size_t)i * 2 + p * part_stride + 1]);
+                q[j] = add_parts(q[j], sa, sb);
+                xr[i] = q[j];
+            }
+            ss += sumsq(q[j]);
+        }
+        const float r = finish(ss);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int i = threadIdx.x + j * kNormThreads;
+            if (i < nvec) yr[i] = normed(q[j], gg[j], r);
+        }
+    } else {
+        float ss = 0.f;
+        for (int i = threadIdx.x; i < nvec; i += kNormThreads) {
+            uint4 q = xr[i];
+            if (nparts > 0) {
+                const float4* pr = prow + (size_t)i * 2;
+                float4 sa = pr[0], sb = pr[1];
+                for (int p = 1; p < nparts; ++p) add4(sa, pr[p * part_stride]), add4(sb, pr[p * part_stride + 1]);
+                q = add_parts(q, sa, sb);
+                xr[i] = q;
+            }
+            ss += sumsq(q);
+        }
+        const float r = finish(ss);
+        for (int i = threadIdx.x; i < nvec; i += kNormThreads) yr[i] = normed(xr[i], g[i], r);
     }
 }
 
@@ -267,9 +328,16 @@ mdt_status launch_rmsnorm(void* stream, int M, int d, void* x, const float* part
     MDT_REQUIRE(x && g && y && (nparts == 0 || part), MDT_ERR_NULL, "a tensor pointer is NULL");
     MDT_REQUIRE(mdt_aligned16(x) && mdt_aligned16(g) && mdt_aligned16(y) && mdt_aligned16(part), MDT_ERR_ALIGN,
                 "tensor pointers must be 16-byte aligned");
-    MDT_LAUNCH("rmsnorm_kernel", rmsnorm_kernel, dim3(M), dim3(kNormThreads), 0, (hipStream_t)stream, (uint4*)x,
-               (const float4*)part, nparts, (long)M * d / 4, (const uint4*)g, d / 8, 1.f / (float)d, eps, (uint4*)y);
-    return mdt_launched("rmsnorm_kernel");
+    const int nvec = d / 8, np = (nvec + kNormThreads - 1) / kNormThreads;
+    auto go = [&](auto kern) {
+        MDT_LAUNCH("rmsnorm_kernel", kern, dim3(M), dim3(kNormThreads), 0, (hipStream_t)stream, (uint4*)x,
+                   (const float4*)part, nparts, (long)M * d / 4, (const uint4*)g, nvec, 1.f / (float)d, eps, (uint4*)y);
+        return mdt_launched("rmsnorm_kernel");
+    };
+    if (np == 1) return go(rmsnorm_kernel<1>);
+    if (np == 2) return go(rmsnorm_kernel<2>);
+    if (np <= 4) return go(rmsnorm_kernel<4>);
+    return go(rmsnorm_kernel<0>);
 }
 
 }  // namespace

@@ -95,7 +95,7 @@ def test_linear_plain_and_residual(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,nsplit", [(64, 512, 4096, 8), (37, 200, 1376, 2), (130, 96, 1024, 3),
-                                          (64, 4096, 11008, 8)])
+                                          (64, 4096, 11008, 8), (16, 6656, 1536, 12), (5, 12288, 512, 4)])
 def test_linear_split_and_add_rmsnorm(M, N, K, nsplit):
     """The slices' fp32 products add up to the product (each within the fp32 dot-product
     bound), and add_rmsnorm closes them into the residual and normalises the new row."""
@@ -160,7 +160,7 @@ def test_linear_swiglu(M, F, K):
     assert _bad(_bits(a), ref, bound) == 0
 
 
-@pytest.mark.parametrize("M,d", [(64, 512), (13, 4096), (1, 136)])
+@pytest.mark.parametrize("M,d", [(64, 512), (13, 4096), (1, 136), (5, 6656), (3, 12288), (2, 40968)])
 def test_rmsnorm_and_embed(M, d):
     import medusa_tree_verification_heads_amd as mdt
     rng = np.random.default_rng(M + d)
