@@ -1,6 +1,6 @@
-// A 64 x NB tile of x W^T for at most 64 x rows, with both operands staged in LDS by
-// direct global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land in LDS
-// without passing through registers).
+// A 16 MT x NB tile of x W^T for at most 16 MT x rows (MT = 4 unless stated: 64 rows),
+// with both operands staged in LDS by direct global-to-LDS loads (global_load_lds_dwordx4:
+// each lane's 16 bytes land in LDS without passing through registers).
 //
 // The inner dimension is walked in chunks of KC dims held in an S-stage ring: while the
 // waves multiply chunk c out of LDS, the loads of chunks c+1 .. c+S-1 are in flight, and
@@ -12,7 +12,7 @@
 // bytes), and the 16 rows of an MFMA fragment read fall into 16 distinct bank groups.
 //
 // Waves: CG column groups x KS inner-dimension groups.  Wave (cg, kh) multiplies x rows
-// 0..63 against weight rows cg NB/CG .. +NB/CG over the k-steps kh, kh + KS, ... of each
+// 0..16 MT - 1 against weight rows cg NB/CG .. +NB/CG over the k-steps kh, kh + KS, ... of each
 // chunk; the KS partial products are then summed through LDS in kh order, and epi(acc)
 // runs on the kh = 0 waves with acc[nt][mt] holding weight rows cg NB/CG + 16 nt + l%16 and
 // x rows 16 mt + 4 (l/16) + e (the 16x16 MFMA output layout).
@@ -69,31 +69,32 @@ __device__ __forceinline__ void chunk_landed(int later) {
     }
 }
 
-template <int KC, int NB, int CG, int KS, int S>
+template <int KC, int NB, int CG, int KS, int S, int MT = 4>
 struct DmaTile {
     static constexpr int NW = CG * KS;
     static constexpr int NT = 64 * NW;
+    static constexpr int MX = 16 * MT;                 // x rows
     static constexpr int kPR = KC / 8;                 // 16-byte pieces per row per chunk
     static constexpr int kWBytes = NB * KC * 2;
-    static constexpr int kXBytes = 64 * KC * 2;
+    static constexpr int kXBytes = MX * KC * 2;
     static constexpr int kStage = kWBytes + kXBytes;
     static constexpr int kIW = NB * kPR / 64 / NW;     // weight load instructions per wave per chunk
-    static constexpr int kIX = 64 * kPR / 64 / NW;     // x load instructions per wave per chunk
+    static constexpr int kIX = MX * kPR / 64 / NW;     // x load instructions per wave per chunk
     static constexpr int kLoads = kIW + kIX;
-    static constexpr int kRedBytes = (KS - 1) * (NB / 16) * 4 * 64 * 16;  // k-group partials
+    static constexpr int kRedBytes = (KS - 1) * (NB / 16) * MT * 64 * 16;  // k-group partials
     static constexpr int kRingBytes = S * kStage;
     static_assert(KC % 128 == 0, "a chunk row spans at least 16 pieces (the swizzle's period)");
     static_assert((KC / 32) % KS == 0, "k-steps divide among the k-groups");
     static_assert(NB % (16 * CG) == 0, "columns divide among the column groups");
-    static_assert(NB * kPR % (64 * NW) == 0 && 64 * kPR % (64 * NW) == 0, "loads divide among the waves");
+    static_assert(NB * kPR % (64 * NW) == 0 && MX * kPR % (64 * NW) == 0, "loads divide among the waves");
     static_assert(S >= 2 && S <= 4, "2 to 4 stages");
     static_assert(kLoads * (S - 2) < 64, "vmcnt range");
 };
 
-template <int KC, int NB, int CG, int KS, int S, int AUX = 0, typename Epi>
+template <int KC, int NB, int CG, int KS, int S, int AUX = 0, int MT = 4, typename Epi>
 __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int M, int d,
                                          int ld, int V, int n0, char* smem, Epi&& epi, int rot = 0) {
-    using P = DmaTile<KC, NB, CG, KS, S>;
+    using P = DmaTile<KC, NB, CG, KS, S, MT>;
     constexpr int kPR = P::kPR;
     constexpr int NTW = NB / CG / 16;   // weight fragments per wave
     constexpr int KSS = KC / 32 / KS;   // k-steps per wave per chunk
@@ -129,31 +130,53 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
         }
     };
 
-    f32x4 acc[NTW][4];
+    f32x4 acc[NTW][MT];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int c) {
         const char* st = smem + (c % S) * P::kStage;
         const bf16_t* ws = (const bf16_t*)st;
         const bf16_t* xs = (const bf16_t*)(st + P::kWBytes);
         const int nsteps = min(KC, d - chunk_of(c) * KC) / 32;
+        if (KSS >= 4 && nsteps == KC / 32) {
+            // a whole chunk with four or more k-steps per wave: every fragment read first,
+            // then the MFMAs (the guarded loop below waits for each step's reads in turn;
+            // with fewer steps per wave it measured as fast or faster)
+            u32x4 a[KSS][MT], b[KSS][NTW];
+#pragma unroll
+            for (int s2 = 0; s2 < KSS; ++s2) {
+                const int pp = (4 * (kh + KS * s2) + g) ^ c16;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) a[s2][mt] = *(const u32x4*)(xs + ((16 * mt + c16) * kPR + pp) * 8);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    b[s2][nt] = *(const u32x4*)(ws + ((cg * (NB / CG) + 16 * nt + c16) * kPR + pp) * 8);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < KSS; ++s2)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16(a[s2][mt], b[s2][nt], acc[nt][mt]);
+            return;
+        }
 #pragma unroll
         for (int s2 = 0; s2 < KSS; ++s2) {
             const int s = kh + KS * s2;
             if (s < nsteps) {
                 const int pp = (4 * s + g) ^ c16;  // rows of a fragment start at multiples of 16
-                u32x4 a[4], b[NTW];
+                u32x4 a[MT], b[NTW];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) a[mt] = *(const u32x4*)(xs + ((16 * mt + c16) * kPR + pp) * 8);
+                for (int mt = 0; mt < MT; ++mt) a[mt] = *(const u32x4*)(xs + ((16 * mt + c16) * kPR + pp) * 8);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
                     b[nt] = *(const u32x4*)(ws + ((cg * (NB / CG) + 16 * nt + c16) * kPR + pp) * 8);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mfma16(a[mt], b[nt], acc[nt][mt]);
+                    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = mfma16(a[mt], b[nt], acc[nt][mt]);
             }
         }
     };
@@ -175,15 +198,15 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
     }
     __syncthreads();  // every wave is done with the ring: it becomes the reduction buffer
     if (KS > 1) {
-        float* red = (float*)smem;  // [KS-1][CG][NTW][4 mt][4 e][64 lanes]
+        float* red = (float*)smem;  // [KS-1][CG][NTW][MT][4 e][64 lanes]
         if (kh > 0) {
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        red[(((((kh - 1) * CG + cg) * NTW + nt) * 4 + mt) * 4 + e) * 64 + lane] = acc[nt][mt][e];
+                        red[(((((kh - 1) * CG + cg) * NTW + nt) * MT + mt) * 4 + e) * 64 + lane] = acc[nt][mt][e];
         }
         __syncthreads();
         if (kh == 0) {
@@ -192,10 +215,10 @@ __device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ x, const bf1
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
+                    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            acc[nt][mt][e] += red[(((((k2 - 1) * CG + cg) * NTW + nt) * 4 + mt) * 4 + e) * 64 + lane];
+                            acc[nt][mt][e] += red[(((((k2 - 1) * CG + cg) * NTW + nt) * MT + mt) * 4 + e) * 64 + lane];
         }
     }
     if (kh == 0) epi(acc);

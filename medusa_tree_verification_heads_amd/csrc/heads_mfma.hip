@@ -4,8 +4,10 @@
 // logits_k = W2_k (SiLU(W1_k h) + h), the LM head logits_0 = W_lm h), but every weight
 // byte now serves B sequences: a GEMV that keeps up to 8 activation vectors in LDS
 // re-streams the weights once per 8 sequences and spends B multiply-adds per weight
-// element on the vector ALUs, while the 64 x 64 MFMA tile (mfma_tile.h) reads each
-// weight row once for all B rows of h.
+// element on the vector ALUs, while an MFMA tile reads each weight row once for all B
+// rows of h.  Hidden sizes that are a multiple of 128 take the DMA-staged tile
+// (dma_tile.h: 128 weight rows per workgroup, both operands loaded straight into LDS);
+// other multiples of 64 the register-staged 64 x 64 tile (mfma_tile.h).
 //
 // Launch 1 streams the rows of W1_0..W1_{K-1} (stacked, K*d rows) and of W_lm: the W1
 // epilogue forms a = SiLU(u) + h in fp32 and stores it as two bf16 rows, a_hi = bf16(a)
@@ -15,8 +17,8 @@
 // the two halves of each product in its epilogue.
 #include <math.h>
 
+#include "dma_tile.h"
 #include "heads_mfma.h"
-#include "mfma_tile.h"
 
 namespace {
 
@@ -96,6 +98,104 @@ __global__ __launch_bounds__(kThreads) void heads_mfma_w2(HeadsArgs a) {
     }
 }
 
+// The same two launches on the DMA-staged tile (dma_tile.h): kDNB weight rows against the
+// 16 MT x rows per workgroup, both fed by direct global-to-LDS loads through a 4-stage ring
+// (3 stages for 64 x rows) of 128-dim chunks, four waves of kDNB/4 weight rows each,
+// weights streamed non-temporally.  Block b walks the chunks from chunk b on, so that
+// neighbouring workgroups read different parts of their weight rows at any one time.
+// Whole heads calls against the register-staged tiles (both launches, weights from HBM):
+// 397 -> 384 us at B = 4, d = 6656 (2.48 GB, 6.5 TB/s); 258 -> 251 us at B = 16, d = 4096.
+// 64-row tiles (two workgroups per CU) were slower: 326 against 319 us for W2 at 33B.
+#ifndef MDT_HDMA_NB
+#define MDT_HDMA_NB 128
+#endif
+#ifndef MDT_HDMA_S
+#define MDT_HDMA_S 4
+#endif
+constexpr int kDNB = MDT_HDMA_NB;
+// stages: MDT_HDMA_S where the ring fits the LDS, else 3
+template <int MT>
+constexpr int kHS = (kDNB + 16 * MT) * 256 * MDT_HDMA_S <= 160 * 1024 ? MDT_HDMA_S : 3;
+template <int MT>
+using HDma = DmaTile<128, kDNB, 4, 1, kHS<MT>, MT>;
+
+// The result tile of a DMA workgroup, [16 MT][kDNB + 1] fp32 at the start of smem.
+template <int MT>
+__device__ __forceinline__ void store_tile(float* zt, const f32x4 (&acc)[kDNB / 64][MT]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int nt = 0; nt < kDNB / 64; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                zt[(mt * 16 + 4 * g + e) * (kDNB + 1) + wave * (kDNB / 4) + 16 * nt + c16] = acc[nt][mt][e];
+}
+
+// grid (K*d/kDNB + ceil(V/kDNB)): W1 tiles first, then W_lm tiles (d a multiple of kDNB,
+// so that a W1 tile lies in one head).
+template <int MT>
+__global__ __launch_bounds__(256) void heads_dma_w1_lm(HeadsArgs a) {
+    using P = HDma<MT>;
+    constexpr int kLds = P::kRingBytes > 16 * MT * (kDNB + 1) * 4 ? P::kRingBytes : 16 * MT * (kDNB + 1) * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    const bool w1 = (int)blockIdx.x < a.w1_tiles;
+    const int n0 = (w1 ? blockIdx.x : blockIdx.x - a.w1_tiles) * kDNB;
+    float* zt = (float*)smem;
+    dma_tile<128, kDNB, 4, 1, kHS<MT>, 2, MT>(
+        a.h, w1 ? a.W1 : a.Wlm, a.B, a.d, a.d, w1 ? a.K * a.d : a.V, n0, smem,
+        [&](const f32x4 (&acc)[kDNB / 64][MT]) { store_tile<MT>(zt, acc); }, blockIdx.x);
+    __syncthreads();
+    for (int it = threadIdx.x; it < a.B * kDNB; it += 256) {
+        const int b = it / kDNB, c = it % kDNB;
+        const float u = zt[b * (kDNB + 1) + c];
+        if (w1) {
+            const int k = n0 / a.d, j = n0 % a.d + c;
+            const float v = u / (1.f + __expf(-u)) + bf16_to_f32(a.h[(size_t)b * a.d + j]);
+            const bf16_t hi = f32_to_bf16(v);
+            const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+            bf16_t* row = a.ahl + ((size_t)k * 2 * a.B + b) * a.d + j;
+            row[0] = hi;
+            row[(size_t)a.B * a.d] = lo;
+        } else if (n0 + c < a.V) {
+            a.logits[(size_t)b * (a.K + 1) * a.V + n0 + c] = u;
+        }
+    }
+}
+
+// grid (ceil(V/kDNB), K).
+template <int MT>
+__global__ __launch_bounds__(256) void heads_dma_w2(HeadsArgs a) {
+    using P = HDma<MT>;
+    constexpr int kLds = P::kRingBytes > 16 * MT * (kDNB + 1) * 4 ? P::kRingBytes : 16 * MT * (kDNB + 1) * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    const int n0 = blockIdx.x * kDNB, k = blockIdx.y;
+    float* zt = (float*)smem;
+    dma_tile<128, kDNB, 4, 1, kHS<MT>, 2, MT>(
+        a.ahl + (size_t)k * 2 * a.B * a.d, a.W2 + (size_t)k * a.V * a.d, 2 * a.B, a.d, a.d, a.V, n0, smem,
+        [&](const f32x4 (&acc)[kDNB / 64][MT]) { store_tile<MT>(zt, acc); }, blockIdx.x + 5 * blockIdx.y);
+    __syncthreads();
+    for (int it = threadIdx.x; it < a.B * kDNB; it += 256) {
+        const int b = it / kDNB, c = it % kDNB;
+        if (n0 + c < a.V)
+            a.logits[((size_t)b * (a.K + 1) + k + 1) * a.V + n0 + c] =
+                zt[b * (kDNB + 1) + c] + zt[(a.B + b) * (kDNB + 1) + c];
+    }
+}
+
+template <int MT1, int MT2>
+mdt_status launch_dma(HeadsArgs a, hipStream_t s) {
+    const int lm_tiles = (a.V + kDNB - 1) / kDNB;
+    a.w1_tiles = a.K * a.d / kDNB;
+    MDT_LAUNCH("heads_mfma_w1_lm", heads_dma_w1_lm<MT1>, dim3(a.w1_tiles + (a.Wlm ? lm_tiles : 0)), dim3(256), 0,
+               s, a);
+    mdt_status st = mdt_launched("heads_mfma_w1_lm");
+    if (st != MDT_OK) return st;
+    MDT_LAUNCH("heads_mfma_w2", heads_dma_w2<MT2>, dim3(lm_tiles, a.K), dim3(256), 0, s, a);
+    return mdt_launched("heads_mfma_w2");
+}
+
 template <int MT1, int MT2>
 mdt_status launch_pair(const HeadsArgs& a, hipStream_t s) {
     const int lm_tiles = (a.V + kNB - 1) / kNB;
@@ -116,6 +216,11 @@ mdt_status mdt_heads_mfma(hipStream_t s, int B, int d, int V, int K, const void*
                           const void* Wlm, float* logits, void* ws) {
     HeadsArgs a{(const bf16_t*)h, (const bf16_t*)W1, (const bf16_t*)W2, (const bf16_t*)Wlm, logits, (bf16_t*)ws,
                 B, d, V, K, K * d / kNB};
+    if (d % kDNB == 0) {
+        if (B <= 8) return launch_dma<1, 1>(a, s);
+        if (B <= 16) return launch_dma<1, 2>(a, s);
+        return launch_dma<2, 4>(a, s);
+    }
     // 16-row m-tiles: B rows of h in launch 1, 2B rows of [a_hi; a_lo] in launch 2
     if (B <= 8) return launch_pair<1, 1>(a, s);
     if (B <= 16) return launch_pair<1, 2>(a, s);

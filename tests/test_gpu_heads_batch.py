@@ -20,19 +20,21 @@ from workloads.configs import PARITY_CASES, scaled
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B", [3, 4, 7, 12, 17, 32])
-def test_heads_batch_matches_oracle(B):
+@pytest.mark.parametrize("B,d", [(3, 512), (4, 512), (7, 512), (12, 512), (17, 512), (32, 512), (5, 576),
+                                 (20, 576)])
+def test_heads_batch_matches_oracle(B, d):
+    """d = 512: the DMA-staged tiles (d a multiple of 128); d = 576: the register-staged ones."""
     import medusa_tree_verification_heads_amd as mdt
     from medusa_tree_verification_heads_amd.step import to_device
-    w = scaled(PARITY_CASES["7b-mini"], name=f"7b-mini-B{B}", B=B)
-    inp = make_inputs(w, 4242 + B, parts=("h", "W1", "W2", "Wlm"))
+    w = scaled(PARITY_CASES["7b-mini"], name=f"7b-mini-B{B}-d{d}", B=B, d=d)
+    inp = make_inputs(w, 4242 + B + d, parts=("h", "W1", "W2", "Wlm"))
     t = {k: to_device(inp[k], "cuda") for k in ("h", "W1", "W2", "Wlm")}
     logits = mdt.medusa_heads(t["h"], t["W1"], t["W2"], t["Wlm"])
     torch.cuda.synchronize()
     g = logits.cpu().numpy().astype(np.float64)
     ref, _ = ostep.medusa_heads(inp["h"], inp["W1"], inp["W2"], inp["Wlm"])
     err = np.abs(g - ref).max(axis=2) / np.abs(ref).max(axis=2)
-    note(f"heads B={B}: max rel err {err.max():.2e}")
+    note(f"heads B={B} d={d}: max rel err {err.max():.2e}")
     assert err.max() <= 1e-4
 
 
