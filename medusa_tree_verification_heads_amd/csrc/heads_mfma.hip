@@ -98,101 +98,111 @@ __global__ __launch_bounds__(kThreads) void heads_mfma_w2(HeadsArgs a) {
     }
 }
 
-// The same two launches on the DMA-staged tile (dma_tile.h): kDNB weight rows against the
+// The same two launches on the DMA-staged tile (dma_tile.h): NB weight rows against the
 // 16 MT x rows per workgroup, both fed by direct global-to-LDS loads through a 4-stage ring
-// (3 stages for 64 x rows) of 128-dim chunks, four waves of kDNB/4 weight rows each,
-// weights streamed non-temporally.  Block b walks the chunks from chunk b on, so that
-// neighbouring workgroups read different parts of their weight rows at any one time.
+// (3 stages where 4 do not fit the LDS) of 128-dim chunks on four waves, weights streamed
+// non-temporally.  Block b walks the chunks from chunk b on, so that neighbouring
+// workgroups read different parts of their weight rows at any one time.  Launch 2 (W2) uses
+// 128-row tiles; launch 1 (W1 + W_lm) 96- or 128-row tiles, whichever grid fills the last
+// round of workgroups (one per CU) better, since the CUs left idle in a short last round
+// stream nothing (a W1 tile may then span two heads; the epilogue places each column).
 // Whole heads calls against the register-staged tiles (both launches, weights from HBM):
 // 397 -> 384 us at B = 4, d = 6656 (2.48 GB, 6.5 TB/s); 258 -> 251 us at B = 16, d = 4096.
 // 64-row tiles (two workgroups per CU) were slower: 326 against 319 us for W2 at 33B.
-#ifndef MDT_HDMA_NB
-#define MDT_HDMA_NB 128
-#endif
-#ifndef MDT_HDMA_S
-#define MDT_HDMA_S 4
-#endif
-constexpr int kDNB = MDT_HDMA_NB;
-// stages: MDT_HDMA_S where the ring fits the LDS, else 3
-template <int MT>
-constexpr int kHS = (kDNB + 16 * MT) * 256 * MDT_HDMA_S <= 160 * 1024 ? MDT_HDMA_S : 3;
-template <int MT>
-using HDma = DmaTile<128, kDNB, 4, 1, kHS<MT>, MT>;
+template <int NB, int MT, int CG, int KS>
+constexpr int kHS = (NB + 16 * MT) * 256 * 4 + (KS - 1) * NB * MT * 64 <= 160 * 1024 ? 4 : 3;
+template <int NB, int MT, int CG, int KS>
+using HDma = DmaTile<128, NB, CG, KS, kHS<NB, MT, CG, KS>, MT>;
+template <int NB, int MT, int CG, int KS>
+constexpr int kHLds = HDma<NB, MT, CG, KS>::kRingBytes > 16 * MT * (NB + 1) * 4 + HDma<NB, MT, CG, KS>::kRedBytes
+                          ? HDma<NB, MT, CG, KS>::kRingBytes
+                          : 16 * MT * (NB + 1) * 4 + HDma<NB, MT, CG, KS>::kRedBytes;
 
-// The result tile of a DMA workgroup, [16 MT][kDNB + 1] fp32 at the start of smem.
-template <int MT>
-__device__ __forceinline__ void store_tile(float* zt, const f32x4 (&acc)[kDNB / 64][MT]) {
+// The product tile of x (at most 16 MT valid rows: M) against weight rows n0.. of W (V rows),
+// left as [16 MT][NB + 1] fp32 at the returned address in smem.
+template <int NB, int MT, int CG, int KS>
+__device__ __forceinline__ const float* head_tile(const bf16_t* x, int M, const bf16_t* W, int V, int d, int n0,
+                                                  int rot, char* smem) {
+    using P = HDma<NB, MT, CG, KS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
+    const int g = lane >> 4, c16 = lane & 15, cg = wave % CG;
+    float* zt = (float*)(smem + P::kRedBytes);  // after the k-groups' partials
+    dma_tile<128, NB, CG, KS, kHS<NB, MT, CG, KS>, 2, MT>(
+        x, W, M, d, d, V, n0, smem,
+        [&](const f32x4 (&acc)[NB / CG / 16][MT]) {
 #pragma unroll
-    for (int nt = 0; nt < kDNB / 64; ++nt)
+            for (int nt = 0; nt < NB / CG / 16; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                zt[(mt * 16 + 4 * g + e) * (kDNB + 1) + wave * (kDNB / 4) + 16 * nt + c16] = acc[nt][mt][e];
+                    for (int e = 0; e < 4; ++e)
+                        zt[(mt * 16 + 4 * g + e) * (NB + 1) + cg * (NB / CG) + 16 * nt + c16] = acc[nt][mt][e];
+        },
+        rot);
+    __syncthreads();
+    return zt;
 }
 
-// grid (K*d/kDNB + ceil(V/kDNB)): W1 tiles first, then W_lm tiles (d a multiple of kDNB,
-// so that a W1 tile lies in one head).
-template <int MT>
+// grid (ceil(K*d/NB) + ceil(V/NB)): W1 tiles first, then W_lm tiles.
+template <int NB, int MT, int CG, int KS>
 __global__ __launch_bounds__(256) void heads_dma_w1_lm(HeadsArgs a) {
-    using P = HDma<MT>;
-    constexpr int kLds = P::kRingBytes > 16 * MT * (kDNB + 1) * 4 ? P::kRingBytes : 16 * MT * (kDNB + 1) * 4;
-    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kHLds<NB, MT, CG, KS>];
     const bool w1 = (int)blockIdx.x < a.w1_tiles;
-    const int n0 = (w1 ? blockIdx.x : blockIdx.x - a.w1_tiles) * kDNB;
-    float* zt = (float*)smem;
-    dma_tile<128, kDNB, 4, 1, kHS<MT>, 2, MT>(
-        a.h, w1 ? a.W1 : a.Wlm, a.B, a.d, a.d, w1 ? a.K * a.d : a.V, n0, smem,
-        [&](const f32x4 (&acc)[kDNB / 64][MT]) { store_tile<MT>(zt, acc); }, blockIdx.x);
-    __syncthreads();
-    for (int it = threadIdx.x; it < a.B * kDNB; it += 256) {
-        const int b = it / kDNB, c = it % kDNB;
-        const float u = zt[b * (kDNB + 1) + c];
+    const int n0 = (w1 ? blockIdx.x : blockIdx.x - a.w1_tiles) * NB;
+    const int nrows = w1 ? a.K * a.d : a.V;
+    const float* zt = head_tile<NB, MT, CG, KS>(a.h, a.B, w1 ? a.W1 : a.Wlm, nrows, a.d, n0, blockIdx.x, smem);
+    for (int it = threadIdx.x; it < a.B * NB; it += 256) {
+        const int b = it / NB, c = it % NB, n = n0 + c;
+        if (n >= nrows) continue;
+        const float u = zt[b * (NB + 1) + c];
         if (w1) {
-            const int k = n0 / a.d, j = n0 % a.d + c;
+            const int k = n / a.d, j = n - k * a.d;
             const float v = u / (1.f + __expf(-u)) + bf16_to_f32(a.h[(size_t)b * a.d + j]);
             const bf16_t hi = f32_to_bf16(v);
             const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
             bf16_t* row = a.ahl + ((size_t)k * 2 * a.B + b) * a.d + j;
             row[0] = hi;
             row[(size_t)a.B * a.d] = lo;
-        } else if (n0 + c < a.V) {
-            a.logits[(size_t)b * (a.K + 1) * a.V + n0 + c] = u;
+        } else {
+            a.logits[(size_t)b * (a.K + 1) * a.V + n] = u;
         }
     }
 }
 
-// grid (ceil(V/kDNB), K).
+// grid (ceil(V/128), K).
 template <int MT>
 __global__ __launch_bounds__(256) void heads_dma_w2(HeadsArgs a) {
-    using P = HDma<MT>;
-    constexpr int kLds = P::kRingBytes > 16 * MT * (kDNB + 1) * 4 ? P::kRingBytes : 16 * MT * (kDNB + 1) * 4;
-    __shared__ __attribute__((aligned(1024))) char smem[kLds];
-    const int n0 = blockIdx.x * kDNB, k = blockIdx.y;
-    float* zt = (float*)smem;
-    dma_tile<128, kDNB, 4, 1, kHS<MT>, 2, MT>(
-        a.ahl + (size_t)k * 2 * a.B * a.d, a.W2 + (size_t)k * a.V * a.d, 2 * a.B, a.d, a.d, a.V, n0, smem,
-        [&](const f32x4 (&acc)[kDNB / 64][MT]) { store_tile<MT>(zt, acc); }, blockIdx.x + 5 * blockIdx.y);
-    __syncthreads();
-    for (int it = threadIdx.x; it < a.B * kDNB; it += 256) {
-        const int b = it / kDNB, c = it % kDNB;
+    __shared__ __attribute__((aligned(1024))) char smem[kHLds<128, MT, 4, 1>];
+    const int n0 = blockIdx.x * 128, k = blockIdx.y;
+    const float* zt = head_tile<128, MT, 4, 1>(a.ahl + (size_t)k * 2 * a.B * a.d, 2 * a.B,
+                                               a.W2 + (size_t)k * a.V * a.d, a.V, a.d, n0,
+                                               blockIdx.x + 5 * blockIdx.y, smem);
+    for (int it = threadIdx.x; it < a.B * 128; it += 256) {
+        const int b = it / 128, c = it % 128;
         if (n0 + c < a.V)
-            a.logits[((size_t)b * (a.K + 1) + k + 1) * a.V + n0 + c] =
-                zt[b * (kDNB + 1) + c] + zt[(a.B + b) * (kDNB + 1) + c];
+            a.logits[((size_t)b * (a.K + 1) + k + 1) * a.V + n0 + c] = zt[b * 129 + c] + zt[(a.B + b) * 129 + c];
     }
 }
 
+// Fraction of the CUs busy over the rounds of `tiles` workgroups, one per CU.
+double round_fill(long tiles, long cus) { return (double)tiles / (double)(((tiles + cus - 1) / cus) * cus); }
+
 template <int MT1, int MT2>
 mdt_status launch_dma(HeadsArgs a, hipStream_t s) {
-    const int lm_tiles = (a.V + kDNB - 1) / kDNB;
-    a.w1_tiles = a.K * a.d / kDNB;
-    MDT_LAUNCH("heads_mfma_w1_lm", heads_dma_w1_lm<MT1>, dim3(a.w1_tiles + (a.Wlm ? lm_tiles : 0)), dim3(256), 0,
-               s, a);
-    mdt_status st = mdt_launched("heads_mfma_w1_lm");
+    const long cus = mdt_num_cus();
+    auto tiles = [&](int nb) { return (a.K * a.d + nb - 1) / nb + (a.Wlm ? (a.V + nb - 1) / nb : 0); };
+    auto go1 = [&](auto kern, int nb) {
+        a.w1_tiles = (a.K * a.d + nb - 1) / nb;
+        MDT_LAUNCH("heads_mfma_w1_lm", kern, dim3(tiles(nb)), dim3(256), 0, s, a);
+        return mdt_launched("heads_mfma_w1_lm");
+    };
+    // 128-row tiles unless 96-row ones fill the last round clearly better (7B, K = 4: 505
+    // workgroups against 378 on 256 CUs)
+    const mdt_status st = round_fill(tiles(128), cus) >= round_fill(tiles(96), cus) - 0.02
+                              ? go1(heads_dma_w1_lm<128, MT1, 4, 1>, 128)
+                              : go1(heads_dma_w1_lm<96, MT1, 2, 2>, 96);
     if (st != MDT_OK) return st;
-    MDT_LAUNCH("heads_mfma_w2", heads_dma_w2<MT2>, dim3(lm_tiles, a.K), dim3(256), 0, s, a);
+    MDT_LAUNCH("heads_mfma_w2", heads_dma_w2<MT2>, dim3((a.V + 127) / 128, a.K), dim3(256), 0, s, a);
     return mdt_launched("heads_mfma_w2");
 }
 
@@ -216,7 +226,7 @@ mdt_status mdt_heads_mfma(hipStream_t s, int B, int d, int V, int K, const void*
                           const void* Wlm, float* logits, void* ws) {
     HeadsArgs a{(const bf16_t*)h, (const bf16_t*)W1, (const bf16_t*)W2, (const bf16_t*)Wlm, logits, (bf16_t*)ws,
                 B, d, V, K, K * d / kNB};
-    if (d % kDNB == 0) {
+    if (d % 128 == 0) {
         if (B <= 8) return launch_dma<1, 1>(a, s);
         if (B <= 16) return launch_dma<1, 2>(a, s);
         return launch_dma<2, 4>(a, s);
