@@ -6,8 +6,8 @@
 // re-streams the weights once per 8 sequences and spends B multiply-adds per weight
 // element on the vector ALUs, while an MFMA tile reads each weight row once for all B
 // rows of h.  Hidden sizes that are a multiple of 128 take the DMA-staged tile
-// (dma_tile.h: 128 weight rows per workgroup, both operands loaded straight into LDS);
-// other multiples of 64 the register-staged 64 x 64 tile (mfma_tile.h).
+// (dma_tile.h: 96 or 128 weight rows per workgroup, both operands loaded straight into
+// LDS); other multiples of 64 the register-staged 64 x 64 tile (mfma_tile.h).
 //
 // Launch 1 streams the rows of W1_0..W1_{K-1} (stacked, K*d rows) and of W_lm: the W1
 // epilogue forms a = SiLU(u) + h in fp32 and stores it as two bf16 rows, a_hi = bf16(a)
