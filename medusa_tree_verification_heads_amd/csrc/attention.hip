@@ -309,7 +309,9 @@ __device__ __forceinline__ void lds_wait16(u32x2 (&v)[8][2]) {
 
 // Per-wave query state: in tile t the lane holds query qi(t) = 16 (QT wave + t) + lane % 16,
 // dims 32 s + 8 g .. +8 of the rotated query (s = 0, 1: x_m; s = 2, 3: x_{m+64}), its
-// running (m, l) (replicated over g) and O^T accumulators (lane: dims 16 db + 4 g + e).
+// running maximum m (replicated over g), the running sum l of the weights of the keys this
+// lane holds (the query's sum is that of its four lanes l, l ^ 16, l ^ 32, l ^ 48, formed
+// once when the state is written) and O^T accumulators (lane: dims 16 db + 4 g + e).
 template <int QT>
 struct QueryState {
     u32x4 bq[QT][4];
@@ -375,7 +377,8 @@ __device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, cons
         if (qi < A.Tpad) {
             const long base = slot * A.Tpad + qi;
             bf16_t* po = A.part_o + base * kDh;
-            const float inv_l = st.l_run[t] > 0.f ? 1.f / st.l_run[t] : 0.f;
+            const float l = xor_sum_16_32(st.l_run[t]);
+            const float inv_l = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 u32x2 w;
@@ -385,7 +388,7 @@ __device__ __forceinline__ void write_partial(const AttnArgs& A, long slot, cons
             }
             if (g == 0) {
                 A.part_ml[base * 2 + 0] = st.m_run[t];
-                A.part_ml[base * 2 + 1] = st.l_run[t];
+                A.part_ml[base * 2 + 1] = l;
             }
         }
     }
@@ -472,7 +475,7 @@ __device__ __forceinline__ void softmax_tile(QkAcc<QT>& sa, int nvalid, bool mas
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float corr = __builtin_amdgcn_exp2f(st.m_run[t] - m_ref);
         const float delta = m_ref - m_base;
-        float tsum = 0.f;
+        float ts[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sums, not one serial chain
         if (__all(delta == 0.f)) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -480,7 +483,7 @@ __device__ __forceinline__ void softmax_tile(QkAcc<QT>& sa, int nvalid, bool mas
                 for (int e = 0; e < 4; ++e) {
                     const float p = __builtin_amdgcn_exp2f(sacc[t][kb][e]);
                     sacc[t][kb][e] = p;
-                    tsum += p;
+                    ts[e] += p;
                 }
         } else {
 #pragma unroll
@@ -489,10 +492,11 @@ __device__ __forceinline__ void softmax_tile(QkAcc<QT>& sa, int nvalid, bool mas
                 for (int e = 0; e < 4; ++e) {
                     const float p = __builtin_amdgcn_exp2f(sacc[t][kb][e] - delta);
                     sacc[t][kb][e] = p;
-                    tsum += p;
+                    ts[e] += p;
                 }
         }
-        st.l_run[t] = st.l_run[t] * corr + xor_sum_16_32(tsum);
+        // this lane's keys only: the four lanes of a query share m and so the rescaling
+        st.l_run[t] = st.l_run[t] * corr + ((ts[0] + ts[1]) + (ts[2] + ts[3]));
         st.m_run[t] = m_new;
         if (__any(corr != 1.f))
 #pragma unroll
