@@ -164,3 +164,85 @@ def test_attention_key_ranges(name):
     eo, ek = rel_err_rows(go, ro), rel_err_rows(gk, rk)
     note(f"  o rel err {eo:.2e}, k_rot rel err {ek:.2e}")
     assert eo <= REL_TOL and ek <= REL_TOL
+
+
+# Per 64-key tile of the prefix: the key's value c in the slowest rotary pair's first
+# dimension (rotated by at most ~0.13 rad at these positions), against a query component of
+# +30 there, puts the tile's scores near -30 c / sqrt(Dh): rising tiles move a row's maximum
+# up by ~9.5 (log2 units) three times, "jump" by ~420 at once after the first tile,
+# "falling" never.
+LARGE_SCHEDULES = {
+    "rising": [7.5, 7.5, 7.5, 5.0, 5.0, 5.0, 2.5, 2.5, 2.5, 0.0, 0.0, 0.0],
+    "falling": [0.0, 0.0, 0.0, 2.5, 2.5, 2.5, 5.0, 5.0, 5.0, 7.5, 7.5, 7.5],
+    "jump": [110.0] + [0.0] * 11,
+}
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("schedule", list(LARGE_SCHEDULES))
+def test_attention_moving_maximum(schedule, dtype, paged):
+    """Online softmax while a row's largest score moves between key tiles by far more than
+    the tile-local range: the running reference and every accumulator are rescaled (by
+    factors down to 2^-420 in "jump"), or later tiles carry weights that vanish.  The keys
+    that hold the weight score near zero, so bf16 operands keep their usual accuracy (a
+    score's bf16 error grows with its size, about |s| 2^-9, which only the keys of
+    negligible weight reach here).  Summary page, "Tree Attention" step 3: still the softmax
+    over the allowed keys, which the float64 oracle computes."""
+    import medusa_tree_verification_heads_amd as mdt
+    bf16 = dtype == "bf16"
+    H, Dh = (2, 128) if bf16 else (2, 32)
+    cs = np.array(LARGE_SCHEDULES[schedule], dtype=np.float32)
+    ot = otree.cartesian_tree((3, 2))
+    T = ot.T
+    L = np.array([700, 333], dtype=np.int32)
+    B = len(L)
+    note(f"attention moving maximum {schedule} {dtype} paged={paged} T={T} prefixes={L.tolist()}")
+    rng = np.random.default_rng(43 + 2 * bf16 + paged + 7 * list(LARGE_SCHEDULES).index(schedule))
+    m = Dh // 2 - 1   # the slowest rotary pair is (m, m + Dh/2)
+
+    def cast(x):
+        return f32_to_bf16_bits(x) if bf16 else x
+
+    qf = rng.standard_normal((B, T, H, Dh)).astype(np.float32)
+    qf[..., m], qf[..., m + Dh // 2] = 30.0, 0.0
+    q = cast(qf)
+    k, v = (_draw(rng, (B, T, H, Dh), 0.5, bf16) for _ in range(2))
+    page = 16
+
+    def cache_keys(shape, slot_pos):
+        x = rng.standard_normal(shape).astype(np.float32) * 0.5
+        x[..., m] = -cs[np.minimum(slot_pos // 64, len(cs) - 1)][..., None]
+        x[..., m + Dh // 2] = 0.0
+        return cast(x)
+
+    if paged:
+        npg = [-(-int(L[b]) // page) for b in range(B)]
+        pool = sum(npg) + 2
+        perm = rng.permutation(pool)
+        pt = np.full((B, max(npg)), -1, dtype=np.int32)
+        pos = np.zeros((pool, page), dtype=np.int64)   # sequence position of each pool row
+        o = 0
+        for b in range(B):
+            pt[b, :npg[b]] = perm[o:o + npg[b]]
+            for j in range(npg[b]):
+                pos[perm[o + j]] = j * page + np.arange(page)
+            o += npg[b]
+        Kc = cache_keys((pool, page, H, Dh), pos)
+        Vc = _draw(rng, (pool, page, H, Dh), 1.0, bf16)
+    else:
+        pt = None
+        cap = int(L.max()) + 3
+        Kc = cache_keys((B, cap, H, Dh), np.broadcast_to(np.arange(cap), (B, cap)))
+        Vc = _draw(rng, (B, cap, H, Dh), 1.0, bf16)
+    tree = mdt.Tree.cartesian((3, 2))
+    cache = mdt.KVCache(_dev(Kc), _dev(Vc), None if pt is None else torch.from_numpy(pt).cuda(), page)
+    out, k_rot = mdt.tree_attention(_dev(q), _dev(k), _dev(v), cache, torch.from_numpy(L).cuda(),
+                                    tree.to_device("cuda"))
+    torch.cuda.synchronize()
+    ro, rk = ostep.tree_attention(q, k, v, Kc, Vc, L, ot, 10000.0, bf16_store=bf16, page_table=pt, page_size=page)
+    go = ostep.to_f64(_host(out))
+    assert np.all(np.isfinite(go))
+    eo, ek = rel_err_rows(go, ro), rel_err_rows(ostep.to_f64(_host(k_rot)), rk)
+    note(f"  o rel err {eo:.2e}, k_rot rel err {ek:.2e}")
+    assert eo <= REL_TOL and ek <= REL_TOL
